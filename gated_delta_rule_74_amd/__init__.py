@@ -1,0 +1,222 @@
+"""Python binding of libkda.so, the MI355X (gfx950) KDA layer forward.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/kda.h``.  PyTorch supplies
+device memory and the current stream.  There is no fallback of any kind: if
+the library has not been built, importing this package raises.
+
+Functions mirror the C entry points by name:
+  kda_prefill, kda_prefill_chunk_prep, kda_prefill_state_pass,
+  kda_decode_step, kda_conv_prologue, kda_prefill_workspace_size,
+  kda_status_string, kda_abi_version
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with "
+        "`python -m gated_delta_rule_74_amd.build` (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+KDA_OK, KDA_EINVAL, KDA_EUNSUPPORTED, KDA_EHIP = 0, 1, 2, 3
+KDA_F32, KDA_BF16 = 0, 1
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+
+class KdaConvDesc(ctypes.Structure):
+    _fields_ = [("xq", _vp), ("xk", _vp), ("xv", _vp), ("wq", _vp),
+                ("wk", _vp), ("wv", _vp), ("width", _i), ("l2norm_qk", _i),
+                ("eps", _f)]
+
+
+def _sig(name, res, args):
+    fn = getattr(_lib, name)
+    fn.restype = res
+    fn.argtypes = args
+    return fn
+
+
+_abi_version = _sig("kda_abi_version", _i, [])
+_status_string = _sig("kda_status_string", ctypes.c_char_p, [_i])
+_ws_size = _sig("kda_prefill_workspace_size", _sz, [_i] * 6 + [_i])
+_prefill = _sig("kda_prefill", _i,
+                [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp] + [_i] * 6 +
+                [_f, ctypes.POINTER(KdaConvDesc), _vp, _sz, _vp])
+_prep = _sig("kda_prefill_chunk_prep", _i,
+             [_vp, _vp, _vp, _i, _vp, _vp, _i] + [_i] * 6 +
+             [_f, ctypes.POINTER(KdaConvDesc), _vp, _sz, _vp])
+_state = _sig("kda_prefill_state_pass", _i,
+              [_i, _vp, _vp, _vp] + [_i] * 6 + [_vp, _sz, _vp])
+_decode = _sig("kda_decode_step", _i,
+               [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp] + [_i] * 4 +
+               [_f, _vp])
+_conv = _sig("kda_conv_prologue", _i,
+             [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp] +
+             [_i] * 5 + [_i, _f, _vp])
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {kda_status_string(status)}")
+
+
+def kda_abi_version() -> int:
+    return _abi_version()
+
+
+def kda_status_string(status: int) -> str:
+    return _status_string(status).decode()
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return KDA_F32
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(st: int, where: str):
+    if st != KDA_OK:
+        raise KdaError(st, where)
+
+
+def kda_prefill_workspace_size(B, T, H, Dk, Dv, chunk, qkv_dtype) -> int:
+    dt = qkv_dtype if isinstance(qkv_dtype, int) else (
+        KDA_BF16 if qkv_dtype == torch.bfloat16 else KDA_F32)
+    return int(_ws_size(B, T, H, Dk, Dv, chunk, dt))
+
+
+def _conv_desc(conv):
+    if conv is None:
+        return None, None
+    keep = [conv[n] for n in ("xq", "xk", "xv", "wq", "wk", "wv")]
+    d = KdaConvDesc(*[_ptr(x) for x in keep],
+                    int(conv.get("width", conv["wq"].shape[-1])),
+                    int(bool(conv.get("l2norm_qk", True))),
+                    float(conv.get("eps", 1e-6)))
+    return ctypes.byref(d), (d, keep)
+
+
+def _prefill_shapes(q, v, g, conv):
+    B, T, H, Dk = g.shape
+    if conv is not None:
+        Dv = conv["xv"].shape[-1] // H
+        io = conv["xq"]
+    else:
+        Dv = v.shape[-1]
+        io = q
+    return B, T, H, Dk, Dv, io
+
+
+def alloc_workspace(B, T, H, Dk, Dv, chunk, dtype, device="cuda"):
+    n = kda_prefill_workspace_size(B, T, H, Dk, Dv, chunk, dtype)
+    if n == 0:
+        raise KdaError(KDA_EUNSUPPORTED, "kda_prefill_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def kda_prefill(q, k, v, g, beta, *, s0=None, chunk=64, scale=1.0,
+                conv=None, o=None, s_out=None, want_state=True,
+                workspace=None, stream=None):
+    """Chunked prefill.  q,k,g [B,T,H,Dk], v [B,T,H,Dv], beta [B,T,H]
+    (q,k,v may be None when `conv` gives raw projections and taps).
+    Returns (o [B,T,H,Dv], final state [B,H,Dk,Dv] fp32 or None)."""
+    B, T, H, Dk, Dv, io = _prefill_shapes(q, v, g, conv)
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=io.dtype, device=g.device)
+    if s_out is None and want_state:
+        s_out = torch.empty((B, H, Dk, Dv), dtype=torch.float32,
+                            device=g.device)
+    if workspace is None:
+        workspace = alloc_workspace(B, T, H, Dk, Dv, chunk, io.dtype,
+                                    g.device)
+    cd, _keep = _conv_desc(conv)
+    st = _prefill(_ptr(q), _ptr(k), _ptr(v), _dt(io), _ptr(g), _ptr(beta),
+                  _dt(g), _ptr(s0), _ptr(s_out), _ptr(o), B, T, H, Dk, Dv,
+                  chunk, scale, cd, _ptr(workspace), workspace.numel(),
+                  _stream(stream))
+    _check(st, "kda_prefill")
+    return o, s_out
+
+
+def kda_prefill_chunk_prep(q, k, v, g, beta, workspace, *, chunk=64,
+                           scale=1.0, conv=None, Dv=None, stream=None):
+    """First prefill phase alone (chunk-local factors -> workspace)."""
+    B, T, H, Dk, Dv_, io = _prefill_shapes(q, v, g, conv)
+    cd, _keep = _conv_desc(conv)
+    st = _prep(_ptr(q), _ptr(k), _ptr(v), _dt(io), _ptr(g), _ptr(beta),
+               _dt(g), B, T, H, Dk, Dv_ if Dv is None else Dv, chunk, scale,
+               cd, _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "kda_prefill_chunk_prep")
+
+
+def kda_prefill_state_pass(workspace, o, *, s0=None, s_out=None, B, T, H,
+                           Dk, Dv, chunk=64, stream=None):
+    """Second prefill phase alone (sequential state pass -> o, s_out)."""
+    st = _state(_dt(o), _ptr(s0), _ptr(s_out), _ptr(o), B, T, H, Dk, Dv,
+                chunk, _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "kda_prefill_state_pass")
+
+
+def kda_decode_step(q, k, v, g, beta, state, *, scale=1.0, o=None,
+                    stream=None):
+    """One decode step; `state` [N,H,Dk,Dv] fp32 is updated in place.
+    Returns o [N,H,Dv]."""
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((N, H, Dv), dtype=q.dtype, device=q.device)
+    st = _decode(_ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(g), _ptr(beta),
+                 _dt(g), _ptr(state), _ptr(o), N, H, Dk, Dv, scale,
+                 _stream(stream))
+    _check(st, "kda_decode_step")
+    return o
+
+
+def kda_conv_prologue(xq, xk, xv, wq, wk, wv, *, H, Dk, Dv, conv_state=None,
+                      l2norm_qk=True, eps=1e-6, q=None, k=None, v=None,
+                      stream=None):
+    """Standalone conv (+ L2 on q, k) prologue.  x* [B,T,H*D] -> q,k
+    [B,T,H,Dk], v [B,T,H,Dv] (the raw inputs' dtype).  conv_state, if given,
+    is fp32 [B,3,H*max(Dk,Dv),W-1], read then updated in place."""
+    B, T, _ = xq.shape
+    W = wq.shape[-1]
+    if q is None:
+        q = torch.empty((B, T, H, Dk), dtype=xq.dtype, device=xq.device)
+    if k is None:
+        k = torch.empty((B, T, H, Dk), dtype=xq.dtype, device=xq.device)
+    if v is None:
+        v = torch.empty((B, T, H, Dv), dtype=xq.dtype, device=xq.device)
+    st = _conv(_ptr(xq), _ptr(xk), _ptr(xv), _dt(xq), _ptr(wq), _ptr(wk),
+               _ptr(wv), W, _ptr(conv_state), _ptr(q), _ptr(k), _ptr(v), B, T,
+               H, Dk, Dv, int(bool(l2norm_qk)), eps, _stream(stream))
+    _check(st, "kda_conv_prologue")
+    return q, k, v

@@ -1,0 +1,238 @@
+// kda_api.hip -- the extern "C" boundary of libkda.so: argument validation
+// and dispatch to the launchers.  Every check happens before any launch, so
+// an error return leaves every output untouched.  See include/kda.h.
+#include "../../include/kda.h"
+
+#include <math.h>
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
+bool dtype_valid(kda_dtype d) { return d == KDA_F32 || d == KDA_BF16; }
+bool pair_ok(kda_dtype io, kda_dtype gt) {
+  return (io == KDA_F32 && gt == KDA_F32) ||
+         (io == KDA_BF16 && (gt == KDA_F32 || gt == KDA_BF16));
+}
+kda_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return KDA_OK;
+  (void)hipGetLastError();
+  return KDA_EHIP;
+}
+
+// shared validation of the prefill family; fills p (without workspace)
+kda_status prefill_check(const void *q, const void *k, const void *v,
+                         kda_dtype io, const void *g, const void *beta,
+                         kda_dtype gt, int B, int T, int H, int Dk, int Dv,
+                         int chunk, float scale, const kda_conv_desc *conv,
+                         bool need_inputs, kda::PrefillParams &p) {
+  if (B <= 0 || T <= 0 || H <= 0 || Dk <= 0 || Dv <= 0 || chunk <= 0)
+    return KDA_EINVAL;
+  if (!dtype_valid(io) || !dtype_valid(gt)) return KDA_EINVAL;
+  if (!isfinite(scale)) return KDA_EINVAL;
+  if (need_inputs) {
+    if (!g || !beta) return KDA_EINVAL;
+    if (!aligned16(g) || !aligned16(beta)) return KDA_EINVAL;
+    if (conv) {
+      if (!conv->xq || !conv->xk || !conv->xv || !conv->wq || !conv->wk ||
+          !conv->wv)
+        return KDA_EINVAL;
+      if (!aligned16(conv->xq) || !aligned16(conv->xk) ||
+          !aligned16(conv->xv) || !aligned16(conv->wq) ||
+          !aligned16(conv->wk) || !aligned16(conv->wv))
+        return KDA_EINVAL;
+      if (conv->width < 2) return KDA_EINVAL;
+      if (conv->l2norm_qk != 0 && conv->l2norm_qk != 1) return KDA_EINVAL;
+      if (!(conv->eps >= 0.f) || !isfinite(conv->eps)) return KDA_EINVAL;
+    } else {
+      if (!q || !k || !v) return KDA_EINVAL;
+      if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return KDA_EINVAL;
+    }
+  }
+  if (!dim_ok(Dk) || !dim_ok(Dv) || !chunk_ok(chunk)) return KDA_EUNSUPPORTED;
+  if (!pair_ok(io, gt)) return KDA_EUNSUPPORTED;
+  if (io == KDA_F32 && Dk == 128 && chunk == 64) return KDA_EUNSUPPORTED;
+  if (need_inputs && conv && conv->width > 4) return KDA_EUNSUPPORTED;
+  const long long nc = ((long long)T + chunk - 1) / chunk;
+  if ((long long)B * H * nc > 0x7fffffffLL) return KDA_EUNSUPPORTED;
+  if ((long long)B * H * (Dv / 16) > 0x7fffffffLL) return KDA_EUNSUPPORTED;
+  p = kda::PrefillParams{};
+  p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+  p.gate_bf16 = (gt == KDA_BF16);
+  p.B = B; p.T = T; p.H = H; p.Dk = Dk; p.Dv = Dv; p.C = chunk;
+  p.NC = (int)nc;
+  p.scale = scale;
+  if (need_inputs && conv) {
+    p.use_conv = 1; p.cw = conv->width; p.l2 = conv->l2norm_qk;
+    p.eps = conv->eps;
+    p.xq = conv->xq; p.xk = conv->xk; p.xv = conv->xv;
+    p.wq = conv->wq; p.wk = conv->wk; p.wv = conv->wv;
+  }
+  return KDA_OK;
+}
+
+size_t ws_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
+                kda_dtype io) {
+  const size_t nc = ((size_t)T + chunk - 1) / chunk;
+  const kda::WsLayout L = kda::ws_layout(Dk, Dv, chunk, io == KDA_BF16 ? 2 : 4);
+  return (size_t)B * H * nc * L.bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char *kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK: success";
+    case KDA_EINVAL: return "KDA_EINVAL: invalid argument";
+    case KDA_EUNSUPPORTED: return "KDA_EUNSUPPORTED: valid but unsupported";
+    case KDA_EHIP: return "KDA_EHIP: HIP launch error";
+  }
+  return "KDA: unknown status";
+}
+
+size_t kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv,
+                                  int chunk, kda_dtype qkv_dtype) {
+  if (B <= 0 || T <= 0 || H <= 0 || !dim_ok(Dk) || !dim_ok(Dv) ||
+      !chunk_ok(chunk) || !dtype_valid(qkv_dtype))
+    return 0;
+  if (qkv_dtype == KDA_F32 && Dk == 128 && chunk == 64) return 0;
+  return ws_bytes(B, T, H, Dk, Dv, chunk, qkv_dtype);
+}
+
+kda_status kda_prefill_chunk_prep(const void *q, const void *k, const void *v,
+                                  kda_dtype qkv_dtype, const void *g,
+                                  const void *beta, kda_dtype gate_dtype,
+                                  int B, int T, int H, int Dk, int Dv,
+                                  int chunk, float scale,
+                                  const kda_conv_desc *conv, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+  kda::PrefillParams p;
+  kda_status st = prefill_check(q, k, v, qkv_dtype, g, beta, gate_dtype, B, T,
+                                H, Dk, Dv, chunk, scale, conv, true, p);
+  if (st != KDA_OK) return st;
+  if (!workspace || !aligned16(workspace)) return KDA_EINVAL;
+  if (workspace_bytes < ws_bytes(B, T, H, Dk, Dv, chunk, qkv_dtype))
+    return KDA_EINVAL;
+  p.ws = (char *)workspace;
+  p.wsb = kda::ws_layout(Dk, Dv, chunk, qkv_dtype == KDA_BF16 ? 2 : 4).bytes;
+  return hip_status(kda::launch_prefill_prep(p, qkv_dtype == KDA_BF16,
+                                             (hipStream_t)stream));
+}
+
+kda_status kda_prefill_state_pass(kda_dtype qkv_dtype, const float *s0,
+                                  float *s_out, void *o, int B, int T, int H,
+                                  int Dk, int Dv, int chunk,
+                                  const void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+  kda::PrefillParams p;
+  kda_status st = prefill_check(nullptr, nullptr, nullptr, qkv_dtype, nullptr,
+                                nullptr, qkv_dtype, B, T, H, Dk, Dv, chunk,
+                                1.0f, nullptr, false, p);
+  if (st != KDA_OK) return st;
+  if (!o || !workspace) return KDA_EINVAL;
+  if (!aligned16(o) || !aligned16(workspace) || (s0 && !aligned16(s0)) ||
+      (s_out && !aligned16(s_out)))
+    return KDA_EINVAL;
+  if (workspace_bytes < ws_bytes(B, T, H, Dk, Dv, chunk, qkv_dtype))
+    return KDA_EINVAL;
+  p.s0 = s0; p.s_out = s_out; p.o = o;
+  p.ws = (char *)workspace;
+  p.wsb = kda::ws_layout(Dk, Dv, chunk, qkv_dtype == KDA_BF16 ? 2 : 4).bytes;
+  return hip_status(kda::launch_state_pass(p, qkv_dtype == KDA_BF16,
+                                           (hipStream_t)stream));
+}
+
+kda_status kda_prefill(const void *q, const void *k, const void *v,
+                       kda_dtype qkv_dtype, const void *g, const void *beta,
+                       kda_dtype gate_dtype, const float *s0, float *s_out,
+                       void *o, int B, int T, int H, int Dk, int Dv,
+                       int chunk, float scale, const kda_conv_desc *conv,
+                       void *workspace, size_t workspace_bytes,
+                       void *stream) {
+  kda::PrefillParams p;
+  kda_status st = prefill_check(q, k, v, qkv_dtype, g, beta, gate_dtype, B, T,
+                                H, Dk, Dv, chunk, scale, conv, true, p);
+  if (st != KDA_OK) return st;
+  if (!o || !workspace) return KDA_EINVAL;
+  if (!aligned16(o) || !aligned16(workspace) || (s0 && !aligned16(s0)) ||
+      (s_out && !aligned16(s_out)))
+    return KDA_EINVAL;
+  if (o == q || o == k || o == v || o == g || o == beta) return KDA_EINVAL;
+  if (workspace_bytes < ws_bytes(B, T, H, Dk, Dv, chunk, qkv_dtype))
+    return KDA_EINVAL;
+  p.s0 = s0; p.s_out = s_out; p.o = o;
+  p.ws = (char *)workspace;
+  p.wsb = kda::ws_layout(Dk, Dv, chunk, qkv_dtype == KDA_BF16 ? 2 : 4).bytes;
+  const int bf = qkv_dtype == KDA_BF16;
+  hipError_t e = kda::launch_prefill_prep(p, bf, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(kda::launch_state_pass(p, bf, (hipStream_t)stream));
+}
+
+kda_status kda_decode_step(const void *q, const void *k, const void *v,
+                           kda_dtype qkv_dtype, const void *g,
+                           const void *beta, kda_dtype gate_dtype,
+                           float *state, void *o, int N, int H, int Dk,
+                           int Dv, float scale, void *stream) {
+  if (N <= 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_EINVAL;
+  if (!q || !k || !v || !g || !beta || !state || !o) return KDA_EINVAL;
+  if (!dtype_valid(qkv_dtype) || !dtype_valid(gate_dtype)) return KDA_EINVAL;
+  if (!isfinite(scale)) return KDA_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) ||
+      !aligned16(beta) || !aligned16(state) || !aligned16(o))
+    return KDA_EINVAL;
+  if (o == q || o == k || o == v || o == g || o == beta || o == state)
+    return KDA_EINVAL;
+  if (!dim_ok(Dk) || !dim_ok(Dv)) return KDA_EUNSUPPORTED;
+  if (!pair_ok(qkv_dtype, gate_dtype)) return KDA_EUNSUPPORTED;
+  if ((long long)N * H > 0x7fffffffLL) return KDA_EUNSUPPORTED;
+  kda::DecodeParams p{};
+  p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+  p.gate_bf16 = gate_dtype == KDA_BF16;
+  p.state = state; p.o = o;
+  p.N = N; p.H = H; p.Dk = Dk; p.Dv = Dv; p.scale = scale;
+  return hip_status(kda::launch_decode(p, qkv_dtype == KDA_BF16,
+                                       (hipStream_t)stream));
+}
+
+kda_status kda_conv_prologue(const void *xq, const void *xk, const void *xv,
+                             kda_dtype dtype, const float *wq,
+                             const float *wk, const float *wv, int width,
+                             float *conv_state, void *q, void *k, void *v,
+                             int B, int T, int H, int Dk, int Dv,
+                             int l2norm_qk, float eps, void *stream) {
+  if (B <= 0 || T <= 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_EINVAL;
+  if (!xq || !xk || !xv || !wq || !wk || !wv || !q || !k || !v)
+    return KDA_EINVAL;
+  if (!dtype_valid(dtype)) return KDA_EINVAL;
+  if (width < 2) return KDA_EINVAL;
+  if (l2norm_qk != 0 && l2norm_qk != 1) return KDA_EINVAL;
+  if (!(eps >= 0.f) || !isfinite(eps)) return KDA_EINVAL;
+  const void *ptrs[] = {xq, xk, xv, wq, wk, wv, q, k, v, conv_state};
+  for (const void *ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return KDA_EINVAL;
+  if (q == xq || k == xk || v == xv) return KDA_EINVAL;
+  if (width > 4 || !dim_ok(Dk) || !dim_ok(Dv)) return KDA_EUNSUPPORTED;
+  if ((long long)B * 3 > 65535 || H > 65535) return KDA_EUNSUPPORTED;
+  kda::ConvParams p{};
+  p.x[0] = xq; p.x[1] = xk; p.x[2] = xv;
+  p.w[0] = wq; p.w[1] = wk; p.w[2] = wv;
+  p.y[0] = q; p.y[1] = k; p.y[2] = v;
+  p.D[0] = Dk; p.D[1] = Dk; p.D[2] = Dv;
+  p.B = B; p.T = T; p.H = H; p.W = width; p.l2 = l2norm_qk;
+  p.io_bf16 = dtype == KDA_BF16;
+  p.eps = eps;
+  p.state = conv_state;
+  p.Dmax = Dk > Dv ? Dk : Dv;
+  return hip_status(kda::launch_conv(p, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+// kda_decode.hip -- one recurrent KDA step for N independent sequences.
+//
+// Per (sequence, head), with e = exp(g) per key channel (see include/kda.h
+// for the sources):
+//   u = S^T (e * k)      value the decayed state predicts for k
+//   y = S^T (e * q)      read-out of the decayed state
+//   delta = beta (v - u)
+//   S <- diag(e) S + k delta^T               (in place)
+//   o = scale (y + (q . k) delta)            (= scale S_new^T q)
+// The state is the only large operand (Dk*Dv fp32 per head), so the kernel
+// is an HBM stream: each workgroup loads its head's state once with 16-byte
+// non-temporal loads into registers, reduces over rows through LDS, and
+// writes it back once.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+constexpr int DEC_THREADS = 256;
+
+__device__ __forceinline__ float dec_gate(const void *p, size_t i, int bf) {
+  return bf ? (float)((const bf16 *)p)[i] : ((const float *)p)[i];
+}
+
+template <typename IO, int DK, int DV>
+__global__ __launch_bounds__(DEC_THREADS) void kda_decode(DecodeParams p) {
+  constexpr int NQ = DV / 4;  // column quads
+  constexpr int NT = (NQ * DK < DEC_THREADS) ? NQ * DK : DEC_THREADS;
+  constexpr int RG = NT / NQ;    // row groups
+  constexpr int RPT = DK / RG;   // rows per thread
+  static_assert(RG * NQ == NT && RPT * RG == DK, "thread mapping");
+
+  __shared__ float s_ek[DK], s_eq[DK], s_e[DK], s_k[DK];
+  __shared__ __attribute__((aligned(16))) float s_part[2][RG][DV];
+  __shared__ __attribute__((aligned(16))) float s_d[DV];
+  __shared__ float s_qk[DEC_THREADS / 64];
+
+  const int tid = threadIdx.x;
+  const size_t nh = blockIdx.x;
+  const int q4 = tid % NQ, rg = tid / NQ;
+  float *Sg = p.state + nh * DK * DV;
+
+  // 1. issue the state loads first: they are the whole cost
+  f32x4 s[RPT];
+  if (tid < NT) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int row = rg + RG * i;
+      s[i] = __builtin_nontemporal_load(
+          (const f32x4 *)(Sg + (size_t)row * DV + 4 * q4));
+    }
+  }
+  // 2. per-channel gate, decayed key and query
+  float qk = 0.f;
+  if (tid < DK) {
+    const float e = __expf(dec_gate(p.g, nh * DK + tid, p.gate_bf16));
+    const float kk = to_f32(((const IO *)p.k)[nh * DK + tid]);
+    const float qq = to_f32(((const IO *)p.q)[nh * DK + tid]);
+    s_e[tid] = e;
+    s_k[tid] = kk;
+    s_ek[tid] = e * kk;
+    s_eq[tid] = e * qq;
+    qk = qq * kk;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) qk += __shfl_xor(qk, off, 64);
+  if ((tid & 63) == 0) s_qk[tid >> 6] = qk;
+  __syncthreads();
+
+  // 3. partial column sums over this thread's rows
+  if (tid < NT) {
+    f32x4 u = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int row = rg + RG * i;
+      u += s[i] * s_ek[row];
+      y += s[i] * s_eq[row];
+    }
+    *(f32x4 *)&s_part[0][rg][4 * q4] = u;
+    *(f32x4 *)&s_part[1][rg][4 * q4] = y;
+  }
+  __syncthreads();
+
+  // 4. per column: delta and output
+  if (tid < DV) {
+    float u = 0.f, y = 0.f;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      u += s_part[0][r][tid];
+      y += s_part[1][r][tid];
+    }
+    float qkt = 0.f;
+#pragma unroll
+    for (int w = 0; w < DEC_THREADS / 64; ++w) qkt += s_qk[w];
+    const float bt = dec_gate(p.beta, nh, p.gate_bf16);
+    const float vv = to_f32(((const IO *)p.v)[nh * DV + tid]);
+    const float d = bt * (vv - u);
+    s_d[tid] = d;
+    ((IO *)p.o)[nh * DV + tid] = from_f32<IO>(p.scale * (y + qkt * d));
+  }
+  __syncthreads();
+
+  // 5. in-place state write: S <- diag(e) S + k delta^T
+  if (tid < NT) {
+    const f32x4 d = *(const f32x4 *)&s_d[4 * q4];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int row = rg + RG * i;
+      const f32x4 sn = s[i] * s_e[row] + d * s_k[row];
+      __builtin_nontemporal_store(sn,
+                                  (f32x4 *)(Sg + (size_t)row * DV + 4 * q4));
+    }
+  }
+}
+
+template <typename IO, int DK, int DV>
+static hipError_t dec_one(const DecodeParams &p, hipStream_t s) {
+  hipLaunchKernelGGL((kda_decode<IO, DK, DV>), dim3((unsigned)(p.N * p.H)),
+                     dim3(DEC_THREADS), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename IO, int DK>
+static hipError_t dec_dv(const DecodeParams &p, hipStream_t s) {
+  switch (p.Dv) {
+    case 16: return dec_one<IO, DK, 16>(p, s);
+    case 32: return dec_one<IO, DK, 32>(p, s);
+    case 64: return dec_one<IO, DK, 64>(p, s);
+    case 128: return dec_one<IO, DK, 128>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename IO>
+static hipError_t dec_dk(const DecodeParams &p, hipStream_t s) {
+  switch (p.Dk) {
+    case 16: return dec_dv<IO, 16>(p, s);
+    case 32: return dec_dv<IO, 32>(p, s);
+    case 64: return dec_dv<IO, 64>(p, s);
+    case 128: return dec_dv<IO, 128>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeParams &p, int io_bf16, hipStream_t s) {
+  return io_bf16 ? dec_dk<bf16>(p, s) : dec_dk<float>(p, s);
+}
+
+}  // namespace kda

@@ -1,0 +1,53 @@
+// kda_internal.h -- launcher interface between the C ABI (kda_api.cpp) and
+// the HIP kernels.  Not installed; not part of the ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace kda {
+
+struct PrefillParams {
+  const void *q, *k, *v;      // [B,T,H,D] (unused when use_conv)
+  const void *g, *beta;       // gates
+  int gate_bf16;              // 1: g/beta are bf16, 0: fp32
+  const float *s0;            // [B,H,Dk,Dv] or null
+  float *s_out;               // [B,H,Dk,Dv] or null
+  void *o;                    // [B,T,H,Dv]
+  int B, T, H, Dk, Dv, C, NC; // NC = ceil(T / C)
+  float scale;
+  int use_conv, cw, l2;       // fused conv prologue
+  float eps;
+  const void *xq, *xk, *xv;
+  const float *wq, *wk, *wv;
+  char *ws;                   // workspace base
+  size_t wsb;                 // bytes per (bh, chunk) block
+};
+
+struct DecodeParams {
+  const void *q, *k, *v, *g, *beta;
+  int gate_bf16;
+  float *state;
+  void *o;
+  int N, H, Dk, Dv;
+  float scale;
+};
+
+struct ConvParams {
+  const void *x[3];
+  const float *w[3];
+  void *y[3];
+  int D[3];
+  int B, T, H, W, l2, io_bf16;
+  float eps;
+  float *state;  // [B,3,H*Dmax,W-1] or null
+  int Dmax;
+};
+
+hipError_t launch_prefill_prep(const PrefillParams &p, int io_bf16,
+                               hipStream_t s);
+hipError_t launch_state_pass(const PrefillParams &p, int io_bf16,
+                             hipStream_t s);
+hipError_t launch_decode(const DecodeParams &p, int io_bf16, hipStream_t s);
+hipError_t launch_conv(const ConvParams &p, hipStream_t s);
+
+}  // namespace kda

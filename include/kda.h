@@ -1,0 +1,167 @@
+/*
+ * kda.h -- C ABI of libkda.so: the Kimi Delta Attention (KDA) layer forward
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  Per head, with a d_k x d_v state S (row i = key channel
+ * i), for each token t:
+ *     S'  = diag(exp(g_t)) S              per-row forgetting, g_t <= 0
+ *     S_t = S' + k_t (beta_t (v_t - S'^T k_t))^T
+ *     o_t = scale * S_t^T q_t
+ * Sources (web pages, cited by title and section):
+ *   [SARNAS] sarnas.ru, "Yandex opened the weights of
+ *     AliceAI-Foundation-80B-A3B-Base: an MoE model trained from scratch",
+ *     section "What exactly changed", KDA paragraph: fixed-size state; the
+ *     value stored for the key is read, compared with the new value, and only
+ *     the difference is written; one forgetting coefficient per row of the
+ *     state matrix.  Section "Rejected decisions": KDA layers keep a QK norm.
+ *   [LQNN-A] m.lqnn.cn news 205170 ("two deep teardowns in two days ..."),
+ *     the AliceAIKDA walk-through: kernel-4 causal conv on q/k/v with an
+ *     incrementally updated cache; the state is multiplied by exp(gate) and
+ *     the delta added; delta = prediction residual times sigmoid beta; on GPU
+ *     a chunked prefill kernel and a fused recurrent (decode) kernel; beta is
+ *     kept in (0,1) when negative eigenvalues are disallowed; the conv kernel
+ *     dimension is validated to be at least 2.
+ *   [LQNN-B] m.lqnn.cn news 255115 ("80B parameters for 3B of compute ..."),
+ *     config-validation list: conv kernel >= 2, chunk size positive.
+ *
+ * Conventions shared by every entry point.
+ *  - All pointers are DEVICE pointers owned by the caller; the library keeps
+ *    no global mutable state and never allocates device memory (the prefill
+ *    workspace is passed in).  Calls are thread-safe.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream) and never synchronises.
+ *  - Tensors are dense, contiguous, row-major.  Pointers must be 16-byte
+ *    aligned.  q, k, g: [B,T,H,Dk]; v, o: [B,T,H,Dv]; beta: [B,T,H];
+ *    states: [B,H,Dk,Dv] fp32 with row i = key channel i.
+ *  - Supported: Dk, Dv in {16,32,64,128}; chunk in {16,32,64}; conv width in
+ *    [2,4]; dtype pairs (q/k/v, g/beta) in {(F32,F32), (BF16,F32),
+ *    (BF16,BF16)}; fp32 q/k/v with Dk = 128 needs chunk <= 32.  Outputs
+ *    o have the q/k/v dtype; states are always fp32.
+ *  - Element values are not checked: g > 0 or beta outside (0,1) are the
+ *    caller's responsibility (the pages keep beta in (0,1)); g = -inf is
+ *    supported and forgets exactly.
+ *  - Errors: arguments are validated before anything is launched.
+ *    KDA_EINVAL: a NULL required pointer, a size <= 0, chunk <= 0, conv
+ *    width < 2, a misaligned pointer, a workspace that is too small.
+ *    KDA_EUNSUPPORTED: a valid request outside the supported set above.
+ *    KDA_EHIP: a HIP launch error (the HIP error is cleared and reported
+ *    through this code only).  Nothing is written on an error return that
+ *    happens before a launch.  No C++ exception crosses this boundary.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+  KDA_OK = 0,
+  KDA_EINVAL = 1,
+  KDA_EUNSUPPORTED = 2,
+  KDA_EHIP = 3
+} kda_status;
+
+typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Optional fused conv prologue for kda_prefill ([LQNN-A] conv paragraph;
+ * [SARNAS] "Rejected decisions" QK norm).  For each channel c of the
+ * projections x* = [B,T,H*D] (q/k/v dtype):
+ *     y[t,c] = sum_{j<width} w[c*width + j] * x[t-width+1+j, c]
+ * with zeros before t = 0 (tap width-1 multiplies the newest input; no bias,
+ * no activation).  If l2norm_qk, q and k are then divided per head by
+ * sqrt(sum y^2 + eps); v is not normalised. */
+typedef struct kda_conv_desc {
+  const void *xq, *xk, *xv;   /* [B,T,H*Dk], [B,T,H*Dk], [B,T,H*Dv]      */
+  const float *wq, *wk, *wv;  /* [H*Dk,width], [H*Dk,width], [H*Dv,width] */
+  int width;                  /* 2..4 */
+  int l2norm_qk;              /* 0 or 1 */
+  float eps;                  /* e.g. 1e-6 */
+} kda_conv_desc;
+
+/* ABI version of this header (bumped on any incompatible change). */
+#define KDA_ABI_VERSION 1
+int kda_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char *kda_status_string(kda_status s);
+
+/* Bytes of device workspace kda_prefill needs for these sizes (0 if the
+ * sizes are invalid or unsupported).  The workspace holds the chunk-local
+ * factors of every (batch, head, chunk); contents need no initialisation. */
+size_t kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv,
+                                  int chunk, kda_dtype qkv_dtype);
+
+/* Chunked prefill ([LQNN-A]: the chunked GPU prefill path; chunk size a
+ * positive config value per [LQNN-B]).
+ *   q,k,v     inputs (ignored, may be NULL, when conv != NULL)
+ *   g, beta   log-decay per key channel [B,T,H,Dk] and write strength
+ *             [B,T,H], in gate_dtype
+ *   s0        initial state [B,H,Dk,Dv] fp32, or NULL for zeros
+ *   s_out     final state [B,H,Dk,Dv] fp32, or NULL; may equal s0
+ *   o         output [B,T,H,Dv] in qkv_dtype; must not alias an input
+ *   chunk     tokens per chunk (16, 32 or 64); T need not be a multiple
+ *   scale     output scale (1.0 reproduces o_t = S_t^T q_t)
+ *   conv      NULL, or the fused conv prologue above
+ *   workspace device buffer of at least kda_prefill_workspace_size() bytes
+ * Runs kda_prefill_chunk_prep then kda_prefill_state_pass on `stream`. */
+kda_status kda_prefill(const void *q, const void *k, const void *v,
+                       kda_dtype qkv_dtype, const void *g, const void *beta,
+                       kda_dtype gate_dtype, const float *s0, float *s_out,
+                       void *o, int B, int T, int H, int Dk, int Dv,
+                       int chunk, float scale, const kda_conv_desc *conv,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* First phase of kda_prefill alone: every (batch, head, chunk) is reduced
+ * to its state-independent factors (the UT-transform of the chunk's
+ * triangular system, decay-weighted keys and queries, and the intra-chunk
+ * query-key matrix), written to `workspace`.  Fully parallel over chunks. */
+kda_status kda_prefill_chunk_prep(const void *q, const void *k, const void *v,
+                                  kda_dtype qkv_dtype, const void *g,
+                                  const void *beta, kda_dtype gate_dtype,
+                                  int B, int T, int H, int Dk, int Dv,
+                                  int chunk, float scale,
+                                  const kda_conv_desc *conv, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/* Second phase of kda_prefill alone: the sequential pass over chunks that
+ * carries the state and writes o and s_out, reading the factors that
+ * kda_prefill_chunk_prep left in `workspace` (same sizes and dtypes). */
+kda_status kda_prefill_state_pass(kda_dtype qkv_dtype, const float *s0,
+                                  float *s_out, void *o, int B, int T, int H,
+                                  int Dk, int Dv, int chunk,
+                                  const void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/* One recurrent decode step for N independent sequences ([LQNN-A]: the
+ * fused recurrent GPU kernel used for generation).
+ *   q,k,g [N,H,Dk]; v [N,H,Dv]; beta [N,H]   (qkv_dtype / gate_dtype)
+ *   state [N,H,Dk,Dv] fp32, read and updated IN PLACE
+ *   o     [N,H,Dv] in qkv_dtype; must not alias an input */
+kda_status kda_decode_step(const void *q, const void *k, const void *v,
+                           kda_dtype qkv_dtype, const void *g,
+                           const void *beta, kda_dtype gate_dtype,
+                           float *state, void *o, int N, int H, int Dk,
+                           int Dv, float scale, void *stream);
+
+/* Standalone conv prologue ([LQNN-A]: kernel-4 causal conv with a cache
+ * updated incrementally).  Same arithmetic as kda_conv_desc; outputs
+ * q,k [B,T,H,Dk] and v [B,T,H,Dv] in `dtype` (the raw inputs' dtype).
+ *   conv_state  NULL (zeros before t = 0), or fp32 [B,3,H*D_max,width-1]
+ *               laid out as [b][stream q,k,v][channel][tap], D_max =
+ *               max(Dk,Dv): read as the inputs before t = 0, then
+ *               overwritten with the last width-1 inputs of history+x. */
+kda_status kda_conv_prologue(const void *xq, const void *xk, const void *xv,
+                             kda_dtype dtype, const float *wq,
+                             const float *wk, const float *wv, int width,
+                             float *conv_state, void *q, void *k, void *v,
+                             int B, int T, int H, int Dk, int Dv,
+                             int l2norm_qk, float eps, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

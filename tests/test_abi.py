@@ -1,0 +1,127 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point
+include/kda.h declares, and rejects invalid arguments before any launch
+(no compute call is made here, so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_74_amd as kda
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "include", "kda.h")
+A = 0x100000  # a 16-byte aligned fake device address (never dereferenced)
+
+
+def _declared():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert {"kda_prefill", "kda_decode_step", "kda_conv_prologue",
+            "kda_prefill_chunk_prep", "kda_prefill_state_pass",
+            "kda_prefill_workspace_size", "kda_status_string",
+            "kda_abi_version"} <= set(names)
+    lib = ctypes.CDLL(kda.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strings():
+    ver = int(re.search(r"#define KDA_ABI_VERSION (\d+)", open(HDR).read())[1])
+    assert kda.kda_abi_version() == ver
+    for s in range(4):
+        assert kda.kda_status_string(s).startswith("KDA_")
+    assert "unknown" in kda.kda_status_string(99)
+
+
+def test_workspace_size():
+    ws = kda.kda_prefill_workspace_size
+    assert ws(1, 8192, 32, 128, 128, 64, kda.KDA_BF16) > 0
+    # grows with the number of chunks; a ragged tail costs a whole chunk
+    assert ws(1, 65, 1, 16, 16, 16, kda.KDA_F32) == \
+        5 * ws(1, 16, 1, 16, 16, 16, kda.KDA_F32)
+    for bad in [(0, 8, 1, 16, 16, 16), (1, 8, 1, 48, 16, 16),
+                (1, 8, 1, 16, 16, 8), (1, 8, 1, 16, 256, 16)]:
+        assert ws(*bad, kda.KDA_BF16) == 0
+    assert ws(1, 64, 1, 128, 128, 64, kda.KDA_F32) == 0  # LDS limit
+
+
+def _prefill(**kw):
+    a = dict(q=A, k=A, v=A, io=kda.KDA_BF16, g=A, beta=A, gt=kda.KDA_F32,
+             s0=None, s_out=None, o=A + 4096, B=1, T=64, H=2, Dk=16, Dv=16,
+             chunk=16, scale=1.0, conv=None, ws=A + 8192, wsb=1 << 40,
+             stream=None)
+    a.update(kw)
+    return kda._prefill(*a.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(B=0), kda.KDA_EINVAL),
+    (dict(T=-1), kda.KDA_EINVAL),
+    (dict(chunk=0), kda.KDA_EINVAL),
+    (dict(q=None), kda.KDA_EINVAL),
+    (dict(g=None), kda.KDA_EINVAL),
+    (dict(o=None), kda.KDA_EINVAL),
+    (dict(ws=None), kda.KDA_EINVAL),
+    (dict(k=A + 8), kda.KDA_EINVAL),          # misaligned
+    (dict(wsb=16), kda.KDA_EINVAL),            # workspace too small
+    (dict(io=7), kda.KDA_EINVAL),
+    (dict(o=A), kda.KDA_EINVAL),               # output aliases an input
+    (dict(scale=float("nan")), kda.KDA_EINVAL),
+    (dict(chunk=48), kda.KDA_EUNSUPPORTED),
+    (dict(Dk=48), kda.KDA_EUNSUPPORTED),
+    (dict(Dv=256), kda.KDA_EUNSUPPORTED),
+    (dict(io=kda.KDA_F32, gt=kda.KDA_BF16), kda.KDA_EUNSUPPORTED),
+    (dict(io=kda.KDA_F32, Dk=128, Dv=128, chunk=64), kda.KDA_EUNSUPPORTED),
+])
+def test_prefill_rejects(kw, want):
+    assert _prefill(**kw) == want
+
+
+@pytest.mark.parametrize("width,l2,want", [(1, 1, kda.KDA_EINVAL),
+                                          (5, 1, kda.KDA_EUNSUPPORTED),
+                                          (4, 2, kda.KDA_EINVAL)])
+def test_prefill_conv_rejects(width, l2, want):
+    d = kda.KdaConvDesc(A, A, A, A, A, A, width, l2, 1e-6)
+    assert _prefill(q=None, k=None, v=None, conv=ctypes.byref(d)) == want
+
+
+def _decode(**kw):
+    a = dict(q=A, k=A, v=A, io=kda.KDA_BF16, g=A, beta=A, gt=kda.KDA_BF16,
+             state=A + 4096, o=A + 8192, N=4, H=2, Dk=16, Dv=16, scale=1.0,
+             stream=None)
+    a.update(kw)
+    return kda._decode(*a.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(N=0), kda.KDA_EINVAL), (dict(state=None), kda.KDA_EINVAL),
+    (dict(v=A + 4), kda.KDA_EINVAL), (dict(o=A + 4096), kda.KDA_EINVAL),
+    (dict(Dk=24), kda.KDA_EUNSUPPORTED),
+    (dict(io=kda.KDA_F32), kda.KDA_EUNSUPPORTED),
+])
+def test_decode_rejects(kw, want):
+    assert _decode(**kw) == want
+
+
+def _conv(**kw):
+    a = dict(xq=A, xk=A, xv=A, dt=kda.KDA_BF16, wq=A, wk=A, wv=A, width=4,
+             state=None, q=A + 4096, k=A + 8192, v=A + 12288, B=1, T=8, H=2,
+             Dk=16, Dv=16, l2=1, eps=1e-6, stream=None)
+    a.update(kw)
+    return kda._conv(*a.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(width=1), kda.KDA_EINVAL), (dict(width=5), kda.KDA_EUNSUPPORTED),
+    (dict(xq=None), kda.KDA_EINVAL), (dict(eps=-1.0), kda.KDA_EINVAL),
+    (dict(q=A), kda.KDA_EINVAL), (dict(Dv=20), kda.KDA_EUNSUPPORTED),
+    (dict(state=A + 2), kda.KDA_EINVAL),
+])
+def test_conv_rejects(kw, want):
+    assert _conv(**kw) == want

@@ -1,0 +1,110 @@
+"""GPU parity of the decode step and the standalone conv prologue (through
+the C ABI) against the fp64 oracle, including the full decode workload
+(256 sequences x 32 heads, 1000 steps in place) on sampled heads, the conv
+cache round trip, and fused prologue == standalone prologue + prefill."""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs as ki
+from gpu_common import TOL, rel_err, say, to_cpu64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import gated_delta_rule_74_amd as m
+    return m
+
+
+@pytest.mark.parametrize("qkv,gate,Dk,Dv", [
+    ("bf16", "bf16", 128, 128), ("bf16", "f32", 64, 32), ("f32", "f32", 16, 16),
+    ("f32", "f32", 128, 128), ("bf16", "bf16", 32, 128), ("bf16", "f32", 128, 16)])
+def test_decode_steps(orc, kda, qkv, gate, Dk, Dv):
+    say(f"decode qkv={qkv} gate={gate} Dk={Dk} Dv={Dv}")
+    N, H = 5, 3
+    st = ki.decode_state(N, H, Dk, Dv, device="cuda")
+    ref = to_cpu64(st)
+    for step in range(6):
+        x = ki.decode_step_inputs(N, H, Dk, Dv, step, qkv=qkv, gate=gate,
+                                  device="cuda")
+        o = kda.kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], st,
+                                scale=0.8)
+        ro, ref = orc.decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"],
+                                  ref, 0.8)
+        torch.cuda.synchronize()
+        eo, es = rel_err(o, ro), rel_err(st, ref)
+        assert eo <= TOL[qkv] and es <= TOL[qkv], (step, eo, es)
+    say(f"  err o={eo:.2e} S={es:.2e}")
+
+
+def test_decode_workload_1000_steps(orc, kda):
+    c = ki.CONFIGS[3]
+    N, H, Dk, Dv, steps = c["N"], c["H"], c["Dk"], c["Dv"], c["steps"]
+    say(f"decode workload N{N} H{H} D{Dk} x{steps} steps (sampled heads)")
+    st = ki.decode_state(N, H, Dk, Dv, std=c["state_std"], device="cuda")
+    pick = [(0, 0), (17, 5), (101, 31), (200, 12), (255, 31), (128, 16)]
+    idx_n = torch.tensor([p[0] for p in pick], device="cuda")
+    idx_h = torch.tensor([p[1] for p in pick], device="cuda")
+    ref = to_cpu64(st[idx_n, idx_h])[:, None]      # [P,1,Dk,Dv]
+    o_keep, inp_keep = [], []
+    for step in range(steps):
+        x = ki.decode_step_inputs(N, H, Dk, Dv, step, device="cuda")
+        o = kda.kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], st)
+        o_keep.append(o[idx_n, idx_h])
+        inp_keep.append({n: t[idx_n, idx_h] for n, t in x.items()})
+    torch.cuda.synchronize()
+    worst = 0.0
+    for step in range(steps):
+        xi = {n: t[:, None] for n, t in inp_keep[step].items()}
+        ro, ref = orc.decode_step(xi["q"], xi["k"], xi["v"], xi["g"],
+                                  xi["beta"], ref)
+        worst = max(worst, rel_err(o_keep[step][:, None], ro))
+    es = rel_err(st[idx_n, idx_h][:, None], ref)
+    say(f"  worst step err o={worst:.2e}, final S err={es:.2e}")
+    assert worst <= 2e-2 and es <= 2e-2
+
+
+@pytest.mark.parametrize("dt,D,W,T,hist", [
+    ("bf16", 128, 4, 300, False), ("bf16", 128, 4, 300, True),
+    ("f32", 16, 2, 70, True), ("f32", 64, 3, 1, True), ("bf16", 32, 4, 65, False)])
+def test_conv_prologue(orc, kda, dt, D, W, T, hist):
+    say(f"conv prologue dt={dt} D={D} W={W} T={T} hist={hist}")
+    B, H = 2, 3
+    x = ki.prefill_inputs(B, T, H, D, D, qkv=dt, conv_width=W, seed=21,
+                          device="cuda")
+    state = None
+    old = None
+    if hist:
+        state = torch.randn((B, 3, H * D, W - 1), device="cuda")
+        old = to_cpu64(state)
+    q, k, v = kda.kda_conv_prologue(x["xq"], x["xk"], x["xv"], x["wq"],
+                                    x["wk"], x["wv"], H=H, Dk=D, Dv=D,
+                                    conv_state=state, eps=1e-6)
+    torch.cuda.synchronize()
+    hist_in = None if old is None else (old[:, 0], old[:, 1], old[:, 2])
+    rq, rk, rv, rh = orc.conv_prologue(x["xq"], x["xk"], x["xv"], x["wq"],
+                                       x["wk"], x["wv"], H, D, D, 1e-6, True,
+                                       hist_in)
+    for name, a, r in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+        e = rel_err(a, r)
+        assert e <= TOL[dt], (name, e)
+    if hist:
+        for i in range(3):
+            assert rel_err(state[:, i], rh[i]) <= 1e-6
+
+
+def test_fused_prologue_matches_standalone(kda):
+    x = ki.prefill_inputs(2, 250, 4, 128, 128, conv_width=4, seed=33,
+                          device="cuda")
+    conv = dict(xq=x["xq"], xk=x["xk"], xv=x["xv"], wq=x["wq"], wk=x["wk"],
+                wv=x["wv"], width=4, l2norm_qk=True, eps=1e-6)
+    of, sf = kda.kda_prefill(None, None, None, x["g"], x["beta"], chunk=64,
+                             conv=conv)
+    q, k, v = kda.kda_conv_prologue(x["xq"], x["xk"], x["xv"], x["wq"],
+                                    x["wk"], x["wv"], H=4, Dk=128, Dv=128)
+    ou, su = kda.kda_prefill(q, k, v, x["g"], x["beta"], chunk=64)
+    torch.cuda.synchronize()
+    assert rel_err(of, to_cpu64(ou)) < 2e-2
+    assert rel_err(sf, to_cpu64(su)) < 2e-2

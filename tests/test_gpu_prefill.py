@@ -1,0 +1,184 @@
+"""GPU parity of the chunked prefill (kda_prefill through the C ABI) against
+the fp64 oracle: small shapes spanning several chunks and ragged tails for
+every supported head size and chunk size, the tiny fp32 workload, -inf and
+extreme gates (exact fallback path), and the full-size workloads on sampled
+heads.  Plus the invariants that pin the chunked algebra on the device:
+split-sequence state carry, prefill == repeated decode steps, no unwritten
+output (poisoned buffers)."""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs as ki
+from gpu_common import TOL, rel_err, say, to_cpu64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import gated_delta_rule_74_amd as m
+    return m
+
+
+def _run(kda, x, chunk, scale=1.0, s0=None, conv=None):
+    o, s = kda.kda_prefill(x.get("q"), x.get("k"), x.get("v"), x["g"],
+                           x["beta"], s0=s0, chunk=chunk, scale=scale,
+                           conv=conv)
+    torch.cuda.synchronize()
+    return o, s
+
+
+CASES = []
+for D in (16, 32, 64, 128):
+    for C in (16, 32, 64):
+        if not (D == 128 and C == 64):
+            CASES.append(("f32", "f32", D, D, C))
+        CASES.append(("bf16", "f32", D, D, C))
+CASES += [("bf16", "bf16", 128, 128, 64), ("bf16", "bf16", 32, 32, 16),
+          ("bf16", "f32", 64, 128, 64), ("bf16", "f32", 128, 32, 32),
+          ("f32", "f32", 16, 64, 32)]
+
+
+@pytest.mark.parametrize("qkv,gate,Dk,Dv,C", CASES)
+def test_prefill_small(orc, kda, qkv, gate, Dk, Dv, C):
+    say(f"prefill small qkv={qkv} gate={gate} Dk={Dk} Dv={Dv} C={C}")
+    x = ki.prefill_inputs(2, 3 * C + 11, 3, Dk, Dv, qkv=qkv, gate=gate,
+                          seed=11 + Dk + C, device="cuda", with_s0=True)
+    o, s = _run(kda, x, C, scale=0.9, s0=x["s0"])
+    ro, rs = orc.recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"],
+                            x["s0"], 0.9)
+    eo, es = rel_err(o, ro), rel_err(s, rs)
+    say(f"  err o={eo:.2e} S={es:.2e}")
+    assert eo <= TOL[qkv] and es <= TOL[qkv]
+
+
+def test_tiny_fp32_workload(orc, kda):
+    c = ki.CONFIGS[0]
+    x = ki.config_prefill_inputs(0, device="cuda")
+    o, s = _run(kda, x, c["chunk"])
+    ro, rs = orc.recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"])
+    eo, es = rel_err(o, ro), rel_err(s, rs)
+    say(f"tiny fp32 workload err o={eo:.2e} S={es:.2e}")
+    assert eo <= 1e-4 and es <= 1e-4
+
+
+@pytest.mark.parametrize("qkv", ["bf16", "f32"])
+def test_forgetting_extremes(orc, kda, qkv):
+    """g = -inf (full and single-channel forgets) and very negative gates
+    send the diagonal blocks down the exact running-product path."""
+    say(f"prefill extremes qkv={qkv}")
+    x = ki.prefill_inputs(1, 150, 2, 32, 32, qkv=qkv, gate="f32", seed=5,
+                          device="cuda", with_s0=True)
+    g = x["g"]
+    g[:, 5] = -float("inf")
+    g[:, 70, :, 3] = -float("inf")
+    g[:, 100:108] = -60.0
+    o, s = _run(kda, x, 64, s0=x["s0"])
+    ro, rs = orc.recurrence(x["q"], x["k"], x["v"], g, x["beta"], x["s0"])
+    eo, es = rel_err(o, ro), rel_err(s, rs)
+    say(f"  err o={eo:.2e} S={es:.2e}")
+    assert eo <= TOL[qkv] and es <= TOL[qkv]
+    # all channels forgotten at every token: o_t = beta_t (q_t . k_t) v_t
+    x["g"].fill_(-float("inf"))
+    o, _ = _run(kda, x, 32, s0=x["s0"])
+    ro, _ = orc.recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"])
+    assert rel_err(o, ro) <= TOL[qkv]
+
+
+def test_split_sequence_carry(kda):
+    """prefill(T1) -> S -> prefill(T2 | S) equals prefill(T1 + T2)."""
+    x = ki.prefill_inputs(2, 300, 4, 128, 128, seed=9, device="cuda",
+                          with_s0=True)
+    o, s = _run(kda, x, 64, s0=x["s0"])
+    a = {n: t[:, :137].contiguous() for n, t in x.items() if n != "s0"}
+    b = {n: t[:, 137:].contiguous() for n, t in x.items() if n != "s0"}
+    oa, sa = _run(kda, a, 64, s0=x["s0"])
+    ob, sb = _run(kda, b, 64, s0=sa)
+    ref = torch.cat([oa, ob], 1).double()
+    assert rel_err(o, ref.cpu().numpy()) < 1e-2
+    assert rel_err(s, sb.double().cpu().numpy()) < 1e-2
+
+
+def test_prefill_equals_decode_steps(kda):
+    x = ki.prefill_inputs(3, 40, 2, 64, 64, qkv="bf16", gate="bf16", seed=4,
+                          device="cuda", with_s0=True)
+    o, s = _run(kda, x, 16, scale=1.3, s0=x["s0"])
+    st = x["s0"].clone()
+    outs = []
+    for t in range(40):
+        sl = {n: x[n][:, t].contiguous() for n in ("q", "k", "v", "g", "beta")}
+        outs.append(kda.kda_decode_step(sl["q"], sl["k"], sl["v"], sl["g"],
+                                        sl["beta"], st, scale=1.3))
+    od = torch.stack(outs, 1)
+    torch.cuda.synchronize()
+    assert rel_err(o, to_cpu64(od)) < 2e-2
+    assert rel_err(s, to_cpu64(st)) < 2e-2
+
+
+def test_poisoned_outputs_fully_written(kda):
+    x = ki.prefill_inputs(1, 200, 3, 128, 64, seed=8, device="cuda")
+    o = torch.full((1, 200, 3, 64), float("nan"), dtype=torch.bfloat16,
+                   device="cuda")
+    s = torch.full((1, 3, 128, 64), float("nan"), device="cuda")
+    ws = kda.alloc_workspace(1, 200, 3, 128, 64, 64, torch.bfloat16)
+    ws.fill_(255)  # NaN patterns everywhere in the workspace
+    kda.kda_prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], chunk=64, o=o,
+                    s_out=s, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(s).all()
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, checked on sampled heads
+
+def test_model_shaped_prefill_t8192(orc, kda):
+    c = ki.CONFIGS[1]
+    say("model-shaped prefill B1 T8192 H32 D128 C64")
+    x = ki.config_prefill_inputs(1, device="cuda")
+    o, s = _run(kda, x, c["chunk"])
+    for h in (0, 13, 31):
+        sl = lambda t: t[:, :, h:h + 1]
+        ro, rs = orc.recurrence(sl(x["q"]), sl(x["k"]), sl(x["v"]),
+                                sl(x["g"]), sl(x["beta"]))
+        eo, es = rel_err(sl(o), ro), rel_err(s[:, h:h + 1], rs)
+        say(f"  head {h}: err o={eo:.2e} S={es:.2e}")
+        assert eo <= 2e-2 and es <= 2e-2
+
+
+def test_conv_prefill_b8_t4096(orc, kda):
+    c = ki.CONFIGS[2]
+    say("conv prefill B8 T4096 H32 D128 C64 (fused prologue)")
+    x = ki.config_prefill_inputs(2, device="cuda")
+    conv = dict(xq=x["xq"], xk=x["xk"], xv=x["xv"], wq=x["wq"], wk=x["wk"],
+                wv=x["wv"], width=4, l2norm_qk=True, eps=1e-6)
+    o, s = _run(kda, x, c["chunk"], conv=conv)
+    D = c["Dk"]
+    for b, h in ((0, 0), (5, 17), (7, 31)):
+        cs = slice(h * D, (h + 1) * D)
+        sub = dict(xq=x["xq"][b:b + 1, :, cs], xk=x["xk"][b:b + 1, :, cs],
+                   xv=x["xv"][b:b + 1, :, cs], wq=x["wq"][cs], wk=x["wk"][cs],
+                   wv=x["wv"][cs], eps=1e-6, l2norm_qk=True)
+        ro, rs = orc.prefill(None, None, None, x["g"][b:b + 1, :, h:h + 1],
+                             x["beta"][b:b + 1, :, h:h + 1], conv=sub)
+        eo = rel_err(o[b:b + 1, :, h:h + 1], ro)
+        es = rel_err(s[b:b + 1, h:h + 1], rs)
+        say(f"  (b={b}, h={h}): err o={eo:.2e} S={es:.2e}")
+        assert eo <= 2e-2 and es <= 2e-2
+
+
+def test_long_context_prefill_t262144(orc, kda):
+    c = ki.CONFIGS[4]
+    say("long-context prefill B1 T262144 H32 D128 C64 (sampled heads)")
+    x = ki.config_prefill_inputs(4, device="cuda")
+    o, s = _run(kda, x, c["chunk"])
+    n = 4096
+    for h in (3, 28):
+        sl = lambda t: t[:, :, h:h + 1]
+        ro, rs = orc.recurrence(sl(x["q"]), sl(x["k"]), sl(x["v"]),
+                                sl(x["g"]), sl(x["beta"]))
+        ef = rel_err(sl(o)[:, :n], ro[:, :n])
+        el = rel_err(sl(o)[:, -n:], ro[:, -n:])
+        es = rel_err(s[:, h:h + 1], rs)
+        say(f"  head {h}: err first={ef:.2e} last={el:.2e} S={es:.2e}")
+        assert ef <= 2e-2 and el <= 2e-2 and es <= 2e-2
