@@ -1,0 +1,306 @@
+"""Benchmark of the KDA forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
+                    [--no-cpu] [--only prefill|decode|conv|long]
+
+Headline (`value`): chunked prefill tokens/s on the model-shaped workload
+B=1, T=8192, H=32, d_k=d_v=128, chunk 64, bf16 q/k/v, fp32 g/beta/state
+(synthetic seeded inputs, resident in HBM before timing).  One step = one
+kda_prefill call (chunk-prep kernel + state-pass kernel).  The decode
+workload (256 sequences x 32 heads, 1000 in-place steps), the fused-conv
+prefill (B=8, T=4096) and the long-context prefill (T=262,144) are timed too
+and reported in `decode` / `extra`.
+
+Kernel durations are measured with HIP events recorded on the stream the
+kernels are launched on.  Rooflines use algorithmic bytes (each input read
+once, each output written once) and MI355X peaks (HBM 8 TB/s, dense bf16
+MFMA 2.5 PFLOP/s).  `traffic` comes from committed rocprofv3 counter runs
+(profiles/traffic.json) and is null when the kernel sources changed since.
+
+The CPU baseline times the fp64 oracle (test infrastructure) on the host
+cores over the whole prefill workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "KDA prefill tokens/s (T=8192,H=32,d=128) + decode-step state GB/s"
+
+
+def prefill_bytes(B, T, H, Dk, Dv, io=2, gate=4, state=4):
+    """Algorithmic HBM bytes of one prefill: q,k,v,g,beta read once, o and
+    the final state written once (S0 = 0 is not read)."""
+    tok = B * T * H
+    return tok * (2 * Dk * io + Dv * io + Dk * gate + gate + Dv * io) + \
+        B * H * Dk * Dv * state
+
+
+def prefill_flops(B, T, H, Dk, Dv, C):
+    """Algorithmic flops per token-head: 6 Dk Dv (three chunk x state
+    products) + C (3 Dk + 2 Dv) (causal halves of A, P, W, U and P Delta)
+    + C^2 / 3 (triangular inverse)."""
+    return B * T * H * (6 * Dk * Dv + C * (3 * Dk + 2 * Dv) + C * C / 3)
+
+
+def decode_bytes(N, H, Dk, Dv, io=2):
+    """State read + written once, q,k,v,g,beta read, o written."""
+    return N * H * (2 * Dk * Dv * 4 + (3 * Dk + Dv + 1 + Dv) * io)
+
+
+def src_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gated_delta_rule_74_amd", "csrc", n),
+                  "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, sources):
+    """Measured HBM bytes per launch from profiles/traffic.json, or None if
+    missing or taken on other kernel sources."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except ValueError:
+        return None
+    rec = d.get("kernels", {}).get(kernel)
+    if not rec or rec.get("src_hash") != src_hash(sources):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", default=None,
+                    choices=[None, "prefill", "decode", "conv", "long"])
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for "
+              f"--gpus {args.gpus}); the multi-GPU design is described in "
+              "DESIGN.md but not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_74_amd as kda
+    import kda_inputs as ki
+
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    K, W = args.steps, args.warmup
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    out = {}
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # ---------------- prefill, model-shaped (headline) ----------------------
+    c1 = ki.CONFIGS[1]
+    B, T, H, Dk, Dv, C = (c1[n] for n in ("B", "T", "H", "Dk", "Dv", "chunk"))
+    run_prefill = args.only in (None, "prefill")
+    if run_prefill:
+        log("prefill: generating inputs")
+        x = ki.config_prefill_inputs(1, device=dev)
+        ws = kda.alloc_workspace(B, T, H, Dk, Dv, C, torch.bfloat16, dev)
+        o = torch.empty((B, T, H, Dv), dtype=torch.bfloat16, device=dev)
+        s = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+
+        def step():
+            kda.kda_prefill(x["q"], x["k"], x["v"], x["g"], x["beta"],
+                            chunk=C, o=o, s_out=s, workspace=ws)
+
+        for _ in range(W):
+            step()
+        torch.cuda.synchronize()
+        log("prefill: timing")
+        e0, e1 = ev(), ev()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(K):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / K
+        # per-kernel durations (same stream, events between the launches)
+        tp, ts = 0.0, 0.0
+        for _ in range(K):
+            a, b_, c_ = ev(), ev(), ev()
+            a.record(stream)
+            kda.kda_prefill_chunk_prep(x["q"], x["k"], x["v"], x["g"],
+                                       x["beta"], ws, chunk=C)
+            b_.record(stream)
+            kda.kda_prefill_state_pass(ws, o, s_out=s, B=B, T=T, H=H, Dk=Dk,
+                                       Dv=Dv, chunk=C)
+            c_.record(stream)
+            torch.cuda.synchronize()
+            tp += a.elapsed_time(b_)
+            ts += b_.elapsed_time(c_)
+        tp, ts = tp / K, ts / K
+        byts = prefill_bytes(B, T, H, Dk, Dv)
+        flops = prefill_flops(B, T, H, Dk, Dv, C)
+        t_k = (tp + ts) * 1e-3
+        gbs = byts / t_k / 1e9
+        srcs = ["kda_prep.hip", "kda_state.hip", "kda_device.h"]
+        tr_p = traffic_for("kda_chunk_prep", srcs)
+        tr_s = traffic_for("kda_state_pass", srcs)
+        out["prefill"] = dict(
+            ms_per_step=ms, tokens_per_s=B * T / (ms * 1e-3),
+            kernel_ms={"kda_chunk_prep": tp, "kda_state_pass": ts},
+            algo_bytes=byts, algo_flops=flops,
+            roofline=dict(
+                kernel="kda_prefill = kda_chunk_prep + kda_state_pass",
+                bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=gbs / HBM_PEAK_GBS,
+                traffic=(None if tr_p is None or tr_s is None
+                         else tr_p + tr_s)),
+            mfma=dict(achieved=flops / t_k / 1e12,
+                      peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                      frac=flops / t_k / 1e12 / MFMA_BF16_PEAK_TFLOPS))
+        log(f"prefill: {ms*1e3:.1f} us/step (prep {tp*1e3:.1f} us, state "
+            f"{ts*1e3:.1f} us), {gbs:.0f} GB/s algorithmic")
+        if not args.no_cpu:
+            import oracle
+            orc = oracle.get()
+            log("prefill: oracle CPU baseline (whole workload)")
+            xc = {n: t.detach().cpu() for n, t in x.items()}
+            t0 = time.perf_counter()
+            orc.recurrence(xc["q"], xc["k"], xc["v"], xc["g"], xc["beta"])
+            dt = time.perf_counter() - t0
+            out["cpu_baseline"] = dict(
+                value=B * T / dt, unit="tokens/s", cores=orc.last_threads,
+                kind="oracle",
+                sample=f"whole prefill workload B{B} T{T} H{H} D{Dk} "
+                       f"(fp64 token loop incl. exact upcast; {dt:.2f} s)")
+            del xc
+        del x, ws, o, s
+        torch.cuda.empty_cache()
+
+    # ---------------- decode workload ---------------------------------------
+    if args.only in (None, "decode") and not args.no_extra:
+        c3 = ki.CONFIGS[3]
+        N, H3, D3, steps = c3["N"], c3["H"], c3["Dk"], c3["steps"]
+        log("decode: generating 1000 steps of inputs")
+        st = ki.decode_state(N, H3, D3, D3, std=c3["state_std"], device=dev)
+        xs = [ki.decode_step_inputs(N, H3, D3, D3, i, device=dev)
+              for i in range(steps)]
+        od = torch.empty((N, H3, D3), dtype=torch.bfloat16, device=dev)
+        for i in range(10):
+            d = xs[i]
+            kda.kda_decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], st,
+                                o=od)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for d in xs:
+            kda.kda_decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], st,
+                                o=od)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        byts = decode_bytes(N, H3, D3, D3)
+        state_b = N * H3 * D3 * D3 * 4 * 2
+        gbs = byts / (ms * 1e-3) / 1e9
+        tr = traffic_for("kda_decode", ["kda_decode.hip", "kda_device.h"])
+        out["decode"] = dict(
+            workload=c3["name"], steps=steps, us_per_step=ms * 1e3,
+            tokens_per_s=N / (ms * 1e-3),
+            state_gbs=state_b / (ms * 1e-3) / 1e9,
+            roofline=dict(kernel="kda_decode", bound="hbm", achieved=gbs,
+                          peak=HBM_PEAK_GBS, unit="GB/s",
+                          frac=gbs / HBM_PEAK_GBS, traffic=tr))
+        log(f"decode: {ms*1e3:.1f} us/step, {gbs:.0f} GB/s")
+        del xs, st
+        torch.cuda.empty_cache()
+
+    # ---------------- fused-conv prefill and long context -------------------
+    extra = {}
+    for cid, tag in ((2, "conv"), (4, "long")):
+        if args.no_extra or args.only not in (None, tag):
+            continue
+        c = ki.CONFIGS[cid]
+        log(f"{tag}: generating inputs")
+        x = ki.config_prefill_inputs(cid, device=dev)
+        Bc, Tc, Hc, Dc, Cc = c["B"], c["T"], c["H"], c["Dk"], c["chunk"]
+        conv = None
+        if c["conv_width"]:
+            conv = dict(xq=x["xq"], xk=x["xk"], xv=x["xv"], wq=x["wq"],
+                        wk=x["wk"], wv=x["wv"], width=c["conv_width"],
+                        l2norm_qk=True, eps=1e-6)
+        ws = kda.alloc_workspace(Bc, Tc, Hc, Dc, Dc, Cc, torch.bfloat16, dev)
+        o = torch.empty((Bc, Tc, Hc, Dc), dtype=torch.bfloat16, device=dev)
+        s = torch.empty((Bc, Hc, Dc, Dc), dtype=torch.float32, device=dev)
+        f = lambda: kda.kda_prefill(x.get("q"), x.get("k"), x.get("v"),
+                                    x["g"], x["beta"], chunk=Cc, conv=conv,
+                                    o=o, s_out=s, workspace=ws)
+        f()
+        torch.cuda.synchronize()
+        reps = 5 if cid == 2 else 3
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        if conv:
+            byts = Bc * Tc * Hc * (3 * Dc * 2 + Dc * 4 + 4 + Dc * 2) + \
+                3 * Hc * Dc * 4 * 4 + Bc * Hc * Dc * Dc * 4
+        else:
+            byts = prefill_bytes(Bc, Tc, Hc, Dc, Dc)
+        gbs = byts / (ms * 1e-3) / 1e9
+        extra[c["name"]] = dict(ms_per_call=ms,
+                                tokens_per_s=Bc * Tc / (ms * 1e-3),
+                                algo_gbs=gbs, hbm_frac=gbs / HBM_PEAK_GBS)
+        log(f"{tag}: {ms:.3f} ms/call, {gbs:.0f} GB/s algorithmic")
+        del x, ws, o, s
+        torch.cuda.empty_cache()
+
+    pf = out.get("prefill")
+    line = {
+        "metric": METRIC,
+        "value": pf["tokens_per_s"] if pf else None,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": pf["ms_per_step"] if pf else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the "
+                "KDA workloads)",
+        "config": {"workload": ki.CONFIGS[1]["name"], "B": B, "T": T, "H": H,
+                   "d_k": Dk, "d_v": Dv, "chunk": C, "qkv": "bf16",
+                   "gate": "f32", "state": "f32"},
+        "roofline": pf["roofline"] if pf else None,
+        "cpu_baseline": out.get("cpu_baseline"),
+        "prefill": ({k: v for k, v in pf.items() if k != "roofline"}
+                    if pf else None),
+        "decode": out.get("decode"),
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

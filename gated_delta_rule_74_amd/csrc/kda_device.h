@@ -117,16 +117,29 @@ __device__ __forceinline__ f32x4 mma16_f32(f32x4 a, f32x4 b, f32x4 c) {
 }
 
 // ---------------------------------------------------------------------------
-// Prefill workspace: one block per (batch*head, chunk), bh-major.
-// All sections are arrays of 1 KiB fragment units (64 lanes x 16 B) except
-// the U tiles (64 lanes x 4 values) and gamma (Dk floats).
+// Prefill workspace: one block per (batch*head, chunk), bh-major.  Layout
+//   [ -W | Qtil | Ktil^T | P | gamma_C | U ]
+// The first five sections are shared by every value-column slab and form
+// one contiguous range [0, off_u); U follows slab-major ([vt][rt]) so each
+// 16-column slab's tiles are contiguous too.  Fragment sections are arrays
+// of 1 KiB units (64 lanes x 16 B); U tiles are 64 lanes x 4 values.
 struct WsLayout {
   int nb, nkt, nvt, tpu, nku, ntu;
-  size_t off_negw, off_qt, off_ktt, off_p, off_u, off_gam, bytes;
+  size_t off_negw, off_qt, off_ktt, off_p, off_gam, off_u, u_slab, bytes;
 };
 
-__host__ __device__ inline size_t ws_align(size_t x) {
+__host__ __device__ constexpr size_t ws_align(size_t x) {
   return (x + 255) & ~(size_t)255;
+}
+
+// bytes of the shared range [0, off_u)
+__host__ __device__ constexpr size_t ws_shared_bytes(int Dk, int C,
+                                                     int io_bytes) {
+  return ws_align(
+      (size_t)(C / 16) * (((Dk / 16) + (io_bytes == 2)) / (1 + (io_bytes == 2))) * 2048 +
+      (size_t)(Dk / 16) * (((C / 16) + (io_bytes == 2)) / (1 + (io_bytes == 2))) * 1024 +
+      (size_t)(C / 16) * (((C / 16) + (io_bytes == 2)) / (1 + (io_bytes == 2))) * 1024 +
+      (size_t)Dk * 4);
 }
 
 __host__ __device__ inline WsLayout ws_layout(int Dk, int Dv, int C,
@@ -143,9 +156,11 @@ __host__ __device__ inline WsLayout ws_layout(int Dk, int Dv, int C,
   L.off_qt = o;   o += (size_t)L.nb * L.nku * 1024;       // Qtil [rt][u]
   L.off_ktt = o;  o += (size_t)L.nkt * L.ntu * 1024;      // Ktil^T [ct][u]
   L.off_p = o;    o += (size_t)L.nb * L.ntu * 1024;       // P    [rt][u]
-  L.off_u = o;    o += (size_t)L.nb * L.nvt * 64 * 4 * io_bytes;  // U tiles
-  o = ws_align(o);
   L.off_gam = o;  o += (size_t)Dk * 4;                    // gamma_C
+  o = ws_align(o);
+  L.off_u = o;                                            // U [vt][rt]
+  L.u_slab = (size_t)L.nb * 64 * 4 * io_bytes;
+  o += L.u_slab * L.nvt;
   L.bytes = ws_align(o);
   return L;
 }

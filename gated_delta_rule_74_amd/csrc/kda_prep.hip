@@ -1,0 +1,770 @@
+// kda_prep.hip -- chunk-local factors of the chunked KDA prefill (gfx950).
+//
+// Method (per head; see include/kda.h for the sources).  The token rule
+//   S' = diag(e_t) S,  e_t = exp(g_t);  S_t = S' + k_t (beta_t (v_t - S'^T k_t))^T;
+//   o_t = scale S_t^T q_t
+// is evaluated over chunks of C tokens in its WY / UT-transform form.  With
+// Gam_r the within-chunk running product of e and S0 the chunk's start state:
+//   A[r,s] = beta_r sum_i k_ri k_si Gam_ri/Gam_si  (s<r),  T = (I + A)^-1
+//   P[r,s] = scale sum_i q_ri k_si Gam_ri/Gam_si   (s<=r)
+//   W = T diag(beta)(K*Gam),  U = T diag(beta) V
+//   Delta = U - W S0,  O = scale (Q*Gam) S0 + P Delta,
+//   S_C = diag(Gam_C) S0 + (K*Gam_C/Gam)^T Delta.
+// This kernel computes every state-independent factor (-W, U, P,
+// Qtil = scale Q*Gam, Ktil^T = (K*Gam_C/Gam)^T, Gam_C) of every
+// (batch*head, chunk) and writes them to the workspace in matrix-core
+// fragment order; kda_state_pass then runs the sequential part.
+//
+// Decay ratios are never formed as Gam_r / Gam_s.  Within a chunk they are
+// products of e over (s, r], split at 16-token sub-chunk boundaries so every
+// factor is a product of values <= 1 (no overflow; g = -inf gives an exact
+// 0).  Only the 16x16 diagonal sub-blocks use a ratio (rho_r / rho_s against
+// the sub-chunk start), and only when every such rho of the chunk is at
+// least 2^-64; otherwise those blocks are summed directly with running
+// products (exact and slow; reached only by extreme forgetting).
+//
+// Execution: a persistent grid (one workgroup of 256 threads per CU) walks
+// the (batch*head, chunk) tasks.  Thread t owns 4 consecutive key channels x
+// 8 consecutive tokens of a task; its raw inputs are fetched with 8/16-byte
+// vector loads into registers one task ahead, so the fetch of task i+1
+// overlaps the matrix-core phases of task i.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+constexpr int PREP_THREADS = 256;
+constexpr int DVMAX = 128;
+constexpr float SAFE_MIN = 5.42101086242752217e-20f;  // 2^-64
+
+template <typename IO> struct Vec4;  // 4 IO values as raw bits
+template <> struct Vec4<bf16> {
+  typedef uint2 raw;
+  __device__ static __forceinline__ void get(raw r, float *f) {
+    f[0] = __uint_as_float(r.x << 16);
+    f[1] = __uint_as_float(r.x & 0xffff0000u);
+    f[2] = __uint_as_float(r.y << 16);
+    f[3] = __uint_as_float(r.y & 0xffff0000u);
+  }
+  __device__ static __forceinline__ raw put(const float *f) {
+    bf16x4 v = {(bf16)f[0], (bf16)f[1], (bf16)f[2], (bf16)f[3]};
+    return __builtin_bit_cast(raw, v);
+  }
+};
+template <> struct Vec4<float> {
+  typedef uint4 raw;
+  __device__ static __forceinline__ void get(raw r, float *f) {
+    f[0] = __uint_as_float(r.x);
+    f[1] = __uint_as_float(r.y);
+    f[2] = __uint_as_float(r.z);
+    f[3] = __uint_as_float(r.w);
+  }
+  __device__ static __forceinline__ raw put(const float *f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
+                      __float_as_uint(f[2]), __float_as_uint(f[3]));
+  }
+};
+
+template <typename IO, int DK, int C> struct PL {  // prep LDS layout
+  static constexpr int NB = C / 16, NKT = DK / 16, TPU = Mma<IO>::TPU;
+  static constexpr int NKU = (NKT + TPU - 1) / TPU;
+  static constexpr int NTU = (NB + TPU - 1) / TPU;
+  static constexpr int KU = 16 * TPU;
+  static constexpr int PE = 16 / (int)sizeof(IO);
+  static constexpr int LDK = DK + PE;  // token-major rows [C][LDK]
+  static constexpr int LDC = C + PE;   // channel-major rows [*][LDC]
+  static constexpr int LDA = C + 4;    // fp32 rows
+  static constexpr int NP2 = NB >= 3 ? (NB - 1) * (NB - 2) / 2 : 0;
+  static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
+  static constexpr size_t TOK = al((size_t)C * LDK * sizeof(IO));
+  // region A (tasks' phase E -> AP): row/column operands of A and P
+  static constexpr size_t oKR = 0, oQR = TOK, oKS = 2 * TOK, oKIR = 3 * TOK;
+  static constexpr size_t endA = 4 * TOK;
+  // region D overlays A (phases T -> WU)
+  static constexpr size_t oTt = 0;
+  static constexpr size_t oTaa = al(oTt + (size_t)C * LDA * 4);
+  static constexpr size_t oTb = al(oTaa + (size_t)NB * 256 * 4);
+  static constexpr size_t oKG = al(oTb + (size_t)C * LDC * sizeof(IO));
+  static constexpr size_t oVT = al(oKG + (size_t)DK * LDC * sizeof(IO));
+  static constexpr size_t endD = al(oVT + (size_t)DVMAX * LDC * sizeof(IO));
+  // A (fp32); during phase E of a fallback task it holds the raw q rows
+  static constexpr size_t oAf = endA > endD ? endA : endD;
+  static constexpr size_t AFB = al((size_t)C * LDA * 4) > TOK
+                                    ? al((size_t)C * LDA * 4) : TOK;
+  // raw k rows (the exact diagonal path reads them)
+  static constexpr size_t oKraw = oAf + AFB;
+  static constexpr size_t oF = al(oKraw + TOK);
+  static constexpr size_t oM = al(oF + (size_t)NB * DK * 4);
+  static constexpr size_t oFb = al(oM + (size_t)(NP2 ? NP2 : 1) * DK * 4);
+  static constexpr size_t oVote = al(oFb + (size_t)2 * NB * 256 * 4);
+  static constexpr size_t total = oVote + 64;
+  __device__ static int p2(int a, int b) { return (a - 2) * (a - 1) / 2 + b; }
+};
+
+template <typename IO, bool CONV> struct Stage {
+  static constexpr int XR = CONV ? 11 : 8;  // rows of q/k/v (conv: +3 halo)
+  typename Vec4<IO>::raw xq[XR], xk[XR], xv[XR];
+  uint4 g[8];
+  uint32_t beta[8], betav[8];
+};
+
+template <typename IO, int DK, int C, bool CONV>
+__device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
+                                          Stage<IO, CONV> &st, int tid) {
+  constexpr int NQ = DK / 4, NTG = C / 8;
+  typedef typename Vec4<IO>::raw R;
+  const int BH = p.B * p.H;
+  const int bh = task % BH, n = task / BH;
+  const int b = bh / p.H, h = bh % p.H;
+  const int T = p.T, H = p.H, Dv = p.Dv;
+  const int t0 = n * C;
+  const int tlast = T - 1;
+  const size_t tok0 = (size_t)b * T;  // first token row of batch b
+  // 64-bit bases of (batch b, head h); in-batch offsets fit in 32 bits
+  const size_t kb = (tok0 * H + h) * DK;
+  const unsigned rowK = (unsigned)(H * DK);
+  if (tid < NQ * NTG) {
+    const int cq = tid % NQ, tg = tid / NQ;
+    const float *gf = (const float *)p.g + kb + 4 * cq;
+    const bf16 *gh = (const bf16 *)p.g + kb + 4 * cq;
+    const float *bf = (const float *)p.beta + tok0 * H + h;
+    const unsigned short *bh16 = (const unsigned short *)p.beta + tok0 * H + h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const unsigned t = (unsigned)min(t0 + 8 * tg + i, tlast);
+      if (p.gate_bf16) {
+        const uint2 v = *(const uint2 *)(gh + t * rowK);
+        st.g[i] = make_uint4(v.x, v.y, 0u, 0u);
+        st.beta[i] = bh16[t * H];
+      } else {
+        st.g[i] = *(const uint4 *)(gf + t * rowK);
+        st.beta[i] = __float_as_uint(bf[t * H]);
+      }
+    }
+    const IO *xq = (const IO *)(CONV ? p.xq : p.q) + kb + 4 * cq;
+    const IO *xk = (const IO *)(CONV ? p.xk : p.k) + kb + 4 * cq;
+#pragma unroll
+    for (int i = 0; i < Stage<IO, CONV>::XR; ++i) {
+      const unsigned t =
+          (unsigned)min(max(t0 + 8 * tg + i - (CONV ? 3 : 0), 0), tlast);
+      st.xq[i] = *(const R *)(xq + t * rowK);
+      st.xk[i] = *(const R *)(xk + t * rowK);
+    }
+  }
+  const int NQV = Dv / 4;
+  if (tid < NQV * NTG) {
+    const int cv = tid % NQV, tg = tid / NQV;
+    const unsigned rowV = (unsigned)(H * Dv);
+    const IO *xv = (const IO *)(CONV ? p.xv : p.v) + (tok0 * H + h) * Dv +
+                   4 * cv;
+    const float *bf = (const float *)p.beta + tok0 * H + h;
+    const unsigned short *bh16 = (const unsigned short *)p.beta + tok0 * H + h;
+#pragma unroll
+    for (int i = 0; i < Stage<IO, CONV>::XR; ++i) {
+      const unsigned t =
+          (unsigned)min(max(t0 + 8 * tg + i - (CONV ? 3 : 0), 0), tlast);
+      st.xv[i] = *(const R *)(xv + t * rowV);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const unsigned t = (unsigned)min(t0 + 8 * tg + i, tlast);
+      st.betav[i] = p.gate_bf16 ? (uint32_t)bh16[t * H]
+                                : __float_as_uint(bf[t * H]);
+    }
+  }
+}
+
+// 4 taps right-aligned (w4[3] multiplies the newest input) for 4 channels
+__device__ __forceinline__ void load_taps(const float *w, int W, float t[4][4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int jj = i - (4 - W);
+      t[j][i] = (jj >= 0) ? w[j * W + jj] : 0.f;
+    }
+}
+
+template <typename IO, int DK, int C, bool CONV>
+__global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
+    PrefillParams p) {
+  using L = PL<IO, DK, C>;
+  using M = Mma<IO>;
+  using V4 = Vec4<IO>;
+  typedef typename M::frag frag;
+  constexpr int NB = L::NB, NKT = L::NKT, TPU = L::TPU, NKU = L::NKU,
+                NTU = L::NTU, KU = L::KU, LDK = L::LDK, LDC = L::LDC,
+                LDA = L::LDA;
+  constexpr int NQ = DK / 4, NTG = C / 8, XR = Stage<IO, CONV>::XR;
+  constexpr int XO = CONV ? 3 : 0;  // first own row inside the x window
+
+  __shared__ __attribute__((aligned(16))) char sm[L::total];
+  IO *Xkr = (IO *)(sm + L::oKR), *Xqr = (IO *)(sm + L::oQR);
+  IO *Xks = (IO *)(sm + L::oKS), *Xkir = (IO *)(sm + L::oKIR);
+  float *Tt = (float *)(sm + L::oTt), *Taa = (float *)(sm + L::oTaa);
+  IO *Tb = (IO *)(sm + L::oTb), *XkgT = (IO *)(sm + L::oKG);
+  IO *XvT = (IO *)(sm + L::oVT);
+  float *Af = (float *)(sm + L::oAf);
+  IO *Aq = (IO *)(sm + L::oAf);  // raw q rows until phase AP
+  IO *Kraw = (IO *)(sm + L::oKraw);
+  float *Fs = (float *)(sm + L::oF), *Mid = (float *)(sm + L::oM);
+  float *FbA = (float *)(sm + L::oFb), *FbP = FbA + NB * 256;
+  int *votes = (int *)(sm + L::oVote);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, m16 = lane & 15;
+  const int BH = p.B * p.H, T = p.T, H = p.H, Dv = p.Dv, nvt = Dv / 16;
+  const int ntask = BH * p.NC;
+  const WsLayout W = ws_layout(DK, Dv, C, (int)sizeof(IO));
+  const bool kthr = tid < NQ * NTG;
+  const int cq = tid % NQ, tg = tid / NQ;
+  const int c0 = 4 * cq, r0 = 8 * tg;
+  const int a = r0 / 16, half = (r0 / 8) & 1;
+  const int NQV = Dv / 4;
+  const bool vthr = tid < NQV * NTG;
+  const int cv = tid % NQV, tgv = tid / NQV;
+
+  Stage<IO, CONV> st;
+  int task = blockIdx.x;
+  if (task < ntask) prep_load<IO, DK, C, CONV>(p, task, st, tid);
+
+  for (; task < ntask; task += gridDim.x) {
+    const int bh = task % BH, n = task / BH;
+    const int b = bh / H, h = bh % H;
+    const int t0 = n * C;
+    char *blk = p.ws + ((size_t)bh * p.NC + n) * p.wsb;
+    for (int i = tid; i < 2 * NB * 256; i += PREP_THREADS) FbA[i] = 0.f;
+
+    // ---- E1: decay, running products within the sub-chunk, conv + L2 -----
+    // Writes the A/P operands (region A), raw k/q rows and F_a; rho and
+    // sigma are running products written out as they are formed.
+    int vote = 0;
+    float F[4] = {1.f, 1.f, 1.f, 1.f};
+    if (kthr) {
+      float e[8][4], kk[8][4], qq[8][4], bt[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool ok = t0 + r0 + i < T;
+        float gv[4];
+        if (p.gate_bf16) {
+          Vec4<bf16>::get(make_uint2(st.g[i].x, st.g[i].y), gv);
+          bt[i] = ok ? __uint_as_float(st.beta[i] << 16) : 0.f;
+        } else {
+          Vec4<float>::get(st.g[i], gv);
+          bt[i] = ok ? __uint_as_float(st.beta[i]) : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) e[i][j] = ok ? __expf(gv[j]) : 1.f;
+      }
+      if (CONV) {
+        float tq[4][4], tk[4][4];
+        load_taps(p.wq + ((size_t)h * DK + c0) * p.cw, p.cw, tq);
+        load_taps(p.wk + ((size_t)h * DK + c0) * p.cw, p.cw, tk);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float sq = 0.f, sk = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) { qq[i][j] = 0.f; kk[i][j] = 0.f; }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int t = t0 + r0 + i + u - XO;
+            const bool ok = t >= 0 && t < T;
+            float xq[4], xk[4];
+            V4::get(st.xq[i + u], xq);
+            V4::get(st.xk[i + u], xk);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              qq[i][j] += ok ? tq[j][u] * xq[j] : 0.f;
+              kk[i][j] += ok ? tk[j][u] * xk[j] : 0.f;
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            sq += qq[i][j] * qq[i][j];
+            sk += kk[i][j] * kk[i][j];
+          }
+          if (p.l2) {
+            // per-token sum over the head: the NQ lanes sharing this token
+#pragma unroll
+            for (int off = NQ / 2; off >= 1; off >>= 1) {
+              sq += __shfl_xor(sq, off, 64);
+              sk += __shfl_xor(sk, off, 64);
+            }
+            const float iq = 1.f / sqrtf(sq + p.eps);
+            const float ik = 1.f / sqrtf(sk + p.eps);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              qq[i][j] *= iq;
+              kk[i][j] *= ik;
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          V4::get(st.xq[i], qq[i]);
+          V4::get(st.xk[i], kk[i]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = r0 + i;
+        if (t0 + r >= T)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) qq[i][j] = kk[i][j] = 0.f;
+        *(typename V4::raw *)(Kraw + r * LDK + c0) = V4::put(kk[i]);
+        *(typename V4::raw *)(Aq + r * LDK + c0) = V4::put(qq[i]);
+      }
+      // this thread's 8-token product, then the other half of the 16-token
+      // sub-chunk (lane ^ NQ) for the cross terms
+      float ltp[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float lt = 1.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lt *= e[i][j];
+        ltp[j] = __shfl_xor(lt, NQ, 64);
+        F[j] = lt * ltp[j];
+      }
+      // forward: rho = inclusive prefix within the sub-chunk
+      {
+        float pr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pr[j] = half ? ltp[j] : 1.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = r0 + i;
+          float xkr[4], xqr[4], xki[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            pr[j] *= e[i][j];
+            if (!(half && i == 7) && !(pr[j] >= SAFE_MIN)) vote = 1;
+            xkr[j] = bt[i] * kk[i][j] * pr[j];
+            xqr[j] = p.scale * qq[i][j] * pr[j];
+            xki[j] = kk[i][j] * __builtin_amdgcn_rcpf(pr[j]);
+          }
+          *(typename V4::raw *)(Xkr + r * LDK + c0) = V4::put(xkr);
+          *(typename V4::raw *)(Xqr + r * LDK + c0) = V4::put(xqr);
+          *(typename V4::raw *)(Xkir + r * LDK + c0) = V4::put(xki);
+        }
+      }
+      // backward: sigma = exclusive suffix within the sub-chunk
+      {
+        float sf[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sf[j] = half ? 1.f : ltp[j];
+#pragma unroll
+        for (int i = 7; i >= 0; --i) {
+          const int r = r0 + i;
+          float xks[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            xks[j] = kk[i][j] * sf[j];
+            sf[j] *= e[i][j];
+          }
+          *(typename V4::raw *)(Xks + r * LDK + c0) = V4::put(xks);
+        }
+      }
+      if (!half) *(f32x4 *)(Fs + a * DK + c0) = f32x4{F[0], F[1], F[2], F[3]};
+    }
+    // beta * V for the W/U phase (V side)
+    float bv[8][4];
+    if (vthr) {
+      float bvt[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool ok = t0 + 8 * tgv + i < T;
+        const float bb = p.gate_bf16 ? __uint_as_float(st.betav[i] << 16)
+                                     : __uint_as_float(st.betav[i]);
+        bvt[i] = ok ? bb : 0.f;
+      }
+      if (CONV) {
+        float tv[4][4];
+        load_taps(p.wv + ((size_t)h * Dv + 4 * cv) * p.cw, p.cw, tv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bv[i][j] = 0.f;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int t = t0 + 8 * tgv + i + u - XO;
+            const bool ok = t >= 0 && t < T;
+            float xv[4];
+            V4::get(st.xv[i + u], xv);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bv[i][j] += ok ? tv[j][u] * xv[j] : 0.f;
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bv[i][j] *= bvt[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float vv[4];
+          V4::get(st.xv[i], vv);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bv[i][j] = bvt[i] * vv[j];
+        }
+      }
+    }
+    {
+      const unsigned long long bal = __ballot(vote);
+      if (lane == 0) votes[wave] = bal != 0ull;
+    }
+    __syncthreads();  // B1: region A, Fs, votes
+
+    // ---- E2: Qtil and Ktil^T units, gamma_C, beta K Gam for W ------------
+    const bool fallback =
+        (votes[0] | votes[1] | votes[2] | votes[3]) != 0;
+    float kgb[8][4];
+    if (kthr) {
+      float fpre[4], fsuf[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { fpre[j] = 1.f; fsuf[j] = 1.f; }
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        const f32x4 f = *(const f32x4 *)(Fs + bb * DK + c0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (bb < a) fpre[j] *= f[j];
+          if (bb > a) fsuf[j] *= f[j];
+        }
+      }
+      const int ct = c0 / 16;
+      float kt[8][4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = r0 + i;
+        float xkr[4], xqr[4], xks[4], qt[4];
+        V4::get(*(const typename V4::raw *)(Xkr + r * LDK + c0), xkr);
+        V4::get(*(const typename V4::raw *)(Xqr + r * LDK + c0), xqr);
+        V4::get(*(const typename V4::raw *)(Xks + r * LDK + c0), xks);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          qt[j] = xqr[j] * fpre[j];
+          kt[i][j] = xks[j] * fsuf[j];
+          kgb[i][j] = xkr[j] * fpre[j];
+        }
+        // Qtil unit (row tile a, channel unit c0/KU): lane m + 16 g
+        const int u = c0 / KU, kin = c0 % KU;
+        const int gq = (kin & 15) / 4, eo = (kin >= 16) ? 4 : 0;
+        const int ln = (r & 15) + 16 * gq;
+        char *dst = blk + W.off_qt + ((size_t)(a * NKU + u) * 64 + ln) * 16 +
+                    eo * sizeof(IO);
+        *(typename V4::raw *)dst = V4::put(qt);
+        if (TPU == 2 && (NKT & 1) && c0 / 16 == NKT - 1) {
+          // odd number of 16-channel tiles: the missing upper half is zero
+          const float z[4] = {0.f, 0.f, 0.f, 0.f};
+          *(typename V4::raw *)(dst + 4 * sizeof(IO)) = V4::put(z);
+        }
+      }
+      // Ktil^T units (row tile = channel tile, k = tokens): per channel, the
+      // 8 tokens split into two runs of 4 consecutive k
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = c0 + j;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int rr = r0 + 4 * hh;  // first token of the run
+          const int u = rr / KU, kin = rr % KU;
+          const int gq = (kin & 15) / 4, eo = (kin >= 16) ? 4 : 0;
+          const int ln = (c & 15) + 16 * gq;
+          float v4[4] = {kt[4 * hh + 0][j], kt[4 * hh + 1][j],
+                         kt[4 * hh + 2][j], kt[4 * hh + 3][j]};
+          char *dst = blk + W.off_ktt + ((size_t)(ct * NTU + u) * 64 + ln) * 16 +
+                      eo * sizeof(IO);
+          *(typename V4::raw *)dst = V4::put(v4);
+          if (TPU == 2 && (NB & 1) && a == NB - 1) {
+            // odd number of sub-chunks: the missing upper half is zero
+            const float z[4] = {0.f, 0.f, 0.f, 0.f};
+            *(typename V4::raw *)(dst + 4 * sizeof(IO)) = V4::put(z);
+          }
+        }
+      }
+      if (a == NB - 1 && half == 1) {
+        *(f32x4 *)((float *)(blk + W.off_gam) + c0) =
+            f32x4{fpre[0] * F[0], fpre[1] * F[1], fpre[2] * F[2],
+                  fpre[3] * F[3]};
+      }
+    }
+    // mid products M_{b->a} = prod_{b<d<a} F_d for sub-chunk pairs a-b >= 2
+    if (L::NP2 > 0) {
+      for (int i = tid; i < L::NP2 * DK; i += PREP_THREADS) {
+        const int c = i % DK, pi = i / DK;
+        int aa = 2, bb = pi;
+        while (bb >= aa - 1) { bb -= aa - 1; ++aa; }
+        float mp = 1.f;
+        for (int d = bb + 1; d < aa; ++d) mp *= Fs[d * DK + c];
+        Mid[pi * DK + c] = mp;
+      }
+    }
+    __syncthreads();  // B2: region A complete
+
+    // stage the next task while this one runs on the matrix cores
+    if (task + (int)gridDim.x < ntask)
+      prep_load<IO, DK, C, CONV>(p, task + gridDim.x, st, tid);
+
+    if (fallback) {
+      // exact diagonal-block sums: task (sub-chunk a, column s, 16 channels)
+      const size_t tokb = (size_t)b * T;
+      for (int w = tid; w < NB * 16 * (DK / 16); w += PREP_THREADS) {
+        const int cg = w % (DK / 16), s = (w / (DK / 16)) % 16,
+                  aa = w / (16 * (DK / 16));
+        float pr[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) pr[c] = 1.f;
+        for (int r = s; r < 16; ++r) {
+          const int tr = t0 + 16 * aa + r;
+          const int trc = min(tr, T - 1);
+          float sa = 0.f, sp = 0.f;
+#pragma unroll
+          for (int c = 0; c < 16; ++c) {
+            const int ch = cg * 16 + c;
+            if (r > s) {
+              const size_t gi = ((tokb + trc) * H + h) * DK + ch;
+              const float gv = p.gate_bf16 ? (float)((const bf16 *)p.g)[gi]
+                                           : ((const float *)p.g)[gi];
+              pr[c] *= (tr < T) ? __expf(gv) : 1.f;
+            }
+            const float ks = to_f32(Kraw[(16 * aa + s) * LDK + ch]);
+            sa += to_f32(Kraw[(16 * aa + r) * LDK + ch]) * ks * pr[c];
+            sp += to_f32(Aq[(16 * aa + r) * LDK + ch]) * ks * pr[c];
+          }
+          const float br = (tr < T)
+              ? (p.gate_bf16 ? (float)((const bf16 *)p.beta)[(tokb + trc) * H + h]
+                             : ((const float *)p.beta)[(tokb + trc) * H + h])
+              : 0.f;
+          if (r > s) atomicAdd(&FbA[(aa * 16 + r) * 16 + s], br * sa);
+          atomicAdd(&FbP[(aa * 16 + r) * 16 + s], p.scale * sp);
+        }
+      }
+      __syncthreads();
+    }
+
+    // ---- AP: A^T and P^T sub-blocks on the matrix cores --------------------
+    for (int tk = wave; tk < NB * (NB + 1) / 2; tk += PREP_THREADS / 64) {
+      int aa = 0, bb = tk;
+      while (bb > aa) { bb -= aa + 1; ++aa; }
+      const bool diag = (aa == bb);
+      f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+      if (diag && fallback) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          accA[j] = FbA[(aa * 16 + m16) * 16 + 4 * g4 + j];
+          accP[j] = FbP[(aa * 16 + m16) * 16 + 4 * g4 + j];
+        }
+      } else {
+        const IO *cb = (diag ? Xkir : Xks) + (16 * bb + m16) * LDK;
+        const IO *kb = Xkr + (16 * aa + m16) * LDK;
+        const IO *qb = Xqr + (16 * aa + m16) * LDK;
+        const float *mid = (aa - bb >= 2) ? Mid + L::p2(aa, bb) * DK : nullptr;
+#pragma unroll
+        for (int u = 0; u < NKU; ++u) {
+          const bool full = (TPU == 1) || (TPU * u + 1 < NKT);
+          frag cf = M::load_k(cb + KU * u, g4, full);
+          if (mid) {
+#pragma unroll
+            for (int ee = 0; ee < M::NE; ++ee) {
+              const int kx = KU * u + M::koff(g4, ee);
+              if (kx < DK) M::set(cf, ee, M::elem(cf, ee) * mid[kx]);
+            }
+          }
+          accA = M::mma(cf, M::load_k(kb + KU * u, g4, full), accA);
+          accP = M::mma(cf, M::load_k(qb + KU * u, g4, full), accP);
+        }
+      }
+      // lane (n = m16, g4): element j is row r = 16aa + m16, col s = 16bb+4g4+j
+      if (diag) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int s = 4 * g4 + j;
+          if (!(s < m16)) accA[j] = 0.f;
+          if (!(s <= m16)) accP[j] = 0.f;
+        }
+      }
+      *(f32x4 *)(Af + (16 * aa + m16) * LDA + 16 * bb + 4 * g4) = accA;
+      {
+        const int u = bb / TPU, hf = bb % TPU;
+        IO *dst = (IO *)(blk + W.off_p + ((size_t)(aa * NTU + u) * 64 + lane) *
+                                             16) + hf * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[j] = from_f32<IO>(accP[j]);
+        if (TPU == 2 && diag && (aa % 2) == 0) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dst[4 + j] = from_f32<IO>(0.f);
+        }
+      }
+    }
+    __syncthreads();  // B3: region A no longer read
+
+    // ---- T0: W/U inputs into the freed region, T zero-filled --------------
+    for (int i = tid; i < C * LDC; i += PREP_THREADS) Tb[i] = from_f32<IO>(0.f);
+    if (kthr) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float lo[4] = {kgb[0][j], kgb[1][j], kgb[2][j], kgb[3][j]};
+        float hi[4] = {kgb[4][j], kgb[5][j], kgb[6][j], kgb[7][j]};
+        IO *row = XkgT + (c0 + j) * LDC + r0;
+        *(typename V4::raw *)row = V4::put(lo);
+        *(typename V4::raw *)(row + 4) = V4::put(hi);
+      }
+    }
+    if (vthr) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float lo[4] = {bv[0][j], bv[1][j], bv[2][j], bv[3][j]};
+        float hi[4] = {bv[4][j], bv[5][j], bv[6][j], bv[7][j]};
+        IO *row = XvT + (4 * cv + j) * LDC + 8 * tgv;
+        *(typename V4::raw *)row = V4::put(lo);
+        *(typename V4::raw *)(row + 4) = V4::put(hi);
+      }
+    }
+    __syncthreads();  // B4
+
+    // ---- T1: inverse of each unit-lower 16x16 diagonal block (fp32) ------
+    if (tid < 16 * NB) {
+      const int aa = tid / 16, s = tid % 16;
+      float col[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float acc = 0.f;
+        const float *arow = Af + (16 * aa + r) * LDA + 16 * aa;
+#pragma unroll
+        for (int cc = 0; cc < r; ++cc) acc += arow[cc] * col[cc];
+        col[r] = (r == s) ? 1.f : ((r < s) ? 0.f : -acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        Tt[(16 * aa + s) * LDA + 16 * aa + r] = col[r];
+        Taa[(aa * 16 + r) * 16 + s] = col[r];
+        Tb[(16 * aa + r) * LDC + 16 * aa + s] = from_f32<IO>(col[r]);
+      }
+    }
+    __syncthreads();
+    // ---- T2: off-diagonal blocks, one block-diagonal at a time -------------
+    //   T_ab = -T_aa * sum_{c=b}^{a-1} A_ac T_cb   (fp32 matrix cores)
+    for (int d = 1; d < NB; ++d) {
+      for (int tk = wave; tk < NB - d; tk += PREP_THREADS / 64) {
+        const int aa = d + tk, bb = tk;
+        f32x4 X = {0.f, 0.f, 0.f, 0.f};
+        for (int cc = bb; cc < aa; ++cc) {
+          const f32x4 af = *(const f32x4 *)(Af + (16 * aa + m16) * LDA +
+                                            16 * cc + 4 * g4);
+          const f32x4 tf = *(const f32x4 *)(Tt + (16 * bb + m16) * LDA +
+                                            16 * cc + 4 * g4);
+          X = mma16_f32(af, tf, X);
+        }
+        const f32x4 ta = *(const f32x4 *)(Taa + (aa * 16 + m16) * 16 + 4 * g4);
+        const f32x4 Tn = -mma16_f32(ta, X, f32x4{0.f, 0.f, 0.f, 0.f});
+        // lane (n = m16, g4) holds T_ab[4g4 + j][m16]
+        *(f32x4 *)(Tt + (16 * bb + m16) * LDA + 16 * aa + 4 * g4) = Tn;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          Tb[(16 * aa + 4 * g4 + j) * LDC + 16 * bb + m16] = from_f32<IO>(Tn[j]);
+      }
+      __syncthreads();
+    }
+
+    // ---- WU: -W (A-operand units) and U (accumulator tiles) ----------------
+    const int nW = NB * NKU, nU = NB * nvt;
+    for (int tk = wave; tk < nW + nU; tk += PREP_THREADS / 64) {
+      if (tk < nW) {
+        const int rt = tk / NKU, u = tk % NKU;
+        f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        const int umax = (16 * rt + 15) / KU;
+        for (int uu = 0; uu <= umax; ++uu) {
+          const bool fullT = (TPU == 1) || (TPU * uu + 1 < NB);
+          const frag tb = M::load_k(Tb + (16 * rt + m16) * LDC + KU * uu, g4,
+                                    fullT);
+#pragma unroll
+          for (int hh = 0; hh < TPU; ++hh) {
+            const int ct = TPU * u + hh;
+            if (ct < NKT) {
+              const frag xa = M::load_k(XkgT + (16 * ct + m16) * LDC + KU * uu,
+                                        g4, fullT);
+              acc[hh] = M::mma(xa, tb, acc[hh]);
+            }
+          }
+        }
+        const frag out = M::pack(-acc[0], -acc[1]);
+        *(frag *)(blk + W.off_negw + ((size_t)(rt * NKU + u) * 64 + lane) *
+                                         16) = out;
+      } else {
+        const int t2 = tk - nW, rt = t2 / nvt, vt = t2 % nvt;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const int umax = (16 * rt + 15) / KU;
+        for (int uu = 0; uu <= umax; ++uu) {
+          const bool fullT = (TPU == 1) || (TPU * uu + 1 < NB);
+          const frag ta = M::load_k(Tb + (16 * rt + m16) * LDC + KU * uu, g4,
+                                    fullT);
+          const frag vb = M::load_k(XvT + (16 * vt + m16) * LDC + KU * uu, g4,
+                                    fullT);
+          acc = M::mma(ta, vb, acc);
+        }
+        IO *dst = (IO *)(blk + W.off_u) +
+                  ((size_t)(vt * NB + rt) * 64 + lane) * 4;
+        float a4[4] = {acc[0], acc[1], acc[2], acc[3]};
+        *(typename V4::raw *)dst = V4::put(a4);
+      }
+    }
+    __syncthreads();  // B5: LDS free for the next task
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <typename IO, int DK, int C>
+struct Fits {
+  static constexpr bool value = PL<IO, DK, C>::total <= 160 * 1024;
+};
+
+static int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+          hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+template <typename IO, int DK, int C>
+static hipError_t prep_one(const PrefillParams &p, hipStream_t s) {
+  if constexpr (!Fits<IO, DK, C>::value) {
+    return hipErrorInvalidValue;
+  } else {
+    const long long ntask = (long long)p.B * p.H * p.NC;
+    const unsigned grid = (unsigned)std::min<long long>(ntask, cu_count());
+    if (p.use_conv)
+      hipLaunchKernelGGL((kda_chunk_prep<IO, DK, C, true>), dim3(grid),
+                         dim3(PREP_THREADS), 0, s, p);
+    else
+      hipLaunchKernelGGL((kda_chunk_prep<IO, DK, C, false>), dim3(grid),
+                         dim3(PREP_THREADS), 0, s, p);
+    return hipGetLastError();
+  }
+}
+
+template <typename IO>
+static hipError_t prep_dk(const PrefillParams &p, hipStream_t s) {
+  switch (p.Dk * 1000 + p.C) {
+    case 16016: return prep_one<IO, 16, 16>(p, s);
+    case 16032: return prep_one<IO, 16, 32>(p, s);
+    case 16064: return prep_one<IO, 16, 64>(p, s);
+    case 32016: return prep_one<IO, 32, 16>(p, s);
+    case 32032: return prep_one<IO, 32, 32>(p, s);
+    case 32064: return prep_one<IO, 32, 64>(p, s);
+    case 64016: return prep_one<IO, 64, 16>(p, s);
+    case 64032: return prep_one<IO, 64, 32>(p, s);
+    case 64064: return prep_one<IO, 64, 64>(p, s);
+    case 128016: return prep_one<IO, 128, 16>(p, s);
+    case 128032: return prep_one<IO, 128, 32>(p, s);
+    case 128064: return prep_one<IO, 128, 64>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_prep(const PrefillParams &p, int io_bf16,
+                               hipStream_t s) {
+  return io_bf16 ? prep_dk<bf16>(p, s) : prep_dk<float>(p, s);
+}
+
+}  // namespace kda
