@@ -159,7 +159,8 @@ def main():
         flops = prefill_flops(B, T, H, Dk, Dv, C)
         t_k = (tp + ts) * 1e-3
         gbs = byts / t_k / 1e9
-        srcs = ["kda_prep.hip", "kda_state.hip", "kda_device.h"]
+        srcs = ["kda_prep_impl.h", "kda_prep_bf16_f32.hip", "kda_state.hip",
+                "kda_device.h"]
         tr_p = traffic_for("kda_chunk_prep", srcs)
         tr_s = traffic_for("kda_state_pass", srcs)
         out["prefill"] = dict(

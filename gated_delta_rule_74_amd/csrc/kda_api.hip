@@ -84,6 +84,15 @@ size_t ws_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
 
 }  // namespace
 
+namespace kda {
+hipError_t launch_prefill_prep(const PrefillParams &p, int io_bf16,
+                               hipStream_t s) {
+  if (!io_bf16) return launch_prefill_prep_f32(p, s);
+  return p.gate_bf16 ? launch_prefill_prep_bf16_bf16(p, s)
+                     : launch_prefill_prep_bf16_f32(p, s);
+}
+}  // namespace kda
+
 extern "C" {
 
 int kda_abi_version(void) { return KDA_ABI_VERSION; }

@@ -45,6 +45,11 @@ struct ConvParams {
 
 hipError_t launch_prefill_prep(const PrefillParams &p, int io_bf16,
                                hipStream_t s);
+// per dtype pair (q/k/v, g/beta); launch_prefill_prep picks one
+hipError_t launch_prefill_prep_f32(const PrefillParams &p, hipStream_t s);
+hipError_t launch_prefill_prep_bf16_f32(const PrefillParams &p, hipStream_t s);
+hipError_t launch_prefill_prep_bf16_bf16(const PrefillParams &p,
+                                         hipStream_t s);
 hipError_t launch_state_pass(const PrefillParams &p, int io_bf16,
                              hipStream_t s);
 hipError_t launch_decode(const DecodeParams &p, int io_bf16, hipStream_t s);

@@ -28,6 +28,7 @@
 // 8 consecutive tokens of a task; its raw inputs are fetched with 8/16-byte
 // vector loads into registers one task ahead, so the fetch of task i+1
 // overlaps the matrix-core phases of task i.
+#pragma once
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -108,10 +109,11 @@ template <typename IO, bool CONV> struct Stage {
   uint32_t beta[8], betav[8];
 };
 
-template <typename IO, int DK, int C, bool CONV>
+template <typename IO, typename GT, int DK, int C, bool CONV>
 __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
                                           Stage<IO, CONV> &st, int tid) {
   constexpr int NQ = DK / 4, NTG = C / 8;
+  constexpr bool GB = sizeof(GT) == 2;  // bf16 gates
   typedef typename Vec4<IO>::raw R;
   const int BH = p.B * p.H;
   const int bh = task % BH, n = task / BH;
@@ -132,7 +134,7 @@ __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const unsigned t = (unsigned)min(t0 + 8 * tg + i, tlast);
-      if (p.gate_bf16) {
+      if (GB) {
         const uint2 v = *(const uint2 *)(gh + t * rowK);
         st.g[i] = make_uint4(v.x, v.y, 0u, 0u);
         st.beta[i] = bh16[t * H];
@@ -168,7 +170,7 @@ __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const unsigned t = (unsigned)min(t0 + 8 * tg + i, tlast);
-      st.betav[i] = p.gate_bf16 ? (uint32_t)bh16[t * H]
+      st.betav[i] = GB ? (uint32_t)bh16[t * H]
                                 : __float_as_uint(bf[t * H]);
     }
   }
@@ -185,7 +187,7 @@ __device__ __forceinline__ void load_taps(const float *w, int W, float t[4][4]) 
     }
 }
 
-template <typename IO, int DK, int C, bool CONV>
+template <typename IO, typename GT, int DK, int C, bool CONV>
 __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     PrefillParams p) {
   using L = PL<IO, DK, C>;
@@ -197,6 +199,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
                 LDA = L::LDA;
   constexpr int NQ = DK / 4, NTG = C / 8, XR = Stage<IO, CONV>::XR;
   constexpr int XO = CONV ? 3 : 0;  // first own row inside the x window
+  constexpr bool GB = sizeof(GT) == 2;  // bf16 gates
 
   __shared__ __attribute__((aligned(16))) char sm[L::total];
   IO *Xkr = (IO *)(sm + L::oKR), *Xqr = (IO *)(sm + L::oQR);
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
 
   Stage<IO, CONV> st;
   int task = blockIdx.x;
-  if (task < ntask) prep_load<IO, DK, C, CONV>(p, task, st, tid);
+  if (task < ntask) prep_load<IO, GT, DK, C, CONV>(p, task, st, tid);
 
   for (; task < ntask; task += gridDim.x) {
     const int bh = task % BH, n = task / BH;
@@ -246,7 +249,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
       for (int i = 0; i < 8; ++i) {
         const bool ok = t0 + r0 + i < T;
         float gv[4];
-        if (p.gate_bf16) {
+        if (GB) {
           Vec4<bf16>::get(make_uint2(st.g[i].x, st.g[i].y), gv);
           bt[i] = ok ? __uint_as_float(st.beta[i] << 16) : 0.f;
         } else {
@@ -374,7 +377,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const bool ok = t0 + 8 * tgv + i < T;
-        const float bb = p.gate_bf16 ? __uint_as_float(st.betav[i] << 16)
+        const float bb = GB ? __uint_as_float(st.betav[i] << 16)
                                      : __uint_as_float(st.betav[i]);
         bvt[i] = ok ? bb : 0.f;
       }
@@ -432,13 +435,21 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
       }
       const int ct = c0 / 16;
       float kt[8][4];
+      typename V4::raw rkr[8], rqr[8], rks[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = r0 + i;
+        rkr[i] = *(const typename V4::raw *)(Xkr + r * LDK + c0);
+        rqr[i] = *(const typename V4::raw *)(Xqr + r * LDK + c0);
+        rks[i] = *(const typename V4::raw *)(Xks + r * LDK + c0);
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int r = r0 + i;
         float xkr[4], xqr[4], xks[4], qt[4];
-        V4::get(*(const typename V4::raw *)(Xkr + r * LDK + c0), xkr);
-        V4::get(*(const typename V4::raw *)(Xqr + r * LDK + c0), xqr);
-        V4::get(*(const typename V4::raw *)(Xks + r * LDK + c0), xks);
+        V4::get(rkr[i], xkr);
+        V4::get(rqr[i], xqr);
+        V4::get(rks[i], xks);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           qt[j] = xqr[j] * fpre[j];
@@ -502,7 +513,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
 
     // stage the next task while this one runs on the matrix cores
     if (task + (int)gridDim.x < ntask)
-      prep_load<IO, DK, C, CONV>(p, task + gridDim.x, st, tid);
+      prep_load<IO, GT, DK, C, CONV>(p, task + gridDim.x, st, tid);
 
     if (fallback) {
       // exact diagonal-block sums: task (sub-chunk a, column s, 16 channels)
@@ -522,7 +533,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
             const int ch = cg * 16 + c;
             if (r > s) {
               const size_t gi = ((tokb + trc) * H + h) * DK + ch;
-              const float gv = p.gate_bf16 ? (float)((const bf16 *)p.g)[gi]
+              const float gv = GB ? (float)((const bf16 *)p.g)[gi]
                                            : ((const float *)p.g)[gi];
               pr[c] *= (tr < T) ? __expf(gv) : 1.f;
             }
@@ -531,7 +542,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
             sp += to_f32(Aq[(16 * aa + r) * LDK + ch]) * ks * pr[c];
           }
           const float br = (tr < T)
-              ? (p.gate_bf16 ? (float)((const bf16 *)p.beta)[(tokb + trc) * H + h]
+              ? (GB ? (float)((const bf16 *)p.beta)[(tokb + trc) * H + h]
                              : ((const float *)p.beta)[(tokb + trc) * H + h])
               : 0.f;
           if (r > s) atomicAdd(&FbA[(aa * 16 + r) * 16 + s], br * sa);
@@ -558,19 +569,25 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
         const IO *kb = Xkr + (16 * aa + m16) * LDK;
         const IO *qb = Xqr + (16 * aa + m16) * LDK;
         const float *mid = (aa - bb >= 2) ? Mid + L::p2(aa, bb) * DK : nullptr;
+        frag cf[NKU], kf[NKU], qf[NKU];
 #pragma unroll
         for (int u = 0; u < NKU; ++u) {
           const bool full = (TPU == 1) || (TPU * u + 1 < NKT);
-          frag cf = M::load_k(cb + KU * u, g4, full);
+          cf[u] = M::load_k(cb + KU * u, g4, full);
+          kf[u] = M::load_k(kb + KU * u, g4, full);
+          qf[u] = M::load_k(qb + KU * u, g4, full);
+        }
+#pragma unroll
+        for (int u = 0; u < NKU; ++u) {
           if (mid) {
 #pragma unroll
             for (int ee = 0; ee < M::NE; ++ee) {
               const int kx = KU * u + M::koff(g4, ee);
-              if (kx < DK) M::set(cf, ee, M::elem(cf, ee) * mid[kx]);
+              if (kx < DK) M::set(cf[u], ee, M::elem(cf[u], ee) * mid[kx]);
             }
           }
-          accA = M::mma(cf, M::load_k(kb + KU * u, g4, full), accA);
-          accP = M::mma(cf, M::load_k(qb + KU * u, g4, full), accP);
+          accA = M::mma(cf[u], kf[u], accA);
+          accP = M::mma(cf[u], qf[u], accP);
         }
       }
       // lane (n = m16, g4): element j is row r = 16aa + m16, col s = 16bb+4g4+j
@@ -672,18 +689,26 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
         const int rt = tk / NKU, u = tk % NKU;
         f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         const int umax = (16 * rt + 15) / KU;
-        for (int uu = 0; uu <= umax; ++uu) {
-          const bool fullT = (TPU == 1) || (TPU * uu + 1 < NB);
-          const frag tb = M::load_k(Tb + (16 * rt + m16) * LDC + KU * uu, g4,
-                                    fullT);
+        frag tb[NTU], xa[NTU][TPU];
 #pragma unroll
-          for (int hh = 0; hh < TPU; ++hh) {
-            const int ct = TPU * u + hh;
-            if (ct < NKT) {
-              const frag xa = M::load_k(XkgT + (16 * ct + m16) * LDC + KU * uu,
-                                        g4, fullT);
-              acc[hh] = M::mma(xa, tb, acc[hh]);
+        for (int uu = 0; uu < NTU; ++uu) {
+          if (uu <= umax) {
+            const bool fullT = (TPU == 1) || (TPU * uu + 1 < NB);
+            tb[uu] = M::load_k(Tb + (16 * rt + m16) * LDC + KU * uu, g4, fullT);
+#pragma unroll
+            for (int hh = 0; hh < TPU; ++hh) {
+              const int ct = (TPU * u + hh) % NKT;
+              xa[uu][hh] = M::load_k(XkgT + (16 * ct + m16) * LDC + KU * uu, g4,
+                                     fullT);
             }
+          }
+        }
+#pragma unroll
+        for (int uu = 0; uu < NTU; ++uu) {
+          if (uu <= umax) {
+#pragma unroll
+            for (int hh = 0; hh < TPU; ++hh)
+              if (TPU * u + hh < NKT) acc[hh] = M::mma(xa[uu][hh], tb[uu], acc[hh]);
           }
         }
         const frag out = M::pack(-acc[0], -acc[1]);
@@ -693,14 +718,18 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
         const int t2 = tk - nW, rt = t2 / nvt, vt = t2 % nvt;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         const int umax = (16 * rt + 15) / KU;
-        for (int uu = 0; uu <= umax; ++uu) {
-          const bool fullT = (TPU == 1) || (TPU * uu + 1 < NB);
-          const frag ta = M::load_k(Tb + (16 * rt + m16) * LDC + KU * uu, g4,
-                                    fullT);
-          const frag vb = M::load_k(XvT + (16 * vt + m16) * LDC + KU * uu, g4,
-                                    fullT);
-          acc = M::mma(ta, vb, acc);
+        frag ta[NTU], vb[NTU];
+#pragma unroll
+        for (int uu = 0; uu < NTU; ++uu) {
+          if (uu <= umax) {
+            const bool fullT = (TPU == 1) || (TPU * uu + 1 < NB);
+            ta[uu] = M::load_k(Tb + (16 * rt + m16) * LDC + KU * uu, g4, fullT);
+            vb[uu] = M::load_k(XvT + (16 * vt + m16) * LDC + KU * uu, g4, fullT);
+          }
         }
+#pragma unroll
+        for (int uu = 0; uu < NTU; ++uu)
+          if (uu <= umax) acc = M::mma(ta[uu], vb[uu], acc);
         IO *dst = (IO *)(blk + W.off_u) +
                   ((size_t)(vt * NB + rt) * 64 + lane) * 4;
         float a4[4] = {acc[0], acc[1], acc[2], acc[3]};
@@ -726,7 +755,7 @@ static int cu_count() {
   return n;
 }
 
-template <typename IO, int DK, int C>
+template <typename IO, typename GT, int DK, int C>
 static hipError_t prep_one(const PrefillParams &p, hipStream_t s) {
   if constexpr (!Fits<IO, DK, C>::value) {
     return hipErrorInvalidValue;
@@ -734,37 +763,32 @@ static hipError_t prep_one(const PrefillParams &p, hipStream_t s) {
     const long long ntask = (long long)p.B * p.H * p.NC;
     const unsigned grid = (unsigned)std::min<long long>(ntask, cu_count());
     if (p.use_conv)
-      hipLaunchKernelGGL((kda_chunk_prep<IO, DK, C, true>), dim3(grid),
+      hipLaunchKernelGGL((kda_chunk_prep<IO, GT, DK, C, true>), dim3(grid),
                          dim3(PREP_THREADS), 0, s, p);
     else
-      hipLaunchKernelGGL((kda_chunk_prep<IO, DK, C, false>), dim3(grid),
+      hipLaunchKernelGGL((kda_chunk_prep<IO, GT, DK, C, false>), dim3(grid),
                          dim3(PREP_THREADS), 0, s, p);
     return hipGetLastError();
   }
 }
 
-template <typename IO>
+template <typename IO, typename GT>
 static hipError_t prep_dk(const PrefillParams &p, hipStream_t s) {
   switch (p.Dk * 1000 + p.C) {
-    case 16016: return prep_one<IO, 16, 16>(p, s);
-    case 16032: return prep_one<IO, 16, 32>(p, s);
-    case 16064: return prep_one<IO, 16, 64>(p, s);
-    case 32016: return prep_one<IO, 32, 16>(p, s);
-    case 32032: return prep_one<IO, 32, 32>(p, s);
-    case 32064: return prep_one<IO, 32, 64>(p, s);
-    case 64016: return prep_one<IO, 64, 16>(p, s);
-    case 64032: return prep_one<IO, 64, 32>(p, s);
-    case 64064: return prep_one<IO, 64, 64>(p, s);
-    case 128016: return prep_one<IO, 128, 16>(p, s);
-    case 128032: return prep_one<IO, 128, 32>(p, s);
-    case 128064: return prep_one<IO, 128, 64>(p, s);
+    case 16016: return prep_one<IO, GT, 16, 16>(p, s);
+    case 16032: return prep_one<IO, GT, 16, 32>(p, s);
+    case 16064: return prep_one<IO, GT, 16, 64>(p, s);
+    case 32016: return prep_one<IO, GT, 32, 16>(p, s);
+    case 32032: return prep_one<IO, GT, 32, 32>(p, s);
+    case 32064: return prep_one<IO, GT, 32, 64>(p, s);
+    case 64016: return prep_one<IO, GT, 64, 16>(p, s);
+    case 64032: return prep_one<IO, GT, 64, 32>(p, s);
+    case 64064: return prep_one<IO, GT, 64, 64>(p, s);
+    case 128016: return prep_one<IO, GT, 128, 16>(p, s);
+    case 128032: return prep_one<IO, GT, 128, 32>(p, s);
+    case 128064: return prep_one<IO, GT, 128, 64>(p, s);
   }
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_prefill_prep(const PrefillParams &p, int io_bf16,
-                               hipStream_t s) {
-  return io_bf16 ? prep_dk<bf16>(p, s) : prep_dk<float>(p, s);
 }
 
 }  // namespace kda
