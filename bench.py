@@ -1,7 +1,8 @@
 """Benchmark of the KDA forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
-                    [--no-cpu] [--only prefill|decode|conv|long]
+                    [--no-cpu] [--only prefill,decode,conv,long,copy]
+                    [--decode-steps N]
 
 Headline (`value`): chunked prefill tokens/s on the model-shaped workload
 B=1, T=8192, H=32, d_k=d_v=128, chunk 64, bf16 q/k/v, fp32 g/beta/state
@@ -90,8 +91,19 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default=None,
-                    choices=[None, "prefill", "decode", "conv", "long"])
+                    help="comma list of: prefill, decode, conv, long, copy "
+                         "(copy = a plain 1 GiB device copy, the reference "
+                         "for scaling HBM byte counters)")
+    ap.add_argument("--decode-steps", type=int, default=None,
+                    help="time fewer decode steps than the workload's 1000 "
+                         "(profiling runs)")
     args = ap.parse_args()
+    only = None if args.only is None else set(args.only.split(","))
+    bad = (only or set()) - {"prefill", "decode", "conv", "long", "copy"}
+    if bad:
+        ap.error(f"unknown --only part(s): {sorted(bad)}")
+    sel = lambda part: (only is None and part != "copy") or \
+        (only is not None and part in only)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for "
               f"--gpus {args.gpus}); the multi-GPU design is described in "
@@ -116,7 +128,7 @@ def main():
     # ---------------- prefill, model-shaped (headline) ----------------------
     c1 = ki.CONFIGS[1]
     B, T, H, Dk, Dv, C = (c1[n] for n in ("B", "T", "H", "Dk", "Dv", "chunk"))
-    run_prefill = args.only in (None, "prefill")
+    run_prefill = sel("prefill")
     if run_prefill:
         log("prefill: generating inputs")
         x = ki.config_prefill_inputs(1, device=dev)
@@ -196,10 +208,12 @@ def main():
         torch.cuda.empty_cache()
 
     # ---------------- decode workload ---------------------------------------
-    if args.only in (None, "decode") and not args.no_extra:
+    if sel("decode") and not args.no_extra:
         c3 = ki.CONFIGS[3]
         N, H3, D3, steps = c3["N"], c3["H"], c3["Dk"], c3["steps"]
-        log("decode: generating 1000 steps of inputs")
+        if args.decode_steps:
+            steps = max(1, min(steps, args.decode_steps))
+        log(f"decode: generating {steps} steps of inputs")
         st = ki.decode_state(N, H3, D3, D3, std=c3["state_std"], device=dev)
         xs = [ki.decode_step_inputs(N, H3, D3, D3, i, device=dev)
               for i in range(steps)]
@@ -235,7 +249,7 @@ def main():
     # ---------------- fused-conv prefill and long context -------------------
     extra = {}
     for cid, tag in ((2, "conv"), (4, "long")):
-        if args.no_extra or args.only not in (None, tag):
+        if args.no_extra or not sel(tag):
             continue
         c = ki.CONFIGS[cid]
         log(f"{tag}: generating inputs")
@@ -275,6 +289,26 @@ def main():
         del x, ws, o, s
         torch.cuda.empty_cache()
 
+    # ---------------- copy reference for the byte counters -----------------
+    if only is not None and "copy" in only:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b2 = torch.empty_like(a)
+        for _ in range(3):
+            b2.copy_(a)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        b2.copy_(a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        out["copy"] = dict(bytes_read=n, bytes_written=n, ms=ms,
+                           gbs=2 * n / (ms * 1e-3) / 1e9)
+        log(f"copy: 1 GiB in {ms:.3f} ms, {2 * n / (ms * 1e-3) / 1e9:.0f} "
+            "GB/s read+write")
+        del a, b2
+
     pf = out.get("prefill")
     line = {
         "metric": METRIC,
@@ -300,6 +334,8 @@ def main():
         "decode": out.get("decode"),
         "extra": extra,
     }
+    if "copy" in out:
+        line["copy"] = out["copy"]
     print(json.dumps(line), flush=True)
 
 

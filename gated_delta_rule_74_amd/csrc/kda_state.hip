@@ -2,286 +2,359 @@
 //
 // Given the chunk-local factors that kda_chunk_prep leaves in the workspace
 // (per (batch*head, chunk): -W, Qtil = scale Q*Gam, Ktil^T, P, Gam_C, U; see
-// kda_prep.hip for their definitions), each chunk n updates
+// kda_prep_impl.h for their definitions), each chunk n updates
 //   Delta = U - W S,   O = Qtil S + P Delta,   S <- diag(Gam_C) S + Ktil^T Delta
 // in order, which is the chunked form of the per-token KDA rule (state rows
 // are key channels; see include/kda.h for the sources).
+//
+// Work split.  A workgroup of four waves owns one (batch*head) and NS
+// consecutive 16-column value slabs.  Every product is split by its output
+// rows, so each wave reads only its own share of the chunk's factors:
+//   * Delta and O: wave w computes token tile w (16 tokens) from its rows of
+//     -W, Qtil, P and U;
+//   * S: wave w owns the state rows of key unit w (32 keys in bf16, 16 in
+//     fp32; units w, w+4, ... when there are more than four) and updates
+//     them from its rows of Ktil^T.
+// The products need the whole S (for Delta and O) and the whole Delta (for
+// S and O) as the second operand, so both are exchanged through LDS in the
+// matrix-core operand layout: two barriers per chunk.  O is produced
+// transposed (O^T = S^T Qtil^T + Delta^T P^T) so that each lane ends up with
+// four consecutive value columns of one token: one vector store per slab.
+//
+// Each wave fetches its factors straight from global memory into registers
+// PD = 3 chunks ahead (three rotating register sets), so the HBM latency of
+// the factors overlaps the two chunk steps before their use; only the
+// exchange round trips and the short MFMA chains sit on the sequential path.
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 
-// ---------------------------------------------------------------------------
-// Sequential state pass.  A workgroup of NW waves owns one (batch*head) and
-// NW consecutive 16-column value slabs; wave w carries the state columns of
-// slab w in registers as accumulator tiles.  Per chunk, the workgroup needs
-// the shared range of the chunk's workspace block plus its own U tiles
-// (about 66 KB for d = 128, C = 64, NW = 4).  They reach LDS through a
-// register-staged pipeline two chunks deep: at chunk n every thread issues
-// the loads of chunk n+2 into one register set, computes chunk n from LDS,
-// and then writes the other register set (chunk n+1, loaded one chunk
-// earlier) into the free LDS buffer.  Only the MFMA chain and its LDS reads
-// sit on the sequential path.
 template <typename IO> struct Vec4T;
 template <> struct Vec4T<bf16> {
   typedef uint2 raw;
-  __device__ static __forceinline__ void get(raw r, float *f) {
-    f[0] = __uint_as_float(r.x << 16);
-    f[1] = __uint_as_float(r.x & 0xffff0000u);
-    f[2] = __uint_as_float(r.y << 16);
-    f[3] = __uint_as_float(r.y & 0xffff0000u);
+  __device__ static __forceinline__ f32x4 get(raw r) {
+    return f32x4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                 __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u)};
+  }
+  __device__ static __forceinline__ raw put(f32x4 f) {
+    bf16x4 v = {(bf16)f[0], (bf16)f[1], (bf16)f[2], (bf16)f[3]};
+    return __builtin_bit_cast(raw, v);
   }
 };
 template <> struct Vec4T<float> {
   typedef uint4 raw;
-  __device__ static __forceinline__ void get(raw r, float *f) {
-    f[0] = __uint_as_float(r.x);
-    f[1] = __uint_as_float(r.y);
-    f[2] = __uint_as_float(r.z);
-    f[3] = __uint_as_float(r.w);
+  __device__ static __forceinline__ f32x4 get(raw r) {
+    return f32x4{__uint_as_float(r.x), __uint_as_float(r.y),
+                 __uint_as_float(r.z), __uint_as_float(r.w)};
+  }
+  __device__ static __forceinline__ raw put(f32x4 f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
+                      __float_as_uint(f[2]), __float_as_uint(f[3]));
   }
 };
 
-template <typename IO, int DK, int C, int NW>
-struct StateCfg {
-  static constexpr size_t SH = ws_shared_bytes(DK, C, (int)sizeof(IO));
-  static constexpr size_t UB = (size_t)(C / 16) * 64 * 4 * sizeof(IO);
-  static constexpr size_t TOT = SH + NW * UB;         // bytes per chunk
-  static constexpr int NL = 2;                        // loader waves
-  static constexpr int NKB = (int)((TOT + 1023) / 1024);   // 1 KiB copies
-  static constexpr int CPW = (NKB + NL - 1) / NL;     // copies per loader
-  static constexpr int NLINE = (int)((SH + 127) / 128 + NW * UB / 128);
-  static constexpr int TPW = (NLINE + 64 * NL - 1) / (64 * NL);  // touches
-  static constexpr int PF = 3;                        // touch distance
-  static constexpr size_t BUF = (size_t)NKB * 1024;
-  static constexpr size_t LDS = 2 * BUF + NL * 256;   // + touch sink
-  static constexpr bool fits = LDS <= 160 * 1024;
+// LDS writes done, then the workgroup barrier; outstanding global loads stay
+// in flight across it
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+constexpr int STATE_WAVES = 4;
+
+template <typename IO, int DK, int C, int NS> struct SP {
+  static constexpr int TPU = Mma<IO>::TPU;
+  static constexpr int NB = C / 16, NKT = DK / 16;
+  static constexpr int NKU = (NKT + TPU - 1) / TPU;  // key units
+  static constexpr int NTU = (NB + TPU - 1) / TPU;   // token units
+  static constexpr int KUW = (NKU + STATE_WAVES - 1) / STATE_WAVES;
+  static constexpr size_t oSU = 0;                          // [NS][NKU]
+  static constexpr size_t oDU = (size_t)NS * NKU * 1024;    // [NS][NTU]
+  static constexpr size_t LDS = oDU + (size_t)NS * NTU * 1024;
 };
 
-__device__ __forceinline__ void dma16(const char *src, char *dst_wave) {
-  __builtin_amdgcn_global_load_lds(
-      (const void *)src, (__attribute__((address_space(3))) void *)dst_wave,
-      16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const char *src, char *dst_wave) {
-  __builtin_amdgcn_global_load_lds(
-      (const void *)src, (__attribute__((address_space(3))) void *)dst_wave,
-      4, 0, 0);
+// one wave's factors of one chunk
+template <typename IO, int DK, int C, int NS> struct FragSet {
+  using G = SP<IO, DK, C, NS>;
+  typedef typename Mma<IO>::frag frag;
+  frag w[G::NKU], q[G::NKU], p[G::NTU];
+  frag k[G::KUW][G::TPU][G::NTU];
+  f32x4 gm[G::KUW][G::TPU];
+  typename Vec4T<IO>::raw u[NS];
+};
+
+template <typename IO, int DK, int C, int NS>
+__device__ __forceinline__ void load_frags(FragSet<IO, DK, C, NS> &f,
+                                           const char *blk, const WsLayout &W,
+                                           int rtc, int wave, int lane,
+                                           int g4, int vt0) {
+  using G = SP<IO, DK, C, NS>;
+  typedef typename Mma<IO>::frag frag;
+  typedef typename Vec4T<IO>::raw URaw;
+  const frag *Lw = (const frag *)(blk + W.off_negw) + lane;
+  const frag *Lq = (const frag *)(blk + W.off_qt) + lane;
+  const frag *Lk = (const frag *)(blk + W.off_ktt) + lane;
+  const frag *Lp = (const frag *)(blk + W.off_p) + lane;
+  const URaw *Lu = (const URaw *)(blk + W.off_u) + lane;
+  const float *Lg = (const float *)(blk + W.off_gam) + 4 * g4;
+#pragma unroll
+  for (int u = 0; u < G::NKU; ++u) f.w[u] = Lw[(rtc * G::NKU + u) * 64];
+#pragma unroll
+  for (int u = 0; u < G::NKU; ++u) f.q[u] = Lq[(rtc * G::NKU + u) * 64];
+  // P units above the diagonal are never written by the prep: their bits
+  // are cleared so the product can run unconditionally
+#pragma unroll
+  for (int u = 0; u < G::NTU; ++u) {
+    const unsigned keep = (G::NTU == 1 || u <= rtc / G::TPU) ? ~0u : 0u;
+    uint4 r = __builtin_bit_cast(uint4, Lp[(rtc * G::NTU + u) * 64]);
+    r.x &= keep; r.y &= keep; r.z &= keep; r.w &= keep;
+    f.p[u] = __builtin_bit_cast(frag, r);
+  }
+#pragma unroll
+  for (int s = 0; s < NS; ++s) f.u[s] = Lu[((vt0 + s) * G::NB + rtc) * 64];
+#pragma unroll
+  for (int j = 0; j < G::KUW; ++j)
+#pragma unroll
+    for (int h = 0; h < G::TPU; ++h) {
+      // key tile of (unit wave + 4j, half h), clamped to a valid one
+      const int t = min(G::TPU * (wave + STATE_WAVES * j) + h, G::NKT - 1);
+#pragma unroll
+      for (int u = 0; u < G::NTU; ++u) f.k[j][h][u] = Lk[(t * G::NTU + u) * 64];
+      f.gm[j][h] = *(const f32x4 *)(Lg + 16 * t);
+    }
 }
 
-template <typename IO, int DK, int C, int NW>
-__global__ __launch_bounds__(64 * (NW + 2), 1) void kda_state_pass(
+template <typename IO, int DK, int C, int NS>
+__global__ __launch_bounds__(64 * STATE_WAVES, 1) void kda_state_pass(
     PrefillParams p) {
   using M = Mma<IO>;
-  using SC = StateCfg<IO, DK, C, NW>;
+  using G = SP<IO, DK, C, NS>;
+  using V4 = Vec4T<IO>;
+  using FS = FragSet<IO, DK, C, NS>;
   typedef typename M::frag frag;
-  constexpr int NB = C / 16, NKT = DK / 16, TPU = M::TPU;
-  constexpr int NKU = (NKT + TPU - 1) / TPU, NTU = (NB + TPU - 1) / TPU;
-  __shared__ __attribute__((aligned(1024))) char sm[SC::LDS];
+  constexpr int NB = G::NB, NKT = G::NKT, TPU = G::TPU, NKU = G::NKU,
+                NTU = G::NTU, KUW = G::KUW;
+  __shared__ __attribute__((aligned(1024))) char sm[G::LDS];
+  frag *SU = (frag *)(sm + G::oSU);  // S as second operand, [NS][NKU] units
+  frag *DU = (frag *)(sm + G::oDU);  // Delta as second operand, [NS][NTU]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool loader = wave >= NW;  // waves NW, NW+1 move data
-  const int lw = wave - NW;        // loader wave index
   const int m16 = lane & 15, g4 = lane >> 4;
   const int Dv = p.Dv, H = p.H, T = p.T, BH = p.B * p.H, NC = p.NC;
-  const int ng = Dv / (16 * NW);  // workgroups per head
+  const int ng = Dv / (16 * NS);  // workgroups per head
   int bh, grp;
   {
     // keep the workgroups of one head on one XCD (blocks go round-robin over
-    // the 8 XCDs), so the later reader of the shared factors hits L2
+    // the 8 XCDs), so they share the head's factors through one L2
     const int b = blockIdx.x;
     if (ng > 1 && (BH & 7) == 0) {
-      const int x = b & 7, j = b >> 3;
-      bh = (j / ng) * 8 + x;
-      grp = j % ng;
+      const int x = b & 7, jj = b >> 3;
+      bh = (jj / ng) * 8 + x;
+      grp = jj % ng;
     } else {
       bh = b / ng;
       grp = b % ng;
     }
   }
   const int bb = bh / H, h = bh % H;
-  const int slab0 = grp * NW, vt = slab0 + (loader ? 0 : wave);
-  const int col = 16 * vt + m16;
+  const int vt0 = grp * NS;
   const WsLayout W = ws_layout(DK, Dv, C, (int)sizeof(IO));
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   const char *ws0 = p.ws + (size_t)bh * NC * p.wsb;
-  const size_t uoff = W.off_u + (size_t)slab0 * SC::UB;
 
-  // ---- loader side ---------------------------------------------------------
-  // the chunk's byte range is [shared factors | this group's U tiles]; copy
-  // block i (1 KiB) of chunk n into LDS buffer `buf`
-  auto copy_chunk = [&](int n, int buf) {
-    const char *blk = ws0 + (size_t)n * p.wsb;
+  // this wave's token tile and key units (wave-uniform); out-of-range
+  // shares are computed on clamped data and never written
+  const bool rv = (NB >= STATE_WAVES) || wave < NB;
+  const int rtc = min(wave, NB - 1);
+  bool kv[KUW];
 #pragma unroll
-    for (int c = 0; c < SC::CPW; ++c) {
-      const int i = lw + c * SC::NL;
-      if (i < SC::NKB) {
-        const size_t o = (size_t)i * 1024 + lane * 16;
-        if (o < SC::TOT)
-          dma16(blk + (o < SC::SH ? o : uoff + (o - SC::SH)),
-                sm + buf * SC::BUF + (size_t)i * 1024);
+  for (int j = 0; j < KUW; ++j)
+    kv[j] = (NKU % STATE_WAVES == 0) || wave + STATE_WAVES * j < NKU;
+
+  // ---- state rows owned by this wave: key tiles TPU*u + hh of its units ---
+  f32x4 S[KUW][TPU][NS];
+#pragma unroll
+  for (int j = 0; j < KUW; ++j)
+#pragma unroll
+    for (int hh = 0; hh < TPU; ++hh)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        S[j][hh][s] = zero;
+        const int t = TPU * (wave + STATE_WAVES * j) + hh;
+        if (p.s0 && kv[j] && t < NKT) {
+          const float *s0 = p.s0 + ((size_t)bh * DK + 16 * t + 4 * g4) * Dv +
+                            16 * (vt0 + s) + m16;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) S[j][hh][s][e] = s0[(size_t)e * Dv];
+        }
       }
-    }
-  };
-  // pull chunk n's lines into L2 (4 bytes per 128-byte line into a sink);
-  // every loader wave issues exactly TPW of these
-  auto touch_chunk = [&](int n) {
-    const char *blk = ws0 + (size_t)n * p.wsb;
-    constexpr int NSH = (int)((SC::SH + 127) / 128);
+  // publish S in operand form
+  auto publish_s = [&]() {
 #pragma unroll
-    for (int c = 0; c < SC::TPW; ++c) {
-      const int ln = min(lw * 64 + lane + c * 64 * SC::NL, SC::NLINE - 1);
-      const size_t o = ln < NSH ? (size_t)ln * 128
-                                : uoff + (size_t)(ln - NSH) * 128;
-      dma4(blk + o, sm + 2 * SC::BUF + lw * 256);
-    }
+    for (int j = 0; j < KUW; ++j)
+      if (kv[j]) {
+        const int u = wave + STATE_WAVES * j;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const bool hi = TPU == 2 && TPU * u + 1 < NKT;
+          SU[(s * NKU + u) * 64 + lane] =
+              M::pack(S[j][0][s], hi ? S[j][TPU - 1][s] : zero);
+        }
+      }
   };
-  // s_waitcnt vmcnt(TPW): this wave's copies (issued before its touches)
-  // have landed; the touches may still be in flight
-  constexpr unsigned WAIT_COPIES = (unsigned)SC::TPW | 0xF70u;
 
-  // ---- compute side: state tiles of slab vt --------------------------------
-  f32x4 S[NKT];
-  if (!loader && p.s0) {
-    const float *s0 = p.s0 + (size_t)bh * DK * Dv + col;
-#pragma unroll
-    for (int t = 0; t < NKT; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) S[t][j] = s0[(size_t)(16 * t + 4 * g4 + j) * Dv];
-  } else {
-#pragma unroll
-    for (int t = 0; t < NKT; ++t) S[t] = zero;
-  }
-  IO *obase = (IO *)p.o + ((size_t)bb * T * H + h) * Dv + col;
+  IO *obase = (IO *)p.o + ((size_t)bb * T * H + h) * Dv + 16 * vt0 + 4 * g4;
   const size_t orow = (size_t)H * Dv;  // elements between tokens
 
-  auto compute = [&](int n) {
-    const char *L = sm + (n & 1) * SC::BUF;
-    const char *LU = L + SC::SH + (size_t)wave * SC::UB;
-    const frag *Lw = (const frag *)(L + W.off_negw) + lane;
-    const frag *Lq = (const frag *)(L + W.off_qt) + lane;
-    const frag *Lk = (const frag *)(L + W.off_ktt) + lane;
-    const frag *Lp = (const frag *)(L + W.off_p) + lane;
-
-    frag Sb[NKU];
+  // one chunk step on the factors in f
+  auto step = [&](int n, const FS &f) {
+    // S at the chunk start, all key units, as the second operand
+    frag sb[NS][NKU];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int u = 0; u < NKU; ++u) sb[s][u] = SU[(s * NKU + u) * 64 + lane];
+    // Delta rows of token tile rtc: U - W S  (-W is stored)
+    f32x4 d[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) d[s] = V4::get(f.u[s]);
 #pragma unroll
     for (int u = 0; u < NKU; ++u)
-      Sb[u] = M::pack(S[TPU * u], (TPU == 2 && TPU * u + 1 < NKT)
-                                      ? S[(TPU * u + 1) % NKT]
-                                      : zero);
-    // Delta = U - W S0, one row tile at a time (its units read as a batch)
-    f32x4 D[NB];
 #pragma unroll
-    for (int rt = 0; rt < NB; ++rt) {
-      frag wf[NKU];
+      for (int s = 0; s < NS; ++s) d[s] = M::mma(f.w[u], sb[s][u], d[s]);
+    if (rv) {
 #pragma unroll
-      for (int u = 0; u < NKU; ++u) wf[u] = Lw[(rt * NKU + u) * 64];
-      float u4[4];
-      Vec4T<IO>::get(*((const typename Vec4T<IO>::raw *)LU + rt * 64 + lane),
-                     u4);
-      D[rt] = f32x4{u4[0], u4[1], u4[2], u4[3]};
-#pragma unroll
-      for (int u = 0; u < NKU; ++u) D[rt] = M::mma(wf[u], Sb[u], D[rt]);
+      for (int s = 0; s < NS; ++s) {
+        frag *dst = DU + (s * NTU + rtc / TPU) * 64 + lane;
+        if (TPU == 2) {
+          // half (rtc & 1) of the token unit: 4 values at byte 8*(rtc&1)
+          bf16x4 v4 = {(bf16)d[s][0], (bf16)d[s][1], (bf16)d[s][2],
+                       (bf16)d[s][3]};
+          *(bf16x4 *)((char *)dst + 8 * (rtc & 1)) = v4;
+        } else {
+          *(f32x4 *)dst = d[s];
+        }
+      }
     }
-    frag Db[NTU];
+    // O^T (value columns x tokens of tile rtc) = S^T Qtil^T + ...
+    f32x4 ot[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) ot[s] = zero;
+#pragma unroll
+    for (int u = 0; u < NKU; ++u)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) ot[s] = M::mma(sb[s][u], f.q[u], ot[s]);
+    lds_barrier();  // Delta complete in DU
+
+    frag db[NS][NTU];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int u = 0; u < NTU; ++u) db[s][u] = DU[(s * NTU + u) * 64 + lane];
+    // S <- diag(gamma_C) S + Ktil^T Delta on the owned key tiles
+#pragma unroll
+    for (int j = 0; j < KUW; ++j)
+#pragma unroll
+      for (int hh = 0; hh < TPU; ++hh)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          f32x4 sn = S[j][hh][s] * f.gm[j][hh];
+#pragma unroll
+          for (int u = 0; u < NTU; ++u) sn = M::mma(f.k[j][hh][u], db[s][u], sn);
+          S[j][hh][s] = sn;
+        }
+    // ... + Delta^T P^T (P is zero above the diagonal)
 #pragma unroll
     for (int u = 0; u < NTU; ++u)
-      Db[u] = M::pack(D[TPU * u], (TPU == 2 && TPU * u + 1 < NB)
-                                      ? D[(TPU * u + 1) % NB]
-                                      : zero);
-    // S_C = diag(gamma_C) S0 + K~^T Delta   (the critical path)
 #pragma unroll
-    for (int t = 0; t < NKT; ++t) {
-      frag kf[NTU];
+      for (int s = 0; s < NS; ++s) ot[s] = M::mma(db[s][u], f.p[u], ot[s]);
+    // lane (g4, m16) holds token 16 rtc + m16, value columns 4 g4 .. 4 g4 + 3
+    const int tok = n * C + 16 * rtc + m16;
+    if (rv && tok < T) {
+      IO *dst = obase + (size_t)tok * orow;
 #pragma unroll
-      for (int u = 0; u < NTU; ++u) kf[u] = Lk[(t * NTU + u) * 64];
-      const f32x4 gm =
-          *(const f32x4 *)((const float *)(L + W.off_gam) + 16 * t + 4 * g4);
-      f32x4 sn = S[t] * gm;
-#pragma unroll
-      for (int u = 0; u < NTU; ++u) sn = M::mma(kf[u], Db[u], sn);
-      S[t] = sn;
+      for (int s = 0; s < NS; ++s)
+        *(typename V4::raw *)(dst + 16 * s) = V4::put(ot[s]);
     }
-    // O = Q~ S0 + P Delta   (S0 survives in Sb)
-    const bool full = (n + 1) * C <= T;
-#pragma unroll
-    for (int rt = 0; rt < NB; ++rt) {
-      frag qf[NKU], pf[NTU];
-#pragma unroll
-      for (int u = 0; u < NKU; ++u) qf[u] = Lq[(rt * NKU + u) * 64];
-#pragma unroll
-      for (int u = 0; u < NTU; ++u)
-        if (u <= rt / TPU) pf[u] = Lp[(rt * NTU + u) * 64];
-      f32x4 O = zero;
-#pragma unroll
-      for (int u = 0; u < NKU; ++u) O = M::mma(qf[u], Sb[u], O);
-#pragma unroll
-      for (int u = 0; u < NTU; ++u)
-        if (u <= rt / TPU) O = M::mma(pf[u], Db[u], O);
-      IO *orow0 = obase + (size_t)(n * C + 16 * rt + 4 * g4) * orow;
-      if (full) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) orow0[j * orow] = from_f32<IO>(O[j]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (n * C + 16 * rt + 4 * g4 + j < T)
-            orow0[j * orow] = from_f32<IO>(O[j]);
-      }
-    }
+    publish_s();
+    lds_barrier();  // S complete in SU
   };
 
-  // prologue: chunk 0 in LDS buffer 0, chunks 1..PF-1 heading to L2
-  if (loader) {
-    copy_chunk(0, 0);
-    for (int m = 1; m < SC::PF && m < NC; ++m) touch_chunk(m);
-    __builtin_amdgcn_s_waitcnt(0);
+  // the upper half of the last token unit stays zero when NB is odd
+  for (int i = tid; i < NS * NTU * 256; i += 64 * STATE_WAVES)
+    ((float *)DU)[i] = 0.f;
+  publish_s();
+  lds_barrier();
+
+  // three rotating factor sets, fetched three chunks ahead
+  FS f0, f1, f2;
+  auto fetch = [&](FS &f, int n) {
+    const char *blk = ws0 + (size_t)min(n, NC - 1) * p.wsb;
+    load_frags<IO, DK, C, NS>(f, blk, W, rtc, wave, lane, g4, vt0);
+  };
+  fetch(f0, 0);
+  fetch(f1, 1);
+  for (int n = 0; n < NC; n += 3) {
+    fetch(f2, n + 2);
+    step(n, f0);
+    if (n + 1 >= NC) break;
+    fetch(f0, n + 3);
+    step(n + 1, f1);
+    if (n + 2 >= NC) break;
+    fetch(f1, n + 4);
+    step(n + 2, f2);
   }
-  for (int n = 0; n < NC; ++n) {
-    __syncthreads();  // buffer n&1 holds chunk n; buffer (n+1)&1 is free
-    if (!loader) {
-      compute(n);
-    } else {
-      if (n + 1 < NC) copy_chunk(n + 1, (n + 1) & 1);
-      if (n + SC::PF < NC) {
-        touch_chunk(n + SC::PF);
-        __builtin_amdgcn_s_waitcnt(WAIT_COPIES);
-      } else {
-        __builtin_amdgcn_s_waitcnt(0);
+
+  if (p.s_out) {
+#pragma unroll
+    for (int j = 0; j < KUW; ++j)
+#pragma unroll
+      for (int hh = 0; hh < TPU; ++hh) {
+        const int t = TPU * (wave + STATE_WAVES * j) + hh;
+        if (kv[j] && t < NKT) {
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            float *so = p.s_out + ((size_t)bh * DK + 16 * t + 4 * g4) * Dv +
+                        16 * (vt0 + s) + m16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) so[(size_t)e * Dv] = S[j][hh][s][e];
+          }
+        }
       }
-    }
-  }
-  if (!loader && p.s_out) {
-#pragma unroll
-    for (int t = 0; t < NKT; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        p.s_out[((size_t)bh * DK + 16 * t + 4 * g4 + j) * Dv + col] = S[t][j];
   }
 }
 
 // ---------------------------------------------------------------------------
-template <typename IO, int DK, int C, int NW>
-static hipError_t state_nw(const PrefillParams &p, hipStream_t s) {
-  if constexpr (!StateCfg<IO, DK, C, NW>::fits) {
-    return hipErrorInvalidValue;
-  } else {
-    const unsigned nblk = (unsigned)(p.B * p.H) * (unsigned)(p.Dv / (16 * NW));
-    hipLaunchKernelGGL((kda_state_pass<IO, DK, C, NW>), dim3(nblk),
-                       dim3(64 * (NW + 2)), 0, s, p);
-    return hipGetLastError();
-  }
+static int state_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+          hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+template <typename IO, int DK, int C, int NS>
+static hipError_t state_ns(const PrefillParams &p, hipStream_t s) {
+  const unsigned nblk = (unsigned)(p.B * p.H) * (unsigned)(p.Dv / (16 * NS));
+  hipLaunchKernelGGL((kda_state_pass<IO, DK, C, NS>), dim3(nblk),
+                     dim3(64 * STATE_WAVES), 0, s, p);
+  return hipGetLastError();
 }
 
 template <typename IO, int DK, int C>
 static hipError_t state_one(const PrefillParams &p, hipStream_t s) {
-  // as many 16-column slabs per workgroup (up to 4) as Dv and LDS allow
-  const int slabs = p.Dv / 16;
-  if (slabs % 4 == 0 && StateCfg<IO, DK, C, 4>::fits)
-    return state_nw<IO, DK, C, 4>(p, s);
-  if (slabs % 2 == 0 && StateCfg<IO, DK, C, 2>::fits)
-    return state_nw<IO, DK, C, 2>(p, s);
-  return state_nw<IO, DK, C, 1>(p, s);
+  // slabs per workgroup: one while that fills the chip, more when the
+  // workgroups would otherwise run in several rounds (each extra slab reuses
+  // the fetched factors)
+  const long long slabs = p.Dv / 16, units = (long long)p.B * p.H * slabs;
+  const long long cus = state_cu_count();
+  constexpr int NSMAX = sizeof(IO) == 2 ? 4 : 2;
+  if (NSMAX >= 4 && slabs % 4 == 0 && units >= 8 * cus)
+    return state_ns<IO, DK, C, NSMAX>(p, s);
+  if (slabs % 2 == 0 && units >= 2 * cus)
+    return state_ns<IO, DK, C, 2>(p, s);
+  return state_ns<IO, DK, C, 1>(p, s);
 }
 
 #define KDA_DISPATCH(FN)                                                    \
