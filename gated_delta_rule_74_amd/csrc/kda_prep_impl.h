@@ -24,7 +24,9 @@
 // products (exact and slow; reached only by extreme forgetting).
 //
 // Execution: a persistent grid (one workgroup of 256 threads per CU) walks
-// the (batch*head, chunk) tasks.  Thread t owns 4 consecutive key channels x
+// the (batch*head, chunk) tasks, last chunk first: the state pass reads the
+// chunks in order right afterwards, so its early chunks are the most recently
+// written ones and tend to still sit in the memory-side cache.  Thread t owns 4 consecutive key channels x
 // 8 consecutive tokens of a task; its raw inputs are fetched with 8/16-byte
 // vector loads into registers one task ahead, so the fetch of task i+1
 // overlaps the matrix-core phases of task i.
@@ -116,7 +118,7 @@ __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
   constexpr bool GB = sizeof(GT) == 2;  // bf16 gates
   typedef typename Vec4<IO>::raw R;
   const int BH = p.B * p.H;
-  const int bh = task % BH, n = task / BH;
+  const int bh = task % BH, n = p.NC - 1 - task / BH;
   const int b = bh / p.H, h = bh % p.H;
   const int T = p.T, H = p.H, Dv = p.Dv;
   const int t0 = n * C;
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
   if (task < ntask) prep_load<IO, GT, DK, C, CONV>(p, task, st, tid);
 
   for (; task < ntask; task += gridDim.x) {
-    const int bh = task % BH, n = task / BH;
+    const int bh = task % BH, n = p.NC - 1 - task / BH;
     const int b = bh / H, h = bh % H;
     const int t0 = n * C;
     char *blk = p.ws + ((size_t)bh * p.NC + n) * p.wsb;

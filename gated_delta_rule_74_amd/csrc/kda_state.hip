@@ -22,9 +22,10 @@
 // four consecutive value columns of one token: one vector store per slab.
 //
 // Each wave fetches its factors straight from global memory into registers
-// PD = 3 chunks ahead (three rotating register sets), so the HBM latency of
-// the factors overlaps the two chunk steps before their use; only the
-// exchange round trips and the short MFMA chains sit on the sequential path.
+// one chunk ahead (two rotating register sets), so their latency overlaps
+// the previous chunk step, and a fifth wave pulls the blocks of later chunks
+// into L2 ahead of that fetch; only the exchange round trips and the short
+// MFMA chains sit on the sequential path.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -60,7 +61,8 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-constexpr int STATE_WAVES = 4;
+constexpr int STATE_WAVES = 4;  // compute waves; one more wave warms L2
+constexpr int STATE_PF = 4;     // chunks between warming and use
 
 template <typename IO, int DK, int C, int NS> struct SP {
   static constexpr int TPU = Mma<IO>::TPU;
@@ -83,7 +85,9 @@ template <typename IO, int DK, int C, int NS> struct FragSet {
   typename Vec4T<IO>::raw u[NS];
 };
 
-template <typename IO, int DK, int C, int NS>
+// Half A (-W, Qtil, U: what the products before the Delta exchange need)
+// or half B (P, Ktil^T, gamma_C) of one wave's factors of a chunk.
+template <int HALF, typename IO, int DK, int C, int NS>
 __device__ __forceinline__ void load_frags(FragSet<IO, DK, C, NS> &f,
                                            const char *blk, const WsLayout &W,
                                            int rtc, int wave, int lane,
@@ -91,41 +95,45 @@ __device__ __forceinline__ void load_frags(FragSet<IO, DK, C, NS> &f,
   using G = SP<IO, DK, C, NS>;
   typedef typename Mma<IO>::frag frag;
   typedef typename Vec4T<IO>::raw URaw;
-  const frag *Lw = (const frag *)(blk + W.off_negw) + lane;
-  const frag *Lq = (const frag *)(blk + W.off_qt) + lane;
-  const frag *Lk = (const frag *)(blk + W.off_ktt) + lane;
-  const frag *Lp = (const frag *)(blk + W.off_p) + lane;
-  const URaw *Lu = (const URaw *)(blk + W.off_u) + lane;
-  const float *Lg = (const float *)(blk + W.off_gam) + 4 * g4;
+  if (HALF == 0) {
+    const frag *Lw = (const frag *)(blk + W.off_negw) + lane;
+    const frag *Lq = (const frag *)(blk + W.off_qt) + lane;
+    const URaw *Lu = (const URaw *)(blk + W.off_u) + lane;
 #pragma unroll
-  for (int u = 0; u < G::NKU; ++u) f.w[u] = Lw[(rtc * G::NKU + u) * 64];
+    for (int u = 0; u < G::NKU; ++u) f.w[u] = Lw[(rtc * G::NKU + u) * 64];
 #pragma unroll
-  for (int u = 0; u < G::NKU; ++u) f.q[u] = Lq[(rtc * G::NKU + u) * 64];
-  // P units above the diagonal are never written by the prep: their bits
-  // are cleared so the product can run unconditionally
+    for (int u = 0; u < G::NKU; ++u) f.q[u] = Lq[(rtc * G::NKU + u) * 64];
 #pragma unroll
-  for (int u = 0; u < G::NTU; ++u) {
-    const unsigned keep = (G::NTU == 1 || u <= rtc / G::TPU) ? ~0u : 0u;
-    uint4 r = __builtin_bit_cast(uint4, Lp[(rtc * G::NTU + u) * 64]);
-    r.x &= keep; r.y &= keep; r.z &= keep; r.w &= keep;
-    f.p[u] = __builtin_bit_cast(frag, r);
-  }
+    for (int s = 0; s < NS; ++s) f.u[s] = Lu[((vt0 + s) * G::NB + rtc) * 64];
+  } else {
+    const frag *Lk = (const frag *)(blk + W.off_ktt) + lane;
+    const frag *Lp = (const frag *)(blk + W.off_p) + lane;
+    const float *Lg = (const float *)(blk + W.off_gam) + 4 * g4;
+    // P units above the diagonal are never written by the prep: their bits
+    // are cleared so the product can run unconditionally
 #pragma unroll
-  for (int s = 0; s < NS; ++s) f.u[s] = Lu[((vt0 + s) * G::NB + rtc) * 64];
-#pragma unroll
-  for (int j = 0; j < G::KUW; ++j)
-#pragma unroll
-    for (int h = 0; h < G::TPU; ++h) {
-      // key tile of (unit wave + 4j, half h), clamped to a valid one
-      const int t = min(G::TPU * (wave + STATE_WAVES * j) + h, G::NKT - 1);
-#pragma unroll
-      for (int u = 0; u < G::NTU; ++u) f.k[j][h][u] = Lk[(t * G::NTU + u) * 64];
-      f.gm[j][h] = *(const f32x4 *)(Lg + 16 * t);
+    for (int u = 0; u < G::NTU; ++u) {
+      const unsigned keep = (G::NTU == 1 || u <= rtc / G::TPU) ? ~0u : 0u;
+      uint4 r = __builtin_bit_cast(uint4, Lp[(rtc * G::NTU + u) * 64]);
+      r.x &= keep; r.y &= keep; r.z &= keep; r.w &= keep;
+      f.p[u] = __builtin_bit_cast(frag, r);
     }
+#pragma unroll
+    for (int j = 0; j < G::KUW; ++j)
+#pragma unroll
+      for (int h = 0; h < G::TPU; ++h) {
+        // key tile of (unit wave + 4j, half h), clamped to a valid one
+        const int t = min(G::TPU * (wave + STATE_WAVES * j) + h, G::NKT - 1);
+#pragma unroll
+        for (int u = 0; u < G::NTU; ++u)
+          f.k[j][h][u] = Lk[(t * G::NTU + u) * 64];
+        f.gm[j][h] = *(const f32x4 *)(Lg + 16 * t);
+      }
+  }
 }
 
 template <typename IO, int DK, int C, int NS>
-__global__ __launch_bounds__(64 * STATE_WAVES, 1) void kda_state_pass(
+__global__ __launch_bounds__(64 * (STATE_WAVES + 1), 1) void kda_state_pass(
     PrefillParams p) {
   using M = Mma<IO>;
   using G = SP<IO, DK, C, NS>;
@@ -161,6 +169,36 @@ __global__ __launch_bounds__(64 * STATE_WAVES, 1) void kda_state_pass(
   const WsLayout W = ws_layout(DK, Dv, C, (int)sizeof(IO));
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   const char *ws0 = p.ws + (size_t)bh * NC * p.wsb;
+
+  if (wave == STATE_WAVES) {
+    // L2 warm-up wave: touches 4 bytes of every 128-byte line of the block of
+    // chunk n + STATE_PF while chunk n is computed (the ng workgroups of the
+    // head split the lines), as direct-to-LDS loads into a sink so nothing
+    // ever waits for them.  It takes part in every barrier of the compute
+    // waves (one before the loop, two per chunk).
+    __shared__ __attribute__((aligned(256))) char sink[256];
+    const int nline = (int)((p.wsb + 127) / 128);
+    const int share = (nline + ng - 1) / ng;
+    const int nk = (share + 63) / 64;
+    auto warm = [&](int n) {
+      const char *blk = ws0 + (size_t)n * p.wsb;
+      for (int k = 0; k < nk; ++k) {
+        const int ln = min(grp * share + min(64 * k + lane, share - 1),
+                           nline - 1);
+        __builtin_amdgcn_global_load_lds(
+            (const void *)(blk + (size_t)ln * 128),
+            (__attribute__((address_space(3))) void *)sink, 4, 0, 0);
+      }
+    };
+    for (int n = 0; n < STATE_PF && n < NC; ++n) warm(n);
+    lds_barrier();
+    for (int n = 0; n < NC; ++n) {
+      if (n + STATE_PF < NC) warm(n + STATE_PF);
+      lds_barrier();
+      lds_barrier();
+    }
+    return;
+  }
 
   // this wave's token tile and key units (wave-uniform); out-of-range
   // shares are computed on clamped data and never written
@@ -207,7 +245,13 @@ __global__ __launch_bounds__(64 * STATE_WAVES, 1) void kda_state_pass(
   const size_t orow = (size_t)H * Dv;  // elements between tokens
 
   // one chunk step on the factors in f
-  auto step = [&](int n, const FS &f) {
+  // the loads of chunk n+1 are spread over chunk n's two phases, each
+  // interleaved with that phase's products, so that issuing them (the
+  // vector memory pipe takes about one 1 KiB fragment per 16 cycles per CU)
+  // overlaps the matrix-core work instead of adding to it
+  auto step = [&](int n, const FS &f, FS &nx) {
+    const char *nblk = ws0 + (size_t)min(n + 1, NC - 1) * p.wsb;
+    load_frags<0, IO, DK, C, NS>(nx, nblk, W, rtc, wave, lane, g4, vt0);
     // S at the chunk start, all key units, as the second operand
     frag sb[NS][NKU];
 #pragma unroll
@@ -244,7 +288,18 @@ __global__ __launch_bounds__(64 * STATE_WAVES, 1) void kda_state_pass(
     for (int u = 0; u < NKU; ++u)
 #pragma unroll
       for (int s = 0; s < NS; ++s) ot[s] = M::mma(sb[s][u], f.q[u], ot[s]);
+    {
+      constexpr int NL = 2 * NKU + NS, NM = 2 * NKU * NS;
+      __builtin_amdgcn_sched_group_barrier(0x100, NS * NKU, 0);  // S reads
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      if (NL > NM) __builtin_amdgcn_sched_group_barrier(0x020, NL - NM, 0);
+    }
     lds_barrier();  // Delta complete in DU
+    load_frags<1, IO, DK, C, NS>(nx, nblk, W, rtc, wave, lane, g4, vt0);
 
     frag db[NS][NTU];
 #pragma unroll
@@ -277,6 +332,17 @@ __global__ __launch_bounds__(64 * STATE_WAVES, 1) void kda_state_pass(
         *(typename V4::raw *)(dst + 16 * s) = V4::put(ot[s]);
     }
     publish_s();
+    {
+      constexpr int NL = NTU + KUW * TPU * (NTU + 1);
+      constexpr int NM = NTU * NS + KUW * TPU * NS * NTU;
+      __builtin_amdgcn_sched_group_barrier(0x100, NS * NTU, 0);  // Delta reads
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      if (NL > NM) __builtin_amdgcn_sched_group_barrier(0x020, NL - NM, 0);
+    }
     lds_barrier();  // S complete in SU
   };
 
@@ -286,23 +352,14 @@ __global__ __launch_bounds__(64 * STATE_WAVES, 1) void kda_state_pass(
   publish_s();
   lds_barrier();
 
-  // three rotating factor sets, fetched three chunks ahead
-  FS f0, f1, f2;
-  auto fetch = [&](FS &f, int n) {
-    const char *blk = ws0 + (size_t)min(n, NC - 1) * p.wsb;
-    load_frags<IO, DK, C, NS>(f, blk, W, rtc, wave, lane, g4, vt0);
-  };
-  fetch(f0, 0);
-  fetch(f1, 1);
-  for (int n = 0; n < NC; n += 3) {
-    fetch(f2, n + 2);
-    step(n, f0);
+  // two rotating factor sets: chunk n+1 is fetched while chunk n is computed
+  FS f0, f1;
+  load_frags<0, IO, DK, C, NS>(f0, ws0, W, rtc, wave, lane, g4, vt0);
+  load_frags<1, IO, DK, C, NS>(f0, ws0, W, rtc, wave, lane, g4, vt0);
+  for (int n = 0; n < NC; n += 2) {
+    step(n, f0, f1);
     if (n + 1 >= NC) break;
-    fetch(f0, n + 3);
-    step(n + 1, f1);
-    if (n + 2 >= NC) break;
-    fetch(f1, n + 4);
-    step(n + 2, f2);
+    step(n + 1, f1, f0);
   }
 
   if (p.s_out) {
@@ -338,22 +395,22 @@ template <typename IO, int DK, int C, int NS>
 static hipError_t state_ns(const PrefillParams &p, hipStream_t s) {
   const unsigned nblk = (unsigned)(p.B * p.H) * (unsigned)(p.Dv / (16 * NS));
   hipLaunchKernelGGL((kda_state_pass<IO, DK, C, NS>), dim3(nblk),
-                     dim3(64 * STATE_WAVES), 0, s, p);
+                     dim3(64 * (STATE_WAVES + 1)), 0, s, p);
   return hipGetLastError();
 }
 
 template <typename IO, int DK, int C>
 static hipError_t state_one(const PrefillParams &p, hipStream_t s) {
-  // slabs per workgroup: one while that fills the chip, more when the
-  // workgroups would otherwise run in several rounds (each extra slab reuses
-  // the fetched factors)
+  // slabs per workgroup: one while that fills the chip, two when the
+  // workgroups would otherwise run in several rounds (the second slab reuses
+  // the fetched factors); more would not fit the registers beside the fifth
+  // wave
   const long long slabs = p.Dv / 16, units = (long long)p.B * p.H * slabs;
   const long long cus = state_cu_count();
-  constexpr int NSMAX = sizeof(IO) == 2 ? 4 : 2;
-  if (NSMAX >= 4 && slabs % 4 == 0 && units >= 8 * cus)
-    return state_ns<IO, DK, C, NSMAX>(p, s);
-  if (slabs % 2 == 0 && units >= 2 * cus)
-    return state_ns<IO, DK, C, 2>(p, s);
+  if constexpr (sizeof(IO) == 2 || DK < 128) {
+    if (slabs % 2 == 0 && units >= 2 * cus)
+      return state_ns<IO, DK, C, 2>(p, s);
+  }
   return state_ns<IO, DK, C, 1>(p, s);
 }
 
