@@ -152,24 +152,26 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / K
-        # per-kernel durations (same stream, events between the launches)
-        tp, ts = 0.0, 0.0
-        for _ in range(K):
-            a, b_, c_ = ev(), ev(), ev()
-            a.record(stream)
-            kda.kda_prefill_chunk_prep(x["q"], x["k"], x["v"], x["g"],
-                                       x["beta"], ws, chunk=C)
-            b_.record(stream)
-            kda.kda_prefill_state_pass(ws, o, s_out=s, B=B, T=T, H=H, Dk=Dk,
-                                       Dv=Dv, chunk=C)
-            c_.record(stream)
+        # per-kernel durations: K back-to-back launches of each kernel alone
+        # (HIP events on the launch stream), so launch gaps are not counted
+        def t_back_to_back(fn):
+            fn()
             torch.cuda.synchronize()
-            tp += a.elapsed_time(b_)
-            ts += b_.elapsed_time(c_)
-        tp, ts = tp / K, ts / K
+            a, b_ = ev(), ev()
+            a.record(stream)
+            for _ in range(K):
+                fn()
+            b_.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b_) / K
+        tp = t_back_to_back(lambda: kda.kda_prefill_chunk_prep(
+            x["q"], x["k"], x["v"], x["g"], x["beta"], ws, chunk=C))
+        ts = t_back_to_back(lambda: kda.kda_prefill_state_pass(
+            ws, o, s_out=s, B=B, T=T, H=H, Dk=Dk, Dv=Dv, chunk=C))
         byts = prefill_bytes(B, T, H, Dk, Dv)
         flops = prefill_flops(B, T, H, Dk, Dv, C)
-        t_k = (tp + ts) * 1e-3
+        # one kda_prefill call = chunk prep + state pass, back to back
+        t_k = ms * 1e-3
         gbs = byts / t_k / 1e9
         srcs = ["kda_prep_impl.h", "kda_prep_bf16_f32.hip", "kda_state.hip",
                 "kda_device.h"]
@@ -180,7 +182,8 @@ def main():
             kernel_ms={"kda_chunk_prep": tp, "kda_state_pass": ts},
             algo_bytes=byts, algo_flops=flops,
             roofline=dict(
-                kernel="kda_prefill = kda_chunk_prep + kda_state_pass",
+                kernel="kda_prefill call (kda_chunk_prep then "
+                       "kda_state_pass)",
                 bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=gbs / HBM_PEAK_GBS,
                 traffic=(None if tr_p is None or tr_s is None

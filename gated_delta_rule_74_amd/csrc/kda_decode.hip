@@ -8,9 +8,12 @@
 //   S <- diag(e) S + k delta^T               (in place)
 //   o = scale (y + (q . k) delta)            (= scale S_new^T q)
 // The state is the only large operand (Dk*Dv fp32 per head), so the kernel
-// is an HBM stream: each workgroup loads its head's state once with 16-byte
-// non-temporal loads into registers, reduces over rows through LDS, and
-// writes it back once.
+// is an HBM stream: each workgroup loads its share of the state once with
+// 16-byte non-temporal loads into registers, reduces over rows through LDS,
+// and writes it back once.  Every sum runs over rows (key channels) for a
+// fixed value column, so a head's columns split over CS workgroups with no
+// exchange between them; each takes 32 columns (128-byte row segments,
+// 16 KiB at d_k = 128), which streams better than whole 64 KiB heads.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -22,23 +25,25 @@ __device__ __forceinline__ float dec_gate(const void *p, size_t i, int bf) {
   return bf ? (float)((const bf16 *)p)[i] : ((const float *)p)[i];
 }
 
-template <typename IO, int DK, int DV>
+template <typename IO, int DK, int DV, int CS>
 __global__ __launch_bounds__(DEC_THREADS) void kda_decode(DecodeParams p) {
-  constexpr int NQ = DV / 4;  // column quads
+  constexpr int DVB = DV / CS;  // value columns of this workgroup
+  constexpr int NQ = DVB / 4;   // column quads
   constexpr int NT = (NQ * DK < DEC_THREADS) ? NQ * DK : DEC_THREADS;
   constexpr int RG = NT / NQ;    // row groups
   constexpr int RPT = DK / RG;   // rows per thread
   static_assert(RG * NQ == NT && RPT * RG == DK, "thread mapping");
 
   __shared__ float s_ek[DK], s_eq[DK], s_e[DK], s_k[DK];
-  __shared__ __attribute__((aligned(16))) float s_part[2][RG][DV];
-  __shared__ __attribute__((aligned(16))) float s_d[DV];
+  __shared__ __attribute__((aligned(16))) float s_part[2][RG][DVB];
+  __shared__ __attribute__((aligned(16))) float s_d[DVB];
   __shared__ float s_qk[DEC_THREADS / 64];
 
   const int tid = threadIdx.x;
-  const size_t nh = blockIdx.x;
+  const size_t nh = blockIdx.x / CS;
+  const int c0 = (blockIdx.x % CS) * DVB;  // first value column
   const int q4 = tid % NQ, rg = tid / NQ;
-  float *Sg = p.state + nh * DK * DV;
+  float *Sg = p.state + nh * DK * DV + c0;
 
   // 1. issue the state loads first: they are the whole cost
   f32x4 s[RPT];
@@ -82,7 +87,7 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode(DecodeParams p) {
   __syncthreads();
 
   // 4. per column: delta and output
-  if (tid < DV) {
+  if (tid < DVB) {
     float u = 0.f, y = 0.f;
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
@@ -93,10 +98,10 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode(DecodeParams p) {
 #pragma unroll
     for (int w = 0; w < DEC_THREADS / 64; ++w) qkt += s_qk[w];
     const float bt = dec_gate(p.beta, nh, p.gate_bf16);
-    const float vv = to_f32(((const IO *)p.v)[nh * DV + tid]);
+    const float vv = to_f32(((const IO *)p.v)[nh * DV + c0 + tid]);
     const float d = bt * (vv - u);
     s_d[tid] = d;
-    ((IO *)p.o)[nh * DV + tid] = from_f32<IO>(p.scale * (y + qkt * d));
+    ((IO *)p.o)[nh * DV + c0 + tid] = from_f32<IO>(p.scale * (y + qkt * d));
   }
   __syncthreads();
 
@@ -115,8 +120,12 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode(DecodeParams p) {
 
 template <typename IO, int DK, int DV>
 static hipError_t dec_one(const DecodeParams &p, hipStream_t s) {
-  hipLaunchKernelGGL((kda_decode<IO, DK, DV>), dim3((unsigned)(p.N * p.H)),
-                     dim3(DEC_THREADS), 0, s, p);
+  // column split: 32 value columns (128-byte row segments) per workgroup
+  // once a head's state exceeds 16 KiB
+  constexpr int CS = (DK * DV * 4 > 16384 && DV >= 64) ? DV / 32 : 1;
+  hipLaunchKernelGGL((kda_decode<IO, DK, DV, CS>),
+                     dim3((unsigned)(p.N * p.H) * CS), dim3(DEC_THREADS), 0, s,
+                     p);
   return hipGetLastError();
 }
 

@@ -20,7 +20,8 @@ def kda():
 
 @pytest.mark.parametrize("qkv,gate,Dk,Dv", [
     ("bf16", "bf16", 128, 128), ("bf16", "f32", 64, 32), ("f32", "f32", 16, 16),
-    ("f32", "f32", 128, 128), ("bf16", "bf16", 32, 128), ("bf16", "f32", 128, 16)])
+    ("f32", "f32", 128, 128), ("bf16", "bf16", 32, 128), ("bf16", "f32", 128, 16),
+    ("bf16", "bf16", 64, 128), ("f32", "f32", 128, 64)])
 def test_decode_steps(orc, kda, qkv, gate, Dk, Dv):
     say(f"decode qkv={qkv} gate={gate} Dk={Dk} Dv={Dv}")
     N, H = 5, 3
