@@ -343,7 +343,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             pr[j] *= e[i][j];
-            if (!(half && i == 7) && !(pr[j] >= SAFE_MIN)) vote = 1;
+            if (!(pr[j] >= SAFE_MIN)) vote = 1;
             xkr[j] = bt[i] * kk[i][j] * pr[j];
             xqr[j] = p.scale * qq[i][j] * pr[j];
             xki[j] = kk[i][j] * __builtin_amdgcn_rcpf(pr[j]);
@@ -617,7 +617,9 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     __syncthreads();  // B3: region A no longer read
 
     // ---- T0: W/U inputs into the freed region, T zero-filled --------------
-    for (int i = tid; i < C * LDC; i += PREP_THREADS) Tb[i] = from_f32<IO>(0.f);
+    static_assert((C * LDC * sizeof(IO)) % 16 == 0, "Tb rows");
+    for (int i = tid; i < (int)(C * LDC * sizeof(IO) / 16); i += PREP_THREADS)
+      ((uint4 *)Tb)[i] = make_uint4(0u, 0u, 0u, 0u);
     if (kthr) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -641,22 +643,38 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     __syncthreads();  // B4
 
     // ---- T1: inverse of each unit-lower 16x16 diagonal block (fp32) ------
-    if (tid < 16 * NB) {
-      const int aa = tid / 16, s = tid % 16;
-      float col[16];
+    // With L the strictly lower block (L^16 = 0),
+    //   (I + L)^-1 = (I - L)(I + L^2)(I + L^4)(I + L^8),
+    // all polynomials in L, so they commute: T = (I + L^8)((I + L^4)((I + L^2)
+    // (I - L))).  One wave per block on the fp32 matrix cores.  A product of
+    // two matrices given in operand form yields the second-operand form of
+    // the result; the first-operand form of X equals the second-operand form
+    // of X^T, so both forms of L^2 and L^4 come from products of L and L^T.
+    if (wave < NB) {
+      const int aa = wave;
+      const float *ab = Af + (16 * aa) * LDA + 16 * aa;
+      const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 LA = *(const f32x4 *)(ab + m16 * LDA + 4 * g4);
+      f32x4 LB, Y;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = 0.f;
-        const float *arow = Af + (16 * aa + r) * LDA + 16 * aa;
-#pragma unroll
-        for (int cc = 0; cc < r; ++cc) acc += arow[cc] * col[cc];
-        col[r] = (r == s) ? 1.f : ((r < s) ? 0.f : -acc);
+      for (int j = 0; j < 4; ++j) {
+        LB[j] = ab[(4 * g4 + j) * LDA + m16];
+        Y[j] = ((4 * g4 + j) == m16 ? 1.f : 0.f) - LB[j];  // I - L
       }
+      const f32x4 L2B = mma16_f32(LA, LB, z4);   // L^2
+      const f32x4 L2A = mma16_f32(LB, LA, z4);   // (L^2)^T: first form of L^2
+      const f32x4 L4B = mma16_f32(L2A, L2B, z4);
+      const f32x4 L4A = mma16_f32(L2B, L2A, z4);
+      const f32x4 L8A = mma16_f32(L4B, L4A, z4);
+      Y = mma16_f32(L2A, Y, Y);
+      Y = mma16_f32(L4A, Y, Y);
+      Y = mma16_f32(L8A, Y, Y);
+      // lane (g4, m16) holds T_aa[4 g4 + j][m16]
+      *(f32x4 *)(Tt + (16 * aa + m16) * LDA + 16 * aa + 4 * g4) = Y;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        Tt[(16 * aa + s) * LDA + 16 * aa + r] = col[r];
-        Taa[(aa * 16 + r) * 16 + s] = col[r];
-        Tb[(16 * aa + r) * LDC + 16 * aa + s] = from_f32<IO>(col[r]);
+      for (int j = 0; j < 4; ++j) {
+        Taa[(aa * 16 + 4 * g4 + j) * 16 + m16] = Y[j];
+        Tb[(16 * aa + 4 * g4 + j) * LDC + 16 * aa + m16] = from_f32<IO>(Y[j]);
       }
     }
     __syncthreads();

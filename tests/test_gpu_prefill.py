@@ -86,6 +86,24 @@ def test_forgetting_extremes(orc, kda, qkv):
     assert rel_err(o, ro) <= TOL[qkv]
 
 
+@pytest.mark.parametrize("qkv", ["f32", "bf16"])
+@pytest.mark.parametrize("pos", [15, 31, 47, 63, 64 + 15])
+def test_forget_at_sub_chunk_end(orc, kda, qkv, pos):
+    """g = -inf exactly on the last token of a 16-token sub-chunk, nothing
+    else extreme in the chunk: the vanished running product of that token
+    must send the diagonal blocks down the exact path (no 0 * inf)."""
+    say(f"prefill forget at {pos} qkv={qkv}")
+    x = ki.prefill_inputs(1, 140, 2, 32, 32, qkv=qkv, gate="f32", seed=21,
+                          device="cuda", with_s0=True)
+    g = x["g"]
+    g[:, pos] = -float("inf")
+    o, s = _run(kda, x, 64, s0=x["s0"])
+    ro, rs = orc.recurrence(x["q"], x["k"], x["v"], g, x["beta"], x["s0"])
+    eo, es = rel_err(o, ro), rel_err(s, rs)
+    say(f"  err o={eo:.2e} S={es:.2e}")
+    assert eo <= TOL[qkv] and es <= TOL[qkv]
+
+
 def test_split_sequence_carry(kda):
     """prefill(T1) -> S -> prefill(T2 | S) equals prefill(T1 + T2)."""
     x = ki.prefill_inputs(2, 300, 4, 128, 128, seed=9, device="cuda",
