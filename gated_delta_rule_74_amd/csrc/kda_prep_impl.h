@@ -555,62 +555,70 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     }
 
     // ---- AP: A^T and P^T sub-blocks on the matrix cores --------------------
-    for (int tk = wave; tk < NB * (NB + 1) / 2; tk += PREP_THREADS / 64) {
-      int aa = 0, bb = tk;
-      while (bb > aa) { bb -= aa + 1; ++aa; }
-      const bool diag = (aa == bb);
-      f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-      if (diag && fallback) {
+    // wave aa takes row block aa (its Xkr / Xqr operands are read once) and
+    // every column block bb <= aa
+    for (int aa = wave; aa < NB; aa += PREP_THREADS / 64) {
+      const IO *kb = Xkr + (16 * aa + m16) * LDK;
+      const IO *qb = Xqr + (16 * aa + m16) * LDK;
+      frag kf[NKU], qf[NKU];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          accA[j] = FbA[(aa * 16 + m16) * 16 + 4 * g4 + j];
-          accP[j] = FbP[(aa * 16 + m16) * 16 + 4 * g4 + j];
-        }
-      } else {
-        const IO *cb = (diag ? Xkir : Xks) + (16 * bb + m16) * LDK;
-        const IO *kb = Xkr + (16 * aa + m16) * LDK;
-        const IO *qb = Xqr + (16 * aa + m16) * LDK;
-        const float *mid = (aa - bb >= 2) ? Mid + L::p2(aa, bb) * DK : nullptr;
-        frag cf[NKU], kf[NKU], qf[NKU];
+      for (int u = 0; u < NKU; ++u) {
+        const bool full = (TPU == 1) || (TPU * u + 1 < NKT);
+        kf[u] = M::load_k(kb + KU * u, g4, full);
+        qf[u] = M::load_k(qb + KU * u, g4, full);
+      }
+      for (int bb = 0; bb <= aa; ++bb) {
+        const bool diag = (aa == bb);
+        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+        if (diag && fallback) {
 #pragma unroll
-        for (int u = 0; u < NKU; ++u) {
-          const bool full = (TPU == 1) || (TPU * u + 1 < NKT);
-          cf[u] = M::load_k(cb + KU * u, g4, full);
-          kf[u] = M::load_k(kb + KU * u, g4, full);
-          qf[u] = M::load_k(qb + KU * u, g4, full);
-        }
-#pragma unroll
-        for (int u = 0; u < NKU; ++u) {
-          if (mid) {
-#pragma unroll
-            for (int ee = 0; ee < M::NE; ++ee) {
-              const int kx = KU * u + M::koff(g4, ee);
-              if (kx < DK) M::set(cf[u], ee, M::elem(cf[u], ee) * mid[kx]);
-            }
+          for (int j = 0; j < 4; ++j) {
+            accA[j] = FbA[(aa * 16 + m16) * 16 + 4 * g4 + j];
+            accP[j] = FbP[(aa * 16 + m16) * 16 + 4 * g4 + j];
           }
-          accA = M::mma(cf[u], kf[u], accA);
-          accP = M::mma(cf[u], qf[u], accP);
+        } else {
+          const IO *cb = (diag ? Xkir : Xks) + (16 * bb + m16) * LDK;
+          const float *mid =
+              (aa - bb >= 2) ? Mid + L::p2(aa, bb) * DK : nullptr;
+          frag cf[NKU];
+#pragma unroll
+          for (int u = 0; u < NKU; ++u) {
+            const bool full = (TPU == 1) || (TPU * u + 1 < NKT);
+            cf[u] = M::load_k(cb + KU * u, g4, full);
+          }
+#pragma unroll
+          for (int u = 0; u < NKU; ++u) {
+            if (mid) {
+#pragma unroll
+              for (int ee = 0; ee < M::NE; ++ee) {
+                const int kx = KU * u + M::koff(g4, ee);
+                if (kx < DK) M::set(cf[u], ee, M::elem(cf[u], ee) * mid[kx]);
+              }
+            }
+            accA = M::mma(cf[u], kf[u], accA);
+            accP = M::mma(cf[u], qf[u], accP);
+          }
         }
-      }
-      // lane (n = m16, g4): element j is row r = 16aa + m16, col s = 16bb+4g4+j
-      if (diag) {
+        // lane (n = m16, g4): element j is row 16aa + m16, col 16bb + 4g4 + j
+        if (diag) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int s = 4 * g4 + j;
-          if (!(s < m16)) accA[j] = 0.f;
-          if (!(s <= m16)) accP[j] = 0.f;
+          for (int j = 0; j < 4; ++j) {
+            const int sc = 4 * g4 + j;
+            if (!(sc < m16)) accA[j] = 0.f;
+            if (!(sc <= m16)) accP[j] = 0.f;
+          }
         }
-      }
-      *(f32x4 *)(Af + (16 * aa + m16) * LDA + 16 * bb + 4 * g4) = accA;
-      {
-        const int u = bb / TPU, hf = bb % TPU;
-        IO *dst = (IO *)(blk + W.off_p + ((size_t)(aa * NTU + u) * 64 + lane) *
-                                             16) + hf * 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dst[j] = from_f32<IO>(accP[j]);
-        if (TPU == 2 && diag && (aa % 2) == 0) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) dst[4 + j] = from_f32<IO>(0.f);
+        *(f32x4 *)(Af + (16 * aa + m16) * LDA + 16 * bb + 4 * g4) = accA;
+        {
+          const int u = bb / TPU, hf = bb % TPU;
+          char *dst = blk + W.off_p + ((size_t)(aa * NTU + u) * 64 + lane) * 16 +
+                      hf * 4 * sizeof(IO);
+          const float a4[4] = {accP[0], accP[1], accP[2], accP[3]};
+          *(typename V4::raw *)dst = V4::put(a4);
+          if (TPU == 2 && diag && (aa % 2) == 0) {
+            const float z[4] = {0.f, 0.f, 0.f, 0.f};
+            *(typename V4::raw *)(dst + 4 * sizeof(IO)) = V4::put(z);
+          }
         }
       }
     }
@@ -703,53 +711,52 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     }
 
     // ---- WU: -W (A-operand units) and U (accumulator tiles) ----------------
-    const int nW = NB * NKU, nU = NB * nvt;
-    for (int tk = wave; tk < nW + nU; tk += PREP_THREADS / 64) {
-      if (tk < nW) {
-        const int rt = tk / NKU, u = tk % NKU;
+    // wave rt takes token tile rt: its rows of T are read once and serve
+    // every key unit of W and every value slab of U
+    for (int rt = wave; rt < NB; rt += PREP_THREADS / 64) {
+      const int umax = (16 * rt + 15) / KU;  // last token unit T row rt uses
+      frag tb[NTU];
+#pragma unroll
+      for (int uu = 0; uu < NTU; ++uu) {
+        const bool fullT = (TPU == 1) || (TPU * uu + 1 < NB);
+        tb[uu] = M::load_k(Tb + (16 * rt + m16) * LDC + KU * min(uu, umax), g4,
+                           fullT);
+      }
+#pragma unroll
+      for (int u = 0; u < NKU; ++u) {
         f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        const int umax = (16 * rt + 15) / KU;
-        frag tb[NTU], xa[NTU][TPU];
+        frag xa[NTU][TPU];
 #pragma unroll
         for (int uu = 0; uu < NTU; ++uu) {
-          if (uu <= umax) {
-            const bool fullT = (TPU == 1) || (TPU * uu + 1 < NB);
-            tb[uu] = M::load_k(Tb + (16 * rt + m16) * LDC + KU * uu, g4, fullT);
+          const bool fullT = (TPU == 1) || (TPU * uu + 1 < NB);
 #pragma unroll
-            for (int hh = 0; hh < TPU; ++hh) {
-              const int ct = (TPU * u + hh) % NKT;
-              xa[uu][hh] = M::load_k(XkgT + (16 * ct + m16) * LDC + KU * uu, g4,
-                                     fullT);
-            }
-          }
-        }
-#pragma unroll
-        for (int uu = 0; uu < NTU; ++uu) {
-          if (uu <= umax) {
-#pragma unroll
-            for (int hh = 0; hh < TPU; ++hh)
-              if (TPU * u + hh < NKT) acc[hh] = M::mma(xa[uu][hh], tb[uu], acc[hh]);
-          }
-        }
-        const frag out = M::pack(-acc[0], -acc[1]);
-        *(frag *)(blk + W.off_negw + ((size_t)(rt * NKU + u) * 64 + lane) *
-                                         16) = out;
-      } else {
-        const int t2 = tk - nW, rt = t2 / nvt, vt = t2 % nvt;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const int umax = (16 * rt + 15) / KU;
-        frag ta[NTU], vb[NTU];
-#pragma unroll
-        for (int uu = 0; uu < NTU; ++uu) {
-          if (uu <= umax) {
-            const bool fullT = (TPU == 1) || (TPU * uu + 1 < NB);
-            ta[uu] = M::load_k(Tb + (16 * rt + m16) * LDC + KU * uu, g4, fullT);
-            vb[uu] = M::load_k(XvT + (16 * vt + m16) * LDC + KU * uu, g4, fullT);
+          for (int hh = 0; hh < TPU; ++hh) {
+            const int ct = (TPU * u + hh) % NKT;
+            xa[uu][hh] = M::load_k(XkgT + (16 * ct + m16) * LDC + KU * uu, g4,
+                                   fullT);
           }
         }
 #pragma unroll
         for (int uu = 0; uu < NTU; ++uu)
-          if (uu <= umax) acc = M::mma(ta[uu], vb[uu], acc);
+          if (uu <= umax)
+#pragma unroll
+            for (int hh = 0; hh < TPU; ++hh)
+              if (TPU * u + hh < NKT) acc[hh] = M::mma(xa[uu][hh], tb[uu], acc[hh]);
+        const frag out = M::pack(-acc[0], -acc[1]);
+        *(frag *)(blk + W.off_negw + ((size_t)(rt * NKU + u) * 64 + lane) *
+                                         16) = out;
+      }
+      for (int vt = 0; vt < nvt; ++vt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        frag vb[NTU];
+#pragma unroll
+        for (int uu = 0; uu < NTU; ++uu) {
+          const bool fullT = (TPU == 1) || (TPU * uu + 1 < NB);
+          vb[uu] = M::load_k(XvT + (16 * vt + m16) * LDC + KU * uu, g4, fullT);
+        }
+#pragma unroll
+        for (int uu = 0; uu < NTU; ++uu)
+          if (uu <= umax) acc = M::mma(tb[uu], vb[uu], acc);
         IO *dst = (IO *)(blk + W.off_u) +
                   ((size_t)(vt * NB + rt) * 64 + lane) * 4;
         float a4[4] = {acc[0], acc[1], acc[2], acc[3]};
