@@ -111,7 +111,10 @@ template <typename IO, bool CONV> struct Stage {
   uint32_t beta[8], betav[8];
 };
 
-template <typename IO, typename GT, int DK, int C, bool CONV>
+// PART selects what to fetch: 1 = g and beta, 2 = q, 4 = k, 8 = v (and the
+// V side's beta); the parts are issued in different phases of the previous
+// task so the vector memory queue drains between them
+template <int PART, typename IO, typename GT, int DK, int C, bool CONV>
 __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
                                           Stage<IO, CONV> &st, int tid) {
   constexpr int NQ = DK / 4, NTG = C / 8;
@@ -135,6 +138,7 @@ __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
     const unsigned short *bh16 = (const unsigned short *)p.beta + tok0 * H + h;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      if (!(PART & 1)) break;
       const unsigned t = (unsigned)min(t0 + 8 * tg + i, tlast);
       if (GB) {
         const uint2 v = *(const uint2 *)(gh + t * rowK);
@@ -151,12 +155,12 @@ __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
     for (int i = 0; i < Stage<IO, CONV>::XR; ++i) {
       const unsigned t =
           (unsigned)min(max(t0 + 8 * tg + i - (CONV ? 3 : 0), 0), tlast);
-      st.xq[i] = *(const R *)(xq + t * rowK);
-      st.xk[i] = *(const R *)(xk + t * rowK);
+      if (PART & 2) st.xq[i] = *(const R *)(xq + t * rowK);
+      if (PART & 4) st.xk[i] = *(const R *)(xk + t * rowK);
     }
   }
   const int NQV = Dv / 4;
-  if (tid < NQV * NTG) {
+  if ((PART & 8) && tid < NQV * NTG) {
     const int cv = tid % NQV, tg = tid / NQV;
     const unsigned rowV = (unsigned)(H * Dv);
     const IO *xv = (const IO *)(CONV ? p.xv : p.v) + (tok0 * H + h) * Dv +
@@ -231,7 +235,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
 
   Stage<IO, CONV> st;
   int task = blockIdx.x;
-  if (task < ntask) prep_load<IO, GT, DK, C, CONV>(p, task, st, tid);
+  if (task < ntask) prep_load<15, IO, GT, DK, C, CONV>(p, task, st, tid);
 
   for (; task < ntask; task += gridDim.x) {
     const int bh = task % BH, n = p.NC - 1 - task / BH;
@@ -513,9 +517,10 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     }
     __syncthreads();  // B2: region A complete
 
-    // stage the next task while this one runs on the matrix cores
-    if (task + (int)gridDim.x < ntask)
-      prep_load<IO, GT, DK, C, CONV>(p, task + gridDim.x, st, tid);
+    // stage the next task while this one runs on the matrix cores, a part
+    // per phase
+    const bool more = task + (int)gridDim.x < ntask;
+    if (more) prep_load<1, IO, GT, DK, C, CONV>(p, task + gridDim.x, st, tid);
 
     if (fallback) {
       // exact diagonal-block sums: task (sub-chunk a, column s, 16 channels)
@@ -623,6 +628,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
       }
     }
     __syncthreads();  // B3: region A no longer read
+    if (more) prep_load<2, IO, GT, DK, C, CONV>(p, task + gridDim.x, st, tid);
 
     // ---- T0: W/U inputs into the freed region, T zero-filled --------------
     static_assert((C * LDC * sizeof(IO)) % 16 == 0, "Tb rows");
@@ -649,6 +655,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
       }
     }
     __syncthreads();  // B4
+    if (more) prep_load<4, IO, GT, DK, C, CONV>(p, task + gridDim.x, st, tid);
 
     // ---- T1: inverse of each unit-lower 16x16 diagonal block (fp32) ------
     // With L the strictly lower block (L^16 = 0),
@@ -710,6 +717,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
       __syncthreads();
     }
 
+    if (more) prep_load<8, IO, GT, DK, C, CONV>(p, task + gridDim.x, st, tid);
     // ---- WU: -W (A-operand units) and U (accumulator tiles) ----------------
     // wave rt takes token tile rt: its rows of T are read once and serve
     // every key unit of W and every value slab of U
