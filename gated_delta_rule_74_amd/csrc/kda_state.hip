@@ -61,69 +61,67 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-constexpr int STATE_WAVES = 4;  // compute waves; one more wave warms L2
-constexpr int STATE_PF = 4;     // chunks between warming and use
+// Wave roles of a workgroup: SW state waves (Delta and the state update),
+// OW output waves (O), and with STATE_WARM one L2 warm-up wave.
+constexpr int SW = 4, OW = 4;
+constexpr bool STATE_WARM = true;
+constexpr int STATE_PF = 4;  // chunks between warming and use
+constexpr int STATE_THREADS = 64 * (SW + OW + (STATE_WARM ? 1 : 0));
 
 template <typename IO, int DK, int C, int NS> struct SP {
   static constexpr int TPU = Mma<IO>::TPU;
   static constexpr int NB = C / 16, NKT = DK / 16;
   static constexpr int NKU = (NKT + TPU - 1) / TPU;  // key units
   static constexpr int NTU = (NB + TPU - 1) / TPU;   // token units
-  static constexpr int KUW = (NKU + STATE_WAVES - 1) / STATE_WAVES;
+  static constexpr int KUW = (NKU + SW - 1) / SW;    // key units per wave
   static constexpr size_t oSU = 0;                          // [NS][NKU]
   static constexpr size_t oDU = (size_t)NS * NKU * 1024;    // [NS][NTU]
   static constexpr size_t LDS = oDU + (size_t)NS * NTU * 1024;
 };
 
-// one wave's factors of one chunk
-template <typename IO, int DK, int C, int NS> struct FragSet {
+// a state wave's factors of one chunk: its rows of -W and U, and of Ktil^T
+// with gamma_C for its key units
+template <typename IO, int DK, int C, int NS> struct SFrag {
   using G = SP<IO, DK, C, NS>;
   typedef typename Mma<IO>::frag frag;
-  frag w[G::NKU], q[G::NKU], p[G::NTU];
+  frag w[G::NKU];
+  typename Vec4T<IO>::raw u[NS];
   frag k[G::KUW][G::TPU][G::NTU];
   f32x4 gm[G::KUW][G::TPU];
-  typename Vec4T<IO>::raw u[NS];
+};
+// an output wave's factors of one chunk: its rows of Qtil and P
+template <typename IO, int DK, int C, int NS> struct OFrag {
+  using G = SP<IO, DK, C, NS>;
+  typedef typename Mma<IO>::frag frag;
+  frag q[G::NKU], p[G::NTU];
 };
 
-// Half A (-W, Qtil, U: what the products before the Delta exchange need)
-// or half B (P, Ktil^T, gamma_C) of one wave's factors of a chunk.
+// half 0 of a state wave's factors (-W, U: needed before the Delta
+// exchange) or half 1 (Ktil^T, gamma_C)
 template <int HALF, typename IO, int DK, int C, int NS>
-__device__ __forceinline__ void load_frags(FragSet<IO, DK, C, NS> &f,
+__device__ __forceinline__ void load_state(SFrag<IO, DK, C, NS> &f,
                                            const char *blk, const WsLayout &W,
-                                           int rtc, int wave, int lane,
-                                           int g4, int vt0) {
+                                           int rtc, int w4, int lane, int g4,
+                                           int vt0) {
   using G = SP<IO, DK, C, NS>;
   typedef typename Mma<IO>::frag frag;
   typedef typename Vec4T<IO>::raw URaw;
   if (HALF == 0) {
     const frag *Lw = (const frag *)(blk + W.off_negw) + lane;
-    const frag *Lq = (const frag *)(blk + W.off_qt) + lane;
     const URaw *Lu = (const URaw *)(blk + W.off_u) + lane;
 #pragma unroll
     for (int u = 0; u < G::NKU; ++u) f.w[u] = Lw[(rtc * G::NKU + u) * 64];
 #pragma unroll
-    for (int u = 0; u < G::NKU; ++u) f.q[u] = Lq[(rtc * G::NKU + u) * 64];
-#pragma unroll
     for (int s = 0; s < NS; ++s) f.u[s] = Lu[((vt0 + s) * G::NB + rtc) * 64];
   } else {
     const frag *Lk = (const frag *)(blk + W.off_ktt) + lane;
-    const frag *Lp = (const frag *)(blk + W.off_p) + lane;
     const float *Lg = (const float *)(blk + W.off_gam) + 4 * g4;
-    // P units above the diagonal are never written by the prep: their bits
-    // are cleared so the product can run unconditionally
-#pragma unroll
-    for (int u = 0; u < G::NTU; ++u) {
-      const unsigned keep = (G::NTU == 1 || u <= rtc / G::TPU) ? ~0u : 0u;
-      uint4 r = __builtin_bit_cast(uint4, Lp[(rtc * G::NTU + u) * 64]);
-      r.x &= keep; r.y &= keep; r.z &= keep; r.w &= keep;
-      f.p[u] = __builtin_bit_cast(frag, r);
-    }
 #pragma unroll
     for (int j = 0; j < G::KUW; ++j)
 #pragma unroll
       for (int h = 0; h < G::TPU; ++h) {
-        // key tile of (unit wave + 4j, half h), clamped to a valid one
-        const int t = min(G::TPU * (wave + STATE_WAVES * j) + h, G::NKT - 1);
+        // key tile of (unit w4 + SW j, half h), clamped to a valid one
+        const int t = min(G::TPU * (w4 + SW * j) + h, G::NKT - 1);
 #pragma unroll
         for (int u = 0; u < G::NTU; ++u)
           f.k[j][h][u] = Lk[(t * G::NTU + u) * 64];
@@ -132,13 +130,51 @@ __device__ __forceinline__ void load_frags(FragSet<IO, DK, C, NS> &f,
   }
 }
 
+// half 0 of an output wave's factors (Qtil) or half 1 (P)
+template <int HALF, typename IO, int DK, int C, int NS>
+__device__ __forceinline__ void load_out(OFrag<IO, DK, C, NS> &f,
+                                         const char *blk, const WsLayout &W,
+                                         int rtc, int lane) {
+  using G = SP<IO, DK, C, NS>;
+  typedef typename Mma<IO>::frag frag;
+  if (HALF == 0) {
+    const frag *Lq = (const frag *)(blk + W.off_qt) + lane;
+#pragma unroll
+    for (int u = 0; u < G::NKU; ++u) f.q[u] = Lq[(rtc * G::NKU + u) * 64];
+  } else {
+    // P units above the diagonal are never written by the prep: their bits
+    // are cleared so the product can run unconditionally
+    const frag *Lp = (const frag *)(blk + W.off_p) + lane;
+#pragma unroll
+    for (int u = 0; u < G::NTU; ++u) {
+      const unsigned keep = (G::NTU == 1 || u <= rtc / G::TPU) ? ~0u : 0u;
+      uint4 r = __builtin_bit_cast(uint4, Lp[(rtc * G::NTU + u) * 64]);
+      r.x &= keep; r.y &= keep; r.z &= keep; r.w &= keep;
+      f.p[u] = __builtin_bit_cast(frag, r);
+    }
+  }
+}
+
+// interleave the next chunk's NL loads with this phase's NM products
+template <int NR, int NM, int NL>
+__device__ __forceinline__ void interleave_loads() {
+  if (NR > 0) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // LDS reads
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+  if (NL > NM) __builtin_amdgcn_sched_group_barrier(0x020, NL - NM, 0);
+}
+
 template <typename IO, int DK, int C, int NS>
-__global__ __launch_bounds__(64 * (STATE_WAVES + 1), 1) void kda_state_pass(
+__global__ __launch_bounds__(STATE_THREADS, 1) void kda_state_pass(
     PrefillParams p) {
   using M = Mma<IO>;
   using G = SP<IO, DK, C, NS>;
   using V4 = Vec4T<IO>;
-  using FS = FragSet<IO, DK, C, NS>;
+  using SF = SFrag<IO, DK, C, NS>;
+  using OF = OFrag<IO, DK, C, NS>;
   typedef typename M::frag frag;
   constexpr int NB = G::NB, NKT = G::NKT, TPU = G::TPU, NKU = G::NKU,
                 NTU = G::NTU, KUW = G::KUW;
@@ -169,13 +205,192 @@ __global__ __launch_bounds__(64 * (STATE_WAVES + 1), 1) void kda_state_pass(
   const WsLayout W = ws_layout(DK, Dv, C, (int)sizeof(IO));
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   const char *ws0 = p.ws + (size_t)bh * NC * p.wsb;
+  const int w4 = wave % 4;                     // index within the role
+  const bool rv = (NB >= 4) || w4 < NB;        // owns a token tile
+  const int rtc = min(w4, NB - 1);             // (clamped) token tile
 
-  if (wave == STATE_WAVES) {
-    // L2 warm-up wave: touches 4 bytes of every 128-byte line of the block of
-    // chunk n + STATE_PF while chunk n is computed (the ng workgroups of the
-    // head split the lines), as direct-to-LDS loads into a sink so nothing
-    // ever waits for them.  It takes part in every barrier of the compute
-    // waves (one before the loop, two per chunk).
+  // the upper half of the last token unit stays zero when NB is odd
+  for (int i = tid; i < NS * NTU * 256; i += STATE_THREADS)
+    ((float *)DU)[i] = 0.f;
+
+  if (wave < SW) {
+    // ================= state waves: Delta and the state update ==========
+    bool kv[KUW];
+#pragma unroll
+    for (int j = 0; j < KUW; ++j)
+      kv[j] = (NKU % SW == 0) || w4 + SW * j < NKU;
+    // state rows owned by this wave: key tiles TPU*u + hh of its units
+    f32x4 S[KUW][TPU][NS];
+#pragma unroll
+    for (int j = 0; j < KUW; ++j)
+#pragma unroll
+      for (int hh = 0; hh < TPU; ++hh)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          S[j][hh][s] = zero;
+          const int t = TPU * (w4 + SW * j) + hh;
+          if (p.s0 && kv[j] && t < NKT) {
+            const float *s0 = p.s0 + ((size_t)bh * DK + 16 * t + 4 * g4) * Dv +
+                              16 * (vt0 + s) + m16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[j][hh][s][e] = s0[(size_t)e * Dv];
+          }
+        }
+    auto publish_s = [&]() {
+#pragma unroll
+      for (int j = 0; j < KUW; ++j)
+        if (kv[j]) {
+          const int u = w4 + SW * j;
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            const bool hi = TPU == 2 && TPU * u + 1 < NKT;
+            SU[(s * NKU + u) * 64 + lane] =
+                M::pack(S[j][0][s], hi ? S[j][TPU - 1][s] : zero);
+          }
+        }
+    };
+    publish_s();
+    lds_barrier();
+
+    auto sstep = [&](int n, const SF &f, SF &nx) {
+      const char *nblk = ws0 + (size_t)min(n + 1, NC - 1) * p.wsb;
+      load_state<0, IO, DK, C, NS>(nx, nblk, W, rtc, w4, lane, g4, vt0);
+      frag sb[NS][NKU];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int u = 0; u < NKU; ++u) sb[s][u] = SU[(s * NKU + u) * 64 + lane];
+      // Delta rows of token tile rtc: U - W S  (-W is stored)
+      f32x4 d[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) d[s] = V4::get(f.u[s]);
+#pragma unroll
+      for (int u = 0; u < NKU; ++u)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) d[s] = M::mma(f.w[u], sb[s][u], d[s]);
+      if (rv) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          frag *dst = DU + (s * NTU + rtc / TPU) * 64 + lane;
+          if (TPU == 2) {
+            // half (rtc & 1) of the token unit: 4 values at byte 8*(rtc&1)
+            bf16x4 v4 = {(bf16)d[s][0], (bf16)d[s][1], (bf16)d[s][2],
+                         (bf16)d[s][3]};
+            *(bf16x4 *)((char *)dst + 8 * (rtc & 1)) = v4;
+          } else {
+            *(f32x4 *)dst = d[s];
+          }
+        }
+      }
+      interleave_loads<NS * NKU, NKU * NS, NKU + NS>();
+      lds_barrier();  // Delta complete in DU
+      load_state<1, IO, DK, C, NS>(nx, nblk, W, rtc, w4, lane, g4, vt0);
+      frag db[NS][NTU];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int u = 0; u < NTU; ++u) db[s][u] = DU[(s * NTU + u) * 64 + lane];
+      // S <- diag(gamma_C) S + Ktil^T Delta on the owned key tiles
+#pragma unroll
+      for (int j = 0; j < KUW; ++j)
+#pragma unroll
+        for (int hh = 0; hh < TPU; ++hh)
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            f32x4 sn = S[j][hh][s] * f.gm[j][hh];
+#pragma unroll
+            for (int u = 0; u < NTU; ++u)
+              sn = M::mma(f.k[j][hh][u], db[s][u], sn);
+            S[j][hh][s] = sn;
+          }
+      publish_s();
+      interleave_loads<NS * NTU, KUW * TPU * NS * NTU, KUW * TPU * (NTU + 1)>();
+      lds_barrier();  // S complete in SU
+    };
+
+    SF f0, f1;
+    load_state<0, IO, DK, C, NS>(f0, ws0, W, rtc, w4, lane, g4, vt0);
+    load_state<1, IO, DK, C, NS>(f0, ws0, W, rtc, w4, lane, g4, vt0);
+    for (int n = 0; n < NC; n += 2) {
+      sstep(n, f0, f1);
+      if (n + 1 >= NC) break;
+      sstep(n + 1, f1, f0);
+    }
+    if (p.s_out) {
+#pragma unroll
+      for (int j = 0; j < KUW; ++j)
+#pragma unroll
+        for (int hh = 0; hh < TPU; ++hh) {
+          const int t = TPU * (w4 + SW * j) + hh;
+          if (kv[j] && t < NKT) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+              float *so = p.s_out + ((size_t)bh * DK + 16 * t + 4 * g4) * Dv +
+                          16 * (vt0 + s) + m16;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) so[(size_t)e * Dv] = S[j][hh][s][e];
+            }
+          }
+        }
+    }
+  } else if (wave < SW + OW) {
+    // ================= output waves: O ==================================
+    IO *obase = (IO *)p.o + ((size_t)bb * T * H + h) * Dv + 16 * vt0 + 4 * g4;
+    const size_t orow = (size_t)H * Dv;  // elements between tokens
+    lds_barrier();
+    auto ostep = [&](int n, const OF &f, OF &nx) {
+      const char *nblk = ws0 + (size_t)min(n + 1, NC - 1) * p.wsb;
+      load_out<0, IO, DK, C, NS>(nx, nblk, W, rtc, lane);
+      // O^T (value columns x tokens of tile rtc) = S^T Qtil^T + Delta^T P^T,
+      // S being the state at the chunk start (SU until the state update)
+      frag sb[NS][NKU];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int u = 0; u < NKU; ++u) sb[s][u] = SU[(s * NKU + u) * 64 + lane];
+      f32x4 ot[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) ot[s] = zero;
+#pragma unroll
+      for (int u = 0; u < NKU; ++u)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) ot[s] = M::mma(sb[s][u], f.q[u], ot[s]);
+      interleave_loads<NS * NKU, NKU * NS, NKU>();
+      lds_barrier();  // Delta complete in DU
+      load_out<1, IO, DK, C, NS>(nx, nblk, W, rtc, lane);
+      frag db[NS][NTU];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int u = 0; u < NTU; ++u) db[s][u] = DU[(s * NTU + u) * 64 + lane];
+#pragma unroll
+      for (int u = 0; u < NTU; ++u)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) ot[s] = M::mma(db[s][u], f.p[u], ot[s]);
+      // lane (g4, m16) holds token 16 rtc + m16, value columns 4 g4 .. 4 g4 + 3
+      const int tok = n * C + 16 * rtc + m16;
+      if (rv && tok < T) {
+        IO *dst = obase + (size_t)tok * orow;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+          *(typename V4::raw *)(dst + 16 * s) = V4::put(ot[s]);
+      }
+      lds_barrier();  // the state update has left SU
+    };
+    OF f0, f1;
+    load_out<0, IO, DK, C, NS>(f0, ws0, W, rtc, lane);
+    load_out<1, IO, DK, C, NS>(f0, ws0, W, rtc, lane);
+    for (int n = 0; n < NC; n += 2) {
+      ostep(n, f0, f1);
+      if (n + 1 >= NC) break;
+      ostep(n + 1, f1, f0);
+    }
+  } else {
+    // ================= L2 warm-up wave ==================================
+    // touches 4 bytes of every 128-byte line of the block of chunk
+    // n + STATE_PF while chunk n is computed (the ng workgroups of the head
+    // split the lines), as direct-to-LDS loads into a sink so nothing ever
+    // waits for them; it takes part in every barrier
     __shared__ __attribute__((aligned(256))) char sink[256];
     const int nline = (int)((p.wsb + 127) / 128);
     const int share = (nline + ng - 1) / ng;
@@ -197,187 +412,6 @@ __global__ __launch_bounds__(64 * (STATE_WAVES + 1), 1) void kda_state_pass(
       lds_barrier();
       lds_barrier();
     }
-    return;
-  }
-
-  // this wave's token tile and key units (wave-uniform); out-of-range
-  // shares are computed on clamped data and never written
-  const bool rv = (NB >= STATE_WAVES) || wave < NB;
-  const int rtc = min(wave, NB - 1);
-  bool kv[KUW];
-#pragma unroll
-  for (int j = 0; j < KUW; ++j)
-    kv[j] = (NKU % STATE_WAVES == 0) || wave + STATE_WAVES * j < NKU;
-
-  // ---- state rows owned by this wave: key tiles TPU*u + hh of its units ---
-  f32x4 S[KUW][TPU][NS];
-#pragma unroll
-  for (int j = 0; j < KUW; ++j)
-#pragma unroll
-    for (int hh = 0; hh < TPU; ++hh)
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        S[j][hh][s] = zero;
-        const int t = TPU * (wave + STATE_WAVES * j) + hh;
-        if (p.s0 && kv[j] && t < NKT) {
-          const float *s0 = p.s0 + ((size_t)bh * DK + 16 * t + 4 * g4) * Dv +
-                            16 * (vt0 + s) + m16;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) S[j][hh][s][e] = s0[(size_t)e * Dv];
-        }
-      }
-  // publish S in operand form
-  auto publish_s = [&]() {
-#pragma unroll
-    for (int j = 0; j < KUW; ++j)
-      if (kv[j]) {
-        const int u = wave + STATE_WAVES * j;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const bool hi = TPU == 2 && TPU * u + 1 < NKT;
-          SU[(s * NKU + u) * 64 + lane] =
-              M::pack(S[j][0][s], hi ? S[j][TPU - 1][s] : zero);
-        }
-      }
-  };
-
-  IO *obase = (IO *)p.o + ((size_t)bb * T * H + h) * Dv + 16 * vt0 + 4 * g4;
-  const size_t orow = (size_t)H * Dv;  // elements between tokens
-
-  // one chunk step on the factors in f
-  // the loads of chunk n+1 are spread over chunk n's two phases, each
-  // interleaved with that phase's products, so that issuing them (the
-  // vector memory pipe takes about one 1 KiB fragment per 16 cycles per CU)
-  // overlaps the matrix-core work instead of adding to it
-  auto step = [&](int n, const FS &f, FS &nx) {
-    const char *nblk = ws0 + (size_t)min(n + 1, NC - 1) * p.wsb;
-    load_frags<0, IO, DK, C, NS>(nx, nblk, W, rtc, wave, lane, g4, vt0);
-    // S at the chunk start, all key units, as the second operand
-    frag sb[NS][NKU];
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int u = 0; u < NKU; ++u) sb[s][u] = SU[(s * NKU + u) * 64 + lane];
-    // Delta rows of token tile rtc: U - W S  (-W is stored)
-    f32x4 d[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) d[s] = V4::get(f.u[s]);
-#pragma unroll
-    for (int u = 0; u < NKU; ++u)
-#pragma unroll
-      for (int s = 0; s < NS; ++s) d[s] = M::mma(f.w[u], sb[s][u], d[s]);
-    if (rv) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        frag *dst = DU + (s * NTU + rtc / TPU) * 64 + lane;
-        if (TPU == 2) {
-          // half (rtc & 1) of the token unit: 4 values at byte 8*(rtc&1)
-          bf16x4 v4 = {(bf16)d[s][0], (bf16)d[s][1], (bf16)d[s][2],
-                       (bf16)d[s][3]};
-          *(bf16x4 *)((char *)dst + 8 * (rtc & 1)) = v4;
-        } else {
-          *(f32x4 *)dst = d[s];
-        }
-      }
-    }
-    // O^T (value columns x tokens of tile rtc) = S^T Qtil^T + ...
-    f32x4 ot[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) ot[s] = zero;
-#pragma unroll
-    for (int u = 0; u < NKU; ++u)
-#pragma unroll
-      for (int s = 0; s < NS; ++s) ot[s] = M::mma(sb[s][u], f.q[u], ot[s]);
-    {
-      constexpr int NL = 2 * NKU + NS, NM = 2 * NKU * NS;
-      __builtin_amdgcn_sched_group_barrier(0x100, NS * NKU, 0);  // S reads
-#pragma unroll
-      for (int i = 0; i < NM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i < NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
-      if (NL > NM) __builtin_amdgcn_sched_group_barrier(0x020, NL - NM, 0);
-    }
-    lds_barrier();  // Delta complete in DU
-    load_frags<1, IO, DK, C, NS>(nx, nblk, W, rtc, wave, lane, g4, vt0);
-
-    frag db[NS][NTU];
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int u = 0; u < NTU; ++u) db[s][u] = DU[(s * NTU + u) * 64 + lane];
-    // S <- diag(gamma_C) S + Ktil^T Delta on the owned key tiles
-#pragma unroll
-    for (int j = 0; j < KUW; ++j)
-#pragma unroll
-      for (int hh = 0; hh < TPU; ++hh)
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          f32x4 sn = S[j][hh][s] * f.gm[j][hh];
-#pragma unroll
-          for (int u = 0; u < NTU; ++u) sn = M::mma(f.k[j][hh][u], db[s][u], sn);
-          S[j][hh][s] = sn;
-        }
-    // ... + Delta^T P^T (P is zero above the diagonal)
-#pragma unroll
-    for (int u = 0; u < NTU; ++u)
-#pragma unroll
-      for (int s = 0; s < NS; ++s) ot[s] = M::mma(db[s][u], f.p[u], ot[s]);
-    // lane (g4, m16) holds token 16 rtc + m16, value columns 4 g4 .. 4 g4 + 3
-    const int tok = n * C + 16 * rtc + m16;
-    if (rv && tok < T) {
-      IO *dst = obase + (size_t)tok * orow;
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-        *(typename V4::raw *)(dst + 16 * s) = V4::put(ot[s]);
-    }
-    publish_s();
-    {
-      constexpr int NL = NTU + KUW * TPU * (NTU + 1);
-      constexpr int NM = NTU * NS + KUW * TPU * NS * NTU;
-      __builtin_amdgcn_sched_group_barrier(0x100, NS * NTU, 0);  // Delta reads
-#pragma unroll
-      for (int i = 0; i < NM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i < NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
-      if (NL > NM) __builtin_amdgcn_sched_group_barrier(0x020, NL - NM, 0);
-    }
-    lds_barrier();  // S complete in SU
-  };
-
-  // the upper half of the last token unit stays zero when NB is odd
-  for (int i = tid; i < NS * NTU * 256; i += 64 * STATE_WAVES)
-    ((float *)DU)[i] = 0.f;
-  publish_s();
-  lds_barrier();
-
-  // two rotating factor sets: chunk n+1 is fetched while chunk n is computed
-  FS f0, f1;
-  load_frags<0, IO, DK, C, NS>(f0, ws0, W, rtc, wave, lane, g4, vt0);
-  load_frags<1, IO, DK, C, NS>(f0, ws0, W, rtc, wave, lane, g4, vt0);
-  for (int n = 0; n < NC; n += 2) {
-    step(n, f0, f1);
-    if (n + 1 >= NC) break;
-    step(n + 1, f1, f0);
-  }
-
-  if (p.s_out) {
-#pragma unroll
-    for (int j = 0; j < KUW; ++j)
-#pragma unroll
-      for (int hh = 0; hh < TPU; ++hh) {
-        const int t = TPU * (wave + STATE_WAVES * j) + hh;
-        if (kv[j] && t < NKT) {
-#pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            float *so = p.s_out + ((size_t)bh * DK + 16 * t + 4 * g4) * Dv +
-                        16 * (vt0 + s) + m16;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) so[(size_t)e * Dv] = S[j][hh][s][e];
-          }
-        }
-      }
   }
 }
 
@@ -395,7 +429,7 @@ template <typename IO, int DK, int C, int NS>
 static hipError_t state_ns(const PrefillParams &p, hipStream_t s) {
   const unsigned nblk = (unsigned)(p.B * p.H) * (unsigned)(p.Dv / (16 * NS));
   hipLaunchKernelGGL((kda_state_pass<IO, DK, C, NS>), dim3(nblk),
-                     dim3(64 * (STATE_WAVES + 1)), 0, s, p);
+                     dim3(STATE_THREADS), 0, s, p);
   return hipGetLastError();
 }
 
@@ -403,8 +437,7 @@ template <typename IO, int DK, int C>
 static hipError_t state_one(const PrefillParams &p, hipStream_t s) {
   // slabs per workgroup: one while that fills the chip, two when the
   // workgroups would otherwise run in several rounds (the second slab reuses
-  // the fetched factors); more would not fit the registers beside the fifth
-  // wave
+  // the fetched factors); more would not fit the registers
   const long long slabs = p.Dv / 16, units = (long long)p.B * p.H * slabs;
   const long long cus = state_cu_count();
   if constexpr (sizeof(IO) == 2 || DK < 128) {
