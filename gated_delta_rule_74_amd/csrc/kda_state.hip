@@ -7,24 +7,26 @@
 // in order, which is the chunked form of the per-token KDA rule (state rows
 // are key channels; see include/kda.h for the sources).
 //
-// Work split.  A workgroup of four waves owns one (batch*head) and NS
-// consecutive 16-column value slabs.  Every product is split by its output
-// rows, so each wave reads only its own share of the chunk's factors:
-//   * Delta and O: wave w computes token tile w (16 tokens) from its rows of
-//     -W, Qtil, P and U;
-//   * S: wave w owns the state rows of key unit w (32 keys in bf16, 16 in
-//     fp32; units w, w+4, ... when there are more than four) and updates
-//     them from its rows of Ktil^T.
-// The products need the whole S (for Delta and O) and the whole Delta (for
-// S and O) as the second operand, so both are exchanged through LDS in the
-// matrix-core operand layout: two barriers per chunk.  O is produced
-// transposed (O^T = S^T Qtil^T + Delta^T P^T) so that each lane ends up with
-// four consecutive value columns of one token: one vector store per slab.
+// Work split.  A workgroup owns one (batch*head) and NS consecutive
+// 16-column value slabs, with three wave roles:
+//   * four state waves: state wave w computes the Delta rows of token tile w
+//     (16 tokens) from its rows of -W and U, and owns the state rows of key
+//     unit w (32 keys in bf16, 16 in fp32; units w, w+4, ... when there are
+//     more than four), which it updates from its rows of Ktil^T;
+//   * four output waves: output wave w computes the O rows of token tile w
+//     from its rows of Qtil and P;
+//   * one warm-up wave that pulls the blocks of later chunks into L2.
+// Every product is split by its output rows, so each wave reads only its
+// own share of the chunk's factors.  The products need the whole S (for
+// Delta and O) and the whole Delta (for S and O) as the second operand, so
+// both are exchanged through LDS in the matrix-core operand layout: two
+// barriers per chunk.  O is produced transposed (O^T = S^T Qtil^T +
+// Delta^T P^T) so that each lane ends up with four consecutive value
+// columns of one token: one vector store per slab.
 //
 // Each wave fetches its factors straight from global memory into registers
-// one chunk ahead (two rotating register sets), so their latency overlaps
-// the previous chunk step, and a fifth wave pulls the blocks of later chunks
-// into L2 ahead of that fetch; only the exchange round trips and the short
+// one chunk ahead (two rotating register sets), the loads interleaved with
+// the current chunk's products; only the exchange round trips and the short
 // MFMA chains sit on the sequential path.
 #include "kda_device.h"
 #include "kda_internal.h"
