@@ -246,7 +246,35 @@ def main():
                           peak=HBM_PEAK_GBS, unit="GB/s",
                           frac=gbs / HBM_PEAK_GBS, traffic=tr))
         log(f"decode: {ms*1e3:.1f} us/step, {gbs:.0f} GB/s")
-        del xs, st
+        # the speculative-decoding verify step: 2 tokens per sequence (one
+        # guessed token), state read and written once per call
+        L = 2
+        xt = ki.prefill_inputs(N, L, H3, D3, D3, qkv="bf16", gate="bf16",
+                               seed=5, device=dev)
+        ot = torch.empty((N, L, H3, D3), dtype=torch.bfloat16, device=dev)
+        reps = max(10, steps // 5)
+        callt = lambda: kda.kda_decode_tokens(xt["q"], xt["k"], xt["v"],
+                                              xt["g"], xt["beta"], st,
+                                              state_out=st, o=ot)
+        for _ in range(5):
+            callt()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(reps):
+            callt()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        mt = e0.elapsed_time(e1) / reps
+        byt = N * H3 * (2 * D3 * D3 * 4 + L * (3 * D3 + 2 * D3 + 1) * 2)
+        out["decode"]["verify_step"] = dict(
+            tokens_per_sequence=L, calls=reps, us_per_call=mt * 1e3,
+            tokens_per_s=N * L / (mt * 1e-3),
+            achieved_gbs=byt / (mt * 1e-3) / 1e9,
+            hbm_frac=byt / (mt * 1e-3) / 1e9 / HBM_PEAK_GBS)
+        log(f"decode verify (L={L}): {mt*1e3:.1f} us/call, "
+            f"{N * L / (mt * 1e-3) / 1e6:.2f} M tokens/s")
+        del xs, st, xt
         torch.cuda.empty_cache()
 
     # ---------------- fused-conv prefill and long context -------------------

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing: build it with "
-        "`python -m gated_delta_rule_74_amd.build` (hipcc, gfx950)")
+        "`python gated_delta_rule_74_amd/build.py` (hipcc, gfx950)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -60,6 +60,9 @@ _state = _sig("kda_prefill_state_pass", _i,
 _decode = _sig("kda_decode_step", _i,
                [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp] + [_i] * 4 +
                [_f, _vp])
+_decode_tokens = _sig("kda_decode_tokens", _i,
+                      [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp, _vp] +
+                      [_i] * 5 + [_f, _vp])
 _conv = _sig("kda_conv_prologue", _i,
              [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp] +
              [_i] * 5 + [_i, _f, _vp])
@@ -199,6 +202,35 @@ def kda_decode_step(q, k, v, g, beta, state, *, scale=1.0, o=None,
                  _stream(stream))
     _check(st, "kda_decode_step")
     return o
+
+
+def kda_decode_tokens(q, k, v, g, beta, state_in, *, state_out=None,
+                      token_states=False, scale=1.0, o=None, stream=None):
+    """L tokens per sequence in one call (the speculative-decoding verify
+    step).  q,k,g [N,L,H,Dk], v [N,L,H,Dv], beta [N,L,H]; state_in
+    [N,H,Dk,Dv] fp32.  state_out: a tensor to write the final state into
+    (pass state_in itself for in place; default: a new tensor).
+    token_states: True for a new [N,L,H,Dk,Dv] tensor of the state after
+    each token, a tensor to fill, or False.  Returns (o, state_out,
+    token_states or None)."""
+    N, L, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((N, L, H, Dv), dtype=q.dtype, device=q.device)
+    if state_out is None:
+        state_out = torch.empty_like(state_in)
+    ts = None
+    if token_states is True:
+        ts = torch.empty((N, L, H, Dk, Dv), dtype=torch.float32,
+                         device=q.device)
+    elif token_states is not False and token_states is not None:
+        ts = token_states
+    st = _decode_tokens(_ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(g),
+                        _ptr(beta), _dt(g), _ptr(state_in), _ptr(state_out),
+                        _ptr(ts), _ptr(o), N, L, H, Dk, Dv, scale,
+                        _stream(stream))
+    _check(st, "kda_decode_tokens")
+    return o, state_out, ts
 
 
 def kda_conv_prologue(xq, xk, xv, wq, wk, wv, *, H, Dk, Dv, conv_state=None,

@@ -1,6 +1,6 @@
 """Build libkda.so (HIP, gfx950) in-tree with hipcc.
 
-    python -m gated_delta_rule_74_amd.build
+    python gated_delta_rule_74_amd/build.py     (or __graft_entry__.build())
 
 Every call recompiles (the objects are small and the check is cheap to keep
 honest).  Packed-fp32 instructions are disabled for all device code.

@@ -206,8 +206,41 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
   kda::DecodeParams p{};
   p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
   p.gate_bf16 = gate_dtype == KDA_BF16;
-  p.state = state; p.o = o;
-  p.N = N; p.H = H; p.Dk = Dk; p.Dv = Dv; p.scale = scale;
+  p.state_in = state; p.state_out = state; p.tstates = nullptr; p.o = o;
+  p.N = N; p.L = 1; p.H = H; p.Dk = Dk; p.Dv = Dv; p.scale = scale;
+  return hip_status(kda::launch_decode(p, qkv_dtype == KDA_BF16,
+                                       (hipStream_t)stream));
+}
+
+kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
+                             kda_dtype qkv_dtype, const void *g,
+                             const void *beta, kda_dtype gate_dtype,
+                             const float *state_in, float *state_out,
+                             float *token_states, void *o, int N, int L,
+                             int H, int Dk, int Dv, float scale,
+                             void *stream) {
+  if (N <= 0 || L <= 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_EINVAL;
+  if (!q || !k || !v || !g || !beta || !state_in || !state_out || !o)
+    return KDA_EINVAL;
+  if (!dtype_valid(qkv_dtype) || !dtype_valid(gate_dtype)) return KDA_EINVAL;
+  if (!isfinite(scale)) return KDA_EINVAL;
+  const void *ptrs[] = {q, k, v, g, beta, state_in, state_out, token_states, o};
+  for (const void *ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return KDA_EINVAL;
+  if (o == q || o == k || o == v || o == g || o == beta || o == state_in ||
+      o == state_out || (token_states && (token_states == state_in ||
+                                          token_states == state_out)))
+    return KDA_EINVAL;
+  if (!dim_ok(Dk) || !dim_ok(Dv)) return KDA_EUNSUPPORTED;
+  if (!pair_ok(qkv_dtype, gate_dtype)) return KDA_EUNSUPPORTED;
+  if ((long long)N * H > 0x7fffffffLL || (long long)N * L * H > 0x7fffffffLL)
+    return KDA_EUNSUPPORTED;
+  kda::DecodeParams p{};
+  p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+  p.gate_bf16 = gate_dtype == KDA_BF16;
+  p.state_in = state_in; p.state_out = state_out; p.tstates = token_states;
+  p.o = o;
+  p.N = N; p.L = L; p.H = H; p.Dk = Dk; p.Dv = Dv; p.scale = scale;
   return hip_status(kda::launch_decode(p, qkv_dtype == KDA_BF16,
                                        (hipStream_t)stream));
 }

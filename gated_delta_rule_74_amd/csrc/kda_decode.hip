@@ -1,19 +1,23 @@
-// kda_decode.hip -- one recurrent KDA step for N independent sequences.
+// kda_decode.hip -- recurrent KDA steps for N independent sequences: one
+// token (the generation step) or L tokens at once (the verify step of
+// speculative decoding).
 //
-// Per (sequence, head), with e = exp(g) per key channel (see include/kda.h
-// for the sources):
+// Per (sequence, head) and token, with e = exp(g) per key channel (see
+// include/kda.h for the sources):
 //   u = S^T (e * k)      value the decayed state predicts for k
 //   y = S^T (e * q)      read-out of the decayed state
 //   delta = beta (v - u)
-//   S <- diag(e) S + k delta^T               (in place)
+//   S <- diag(e) S + k delta^T
 //   o = scale (y + (q . k) delta)            (= scale S_new^T q)
 // The state is the only large operand (Dk*Dv fp32 per head), so the kernel
 // is an HBM stream: each workgroup loads its share of the state once with
-// 16-byte non-temporal loads into registers, reduces over rows through LDS,
-// and writes it back once.  Every sum runs over rows (key channels) for a
-// fixed value column, so a head's columns split over CS workgroups with no
-// exchange between them; each takes 32 columns (128-byte row segments,
-// 16 KiB at d_k = 128), which streams better than whole 64 KiB heads.
+// 16-byte non-temporal loads into registers, carries it through the L
+// tokens there (reducing over rows through LDS), and writes it back once
+// (plus once per token when the per-token states are asked for).  Every sum
+// runs over rows (key channels) for a fixed value column, so a head's
+// columns split over CS workgroups with no exchange between them; each
+// takes 32 columns (128-byte row segments, 16 KiB at d_k = 128), which
+// streams better than whole 64 KiB heads.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -34,16 +38,20 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode(DecodeParams p) {
   constexpr int RPT = DK / RG;   // rows per thread
   static_assert(RG * NQ == NT && RPT * RG == DK, "thread mapping");
 
-  __shared__ float s_ek[DK], s_eq[DK], s_e[DK], s_k[DK];
+  // per-token key-side vectors, double-buffered by token parity so the
+  // next token's can be written while the state update still reads these
+  __shared__ float s_ek[2][DK], s_eq[2][DK], s_e[2][DK], s_k[2][DK];
   __shared__ __attribute__((aligned(16))) float s_part[2][RG][DVB];
   __shared__ __attribute__((aligned(16))) float s_d[DVB];
   __shared__ float s_qk[DEC_THREADS / 64];
 
   const int tid = threadIdx.x;
-  const size_t nh = blockIdx.x / CS;
-  const int c0 = (blockIdx.x % CS) * DVB;  // first value column
+  const int L = p.L, H = p.H;
+  const size_t nh = blockIdx.x / CS;           // n * H + h
+  const size_t n = nh / H, h = nh % H;
+  const int c0 = (blockIdx.x % CS) * DVB;      // first value column
   const int q4 = tid % NQ, rg = tid / NQ;
-  float *Sg = p.state + nh * DK * DV + c0;
+  const size_t so = nh * DK * DV + c0;         // state offset of this share
 
   // 1. issue the state loads first: they are the whole cost
   f32x4 s[RPT];
@@ -52,69 +60,86 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode(DecodeParams p) {
     for (int i = 0; i < RPT; ++i) {
       const int row = rg + RG * i;
       s[i] = __builtin_nontemporal_load(
-          (const f32x4 *)(Sg + (size_t)row * DV + 4 * q4));
+          (const f32x4 *)(p.state_in + so + (size_t)row * DV + 4 * q4));
     }
   }
-  // 2. per-channel gate, decayed key and query
-  float qk = 0.f;
-  if (tid < DK) {
-    const float e = __expf(dec_gate(p.g, nh * DK + tid, p.gate_bf16));
-    const float kk = to_f32(((const IO *)p.k)[nh * DK + tid]);
-    const float qq = to_f32(((const IO *)p.q)[nh * DK + tid]);
-    s_e[tid] = e;
-    s_k[tid] = kk;
-    s_ek[tid] = e * kk;
-    s_eq[tid] = e * qq;
-    qk = qq * kk;
-  }
+  for (int t = 0; t < L; ++t) {
+    const int pb = t & 1;
+    const size_t ti = (n * L + t) * H + h;     // (sequence, token, head)
+    // 2. per-channel gate, decayed key and query
+    float qk = 0.f;
+    if (tid < DK) {
+      const float e = __expf(dec_gate(p.g, ti * DK + tid, p.gate_bf16));
+      const float kk = to_f32(((const IO *)p.k)[ti * DK + tid]);
+      const float qq = to_f32(((const IO *)p.q)[ti * DK + tid]);
+      s_e[pb][tid] = e;
+      s_k[pb][tid] = kk;
+      s_ek[pb][tid] = e * kk;
+      s_eq[pb][tid] = e * qq;
+      qk = qq * kk;
+    }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) qk += __shfl_xor(qk, off, 64);
-  if ((tid & 63) == 0) s_qk[tid >> 6] = qk;
-  __syncthreads();
+    for (int off = 32; off >= 1; off >>= 1) qk += __shfl_xor(qk, off, 64);
+    if ((tid & 63) == 0) s_qk[tid >> 6] = qk;
+    __syncthreads();
 
-  // 3. partial column sums over this thread's rows
+    // 3. partial column sums over this thread's rows
+    if (tid < NT) {
+      f32x4 u = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int row = rg + RG * i;
+        u += s[i] * s_ek[pb][row];
+        y += s[i] * s_eq[pb][row];
+      }
+      *(f32x4 *)&s_part[0][rg][4 * q4] = u;
+      *(f32x4 *)&s_part[1][rg][4 * q4] = y;
+    }
+    __syncthreads();
+
+    // 4. per column: delta and output
+    if (tid < DVB) {
+      float u = 0.f, y = 0.f;
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        u += s_part[0][r][tid];
+        y += s_part[1][r][tid];
+      }
+      float qkt = 0.f;
+#pragma unroll
+      for (int w = 0; w < DEC_THREADS / 64; ++w) qkt += s_qk[w];
+      const float bt = dec_gate(p.beta, ti, p.gate_bf16);
+      const float vv = to_f32(((const IO *)p.v)[ti * DV + c0 + tid]);
+      const float d = bt * (vv - u);
+      s_d[tid] = d;
+      ((IO *)p.o)[ti * DV + c0 + tid] = from_f32<IO>(p.scale * (y + qkt * d));
+    }
+    __syncthreads();
+
+    // 5. S <- diag(e) S + k delta^T, in registers; optionally stored
+    if (tid < NT) {
+      const f32x4 d = *(const f32x4 *)&s_d[4 * q4];
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int row = rg + RG * i;
+        s[i] = s[i] * s_e[pb][row] + d * s_k[pb][row];
+      }
+      if (p.tstates) {
+        float *ts = p.tstates + ti * DK * DV + c0;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+          __builtin_nontemporal_store(
+              s[i], (f32x4 *)(ts + (size_t)(rg + RG * i) * DV + 4 * q4));
+      }
+    }
+  }
+  // 6. the state after the last token
   if (tid < NT) {
-    f32x4 u = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int row = rg + RG * i;
-      u += s[i] * s_ek[row];
-      y += s[i] * s_eq[row];
-    }
-    *(f32x4 *)&s_part[0][rg][4 * q4] = u;
-    *(f32x4 *)&s_part[1][rg][4 * q4] = y;
-  }
-  __syncthreads();
-
-  // 4. per column: delta and output
-  if (tid < DVB) {
-    float u = 0.f, y = 0.f;
-#pragma unroll
-    for (int r = 0; r < RG; ++r) {
-      u += s_part[0][r][tid];
-      y += s_part[1][r][tid];
-    }
-    float qkt = 0.f;
-#pragma unroll
-    for (int w = 0; w < DEC_THREADS / 64; ++w) qkt += s_qk[w];
-    const float bt = dec_gate(p.beta, nh, p.gate_bf16);
-    const float vv = to_f32(((const IO *)p.v)[nh * DV + c0 + tid]);
-    const float d = bt * (vv - u);
-    s_d[tid] = d;
-    ((IO *)p.o)[nh * DV + c0 + tid] = from_f32<IO>(p.scale * (y + qkt * d));
-  }
-  __syncthreads();
-
-  // 5. in-place state write: S <- diag(e) S + k delta^T
-  if (tid < NT) {
-    const f32x4 d = *(const f32x4 *)&s_d[4 * q4];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int row = rg + RG * i;
-      const f32x4 sn = s[i] * s_e[row] + d * s_k[row];
-      __builtin_nontemporal_store(sn,
-                                  (f32x4 *)(Sg + (size_t)row * DV + 4 * q4));
-    }
+    for (int i = 0; i < RPT; ++i)
+      __builtin_nontemporal_store(
+          s[i], (f32x4 *)(p.state_out + so + (size_t)(rg + RG * i) * DV +
+                          4 * q4));
   }
 }
 

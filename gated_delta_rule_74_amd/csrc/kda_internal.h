@@ -24,11 +24,13 @@ struct PrefillParams {
 };
 
 struct DecodeParams {
-  const void *q, *k, *v, *g, *beta;
+  const void *q, *k, *v, *g, *beta;  // [N,L,H,*], beta [N,L,H]
   int gate_bf16;
-  float *state;
-  void *o;
-  int N, H, Dk, Dv;
+  const float *state_in;  // [N,H,Dk,Dv]
+  float *state_out;       // [N,H,Dk,Dv], may equal state_in
+  float *tstates;         // [N,L,H,Dk,Dv] or null
+  void *o;                // [N,L,H,Dv]
+  int N, L, H, Dk, Dv;
   float scale;
 };
 

@@ -23,6 +23,10 @@
  *     dimension is validated to be at least 2.
  *   [LQNN-B] m.lqnn.cn news 255115 ("80B parameters for 3B of compute ..."),
  *     config-validation list: conv kernel >= 2, chunk size positive.
+ *   [AREX] arex-research.com, "Yandex open-sources
+ *     AliceAI-Foundation-80B-A3B-Base ...", deployment paragraph: vLLM
+ *     serving with multi-token-prediction speculative decoding, one guessed
+ *     token per step.
  *
  * Conventions shared by every entry point.
  *  - All pointers are DEVICE pointers owned by the caller; the library keeps
@@ -83,7 +87,7 @@ typedef struct kda_conv_desc {
 } kda_conv_desc;
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 int kda_abi_version(void);
 
 /* Static text for a status code (never NULL). */
@@ -146,6 +150,30 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
                            const void *beta, kda_dtype gate_dtype,
                            float *state, void *o, int N, int H, int Dk,
                            int Dv, float scale, void *stream);
+
+/* L tokens of the recurrent rule per sequence in one call: the verify step
+ * of speculative decoding with the multi-token-prediction head ([AREX]
+ * deployment paragraph and [LQNN-A] serving notes: speculative decoding
+ * through the model's MTP module, one guessed token per step, so L = 2),
+ * or a short prompt extension.  Equal, up to rounding, to L successive
+ * kda_decode_step calls; the state is read once, carried through the L
+ * tokens and written once.
+ *   q,k,g [N,L,H,Dk]; v [N,L,H,Dv]; beta [N,L,H]   (qkv_dtype / gate_dtype)
+ *   state_in      [N,H,Dk,Dv] fp32, the state before the first token
+ *   state_out     [N,H,Dk,Dv] fp32, the state after the last token; may
+ *                 equal state_in (in place)
+ *   token_states  [N,L,H,Dk,Dv] fp32 or NULL: the state after each token,
+ *                 so a caller that accepts only the first a tokens of a
+ *                 sequence continues from token_states[n][a-1]; must not
+ *                 alias state_in or state_out
+ *   o             [N,L,H,Dv] in qkv_dtype; must not alias an input
+ * Errors as for kda_decode_step; L <= 0 is KDA_EINVAL. */
+kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
+                             kda_dtype qkv_dtype, const void *g,
+                             const void *beta, kda_dtype gate_dtype,
+                             const float *state_in, float *state_out,
+                             float *token_states, void *o, int N, int L,
+                             int H, int Dk, int Dv, float scale, void *stream);
 
 /* Standalone conv prologue ([LQNN-A]: kernel-4 causal conv with a cache
  * updated incrementally).  Same arithmetic as kda_conv_desc; outputs

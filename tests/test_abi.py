@@ -22,7 +22,8 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert {"kda_prefill", "kda_decode_step", "kda_conv_prologue",
+    assert {"kda_prefill", "kda_decode_step", "kda_decode_tokens",
+            "kda_conv_prologue",
             "kda_prefill_chunk_prep", "kda_prefill_state_pass",
             "kda_prefill_workspace_size", "kda_status_string",
             "kda_abi_version"} <= set(names)
@@ -107,6 +108,27 @@ def _decode(**kw):
 ])
 def test_decode_rejects(kw, want):
     assert _decode(**kw) == want
+
+
+def _decode_tokens(**kw):
+    a = dict(q=A, k=A, v=A, io=kda.KDA_BF16, g=A, beta=A, gt=kda.KDA_BF16,
+             s_in=A + 4096, s_out=A + 4096, ts=None, o=A + 8192, N=2, L=2,
+             H=2, Dk=16, Dv=16, scale=1.0, stream=None)
+    a.update(kw)
+    return kda._decode_tokens(*a.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(L=0), kda.KDA_EINVAL), (dict(N=-1), kda.KDA_EINVAL),
+    (dict(s_in=None), kda.KDA_EINVAL), (dict(s_out=None), kda.KDA_EINVAL),
+    (dict(o=A), kda.KDA_EINVAL), (dict(o=A + 4096), kda.KDA_EINVAL),
+    (dict(ts=A + 4096), kda.KDA_EINVAL), (dict(ts=A + 12290), kda.KDA_EINVAL),
+    (dict(scale=float("inf")), kda.KDA_EINVAL),
+    (dict(Dk=48), kda.KDA_EUNSUPPORTED),
+    (dict(io=kda.KDA_F32, gt=kda.KDA_BF16), kda.KDA_EUNSUPPORTED),
+])
+def test_decode_tokens_rejects(kw, want):
+    assert _decode_tokens(**kw) == want
 
 
 def _conv(**kw):

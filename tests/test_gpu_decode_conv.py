@@ -67,6 +67,42 @@ def test_decode_workload_1000_steps(orc, kda):
     assert worst <= 2e-2 and es <= 2e-2
 
 
+@pytest.mark.parametrize("qkv,gate,Dk,Dv,L", [
+    ("bf16", "bf16", 128, 128, 2), ("bf16", "f32", 64, 128, 5),
+    ("f32", "f32", 32, 16, 3), ("f32", "f32", 128, 128, 1),
+    ("bf16", "bf16", 16, 64, 8)])
+def test_decode_tokens(orc, kda, qkv, gate, Dk, Dv, L):
+    """L tokens per sequence in one call against the oracle's token loop:
+    outputs, final state, and the state after every token; the input state
+    is left alone out of place, and in place gives the same bits."""
+    say(f"decode tokens qkv={qkv} gate={gate} Dk={Dk} Dv={Dv} L={L}")
+    N, H = 6, 3
+    x = ki.prefill_inputs(N, L, H, Dk, Dv, qkv=qkv, gate=gate, seed=31 + L,
+                          device="cuda", with_s0=True)
+    s_in = x["s0"].clone()
+    o, s_out, ts = kda.kda_decode_tokens(x["q"], x["k"], x["v"], x["g"],
+                                         x["beta"], s_in, token_states=True,
+                                         scale=0.7)
+    torch.cuda.synchronize()
+    ro, rs = orc.recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"],
+                            x["s0"], 0.7)
+    eo, es = rel_err(o, ro), rel_err(s_out, rs)
+    say(f"  err o={eo:.2e} S={es:.2e}")
+    assert eo <= TOL[qkv] and es <= TOL[qkv]
+    for t in range(L):
+        cut = {n: x[n][:, :t + 1] for n in ("q", "k", "v", "g", "beta")}
+        _, rst = orc.recurrence(cut["q"], cut["k"], cut["v"], cut["g"],
+                                cut["beta"], x["s0"], 0.7)
+        assert rel_err(ts[:, t], rst) <= TOL[qkv], t
+    assert torch.equal(s_in, x["s0"])
+    st2 = x["s0"].clone()
+    o2, s2, _ = kda.kda_decode_tokens(x["q"], x["k"], x["v"], x["g"],
+                                      x["beta"], st2, state_out=st2,
+                                      scale=0.7)
+    torch.cuda.synchronize()
+    assert s2 is st2 and torch.equal(o2, o) and torch.equal(st2, s_out)
+
+
 @pytest.mark.parametrize("dt,D,W,T,hist", [
     ("bf16", 128, 4, 300, False), ("bf16", 128, 4, 300, True),
     ("f32", 16, 2, 70, True), ("f32", 64, 3, 1, True), ("bf16", 32, 4, 65, False)])
