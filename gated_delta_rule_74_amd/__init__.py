@@ -62,7 +62,7 @@ _decode = _sig("kda_decode_step", _i,
                [_f, _vp])
 _decode_tokens = _sig("kda_decode_tokens", _i,
                       [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp, _vp] +
-                      [_i] * 5 + [_f, _vp])
+                      [_i] * 5 + [_f, ctypes.POINTER(KdaConvDesc), _vp, _vp])
 _conv = _sig("kda_conv_prologue", _i,
              [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp] +
              [_i] * 5 + [_i, _f, _vp])
@@ -205,30 +205,41 @@ def kda_decode_step(q, k, v, g, beta, state, *, scale=1.0, o=None,
 
 
 def kda_decode_tokens(q, k, v, g, beta, state_in, *, state_out=None,
-                      token_states=False, scale=1.0, o=None, stream=None):
+                      token_states=False, scale=1.0, o=None, conv=None,
+                      conv_state=None, stream=None):
     """L tokens per sequence in one call (the speculative-decoding verify
-    step).  q,k,g [N,L,H,Dk], v [N,L,H,Dv], beta [N,L,H]; state_in
-    [N,H,Dk,Dv] fp32.  state_out: a tensor to write the final state into
-    (pass state_in itself for in place; default: a new tensor).
-    token_states: True for a new [N,L,H,Dk,Dv] tensor of the state after
-    each token, a tensor to fill, or False.  Returns (o, state_out,
+    step, or with L = 1 the generation step).  q,k,g [N,L,H,Dk],
+    v [N,L,H,Dv], beta [N,L,H]; state_in [N,H,Dk,Dv] fp32.  state_out: a
+    tensor to write the final state into (pass state_in itself for in
+    place; default: a new tensor).  token_states: True for a new
+    [N,L,H,Dk,Dv] tensor of the state after each token, a tensor to fill,
+    or False.  conv: dict(xq, xk, xv [N,L,H*D], wq, wk, wv, width,
+    l2norm_qk, eps) to make q, k, v from raw projections (q, k, v may then
+    be None), with conv_state the fp32 history [N,3,H*max(Dk,Dv),W-1]
+    (rolled forward in place) or None.  Returns (o, state_out,
     token_states or None)."""
-    N, L, H, Dk = q.shape
-    Dv = v.shape[-1]
+    N, L, H, Dk = g.shape
+    if conv is not None:
+        Dv = conv["xv"].shape[-1] // H
+        io = conv["xq"]
+    else:
+        Dv = v.shape[-1]
+        io = q
     if o is None:
-        o = torch.empty((N, L, H, Dv), dtype=q.dtype, device=q.device)
+        o = torch.empty((N, L, H, Dv), dtype=io.dtype, device=g.device)
     if state_out is None:
         state_out = torch.empty_like(state_in)
     ts = None
     if token_states is True:
         ts = torch.empty((N, L, H, Dk, Dv), dtype=torch.float32,
-                         device=q.device)
+                         device=g.device)
     elif token_states is not False and token_states is not None:
         ts = token_states
-    st = _decode_tokens(_ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(g),
+    cd, _keep = _conv_desc(conv)
+    st = _decode_tokens(_ptr(q), _ptr(k), _ptr(v), _dt(io), _ptr(g),
                         _ptr(beta), _dt(g), _ptr(state_in), _ptr(state_out),
-                        _ptr(ts), _ptr(o), N, L, H, Dk, Dv, scale,
-                        _stream(stream))
+                        _ptr(ts), _ptr(o), N, L, H, Dk, Dv, scale, cd,
+                        _ptr(conv_state), _stream(stream))
     _check(st, "kda_decode_tokens")
     return o, state_out, ts
 

@@ -218,18 +218,38 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
                              const float *state_in, float *state_out,
                              float *token_states, void *o, int N, int L,
                              int H, int Dk, int Dv, float scale,
+                             const kda_conv_desc *conv, float *conv_state,
                              void *stream) {
   if (N <= 0 || L <= 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_EINVAL;
-  if (!q || !k || !v || !g || !beta || !state_in || !state_out || !o)
-    return KDA_EINVAL;
+  if (!g || !beta || !state_in || !state_out || !o) return KDA_EINVAL;
+  if (!conv && (!q || !k || !v)) return KDA_EINVAL;
+  if (!conv && conv_state) return KDA_EINVAL;
+  if (conv) {
+    if (!conv->xq || !conv->xk || !conv->xv || !conv->wq || !conv->wk ||
+        !conv->wv)
+      return KDA_EINVAL;
+    if (conv->width < 2) return KDA_EINVAL;
+    if (conv->l2norm_qk != 0 && conv->l2norm_qk != 1) return KDA_EINVAL;
+    if (!(conv->eps >= 0.f) || !isfinite(conv->eps)) return KDA_EINVAL;
+    const void *cp[] = {conv->xq, conv->xk, conv->xv, conv->wq, conv->wk,
+                        conv->wv, conv_state};
+    for (const void *ptr : cp)
+      if (ptr && !aligned16(ptr)) return KDA_EINVAL;
+    if (conv->width > 4) return KDA_EUNSUPPORTED;
+  }
   if (!dtype_valid(qkv_dtype) || !dtype_valid(gate_dtype)) return KDA_EINVAL;
   if (!isfinite(scale)) return KDA_EINVAL;
   const void *ptrs[] = {q, k, v, g, beta, state_in, state_out, token_states, o};
   for (const void *ptr : ptrs)
     if (ptr && !aligned16(ptr)) return KDA_EINVAL;
-  if (o == q || o == k || o == v || o == g || o == beta || o == state_in ||
-      o == state_out || (token_states && (token_states == state_in ||
-                                          token_states == state_out)))
+  if ((q && o == q) || (k && o == k) || (v && o == v) || o == g ||
+      o == beta || o == state_in || o == state_out ||
+      (token_states && (token_states == state_in ||
+                        token_states == state_out)))
+    return KDA_EINVAL;
+  if (conv && (o == conv->xq || o == conv->xk || o == conv->xv ||
+               (conv_state && ((const void *)conv_state == o ||
+                               conv_state == state_out))))
     return KDA_EINVAL;
   if (!dim_ok(Dk) || !dim_ok(Dv)) return KDA_EUNSUPPORTED;
   if (!pair_ok(qkv_dtype, gate_dtype)) return KDA_EUNSUPPORTED;
@@ -241,8 +261,25 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
   p.state_in = state_in; p.state_out = state_out; p.tstates = token_states;
   p.o = o;
   p.N = N; p.L = L; p.H = H; p.Dk = Dk; p.Dv = Dv; p.scale = scale;
-  return hip_status(kda::launch_decode(p, qkv_dtype == KDA_BF16,
-                                       (hipStream_t)stream));
+  const int Dmax = Dk > Dv ? Dk : Dv;
+  if (conv) {
+    p.xq = conv->xq; p.xk = conv->xk; p.xv = conv->xv;
+    p.wq = conv->wq; p.wk = conv->wk; p.wv = conv->wv;
+    p.cw = conv->width; p.l2 = conv->l2norm_qk; p.eps = conv->eps;
+    p.cstate = conv_state; p.Dmax = Dmax;
+  }
+  hipError_t e = kda::launch_decode(p, qkv_dtype == KDA_BF16,
+                                    (hipStream_t)stream);
+  if (e != hipSuccess || !conv || !conv_state) return hip_status(e);
+  // roll the conv history forward by the L raw inputs (after the decode
+  // kernel has read the old history on the same stream)
+  kda::ConvParams c{};
+  c.x[0] = conv->xq; c.x[1] = conv->xk; c.x[2] = conv->xv;
+  c.D[0] = Dk; c.D[1] = Dk; c.D[2] = Dv;
+  c.B = N; c.T = L; c.H = H; c.W = conv->width;
+  c.io_bf16 = qkv_dtype == KDA_BF16;
+  c.state = conv_state; c.Dmax = Dmax;
+  return hip_status(kda::launch_conv_cache(c, (hipStream_t)stream));
 }
 
 kda_status kda_conv_prologue(const void *xq, const void *xk, const void *xv,

@@ -114,4 +114,17 @@ hipError_t launch_conv(const ConvParams &p, hipStream_t s) {
   return p.io_bf16 ? conv_t<bf16>(p, s) : conv_t<float>(p, s);
 }
 
+hipError_t launch_conv_cache(const ConvParams &p, hipStream_t s) {
+  const size_t total = (size_t)p.B * 3 * p.H * p.Dmax;
+  if (p.io_bf16)
+    hipLaunchKernelGGL(kda_conv_cache<bf16>,
+                       dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                       p);
+  else
+    hipLaunchKernelGGL(kda_conv_cache<float>,
+                       dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                       p);
+  return hipGetLastError();
+}
+
 }  // namespace kda

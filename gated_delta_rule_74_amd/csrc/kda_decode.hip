@@ -29,7 +29,34 @@ __device__ __forceinline__ float dec_gate(const void *p, size_t i, int bf) {
   return bf ? (float)((const bf16 *)p)[i] : ((const float *)p)[i];
 }
 
-template <typename IO, int DK, int DV, int CS>
+// a channel's conv taps right-aligned into 4 (tap 3 multiplies the newest
+// input) and its last 3 inputs before the first token (oldest first; from
+// the history when given, zeros beyond it)
+struct ConvLane {
+  float w[4], h[3];
+  __device__ void init(const float *taps, const float *hist, int W) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int jj = j - (4 - W);
+      w[j] = jj >= 0 ? taps[jj] : 0.f;
+    }
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+      const int mm = m - (3 - (W - 1));  // history entry of slot m
+      h[m] = (hist && mm >= 0) ? hist[mm] : 0.f;
+    }
+  }
+  // conv output for the next input x, then x joins the history
+  __device__ float step(float x) {
+    const float y = w[0] * h[0] + w[1] * h[1] + w[2] * h[2] + w[3] * x;
+    h[0] = h[1];
+    h[1] = h[2];
+    h[2] = x;
+    return y;
+  }
+};
+
+template <typename IO, int DK, int DV, int CS, bool CONV>
 __global__ __launch_bounds__(DEC_THREADS) void kda_decode(DecodeParams p) {
   constexpr int DVB = DV / CS;  // value columns of this workgroup
   constexpr int NQ = DVB / 4;   // column quads
@@ -44,6 +71,7 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) float s_part[2][RG][DVB];
   __shared__ __attribute__((aligned(16))) float s_d[DVB];
   __shared__ float s_qk[DEC_THREADS / 64];
+  __shared__ float s_l2[2][2][DEC_THREADS / 64];  // conv: q/k sums of squares
 
   const int tid = threadIdx.x;
   const int L = p.L, H = p.H;
@@ -63,15 +91,62 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode(DecodeParams p) {
           (const f32x4 *)(p.state_in + so + (size_t)row * DV + 4 * q4));
     }
   }
+  // fused conv prologue: this thread's q/k channel (tid < DK) and value
+  // column (tid < DVB) keep their taps and last inputs in registers
+  ConvLane cq, ck, cv;
+  if (CONV) {
+    const int W = p.cw;
+    const size_t hs = (size_t)H * p.Dmax * (W - 1);  // one stream's history
+    const float *hist = p.cstate ? p.cstate + n * 3 * hs : nullptr;
+    if (tid < DK) {
+      const size_t ch = h * DK + tid;
+      cq.init(p.wq + ch * W, hist ? hist + ch * (W - 1) : nullptr, W);
+      ck.init(p.wk + ch * W, hist ? hist + hs + ch * (W - 1) : nullptr, W);
+    }
+    if (tid < DVB) {
+      const size_t ch = h * DV + c0 + tid;
+      cv.init(p.wv + ch * W, hist ? hist + 2 * hs + ch * (W - 1) : nullptr, W);
+    }
+  }
   for (int t = 0; t < L; ++t) {
     const int pb = t & 1;
     const size_t ti = (n * L + t) * H + h;     // (sequence, token, head)
+    float qc = 0.f, kc = 0.f;
+    if (CONV) {
+      if (tid < DK) {
+        qc = cq.step(to_f32(((const IO *)p.xq)[ti * DK + tid]));
+        kc = ck.step(to_f32(((const IO *)p.xk)[ti * DK + tid]));
+      }
+      if (p.l2) {
+        // per-head L2 norm of q and k
+        float sq = qc * qc, sk = kc * kc;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+          sq += __shfl_xor(sq, off, 64);
+          sk += __shfl_xor(sk, off, 64);
+        }
+        if ((tid & 63) == 0) {
+          s_l2[pb][0][tid >> 6] = sq;
+          s_l2[pb][1][tid >> 6] = sk;
+        }
+        __syncthreads();
+        sq = 0.f;
+        sk = 0.f;
+#pragma unroll
+        for (int w = 0; w < DEC_THREADS / 64; ++w) {
+          sq += s_l2[pb][0][w];
+          sk += s_l2[pb][1][w];
+        }
+        qc *= 1.f / sqrtf(sq + p.eps);
+        kc *= 1.f / sqrtf(sk + p.eps);
+      }
+    }
     // 2. per-channel gate, decayed key and query
     float qk = 0.f;
     if (tid < DK) {
       const float e = __expf(dec_gate(p.g, ti * DK + tid, p.gate_bf16));
-      const float kk = to_f32(((const IO *)p.k)[ti * DK + tid]);
-      const float qq = to_f32(((const IO *)p.q)[ti * DK + tid]);
+      const float kk = CONV ? kc : to_f32(((const IO *)p.k)[ti * DK + tid]);
+      const float qq = CONV ? qc : to_f32(((const IO *)p.q)[ti * DK + tid]);
       s_e[pb][tid] = e;
       s_k[pb][tid] = kk;
       s_ek[pb][tid] = e * kk;
@@ -109,7 +184,9 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode(DecodeParams p) {
 #pragma unroll
       for (int w = 0; w < DEC_THREADS / 64; ++w) qkt += s_qk[w];
       const float bt = dec_gate(p.beta, ti, p.gate_bf16);
-      const float vv = to_f32(((const IO *)p.v)[ti * DV + c0 + tid]);
+      const float vv =
+          CONV ? cv.step(to_f32(((const IO *)p.xv)[ti * DV + c0 + tid]))
+               : to_f32(((const IO *)p.v)[ti * DV + c0 + tid]);
       const float d = bt * (vv - u);
       s_d[tid] = d;
       ((IO *)p.o)[ti * DV + c0 + tid] = from_f32<IO>(p.scale * (y + qkt * d));
@@ -148,9 +225,13 @@ static hipError_t dec_one(const DecodeParams &p, hipStream_t s) {
   // column split: 32 value columns (128-byte row segments) per workgroup
   // once a head's state exceeds 16 KiB
   constexpr int CS = (DK * DV * 4 > 16384 && DV >= 64) ? DV / 32 : 1;
-  hipLaunchKernelGGL((kda_decode<IO, DK, DV, CS>),
-                     dim3((unsigned)(p.N * p.H) * CS), dim3(DEC_THREADS), 0, s,
-                     p);
+  const dim3 grid((unsigned)(p.N * p.H) * CS);
+  if (p.xq)
+    hipLaunchKernelGGL((kda_decode<IO, DK, DV, CS, true>), grid,
+                       dim3(DEC_THREADS), 0, s, p);
+  else
+    hipLaunchKernelGGL((kda_decode<IO, DK, DV, CS, false>), grid,
+                       dim3(DEC_THREADS), 0, s, p);
   return hipGetLastError();
 }
 

@@ -32,6 +32,13 @@ struct DecodeParams {
   void *o;                // [N,L,H,Dv]
   int N, L, H, Dk, Dv;
   float scale;
+  // optional fused conv prologue (xq != null): raw inputs [N,L,H*D], taps
+  // [H*D,cw], history [N,3,H*Dmax,cw-1] (null: zeros)
+  const void *xq, *xk, *xv;
+  const float *wq, *wk, *wv;
+  int cw, l2, Dmax;
+  float eps;
+  const float *cstate;
 };
 
 struct ConvParams {
@@ -56,5 +63,7 @@ hipError_t launch_state_pass(const PrefillParams &p, int io_bf16,
                              hipStream_t s);
 hipError_t launch_decode(const DecodeParams &p, int io_bf16, hipStream_t s);
 hipError_t launch_conv(const ConvParams &p, hipStream_t s);
+// the history update alone (after a consumer of the old history has run)
+hipError_t launch_conv_cache(const ConvParams &p, hipStream_t s);
 
 }  // namespace kda

@@ -87,7 +87,7 @@ typedef struct kda_conv_desc {
 } kda_conv_desc;
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 int kda_abi_version(void);
 
 /* Static text for a status code (never NULL). */
@@ -167,13 +167,26 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
  *                 sequence continues from token_states[n][a-1]; must not
  *                 alias state_in or state_out
  *   o             [N,L,H,Dv] in qkv_dtype; must not alias an input
+ *   conv          NULL, or a fused conv prologue ([LQNN-A]: the kernel-4
+ *                 conv whose cache is updated incrementally with the
+ *                 state): q,k,v are then made from the raw projections
+ *                 conv->x* [N,L,H*D] (q, k, v may be NULL), with the
+ *                 taps, width and L2 norm of kda_conv_desc
+ *   conv_state    with conv: NULL (zeros before the first token), or the
+ *                 fp32 history [N,3,H*D_max,width-1] of kda_conv_prologue,
+ *                 read as the inputs before the first token and then
+ *                 rolled forward to end with the L new raw inputs
+ *                 (conv_state must be NULL without conv)
+ * With conv and L = 1 this is the generation step with its conv cache.
  * Errors as for kda_decode_step; L <= 0 is KDA_EINVAL. */
 kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
                              kda_dtype qkv_dtype, const void *g,
                              const void *beta, kda_dtype gate_dtype,
                              const float *state_in, float *state_out,
                              float *token_states, void *o, int N, int L,
-                             int H, int Dk, int Dv, float scale, void *stream);
+                             int H, int Dk, int Dv, float scale,
+                             const kda_conv_desc *conv, float *conv_state,
+                             void *stream);
 
 /* Standalone conv prologue ([LQNN-A]: kernel-4 causal conv with a cache
  * updated incrementally).  Same arithmetic as kda_conv_desc; outputs

@@ -113,7 +113,8 @@ def test_decode_rejects(kw, want):
 def _decode_tokens(**kw):
     a = dict(q=A, k=A, v=A, io=kda.KDA_BF16, g=A, beta=A, gt=kda.KDA_BF16,
              s_in=A + 4096, s_out=A + 4096, ts=None, o=A + 8192, N=2, L=2,
-             H=2, Dk=16, Dv=16, scale=1.0, stream=None)
+             H=2, Dk=16, Dv=16, scale=1.0, conv=None, cstate=None,
+             stream=None)
     a.update(kw)
     return kda._decode_tokens(*a.values())
 
@@ -126,9 +127,32 @@ def _decode_tokens(**kw):
     (dict(scale=float("inf")), kda.KDA_EINVAL),
     (dict(Dk=48), kda.KDA_EUNSUPPORTED),
     (dict(io=kda.KDA_F32, gt=kda.KDA_BF16), kda.KDA_EUNSUPPORTED),
+    (dict(cstate=A + 16384), kda.KDA_EINVAL),  # a history without a conv
 ])
 def test_decode_tokens_rejects(kw, want):
     assert _decode_tokens(**kw) == want
+
+
+def _cdesc(**kw):
+    d = dict(xq=A, xk=A, xv=A, wq=A, wk=A, wv=A, width=4, l2norm_qk=1,
+             eps=1e-6)
+    d.update(kw)
+    return ctypes.byref(kda.KdaConvDesc(*d.values()))
+
+
+@pytest.mark.parametrize("ckw,kw,want", [
+    (dict(width=1), {}, kda.KDA_EINVAL), (dict(width=5), {},
+                                          kda.KDA_EUNSUPPORTED),
+    (dict(xv=None), {}, kda.KDA_EINVAL), (dict(eps=-1.0), {}, kda.KDA_EINVAL),
+    (dict(l2norm_qk=2), {}, kda.KDA_EINVAL),
+    ({}, dict(cstate=A + 8192), kda.KDA_EINVAL),    # history aliases o
+    ({}, dict(cstate=A + 16386), kda.KDA_EINVAL),   # misaligned history
+    (dict(xq=A + 8192), {}, kda.KDA_EINVAL),        # o aliases a raw input
+])
+def test_decode_tokens_conv_rejects(ckw, kw, want):
+    args = dict(conv=_cdesc(**ckw), q=None, k=None, v=None)
+    args.update(kw)
+    assert _decode_tokens(**args) == want
 
 
 def _conv(**kw):

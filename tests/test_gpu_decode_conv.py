@@ -145,3 +145,62 @@ def test_fused_prologue_matches_standalone(kda):
     torch.cuda.synchronize()
     assert rel_err(of, to_cpu64(ou)) < 2e-2
     assert rel_err(sf, to_cpu64(su)) < 2e-2
+
+
+def _cut(x, a, b):
+    return {n: x[n][:, a:b] for n in ("xq", "xk", "xv", "g", "beta")}
+
+
+@pytest.mark.parametrize("qkv,gate,Dk,Dv,W,splits,hist", [
+    ("bf16", "bf16", 128, 128, 4, (1, 1, 1), True),
+    ("bf16", "f32", 64, 128, 3, (3, 1), True),
+    ("f32", "f32", 32, 16, 2, (5,), False),
+    ("f32", "f32", 128, 64, 4, (1, 2), False),
+    ("bf16", "bf16", 128, 32, 4, (2, 1, 4), True),
+    ("f32", "f32", 16, 16, 3, (1, 1), True)])
+def test_decode_tokens_conv(orc, kda, qkv, gate, Dk, Dv, W, splits, hist):
+    """Decode calls with the conv prologue fused (raw projections in), the
+    conv history and the recurrent state carried from call to call, against
+    the oracle's conv + recurrence over the whole token run: outputs, final
+    state and the rolled conv history."""
+    say(f"decode tokens + conv qkv={qkv} gate={gate} Dk={Dk} Dv={Dv} W={W} "
+        f"splits={splits} hist={hist}")
+    N, H, T = 4, 3, sum(splits)
+    Dm = max(Dk, Dv)
+    x = ki.prefill_inputs(N, T, H, Dk, Dv, qkv=qkv, gate=gate, conv_width=W,
+                          seed=41 + T, device="cuda", with_s0=True)
+    cache = None
+    hist_in = None
+    if hist:
+        cache = torch.randn((N, 3, H * Dm, W - 1), device="cuda")
+        old = to_cpu64(cache)
+        hist_in = tuple(old[:, i, :H * D] for i, D in enumerate((Dk, Dk, Dv)))
+    st = x["s0"].clone()
+    outs, t0 = [], 0
+    for L in splits:
+        c = _cut(x, t0, t0 + L)
+        conv = dict(xq=c["xq"].contiguous(), xk=c["xk"].contiguous(),
+                    xv=c["xv"].contiguous(), wq=x["wq"], wk=x["wk"],
+                    wv=x["wv"], width=W, l2norm_qk=True, eps=1e-6)
+        o, _, _ = kda.kda_decode_tokens(None, None, None,
+                                        c["g"].contiguous(),
+                                        c["beta"].contiguous(), st,
+                                        state_out=st, scale=0.6, conv=conv,
+                                        conv_state=cache)
+        outs.append(o)
+        t0 += L
+        if cache is None:
+            break   # without a history only one call continues correctly
+    torch.cuda.synchronize()
+    T = t0
+    rq, rk, rv, rh = orc.conv_prologue(x["xq"][:, :T], x["xk"][:, :T],
+                                       x["xv"][:, :T], x["wq"], x["wk"],
+                                       x["wv"], H, Dk, Dv, 1e-6, True, hist_in)
+    ro, rs = orc.recurrence(rq, rk, rv, x["g"][:, :T], x["beta"][:, :T],
+                            x["s0"], 0.6)
+    eo, es = rel_err(torch.cat(outs, 1), ro), rel_err(st, rs)
+    say(f"  err o={eo:.2e} S={es:.2e}")
+    assert eo <= TOL[qkv] and es <= TOL[qkv]
+    if hist:
+        for i, D in enumerate((Dk, Dk, Dv)):
+            assert rel_err(cache[:, i, :H * D], rh[i]) <= 1e-6, i
