@@ -1,7 +1,7 @@
 """Benchmark of the KDA forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
-                    [--no-cpu] [--only prefill,decode,conv,long,copy]
+                    [--no-cpu] [--only prefill,decode,tokens,conv,long,copy]
                     [--decode-steps N]
 
 Headline (`value`): chunked prefill tokens/s on the model-shaped workload
@@ -91,15 +91,18 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="comma list of: prefill, decode, conv, long, copy "
-                         "(copy = a plain 1 GiB device copy, the reference "
-                         "for scaling HBM byte counters)")
+                    help="comma list of: prefill, decode, tokens, conv, long, "
+                         "copy (tokens = the verify step and the generation "
+                         "step with the fused conv; copy = a plain 1 GiB "
+                         "device copy, the reference for scaling HBM byte "
+                         "counters)")
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="time fewer decode steps than the workload's 1000 "
                          "(profiling runs)")
     args = ap.parse_args()
     only = None if args.only is None else set(args.only.split(","))
-    bad = (only or set()) - {"prefill", "decode", "conv", "long", "copy"}
+    bad = (only or set()) - {"prefill", "decode", "tokens", "conv", "long",
+                           "copy"}
     if bad:
         ap.error(f"unknown --only part(s): {sorted(bad)}")
     sel = lambda part: (only is None and part != "copy") or \
@@ -211,11 +214,11 @@ def main():
         torch.cuda.empty_cache()
 
     # ---------------- decode workload ---------------------------------------
+    c3 = ki.CONFIGS[3]
+    N, H3, D3, steps = c3["N"], c3["H"], c3["Dk"], c3["steps"]
+    if args.decode_steps:
+        steps = max(1, min(steps, args.decode_steps))
     if sel("decode") and not args.no_extra:
-        c3 = ki.CONFIGS[3]
-        N, H3, D3, steps = c3["N"], c3["H"], c3["Dk"], c3["steps"]
-        if args.decode_steps:
-            steps = max(1, min(steps, args.decode_steps))
         log(f"decode: generating {steps} steps of inputs")
         st = ki.decode_state(N, H3, D3, D3, std=c3["state_std"], device=dev)
         xs = [ki.decode_step_inputs(N, H3, D3, D3, i, device=dev)
@@ -246,6 +249,13 @@ def main():
                           peak=HBM_PEAK_GBS, unit="GB/s",
                           frac=gbs / HBM_PEAK_GBS, traffic=tr))
         log(f"decode: {ms*1e3:.1f} us/step, {gbs:.0f} GB/s")
+        del xs, st
+        torch.cuda.empty_cache()
+
+    # ---------------- multi-token and conv decode calls ---------------------
+    if sel("tokens") and not args.no_extra:
+        st = ki.decode_state(N, H3, D3, D3, std=c3["state_std"], device=dev)
+        dtok = out["decode_tokens"] = {}
         # the speculative-decoding verify step: 2 tokens per sequence (one
         # guessed token), state read and written once per call
         L = 2
@@ -267,14 +277,47 @@ def main():
         torch.cuda.synchronize()
         mt = e0.elapsed_time(e1) / reps
         byt = N * H3 * (2 * D3 * D3 * 4 + L * (3 * D3 + 2 * D3 + 1) * 2)
-        out["decode"]["verify_step"] = dict(
+        dtok["verify_step"] = dict(
             tokens_per_sequence=L, calls=reps, us_per_call=mt * 1e3,
             tokens_per_s=N * L / (mt * 1e-3),
             achieved_gbs=byt / (mt * 1e-3) / 1e9,
             hbm_frac=byt / (mt * 1e-3) / 1e9 / HBM_PEAK_GBS)
         log(f"decode verify (L={L}): {mt*1e3:.1f} us/call, "
             f"{N * L / (mt * 1e-3) / 1e6:.2f} M tokens/s")
-        del xs, st, xt
+        # the generation step with the conv prologue fused: raw projections
+        # in, width-4 conv over the rolling history, history rolled forward
+        W = 4
+        xc = ki.prefill_inputs(N, 1, H3, D3, D3, qkv="bf16", gate="bf16",
+                               conv_width=W, seed=6, device=dev)
+        cache = torch.zeros((N, 3, H3 * D3, W - 1), device=dev)
+        oc = torch.empty((N, 1, H3, D3), dtype=torch.bfloat16, device=dev)
+        conv = dict(xq=xc["xq"], xk=xc["xk"], xv=xc["xv"], wq=xc["wq"],
+                    wk=xc["wk"], wv=xc["wv"], width=W, l2norm_qk=True,
+                    eps=1e-6)
+        callc = lambda: kda.kda_decode_tokens(None, None, None, xc["g"],
+                                              xc["beta"], st, state_out=st,
+                                              o=oc, conv=conv,
+                                              conv_state=cache)
+        for _ in range(5):
+            callc()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(reps):
+            callc()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        mc = e0.elapsed_time(e1) / reps
+        # state in + out, raw x, g, beta, o, conv history read + written
+        byc = (N * H3 * (2 * D3 * D3 * 4 + (3 * D3 + 2 * D3 + 1) * 2)
+               + 2 * cache.numel() * 4)
+        dtok["conv_step"] = dict(
+            conv_width=W, calls=reps, us_per_call=mc * 1e3,
+            tokens_per_s=N / (mc * 1e-3),
+            achieved_gbs=byc / (mc * 1e-3) / 1e9,
+            hbm_frac=byc / (mc * 1e-3) / 1e9 / HBM_PEAK_GBS)
+        log(f"decode step with fused conv: {mc*1e3:.1f} us/call")
+        del st, xt, xc, cache
         torch.cuda.empty_cache()
 
     # ---------------- fused-conv prefill and long context -------------------

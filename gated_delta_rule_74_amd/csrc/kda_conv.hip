@@ -74,27 +74,49 @@ __global__ __launch_bounds__(CONV_THREADS) void kda_conv_fwd(ConvParams p) {
   }
 }
 
-// new cache[m] = (history ++ x)[T - (W-1) + m], m < W-1; one thread per
-// (batch, stream, channel) walking m upwards (it reads old[T+m] with
-// T + m > m before overwriting entry m).
-template <typename IO>
+// new cache[m] = (history ++ x)[T - M + m], m < M = W-1; one thread per
+// 4 adjacent channels of one (batch, stream): their 4*M history entries
+// are contiguous, so they move as M 16-byte loads and stores.
+template <typename IO, int M>
 __global__ void kda_conv_cache(ConvParams p) {
-  const int W = p.W, T = p.T, H = p.H;
-  const size_t total = (size_t)p.B * 3 * H * p.Dmax;
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= total) return;
-  const int ch = (int)(i % ((size_t)H * p.Dmax));
-  const size_t bs = i / ((size_t)H * p.Dmax);
+  const int T = p.T, H = p.H;
+  const size_t C = (size_t)H * p.Dmax;  // history channels per stream
+  const size_t i = 4 * ((size_t)blockIdx.x * blockDim.x + threadIdx.x);
+  if (i >= (size_t)p.B * 3 * C) return;
+  const int ch = (int)(i % C);
+  const size_t bs = i / C;
   const int sidx = (int)(bs % 3), b = (int)(bs / 3);
   const int D = p.D[sidx];
-  if (ch >= H * D) return;
-  float *st = p.state + i * (W - 1);
-  const IO *x = (const IO *)p.x[sidx];
-  for (int m = 0; m < W - 1; ++m) {
-    const int tau = T - (W - 1) + m;
-    st[m] = (tau >= 0) ? to_f32(x[((size_t)b * T + tau) * H * D + ch])
-                       : st[T + m];
+  if (ch >= H * D) return;  // H*D is a multiple of 4: all 4 or none
+  f32x4 *st = (f32x4 *)(p.state + i * M);
+  float old[4 * M], nw[4 * M];  // entry m of channel ch+c at c*M + m
+#pragma unroll
+  for (int j = 0; j < M; ++j) *(f32x4 *)&old[4 * j] = st[j];
+  const IO *x = (const IO *)p.x[sidx] + (size_t)b * T * H * D + ch;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int tau = T - M + m;
+      nw[c * M + m] = tau >= 0 ? to_f32(x[(size_t)tau * H * D + c])
+                               : old[c * M + T + m];
+    }
   }
+#pragma unroll
+  for (int j = 0; j < M; ++j) st[j] = *(const f32x4 *)&nw[4 * j];
+}
+
+template <typename IO>
+static hipError_t cache_t(const ConvParams &p, hipStream_t s) {
+  const size_t threads = (size_t)p.B * 3 * p.H * p.Dmax / 4;
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  switch (p.W) {
+    case 2: hipLaunchKernelGGL((kda_conv_cache<IO, 1>), grid, dim3(256), 0, s, p); break;
+    case 3: hipLaunchKernelGGL((kda_conv_cache<IO, 2>), grid, dim3(256), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((kda_conv_cache<IO, 3>), grid, dim3(256), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <typename IO>
@@ -104,10 +126,7 @@ static hipError_t conv_t(const ConvParams &p, hipStream_t s) {
   hipLaunchKernelGGL(kda_conv_fwd<IO>, grid, dim3(CONV_THREADS), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !p.state) return e;
-  const size_t total = (size_t)p.B * 3 * p.H * p.Dmax;
-  hipLaunchKernelGGL(kda_conv_cache<IO>, dim3((unsigned)((total + 255) / 256)),
-                     dim3(256), 0, s, p);
-  return hipGetLastError();
+  return cache_t<IO>(p, s);
 }
 
 hipError_t launch_conv(const ConvParams &p, hipStream_t s) {
@@ -115,16 +134,7 @@ hipError_t launch_conv(const ConvParams &p, hipStream_t s) {
 }
 
 hipError_t launch_conv_cache(const ConvParams &p, hipStream_t s) {
-  const size_t total = (size_t)p.B * 3 * p.H * p.Dmax;
-  if (p.io_bf16)
-    hipLaunchKernelGGL(kda_conv_cache<bf16>,
-                       dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                       p);
-  else
-    hipLaunchKernelGGL(kda_conv_cache<float>,
-                       dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                       p);
-  return hipGetLastError();
+  return p.io_bf16 ? cache_t<bf16>(p, s) : cache_t<float>(p, s);
 }
 
 }  // namespace kda

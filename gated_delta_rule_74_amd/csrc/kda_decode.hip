@@ -12,7 +12,8 @@
 // The state is the only large operand (Dk*Dv fp32 per head), so the kernel
 // is an HBM stream: each workgroup loads its share of the state once with
 // 16-byte non-temporal loads into registers, carries it through the L
-// tokens there (reducing over rows through LDS), and writes it back once
+// tokens there (reducing over rows with lane shuffles, then over waves
+// through LDS), and writes it back once
 // (plus once per token when the per-token states are asked for).  Every sum
 // runs over rows (key channels) for a fixed value column, so a head's
 // columns split over CS workgroups with no exchange between them; each
@@ -25,8 +26,14 @@ namespace kda {
 
 constexpr int DEC_THREADS = 256;
 
-__device__ __forceinline__ float dec_gate(const void *p, size_t i, int bf) {
-  return bf ? (float)((const bf16 *)p)[i] : ((const float *)p)[i];
+// a gate or beta element as loaded (fp32 bits, or bf16 bits in the low
+// half); converted only where it is used so a prefetch does not wait
+__device__ __forceinline__ unsigned dec_raw(const void *p, size_t i, int bf) {
+  return bf ? (unsigned)((const unsigned short *)p)[i]
+            : ((const unsigned *)p)[i];
+}
+__device__ __forceinline__ float dec_val(unsigned raw, int bf) {
+  return __uint_as_float(bf ? raw << 16 : raw);
 }
 
 // a channel's conv taps right-aligned into 4 (tap 3 multiplies the newest
@@ -56,6 +63,28 @@ struct ConvLane {
   }
 };
 
+// one token's inputs for this thread, as loaded: key channel tid's gate,
+// query and key (tid < d_k), value column tid (tid < value columns), and
+// the head's beta (raw projections in place of q, k, v with the conv)
+template <typename IO>
+struct TokIn {
+  unsigned g, b;
+  IO q, k, v;
+};
+
+template <typename IO, int DK, bool CONV>
+__device__ __forceinline__ void load_tok(TokIn<IO> &r, const DecodeParams &p,
+                                         size_t ti, int tid, int dvb,
+                                         size_t vcol) {
+  if (tid < DK) {
+    r.g = dec_raw(p.g, ti * DK + tid, p.gate_bf16);
+    r.q = ((const IO *)(CONV ? p.xq : p.q))[ti * DK + tid];
+    r.k = ((const IO *)(CONV ? p.xk : p.k))[ti * DK + tid];
+  }
+  if (tid < dvb) r.v = ((const IO *)(CONV ? p.xv : p.v))[vcol];
+  r.b = dec_raw(p.beta, ti, p.gate_bf16);
+}
+
 template <typename IO, int DK, int DV, int CS, bool CONV>
 __global__ __launch_bounds__(DEC_THREADS) void kda_decode(DecodeParams p) {
   constexpr int DVB = DV / CS;  // value columns of this workgroup
@@ -63,21 +92,29 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode(DecodeParams p) {
   constexpr int NT = (NQ * DK < DEC_THREADS) ? NQ * DK : DEC_THREADS;
   constexpr int RG = NT / NQ;    // row groups
   constexpr int RPT = DK / RG;   // rows per thread
-  static_assert(RG * NQ == NT && RPT * RG == DK, "thread mapping");
+  constexpr int NW = NT / 64;    // waves holding state
+  constexpr int WK = DK > 64 ? DK / 64 : 1;  // waves holding key channels
+  static_assert(RG * NQ == NT && RPT * RG == DK && NW * 64 == NT &&
+                    NQ < 64,
+                "thread mapping");
 
-  // per-token key-side vectors, double-buffered by token parity so the
-  // next token's can be written while the state update still reads these
-  __shared__ float s_ek[2][DK], s_eq[2][DK], s_e[2][DK], s_k[2][DK];
-  __shared__ __attribute__((aligned(16))) float s_part[2][RG][DVB];
-  __shared__ __attribute__((aligned(16))) float s_d[DVB];
-  __shared__ float s_qk[DEC_THREADS / 64];
-  __shared__ float s_l2[2][2][DEC_THREADS / 64];  // conv: q/k sums of squares
+  // per-token vectors, double-buffered by token parity: token t+1 writes
+  // one set while the last readers of token t may still read the other
+  __shared__ float s_e[2][DK], s_k[2][DK], s_ek[2][DK], s_eq[2][DK];
+  __shared__ float s_v[2][DVB];
+  __shared__ float s_red[2][3][WK];        // per wave: q.k, |q|^2, |k|^2
+  __shared__ f32x4 s_part[2][2][NW][NQ];   // per wave: column sums u, y
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int L = p.L, H = p.H;
-  const size_t nh = blockIdx.x / CS;           // n * H + h
+  // consecutive workgroups go to the 8 XCDs in turn; renumber so that the
+  // CS column shares of a head run on one XCD one after another, which
+  // keeps the head's DRAM pages and L2 lines on one die
+  const unsigned G = gridDim.x, G8 = G & ~7u, b = blockIdx.x;
+  const unsigned wid = b < G8 ? (b & 7) * (G8 >> 3) + (b >> 3) : b;
+  const size_t nh = wid / CS;                  // n * H + h
   const size_t n = nh / H, h = nh % H;
-  const int c0 = (blockIdx.x % CS) * DVB;      // first value column
+  const int c0 = (wid % CS) * DVB;             // first value column
   const int q4 = tid % NQ, rg = tid / NQ;
   const size_t so = nh * DK * DV + c0;         // state offset of this share
 
@@ -91,6 +128,11 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode(DecodeParams p) {
           (const f32x4 *)(p.state_in + so + (size_t)row * DV + 4 * q4));
     }
   }
+  // token inputs: token 0 now, then each next token one step ahead
+  auto tok_index = [&](int t) { return (n * L + t) * H + h; };
+  TokIn<IO> cur, nxt;
+  load_tok<IO, DK, CONV>(cur, p, tok_index(0), tid, DVB,
+                         tok_index(0) * DV + c0 + tid);
   // fused conv prologue: this thread's q/k channel (tid < DK) and value
   // column (tid < DVB) keep their taps and last inputs in registers
   ConvLane cq, ck, cv;
@@ -108,57 +150,48 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode(DecodeParams p) {
       cv.init(p.wv + ch * W, hist ? hist + 2 * hs + ch * (W - 1) : nullptr, W);
     }
   }
+  const bool l2 = CONV && p.l2;
+
   for (int t = 0; t < L; ++t) {
     const int pb = t & 1;
-    const size_t ti = (n * L + t) * H + h;     // (sequence, token, head)
-    float qc = 0.f, kc = 0.f;
-    if (CONV) {
-      if (tid < DK) {
-        qc = cq.step(to_f32(((const IO *)p.xq)[ti * DK + tid]));
-        kc = ck.step(to_f32(((const IO *)p.xk)[ti * DK + tid]));
-      }
-      if (p.l2) {
-        // per-head L2 norm of q and k
-        float sq = qc * qc, sk = kc * kc;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-          sq += __shfl_xor(sq, off, 64);
-          sk += __shfl_xor(sk, off, 64);
-        }
-        if ((tid & 63) == 0) {
-          s_l2[pb][0][tid >> 6] = sq;
-          s_l2[pb][1][tid >> 6] = sk;
-        }
-        __syncthreads();
-        sq = 0.f;
-        sk = 0.f;
-#pragma unroll
-        for (int w = 0; w < DEC_THREADS / 64; ++w) {
-          sq += s_l2[pb][0][w];
-          sk += s_l2[pb][1][w];
-        }
-        qc *= 1.f / sqrtf(sq + p.eps);
-        kc *= 1.f / sqrtf(sk + p.eps);
-      }
-    }
-    // 2. per-channel gate, decayed key and query
-    float qk = 0.f;
+    const size_t ti = tok_index(t);
+    if (t + 1 < L)
+      load_tok<IO, DK, CONV>(nxt, p, tok_index(t + 1), tid, DVB,
+                             tok_index(t + 1) * DV + c0 + tid);
+
+    // 2. per key channel: gate, key, decayed key and query (unnormalised
+    //    with the conv: the per-head L2 factors come out of every sum)
+    float qq = 0.f, kk = 0.f;
     if (tid < DK) {
-      const float e = __expf(dec_gate(p.g, ti * DK + tid, p.gate_bf16));
-      const float kk = CONV ? kc : to_f32(((const IO *)p.k)[ti * DK + tid]);
-      const float qq = CONV ? qc : to_f32(((const IO *)p.q)[ti * DK + tid]);
+      const float e = __expf(dec_val(cur.g, p.gate_bf16));
+      kk = CONV ? ck.step(to_f32(cur.k)) : to_f32(cur.k);
+      qq = CONV ? cq.step(to_f32(cur.q)) : to_f32(cur.q);
       s_e[pb][tid] = e;
       s_k[pb][tid] = kk;
       s_ek[pb][tid] = e * kk;
       s_eq[pb][tid] = e * qq;
-      qk = qq * kk;
     }
+    if (tid < DVB)
+      s_v[pb][tid] = CONV ? cv.step(to_f32(cur.v)) : to_f32(cur.v);
+    if (wv < WK) {
+      float a = qq * kk, b = qq * qq, c = kk * kk;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) qk += __shfl_xor(qk, off, 64);
-    if ((tid & 63) == 0) s_qk[tid >> 6] = qk;
+      for (int off = 32; off >= 1; off >>= 1) {
+        a += __shfl_xor(a, off, 64);
+        if (l2) {
+          b += __shfl_xor(b, off, 64);
+          c += __shfl_xor(c, off, 64);
+        }
+      }
+      if (lane == 0) {
+        s_red[pb][0][wv] = a;
+        s_red[pb][1][wv] = b;
+        s_red[pb][2][wv] = c;
+      }
+    }
     __syncthreads();
 
-    // 3. partial column sums over this thread's rows
+    // 3. column sums over this thread's rows, then over the wave's rows
     if (tid < NT) {
       f32x4 u = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -167,35 +200,52 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode(DecodeParams p) {
         u += s[i] * s_ek[pb][row];
         y += s[i] * s_eq[pb][row];
       }
-      *(f32x4 *)&s_part[0][rg][4 * q4] = u;
-      *(f32x4 *)&s_part[1][rg][4 * q4] = y;
-    }
-    __syncthreads();
-
-    // 4. per column: delta and output
-    if (tid < DVB) {
-      float u = 0.f, y = 0.f;
 #pragma unroll
-      for (int r = 0; r < RG; ++r) {
-        u += s_part[0][r][tid];
-        y += s_part[1][r][tid];
+      for (int off = NQ; off < 64; off <<= 1) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          u[c] += __shfl_xor(u[c], off, 64);
+          y[c] += __shfl_xor(y[c], off, 64);
+        }
       }
-      float qkt = 0.f;
-#pragma unroll
-      for (int w = 0; w < DEC_THREADS / 64; ++w) qkt += s_qk[w];
-      const float bt = dec_gate(p.beta, ti, p.gate_bf16);
-      const float vv =
-          CONV ? cv.step(to_f32(((const IO *)p.xv)[ti * DV + c0 + tid]))
-               : to_f32(((const IO *)p.v)[ti * DV + c0 + tid]);
-      const float d = bt * (vv - u);
-      s_d[tid] = d;
-      ((IO *)p.o)[ti * DV + c0 + tid] = from_f32<IO>(p.scale * (y + qkt * d));
+      if (lane < NQ) {
+        s_part[pb][0][wv][lane] = u;
+        s_part[pb][1][wv][lane] = y;
+      }
     }
     __syncthreads();
 
-    // 5. S <- diag(e) S + k delta^T, in registers; optionally stored
+    // 4. every thread finishes its own four columns: delta, the output
+    //    (row group 0), and S <- diag(e) S + k delta^T in registers
     if (tid < NT) {
-      const f32x4 d = *(const f32x4 *)&s_d[4 * q4];
+      f32x4 u = s_part[pb][0][0][q4], y = s_part[pb][1][0][q4];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) {
+        u += s_part[pb][0][w][q4];
+        y += s_part[pb][1][w][q4];
+      }
+      float qk = s_red[pb][0][0], q2 = s_red[pb][1][0], k2 = s_red[pb][2][0];
+#pragma unroll
+      for (int w = 1; w < WK; ++w) {
+        qk += s_red[pb][0][w];
+        q2 += s_red[pb][1][w];
+        k2 += s_red[pb][2][w];
+      }
+      float rq = 1.f, rk = 1.f;
+      if (l2) {
+        rq = 1.f / sqrtf(q2 + p.eps);
+        rk = 1.f / sqrtf(k2 + p.eps);
+      }
+      const f32x4 vv = *(const f32x4 *)&s_v[pb][4 * q4];
+      const float bt = dec_val(cur.b, p.gate_bf16);
+      f32x4 d = bt * (vv - rk * u);
+      if (rg == 0) {
+        const f32x4 o = p.scale * (rq * y + (rq * rk * qk) * d);
+        IO *dst = (IO *)p.o + ti * DV + c0 + 4 * q4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dst[c] = from_f32<IO>(o[c]);
+      }
+      d *= rk;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         const int row = rg + RG * i;
@@ -209,8 +259,9 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode(DecodeParams p) {
               s[i], (f32x4 *)(ts + (size_t)(rg + RG * i) * DV + 4 * q4));
       }
     }
+    cur = nxt;
   }
-  // 6. the state after the last token
+  // 5. the state after the last token
   if (tid < NT) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
