@@ -406,6 +406,7 @@ def main():
         "prefill": ({k: v for k, v in pf.items() if k != "roofline"}
                     if pf else None),
         "decode": out.get("decode"),
+        "decode_tokens": out.get("decode_tokens"),
         "extra": extra,
     }
     if "copy" in out:
