@@ -1,7 +1,7 @@
 """Benchmark of the KDA forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
-                    [--no-cpu] [--only prefill,decode,tokens,conv,long,copy]
+                    [--no-cpu] [--only prefill,decode,tokens,conv,long,gdn,copy]
                     [--decode-steps N]
 
 Headline (`value`): chunked prefill tokens/s on the model-shaped workload
@@ -92,17 +92,18 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default=None,
                     help="comma list of: prefill, decode, tokens, conv, long, "
-                         "copy (tokens = the verify step and the generation "
-                         "step with the fused conv; copy = a plain 1 GiB "
-                         "device copy, the reference for scaling HBM byte "
-                         "counters)")
+                         "gdn, copy (tokens = the verify step and the "
+                         "generation step with the fused conv; gdn = the "
+                         "headline prefill with one gate per token-head; "
+                         "copy = a plain 1 GiB device copy, the reference "
+                         "for scaling HBM byte counters)")
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="time fewer decode steps than the workload's 1000 "
                          "(profiling runs)")
     args = ap.parse_args()
     only = None if args.only is None else set(args.only.split(","))
     bad = (only or set()) - {"prefill", "decode", "tokens", "conv", "long",
-                           "copy"}
+                           "gdn", "copy"}
     if bad:
         ap.error(f"unknown --only part(s): {sorted(bad)}")
     sel = lambda part: (only is None and part != "copy") or \
@@ -322,12 +323,20 @@ def main():
 
     # ---------------- fused-conv prefill and long context -------------------
     extra = {}
-    for cid, tag in ((2, "conv"), (4, "long")):
+    for cid, tag in ((2, "conv"), (4, "long"), (1, "gdn")):
         if args.no_extra or not sel(tag):
             continue
         c = ki.CONFIGS[cid]
         log(f"{tag}: generating inputs")
-        x = ki.config_prefill_inputs(cid, device=dev)
+        if tag == "gdn":
+            # the headline shape with one gate per token-head (the Gated
+            # DeltaNet special case): g shrinks from [B,T,H,Dk] to [B,T,H]
+            x = ki.prefill_inputs(c["B"], c["T"], c["H"], c["Dk"], c["Dv"],
+                                  qkv=c["qkv"], gate=c["gate"],
+                                  seed=ki.SEED_BASE + 11, device=dev,
+                                  gate_per_head=True)
+        else:
+            x = ki.config_prefill_inputs(cid, device=dev)
         Bc, Tc, Hc, Dc, Cc = c["B"], c["T"], c["H"], c["Dk"], c["chunk"]
         conv = None
         if c["conv_width"]:
@@ -353,10 +362,13 @@ def main():
         if conv:
             byts = Bc * Tc * Hc * (3 * Dc * 2 + Dc * 4 + 4 + Dc * 2) + \
                 3 * Hc * Dc * 4 * 4 + Bc * Hc * Dc * Dc * 4
+        elif tag == "gdn":
+            byts = prefill_bytes(Bc, Tc, Hc, Dc, Dc) - Bc * Tc * Hc * (Dc - 1) * 4
         else:
             byts = prefill_bytes(Bc, Tc, Hc, Dc, Dc)
         gbs = byts / (ms * 1e-3) / 1e9
-        extra[c["name"]] = dict(ms_per_call=ms,
+        name = c["name"] + ("_head_gate" if tag == "gdn" else "")
+        extra[name] = dict(ms_per_call=ms,
                                 tokens_per_s=Bc * Tc / (ms * 1e-3),
                                 algo_gbs=gbs, hbm_frac=gbs / HBM_PEAK_GBS)
         log(f"{tag}: {ms:.3f} ms/call, {gbs:.0f} GB/s algorithmic")

@@ -29,6 +29,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 KDA_OK, KDA_EINVAL, KDA_EUNSUPPORTED, KDA_EHIP = 0, 1, 2, 3
 KDA_F32, KDA_BF16 = 0, 1
+KDA_GATE_HEAD = 16  # gate-dtype flag: g holds one log-decay per token-head
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 
@@ -90,6 +91,16 @@ def _dt(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _gate_dt(g, per_channel_ndim: int) -> int:
+    """Gate dtype code; a g with one dimension fewer than the per-channel
+    layout is the per-head (scalar) gate."""
+    if g.dim() == per_channel_ndim:
+        return _dt(g)
+    if g.dim() == per_channel_ndim - 1:
+        return _dt(g) | KDA_GATE_HEAD
+    raise ValueError(f"g has {g.dim()} dimensions")
+
+
 def _ptr(t):
     if t is None:
         return None
@@ -129,7 +140,11 @@ def _conv_desc(conv):
 
 
 def _prefill_shapes(q, v, g, conv):
-    B, T, H, Dk = g.shape
+    if g.dim() == 4:
+        B, T, H, Dk = g.shape
+    else:  # per-head gate [B,T,H]
+        B, T, H = g.shape
+        Dk = q.shape[-1] if conv is None else conv["xq"].shape[-1] // H
     if conv is not None:
         Dv = conv["xv"].shape[-1] // H
         io = conv["xq"]
@@ -150,7 +165,8 @@ def kda_prefill(q, k, v, g, beta, *, s0=None, chunk=64, scale=1.0,
                 conv=None, o=None, s_out=None, want_state=True,
                 workspace=None, stream=None):
     """Chunked prefill.  q,k,g [B,T,H,Dk], v [B,T,H,Dv], beta [B,T,H]
-    (q,k,v may be None when `conv` gives raw projections and taps).
+    (q,k,v may be None when `conv` gives raw projections and taps; g may
+    be [B,T,H], one log-decay per token-head shared by the key channels).
     Returns (o [B,T,H,Dv], final state [B,H,Dk,Dv] fp32 or None)."""
     B, T, H, Dk, Dv, io = _prefill_shapes(q, v, g, conv)
     if o is None:
@@ -163,7 +179,7 @@ def kda_prefill(q, k, v, g, beta, *, s0=None, chunk=64, scale=1.0,
                                     g.device)
     cd, _keep = _conv_desc(conv)
     st = _prefill(_ptr(q), _ptr(k), _ptr(v), _dt(io), _ptr(g), _ptr(beta),
-                  _dt(g), _ptr(s0), _ptr(s_out), _ptr(o), B, T, H, Dk, Dv,
+                  _gate_dt(g, 4), _ptr(s0), _ptr(s_out), _ptr(o), B, T, H, Dk, Dv,
                   chunk, scale, cd, _ptr(workspace), workspace.numel(),
                   _stream(stream))
     _check(st, "kda_prefill")
@@ -176,7 +192,7 @@ def kda_prefill_chunk_prep(q, k, v, g, beta, workspace, *, chunk=64,
     B, T, H, Dk, Dv_, io = _prefill_shapes(q, v, g, conv)
     cd, _keep = _conv_desc(conv)
     st = _prep(_ptr(q), _ptr(k), _ptr(v), _dt(io), _ptr(g), _ptr(beta),
-               _dt(g), B, T, H, Dk, Dv_ if Dv is None else Dv, chunk, scale,
+               _gate_dt(g, 4), B, T, H, Dk, Dv_ if Dv is None else Dv, chunk, scale,
                cd, _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "kda_prefill_chunk_prep")
 
@@ -198,7 +214,7 @@ def kda_decode_step(q, k, v, g, beta, state, *, scale=1.0, o=None,
     if o is None:
         o = torch.empty((N, H, Dv), dtype=q.dtype, device=q.device)
     st = _decode(_ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(g), _ptr(beta),
-                 _dt(g), _ptr(state), _ptr(o), N, H, Dk, Dv, scale,
+                 _gate_dt(g, 3), _ptr(state), _ptr(o), N, H, Dk, Dv, scale,
                  _stream(stream))
     _check(st, "kda_decode_step")
     return o
@@ -218,7 +234,11 @@ def kda_decode_tokens(q, k, v, g, beta, state_in, *, state_out=None,
     be None), with conv_state the fp32 history [N,3,H*max(Dk,Dv),W-1]
     (rolled forward in place) or None.  Returns (o, state_out,
     token_states or None)."""
-    N, L, H, Dk = g.shape
+    if g.dim() == 4:
+        N, L, H, Dk = g.shape
+    else:  # per-head gate [N,L,H]
+        N, L, H = g.shape
+        Dk = q.shape[-1] if conv is None else conv["xq"].shape[-1] // H
     if conv is not None:
         Dv = conv["xv"].shape[-1] // H
         io = conv["xq"]
@@ -237,7 +257,7 @@ def kda_decode_tokens(q, k, v, g, beta, state_in, *, state_out=None,
         ts = token_states
     cd, _keep = _conv_desc(conv)
     st = _decode_tokens(_ptr(q), _ptr(k), _ptr(v), _dt(io), _ptr(g),
-                        _ptr(beta), _dt(g), _ptr(state_in), _ptr(state_out),
+                        _ptr(beta), _gate_dt(g, 4), _ptr(state_in), _ptr(state_out),
                         _ptr(ts), _ptr(o), N, L, H, Dk, Dv, scale, cd,
                         _ptr(conv_state), _stream(stream))
     _check(st, "kda_decode_tokens")

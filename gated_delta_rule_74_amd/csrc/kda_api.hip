@@ -14,7 +14,14 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
 bool dtype_valid(kda_dtype d) { return d == KDA_F32 || d == KDA_BF16; }
+// a gate dtype: KDA_F32 or KDA_BF16, optionally with KDA_GATE_HEAD
+bool gate_valid(kda_dtype d) {
+  return dtype_valid((kda_dtype)(d & ~KDA_GATE_HEAD));
+}
+kda_dtype gate_base(kda_dtype d) { return (kda_dtype)(d & ~KDA_GATE_HEAD); }
+int gate_head(kda_dtype d) { return (d & KDA_GATE_HEAD) ? 1 : 0; }
 bool pair_ok(kda_dtype io, kda_dtype gt) {
+  gt = gate_base(gt);
   return (io == KDA_F32 && gt == KDA_F32) ||
          (io == KDA_BF16 && (gt == KDA_F32 || gt == KDA_BF16));
 }
@@ -32,7 +39,7 @@ kda_status prefill_check(const void *q, const void *k, const void *v,
                          bool need_inputs, kda::PrefillParams &p) {
   if (B <= 0 || T <= 0 || H <= 0 || Dk <= 0 || Dv <= 0 || chunk <= 0)
     return KDA_EINVAL;
-  if (!dtype_valid(io) || !dtype_valid(gt)) return KDA_EINVAL;
+  if (!dtype_valid(io) || !gate_valid(gt)) return KDA_EINVAL;
   if (!isfinite(scale)) return KDA_EINVAL;
   if (need_inputs) {
     if (!g || !beta) return KDA_EINVAL;
@@ -62,7 +69,8 @@ kda_status prefill_check(const void *q, const void *k, const void *v,
   if ((long long)B * H * (Dv / 16) > 0x7fffffffLL) return KDA_EUNSUPPORTED;
   p = kda::PrefillParams{};
   p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
-  p.gate_bf16 = (gt == KDA_BF16);
+  p.gate_bf16 = gate_base(gt) == KDA_BF16;
+  p.gate_head = gate_head(gt);
   p.B = B; p.T = T; p.H = H; p.Dk = Dk; p.Dv = Dv; p.C = chunk;
   p.NC = (int)nc;
   p.scale = scale;
@@ -193,7 +201,7 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
                            int Dv, float scale, void *stream) {
   if (N <= 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_EINVAL;
   if (!q || !k || !v || !g || !beta || !state || !o) return KDA_EINVAL;
-  if (!dtype_valid(qkv_dtype) || !dtype_valid(gate_dtype)) return KDA_EINVAL;
+  if (!dtype_valid(qkv_dtype) || !gate_valid(gate_dtype)) return KDA_EINVAL;
   if (!isfinite(scale)) return KDA_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) ||
       !aligned16(beta) || !aligned16(state) || !aligned16(o))
@@ -205,7 +213,8 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
   if ((long long)N * H > 0x7fffffffLL) return KDA_EUNSUPPORTED;
   kda::DecodeParams p{};
   p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
-  p.gate_bf16 = gate_dtype == KDA_BF16;
+  p.gate_bf16 = gate_base(gate_dtype) == KDA_BF16;
+  p.gate_head = gate_head(gate_dtype);
   p.state_in = state; p.state_out = state; p.tstates = nullptr; p.o = o;
   p.N = N; p.L = 1; p.H = H; p.Dk = Dk; p.Dv = Dv; p.scale = scale;
   return hip_status(kda::launch_decode(p, qkv_dtype == KDA_BF16,
@@ -237,7 +246,7 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
       if (ptr && !aligned16(ptr)) return KDA_EINVAL;
     if (conv->width > 4) return KDA_EUNSUPPORTED;
   }
-  if (!dtype_valid(qkv_dtype) || !dtype_valid(gate_dtype)) return KDA_EINVAL;
+  if (!dtype_valid(qkv_dtype) || !gate_valid(gate_dtype)) return KDA_EINVAL;
   if (!isfinite(scale)) return KDA_EINVAL;
   const void *ptrs[] = {q, k, v, g, beta, state_in, state_out, token_states, o};
   for (const void *ptr : ptrs)
@@ -257,7 +266,8 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
     return KDA_EUNSUPPORTED;
   kda::DecodeParams p{};
   p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
-  p.gate_bf16 = gate_dtype == KDA_BF16;
+  p.gate_bf16 = gate_base(gate_dtype) == KDA_BF16;
+  p.gate_head = gate_head(gate_dtype);
   p.state_in = state_in; p.state_out = state_out; p.tstates = token_states;
   p.o = o;
   p.N = N; p.L = L; p.H = H; p.Dk = Dk; p.Dv = Dv; p.scale = scale;

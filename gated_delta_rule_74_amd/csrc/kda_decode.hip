@@ -77,7 +77,7 @@ __device__ __forceinline__ void load_tok(TokIn<IO> &r, const DecodeParams &p,
                                          size_t ti, int tid, int dvb,
                                          size_t vcol) {
   if (tid < DK) {
-    r.g = dec_raw(p.g, ti * DK + tid, p.gate_bf16);
+    r.g = dec_raw(p.g, p.gate_head ? ti : ti * DK + tid, p.gate_bf16);
     r.q = ((const IO *)(CONV ? p.xq : p.q))[ti * DK + tid];
     r.k = ((const IO *)(CONV ? p.xk : p.k))[ti * DK + tid];
   }

@@ -10,6 +10,7 @@ struct PrefillParams {
   const void *q, *k, *v;      // [B,T,H,D] (unused when use_conv)
   const void *g, *beta;       // gates
   int gate_bf16;              // 1: g/beta are bf16, 0: fp32
+  int gate_head;              // 1: g is [B,T,H], one value per head
   const float *s0;            // [B,H,Dk,Dv] or null
   float *s_out;               // [B,H,Dk,Dv] or null
   void *o;                    // [B,T,H,Dv]
@@ -26,6 +27,7 @@ struct PrefillParams {
 struct DecodeParams {
   const void *q, *k, *v, *g, *beta;  // [N,L,H,*], beta [N,L,H]
   int gate_bf16;
+  int gate_head;          // 1: g is [N,L,H], one value per head
   const float *state_in;  // [N,H,Dk,Dv]
   float *state_out;       // [N,H,Dk,Dv], may equal state_in
   float *tstates;         // [N,L,H,Dk,Dv] or null

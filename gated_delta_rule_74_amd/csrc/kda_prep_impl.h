@@ -140,7 +140,13 @@ __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
     for (int i = 0; i < 8; ++i) {
       if (!(PART & 1)) break;
       const unsigned t = (unsigned)min(t0 + 8 * tg + i, tlast);
-      if (GB) {
+      if (p.gate_head) {
+        // one gate per (token, head): kept as loaded in .x, widened in E1
+        const size_t gi = (tok0 + t) * H + h;
+        st.g[i].x = GB ? (unsigned)((const unsigned short *)p.g)[gi]
+                       : ((const unsigned *)p.g)[gi];
+        st.beta[i] = GB ? (uint32_t)bh16[t * H] : __float_as_uint(bf[t * H]);
+      } else if (GB) {
         const uint2 v = *(const uint2 *)(gh + t * rowK);
         st.g[i] = make_uint4(v.x, v.y, 0u, 0u);
         st.beta[i] = bh16[t * H];
@@ -262,8 +268,17 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
           Vec4<float>::get(st.g[i], gv);
           bt[i] = ok ? __uint_as_float(st.beta[i]) : 0.f;
         }
+        if (p.gate_head) {
+          // the head's one gate, shared by the 4 channels: one exp
+          const float e0 =
+              ok ? __expf(__uint_as_float(GB ? st.g[i].x << 16 : st.g[i].x))
+                 : 1.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) e[i][j] = ok ? __expf(gv[j]) : 1.f;
+          for (int j = 0; j < 4; ++j) e[i][j] = e0;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) e[i][j] = ok ? __expf(gv[j]) : 1.f;
+        }
       }
       if (CONV) {
         float tq[4][4], tk[4][4];
@@ -539,7 +554,8 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
           for (int c = 0; c < 16; ++c) {
             const int ch = cg * 16 + c;
             if (r > s) {
-              const size_t gi = ((tokb + trc) * H + h) * DK + ch;
+              const size_t gi = p.gate_head ? (tokb + trc) * H + h
+                                            : ((tokb + trc) * H + h) * DK + ch;
               const float gv = GB ? (float)((const bf16 *)p.g)[gi]
                                            : ((const float *)p.g)[gi];
               pr[c] *= (tr < T) ? __expf(gv) : 1.f;

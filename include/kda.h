@@ -41,9 +41,12 @@
  *    [2,4]; dtype pairs (q/k/v, g/beta) in {(F32,F32), (BF16,F32),
  *    (BF16,BF16)}; fp32 q/k/v with Dk = 128 needs chunk <= 32.  Outputs
  *    o have the q/k/v dtype; states are always fp32.
- *  - Element values are not checked: g > 0 or beta outside (0,1) are the
- *    caller's responsibility (the pages keep beta in (0,1)); g = -inf is
- *    supported and forgets exactly.
+ *  - Element values are not checked: g > 0 or beta outside (0,2) are the
+ *    caller's responsibility (the pages keep beta in (0,1), or (0,2) with
+ *    negative eigenvalues allowed); g = -inf is supported and forgets
+ *    exactly.
+ *  - gate_dtype may carry the KDA_GATE_HEAD flag (one log-decay per token
+ *    and head); a q/k/v dtype with the flag is KDA_EINVAL.
  *  - Errors: arguments are validated before anything is launched.
  *    KDA_EINVAL: a NULL required pointer, a size <= 0, chunk <= 0, conv
  *    width < 2, a misaligned pointer, a workspace that is too small.
@@ -69,7 +72,23 @@ typedef enum kda_status {
   KDA_EHIP = 3
 } kda_status;
 
-typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+typedef enum kda_dtype {
+  KDA_F32 = 0,
+  KDA_BF16 = 1,
+  /* Flag for a gate_dtype argument only (OR it into KDA_F32 or KDA_BF16):
+   * g then holds ONE log-decay per token and head, [B,T,H] (decode:
+   * [N,H] / [N,L,H]), shared by every key channel -- the single forgetting
+   * coefficient of Gated DeltaNet, which [SARNAS] (KDA paragraph) names as
+   * what KDA refines into one coefficient per state row.  The result is
+   * exactly that of the per-channel gate with g repeated over d_k; only g's
+   * traffic shrinks (d_k-fold). */
+  KDA_GATE_HEAD = 16
+} kda_dtype;
+
+/* beta ([LQNN-A] configuration checks): the model keeps beta in (0,1) so
+ * the update contracts; with "negative eigenvalues" allowed it may reach
+ * (0,2) (the transition I - beta k k^T then has an eigenvalue in (-1,0) for
+ * a unit k).  No entry point clamps or checks beta's values. */
 
 /* Optional fused conv prologue for kda_prefill ([LQNN-A] conv paragraph;
  * [SARNAS] "Rejected decisions" QK norm).  For each channel c of the
@@ -87,7 +106,7 @@ typedef struct kda_conv_desc {
 } kda_conv_desc;
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 int kda_abi_version(void);
 
 /* Static text for a status code (never NULL). */
@@ -102,7 +121,8 @@ size_t kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv,
 /* Chunked prefill ([LQNN-A]: the chunked GPU prefill path; chunk size a
  * positive config value per [LQNN-B]).
  *   q,k,v     inputs (ignored, may be NULL, when conv != NULL)
- *   g, beta   log-decay per key channel [B,T,H,Dk] and write strength
+ *   g, beta   log-decay per key channel [B,T,H,Dk] (or per head [B,T,H]
+ *             with KDA_GATE_HEAD in gate_dtype) and write strength
  *             [B,T,H], in gate_dtype
  *   s0        initial state [B,H,Dk,Dv] fp32, or NULL for zeros
  *   s_out     final state [B,H,Dk,Dv] fp32, or NULL; may equal s0
@@ -142,7 +162,8 @@ kda_status kda_prefill_state_pass(kda_dtype qkv_dtype, const float *s0,
 
 /* One recurrent decode step for N independent sequences ([LQNN-A]: the
  * fused recurrent GPU kernel used for generation).
- *   q,k,g [N,H,Dk]; v [N,H,Dv]; beta [N,H]   (qkv_dtype / gate_dtype)
+ *   q,k,g [N,H,Dk]; v [N,H,Dv]; beta [N,H]   (qkv_dtype / gate_dtype;
+ *   g is [N,H] with KDA_GATE_HEAD)
  *   state [N,H,Dk,Dv] fp32, read and updated IN PLACE
  *   o     [N,H,Dv] in qkv_dtype; must not alias an input */
 kda_status kda_decode_step(const void *q, const void *k, const void *v,
@@ -158,7 +179,8 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
  * or a short prompt extension.  Equal, up to rounding, to L successive
  * kda_decode_step calls; the state is read once, carried through the L
  * tokens and written once.
- *   q,k,g [N,L,H,Dk]; v [N,L,H,Dv]; beta [N,L,H]   (qkv_dtype / gate_dtype)
+ *   q,k,g [N,L,H,Dk]; v [N,L,H,Dv]; beta [N,L,H]   (qkv_dtype / gate_dtype;
+ *   g is [N,L,H] with KDA_GATE_HEAD)
  *   state_in      [N,H,Dk,Dv] fp32, the state before the first token
  *   state_out     [N,H,Dk,Dv] fp32, the state after the last token; may
  *                 equal state_in (in place)

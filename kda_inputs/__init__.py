@@ -93,12 +93,16 @@ def _gate(z: torch.Tensor, gate_kind: str) -> torch.Tensor:
 
 def prefill_inputs(B, T, H, Dk, Dv, qkv="bf16", gate="f32",
                    gate_kind="softplus", conv_width=0, seed=SEED_BASE,
-                   device="cpu", with_s0=False, s0_std=0.1):
+                   device="cpu", with_s0=False, s0_std=0.1,
+                   gate_per_head=False, beta_max=1.0):
     """Draw one prefill batch.  Returns a dict with q,k,g [B,T,H,Dk],
     v [B,T,H,Dv], beta [B,T,H] (and s0 [B,H,Dk,Dv] fp32 if with_s0).
     With conv_width > 0 it also holds raw xq,xk [B,T,H*Dk], xv [B,T,H*Dv]
     (qkv dtype, N(0,1)) and fp32 taps wq,wk [H*Dk,W], wv [H*Dv,W] ~ N(0,1/4);
-    q, k, v are then absent (the conv prologue makes them)."""
+    q, k, v are then absent (the conv prologue makes them).
+    gate_per_head: g is [B,T,H] (one log-decay per token-head, same
+    distribution).  beta_max: beta = beta_max * sigmoid(z) (2.0 for the
+    "negative eigenvalues" range (0,2))."""
     qdt, gdt = _DT[qkv], _DT[gate]
     out = {}
 
@@ -121,8 +125,10 @@ def prefill_inputs(B, T, H, Dk, Dv, qkv="bf16", gate="f32",
         out["q"] = blocks("q", (H, Dk), _unit, qdt)
         out["k"] = blocks("k", (H, Dk), _unit, qdt)
         out["v"] = blocks("v", (H, Dv), lambda z: z, qdt)
-    out["g"] = blocks("g", (H, Dk), lambda z: _gate(z, gate_kind), gdt)
-    out["beta"] = blocks("beta", (H,), torch.sigmoid, gdt)
+    out["g"] = blocks("g", (H,) if gate_per_head else (H, Dk),
+                      lambda z: _gate(z, gate_kind), gdt)
+    out["beta"] = blocks("beta", (H,),
+                         lambda z: beta_max * torch.sigmoid(z), gdt)
     if with_s0:
         out["s0"] = s0_std * _randn((B, H, Dk, Dv), device, seed, _ID["s0"])
     return out
@@ -146,7 +152,8 @@ def decode_state(N, H, Dk, Dv, std=0.1, seed=SEED_BASE + 3, device="cpu"):
 
 
 def decode_step_inputs(N, H, Dk, Dv, step, qkv="bf16", gate="bf16",
-                       seed=SEED_BASE + 3, device="cpu"):
+                       seed=SEED_BASE + 3, device="cpu", gate_per_head=False,
+                       beta_max=1.0):
     """Fresh single-token inputs for decode step `step`, distributed as the
     tiny workload: q,k unit per head, v ~ N(0,1), g = -softplus(N(0,1)),
     beta = sigmoid(N(0,1))."""
@@ -157,6 +164,7 @@ def decode_step_inputs(N, H, Dk, Dv, step, qkv="bf16", gate="bf16",
         q=_unit(r("q", (N, H, Dk))).to(qdt),
         k=_unit(r("k", (N, H, Dk))).to(qdt),
         v=r("v", (N, H, Dv)).to(qdt),
-        g=(-F.softplus(r("g", (N, H, Dk)))).to(gdt),
-        beta=torch.sigmoid(r("beta", (N, H))).to(gdt),
+        g=(-F.softplus(r("g", (N, H) if gate_per_head else (N, H, Dk)))
+           ).to(gdt),
+        beta=(beta_max * torch.sigmoid(r("beta", (N, H)))).to(gdt),
     )

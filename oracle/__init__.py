@@ -72,11 +72,16 @@ class Oracle:
 
     # -- API -------------------------------------------------------------
     def recurrence(self, q, k, v, g, beta, s0=None, scale=1.0):
-        """Token loop.  q,k,g [B,T,H,Dk]; v [B,T,H,Dv]; beta [B,T,H];
+        """Token loop.  q,k,g [B,T,H,Dk] (g may be [B,T,H]: one log-decay
+        per token-head for every row); v [B,T,H,Dv]; beta [B,T,H];
         s0 [B,H,Dk,Dv] or None.  Returns (o [B,T,H,Dv], S_T [B,H,Dk,Dv])."""
         q, k, v, g, beta, s0 = (self._f64(x) for x in (q, k, v, g, beta, s0))
         B, T, H, Dk = q.shape
         Dv = v.shape[-1]
+        if g.ndim == 3:
+            # one log-decay per token-head (the Gated DeltaNet gate): the
+            # same coefficient on every row of the state
+            g = np.ascontiguousarray(np.repeat(g[..., None], Dk, axis=-1))
         assert k.shape == q.shape and g.shape == q.shape
         assert v.shape == (B, T, H, Dv) and beta.shape == (B, T, H)
         if s0 is not None:

@@ -23,7 +23,12 @@ What each pin fixes (pages: see the header of oracle/kda_oracle.h):
                   beta_t ||v_t|| ("the state update is contractive").
   scalar_gate     g equal across channels reduces to the ungated delta rule
                   on values rescaled by the cumulative decay (Gated DeltaNet
-                  special case).
+                  special case), given as [B,T,H,Dk] and as the per-head
+                  [B,T,H] gate.
+  neg_eigen       beta in (1,2) ("negative eigenvalues" allowed), g = 0,
+                  v = 0, |k| = 1: the k-component of the state is scaled by
+                  1 - beta < 0 and the rest is untouched; beta = 2 is a
+                  reflection, so the same token twice restores S0.
   linearity       (S0, V) -> (o, S_T) is linear for fixed q, k, g, beta.
   column_split    value columns are independent of each other.
   head_perm       heads and batch rows are independent.
@@ -187,6 +192,35 @@ def pin_scalar_gate(orc):
                             s0, 1.0)
     _close(o, og * A[..., None], tol=1e-11, what="o")
     _close(s, sg * A[:, -1, :, None, None], tol=1e-11, what="S")
+    oh, sh = orc.recurrence(q, k, v, a, beta, s0, 1.0)  # per-head layout
+    _close(oh, og * A[..., None], tol=1e-11, what="o (per-head gate)")
+    _close(sh, sg * A[:, -1, :, None, None], tol=1e-11,
+           what="S (per-head gate)")
+
+
+def pin_neg_eigen(orc):
+    """Transition I - beta k k^T with beta in (1,2): eigenvalue 1 - beta on
+    k, 1 elsewhere."""
+    rng = np.random.default_rng(12)
+    Dk, Dv = 6, 4
+    k = rng.standard_normal(Dk)
+    k /= np.linalg.norm(k)
+    s0 = rng.standard_normal((1, 1, Dk, Dv))
+    z = np.zeros((1, 1, 1, Dk))
+    kk = k.reshape(1, 1, 1, Dk)
+    for b in (1.3, 1.9):
+        _, s = orc.recurrence(z, kk, np.zeros((1, 1, 1, Dv)), z,
+                              np.full((1, 1, 1), b), s0, 1.0)
+        _close(k @ s[0, 0], (1.0 - b) * (k @ s0[0, 0]), tol=1e-13,
+               what=f"k-component, beta={b}")
+        perp = np.eye(Dk) - np.outer(k, k)
+        _close(perp @ s[0, 0], perp @ s0[0, 0], tol=1e-13,
+               what=f"orthogonal part, beta={b}")
+    two = np.full((1, 2, 1), 2.0)
+    _, s = orc.recurrence(np.zeros((1, 2, 1, Dk)), np.repeat(kk, 2, axis=1),
+                          np.zeros((1, 2, 1, Dv)), np.zeros((1, 2, 1, Dk)),
+                          two, s0, 1.0)
+    _close(s, s0, tol=1e-13, what="reflection twice")
 
 
 def pin_linearity(orc):
@@ -276,5 +310,5 @@ def pin_l2_numpy(orc):
 
 ALL_PINS = [pin_one_token, pin_frozen, pin_pure_decay, pin_forget_restart,
             pin_retrieval, pin_dense_unrolled, pin_contraction,
-            pin_scalar_gate, pin_linearity, pin_column_split, pin_head_perm,
+            pin_scalar_gate, pin_neg_eigen, pin_linearity, pin_column_split, pin_head_perm,
             pin_conv_torch, pin_conv_identity, pin_l2_numpy]

@@ -79,6 +79,12 @@ def _prefill(**kw):
     (dict(Dv=256), kda.KDA_EUNSUPPORTED),
     (dict(io=kda.KDA_F32, gt=kda.KDA_BF16), kda.KDA_EUNSUPPORTED),
     (dict(io=kda.KDA_F32, Dk=128, Dv=128, chunk=64), kda.KDA_EUNSUPPORTED),
+    # the per-head gate flag belongs to the gate dtype only
+    (dict(io=kda.KDA_BF16 | kda.KDA_GATE_HEAD), kda.KDA_EINVAL),
+    (dict(gt=2 | kda.KDA_GATE_HEAD), kda.KDA_EINVAL),
+    (dict(io=kda.KDA_F32, gt=kda.KDA_BF16 | kda.KDA_GATE_HEAD),
+     kda.KDA_EUNSUPPORTED),
+    (dict(gt=kda.KDA_F32 | kda.KDA_GATE_HEAD, B=0), kda.KDA_EINVAL),
 ])
 def test_prefill_rejects(kw, want):
     assert _prefill(**kw) == want
@@ -105,6 +111,9 @@ def _decode(**kw):
     (dict(v=A + 4), kda.KDA_EINVAL), (dict(o=A + 4096), kda.KDA_EINVAL),
     (dict(Dk=24), kda.KDA_EUNSUPPORTED),
     (dict(io=kda.KDA_F32), kda.KDA_EUNSUPPORTED),
+    (dict(io=kda.KDA_F32 | kda.KDA_GATE_HEAD), kda.KDA_EINVAL),
+    (dict(gt=3 | kda.KDA_GATE_HEAD), kda.KDA_EINVAL),
+    (dict(gt=kda.KDA_BF16 | kda.KDA_GATE_HEAD, state=None), kda.KDA_EINVAL),
 ])
 def test_decode_rejects(kw, want):
     assert _decode(**kw) == want
@@ -128,6 +137,8 @@ def _decode_tokens(**kw):
     (dict(Dk=48), kda.KDA_EUNSUPPORTED),
     (dict(io=kda.KDA_F32, gt=kda.KDA_BF16), kda.KDA_EUNSUPPORTED),
     (dict(cstate=A + 16384), kda.KDA_EINVAL),  # a history without a conv
+    (dict(io=kda.KDA_BF16 | kda.KDA_GATE_HEAD), kda.KDA_EINVAL),
+    (dict(gt=kda.KDA_GATE_HEAD | 5), kda.KDA_EINVAL),
 ])
 def test_decode_tokens_rejects(kw, want):
     assert _decode_tokens(**kw) == want
