@@ -188,6 +188,34 @@ __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
   }
 }
 
+// block j of the A/P sub-block list: (aa, bb), bb <= aa.  With four
+// sub-chunks the order spreads the four costly blocks (the three that need
+// mid products, and the last row) over the four waves.
+template <int NB>
+__device__ __forceinline__ void ap_block(int j, int &aa, int &bb) {
+  if constexpr (NB == 4) {
+    switch (j) {
+      case 0: aa = 0; bb = 0; break;
+      case 1: aa = 1; bb = 0; break;
+      case 2: aa = 2; bb = 0; break;
+      case 3: aa = 3; bb = 0; break;
+      case 4: aa = 3; bb = 3; break;
+      case 5: aa = 1; bb = 1; break;
+      case 6: aa = 2; bb = 1; break;
+      case 7: aa = 3; bb = 1; break;
+      case 8: aa = 3; bb = 2; break;
+      default: aa = 2; bb = 2; break;
+    }
+  } else {
+    aa = 0;
+    while (j > aa) {
+      j -= aa + 1;
+      ++aa;
+    }
+    bb = j;
+  }
+}
+
 // 4 taps right-aligned (w4[3] multiplies the newest input) for 4 channels
 __device__ __forceinline__ void load_taps(const float *w, int W, float t[4][4]) {
 #pragma unroll
@@ -226,7 +254,8 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
   float *FbA = (float *)(sm + L::oFb), *FbP = FbA + NB * 256;
   int *votes = (int *)(sm + L::oVote);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, m16 = lane & 15;
   const int BH = p.B * p.H, T = p.T, H = p.H, Dv = p.Dv, nvt = Dv / 16;
   const int ntask = BH * p.NC;
@@ -576,9 +605,12 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     }
 
     // ---- AP: A^T and P^T sub-blocks on the matrix cores --------------------
-    // wave aa takes row block aa (its Xkr / Xqr operands are read once) and
-    // every column block bb <= aa
-    for (int aa = wave; aa < NB; aa += PREP_THREADS / 64) {
+    // the NB(NB+1)/2 blocks (aa, bb <= aa) are dealt to the waves in an
+    // order that evens out their cost (blocks two or more sub-chunks apart
+    // also scale an operand by the mid products)
+    for (int j = wave; j < NB * (NB + 1) / 2; j += PREP_THREADS / 64) {
+      int aa, bb;
+      ap_block<NB>(j, aa, bb);
       const IO *kb = Xkr + (16 * aa + m16) * LDK;
       const IO *qb = Xqr + (16 * aa + m16) * LDK;
       frag kf[NKU], qf[NKU];
@@ -588,7 +620,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
         kf[u] = M::load_k(kb + KU * u, g4, full);
         qf[u] = M::load_k(qb + KU * u, g4, full);
       }
-      for (int bb = 0; bb <= aa; ++bb) {
+      {
         const bool diag = (aa == bb);
         f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
         if (diag && fallback) {
