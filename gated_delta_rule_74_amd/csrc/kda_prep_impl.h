@@ -100,7 +100,11 @@ template <typename IO, int DK, int C> struct PL {  // prep LDS layout
   static constexpr size_t oM = al(oF + (size_t)NB * DK * 4);
   static constexpr size_t oFb = al(oM + (size_t)(NP2 ? NP2 : 1) * DK * 4);
   static constexpr size_t oVote = al(oFb + (size_t)2 * NB * 256 * 4);
-  static constexpr size_t total = oVote + 64;
+  // channel-major copy of the k*sigma operand (bf16 only: the Ktil^T units
+  // are assembled from it 16 bytes per lane)
+  static constexpr size_t oKST = al(oVote + 64);
+  static constexpr size_t total =
+      oKST + (TPU == 2 ? (size_t)DK * LDC * sizeof(IO) : 0);
   __device__ static int p2(int a, int b) { return (a - 2) * (a - 1) / 2 + b; }
 };
 
@@ -253,6 +257,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
   float *Fs = (float *)(sm + L::oF), *Mid = (float *)(sm + L::oM);
   float *FbA = (float *)(sm + L::oFb), *FbP = FbA + NB * 256;
   int *votes = (int *)(sm + L::oVote);
+  IO *XksT = (IO *)(sm + L::oKST);  // [DK][LDC], bf16 only
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -406,6 +411,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
         float sf[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) sf[j] = half ? 1.f : ltp[j];
+        float xkc[4][8];  // the same values by channel
 #pragma unroll
         for (int i = 7; i >= 0; --i) {
           const int r = r0 + i;
@@ -413,9 +419,20 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             xks[j] = kk[i][j] * sf[j];
+            xkc[j][i] = xks[j];
             sf[j] *= e[i][j];
           }
           *(typename V4::raw *)(Xks + r * LDK + c0) = V4::put(xks);
+        }
+        if constexpr (TPU == 2) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *(typename V4::raw *)(XksT + (c0 + j) * LDC + r0) =
+                V4::put(&xkc[j][0]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *(typename V4::raw *)(XksT + (c0 + j) * LDC + r0 + 4) =
+                V4::put(&xkc[j][4]);
         }
       }
       if (!half) *(f32x4 *)(Fs + a * DK + c0) = f32x4{F[0], F[1], F[2], F[3]};
@@ -483,62 +500,52 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
           if (bb > a) fsuf[j] *= f[j];
         }
       }
-      const int ct = c0 / 16;
-      float kt[8][4];
-      typename V4::raw rkr[8], rqr[8], rks[8];
+      typename V4::raw rkr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        rkr[i] = *(const typename V4::raw *)(Xkr + (r0 + i) * LDK + c0);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int r = r0 + i;
-        rkr[i] = *(const typename V4::raw *)(Xkr + r * LDK + c0);
-        rqr[i] = *(const typename V4::raw *)(Xqr + r * LDK + c0);
-        rks[i] = *(const typename V4::raw *)(Xks + r * LDK + c0);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = r0 + i;
-        float xkr[4], xqr[4], xks[4], qt[4];
+        float xkr[4];
         V4::get(rkr[i], xkr);
-        V4::get(rqr[i], xqr);
-        V4::get(rks[i], xks);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kgb[i][j] = xkr[j] * fpre[j];
+      }
+      if constexpr (TPU == 1) {
+        // fp32 units: a lane's 16-byte slot is 4 consecutive k, which this
+        // thread holds, so it stores its own Qtil and Ktil^T values
+        const int ct = c0 / 16;
+        float kt[8][4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = r0 + i;
+          float xqr[4], xks[4], qt[4];
+          V4::get(*(const typename V4::raw *)(Xqr + r * LDK + c0), xqr);
+          V4::get(*(const typename V4::raw *)(Xks + r * LDK + c0), xks);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            qt[j] = xqr[j] * fpre[j];
+            kt[i][j] = xks[j] * fsuf[j];
+          }
+          const int u = c0 / KU, gq = (c0 % KU) / 4;
+          const int ln = (r & 15) + 16 * gq;
+          *(typename V4::raw *)(blk + W.off_qt +
+                                ((size_t)(a * NKU + u) * 64 + ln) * 16) =
+              V4::put(qt);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          qt[j] = xqr[j] * fpre[j];
-          kt[i][j] = xks[j] * fsuf[j];
-          kgb[i][j] = xkr[j] * fpre[j];
-        }
-        // Qtil unit (row tile a, channel unit c0/KU): lane m + 16 g
-        const int u = c0 / KU, kin = c0 % KU;
-        const int gq = (kin & 15) / 4, eo = (kin >= 16) ? 4 : 0;
-        const int ln = (r & 15) + 16 * gq;
-        char *dst = blk + W.off_qt + ((size_t)(a * NKU + u) * 64 + ln) * 16 +
-                    eo * sizeof(IO);
-        *(typename V4::raw *)dst = V4::put(qt);
-        if (TPU == 2 && (NKT & 1) && c0 / 16 == NKT - 1) {
-          // odd number of 16-channel tiles: the missing upper half is zero
-          const float z[4] = {0.f, 0.f, 0.f, 0.f};
-          *(typename V4::raw *)(dst + 4 * sizeof(IO)) = V4::put(z);
-        }
-      }
-      // Ktil^T units (row tile = channel tile, k = tokens): per channel, the
-      // 8 tokens split into two runs of 4 consecutive k
+          const int c = c0 + j;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = c0 + j;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int rr = r0 + 4 * hh;  // first token of the run
-          const int u = rr / KU, kin = rr % KU;
-          const int gq = (kin & 15) / 4, eo = (kin >= 16) ? 4 : 0;
-          const int ln = (c & 15) + 16 * gq;
-          float v4[4] = {kt[4 * hh + 0][j], kt[4 * hh + 1][j],
-                         kt[4 * hh + 2][j], kt[4 * hh + 3][j]};
-          char *dst = blk + W.off_ktt + ((size_t)(ct * NTU + u) * 64 + ln) * 16 +
-                      eo * sizeof(IO);
-          *(typename V4::raw *)dst = V4::put(v4);
-          if (TPU == 2 && (NB & 1) && a == NB - 1) {
-            // odd number of sub-chunks: the missing upper half is zero
-            const float z[4] = {0.f, 0.f, 0.f, 0.f};
-            *(typename V4::raw *)(dst + 4 * sizeof(IO)) = V4::put(z);
+          for (int hh = 0; hh < 2; ++hh) {
+            const int rr = r0 + 4 * hh;  // first token of the run
+            const int u = rr / KU, gq = (rr % KU) / 4;
+            const int ln = (c & 15) + 16 * gq;
+            float v4[4] = {kt[4 * hh + 0][j], kt[4 * hh + 1][j],
+                           kt[4 * hh + 2][j], kt[4 * hh + 3][j]};
+            *(typename V4::raw *)(blk + W.off_ktt +
+                                  ((size_t)(ct * NTU + u) * 64 + ln) * 16) =
+                V4::put(v4);
           }
         }
       }
@@ -546,6 +553,82 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
         *(f32x4 *)((float *)(blk + W.off_gam) + c0) =
             f32x4{fpre[0] * F[0], fpre[1] * F[1], fpre[2] * F[2],
                   fpre[3] * F[3]};
+      }
+    }
+    if constexpr (TPU == 2) {
+      // bf16 units: a lane's 16-byte slot holds k = 4g..4g+3 and
+      // 16+4g..16+4g+3 of its unit, which two different threads produced in
+      // E1, so the slots are assembled here from LDS and written whole (one
+      // coalesced 1 KiB store per unit).  Values beyond d_k or the chunk
+      // (an odd number of 16-wide tiles) are zero.
+      constexpr int NW4 = PREP_THREADS / 64;
+      constexpr bool QHI = DK > 16;  // the unit's upper 16 channels exist
+      constexpr bool KHI = C > 16;   // the unit's upper 16 tokens exist
+      // every load below is unconditional (all addresses lie inside the
+      // arrays) so the compiler can batch them ahead of the arithmetic
+#pragma unroll
+      for (int it = 0; it < (NB * NKU + NW4 - 1) / NW4; ++it) {
+        // Qtil = scale Q*Gam: row tile aa (sub-chunk aa), channel unit u
+        const int w = wave + NW4 * it;
+        if constexpr ((NB * NKU) % NW4 != 0) {
+          if (w >= NB * NKU) break;
+        }
+        const int aa = w / NKU, u = w % NKU;
+        const int tok = 16 * aa + m16;
+        const int ch0 = KU * u + 4 * g4, ch1 = QHI ? ch0 + 16 : ch0;
+        f32x4 f0 = {1.f, 1.f, 1.f, 1.f}, f1 = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+        for (int bb = 0; bb < NB - 1; ++bb) {
+          const f32x4 l0 = *(const f32x4 *)(Fs + bb * DK + ch0);
+          const f32x4 l1 = *(const f32x4 *)(Fs + bb * DK + ch1);
+          if (bb < aa) {
+            f0 *= l0;
+            f1 *= l1;
+          }
+        }
+        float x0[4], x1[4], y0[4], y1[4];
+        V4::get(*(const typename V4::raw *)(Xqr + tok * LDK + ch0), x0);
+        V4::get(*(const typename V4::raw *)(Xqr + tok * LDK + ch1), x1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          y0[j] = x0[j] * f0[j];
+          y1[j] = QHI ? x1[j] * f1[j] : 0.f;
+        }
+        const typename V4::raw lo = V4::put(y0), up = V4::put(y1);
+        *(uint4 *)(blk + W.off_qt + ((size_t)(aa * NKU + u) * 64 + lane) * 16) =
+            make_uint4(lo.x, lo.y, up.x, up.y);
+      }
+#pragma unroll
+      for (int it = 0; it < (NKT * NTU + NW4 - 1) / NW4; ++it) {
+        // Ktil^T = (K*Gam_C/Gam)^T: channel tile ct, token unit u
+        const int w = wave + NW4 * it;
+        if constexpr ((NKT * NTU) % NW4 != 0) {
+          if (w >= NKT * NTU) break;
+        }
+        const int ct = w / NTU, u = w % NTU;
+        const int ch = 16 * ct + m16;
+        const int tk0 = KU * u + 4 * g4, tk1 = KHI ? tk0 + 16 : tk0;
+        const int a0 = 2 * u;  // sub-chunk of tk0; tk1 lies in a0 + 1
+        float fl[NB];
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) fl[bb] = Fs[bb * DK + ch];
+        float s0 = 1.f, s1 = 1.f;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+          if (bb > a0) s0 *= fl[bb];
+          if (bb > a0 + 1) s1 *= fl[bb];
+        }
+        float x0[4], x1[4], y0[4], y1[4];
+        V4::get(*(const typename V4::raw *)(XksT + ch * LDC + tk0), x0);
+        V4::get(*(const typename V4::raw *)(XksT + ch * LDC + tk1), x1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          y0[j] = x0[j] * s0;
+          y1[j] = KHI ? x1[j] * s1 : 0.f;
+        }
+        const typename V4::raw lo = V4::put(y0), up = V4::put(y1);
+        *(uint4 *)(blk + W.off_ktt + ((size_t)(ct * NTU + u) * 64 + lane) * 16) =
+            make_uint4(lo.x, lo.y, up.x, up.y);
       }
     }
     // mid products M_{b->a} = prod_{b<d<a} F_d for sub-chunk pairs a-b >= 2
