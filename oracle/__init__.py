@@ -50,6 +50,9 @@ class Oracle:
         lib.kda_oracle_recurrence.restype = ctypes.c_int
         lib.kda_oracle_recurrence.argtypes = [_I64] * 5 + [_P] * 6 + [
             ctypes.c_double, _P, _P]
+        lib.kda_oracle_backward.restype = ctypes.c_int
+        lib.kda_oracle_backward.argtypes = [_I64] * 5 + [_P] * 6 + [
+            ctypes.c_double] + [_P] * 8
         lib.kda_oracle_causal_conv.restype = None
         lib.kda_oracle_causal_conv.argtypes = [_I64] * 4 + [_P] * 5
         lib.kda_oracle_l2norm.restype = None
@@ -93,6 +96,35 @@ class Oracle:
             self._ptr(g), self._ptr(beta), self._ptr(s0), float(scale),
             self._ptr(o), self._ptr(s_out))
         return o, s_out
+
+    def backward(self, q, k, v, g, beta, s0, scale, do, dsT=None):
+        """Gradient of the token loop for the loss sum(o*do) + sum(S_T*dsT).
+        Shapes as recurrence(); do [B,T,H,Dv], dsT [B,H,Dk,Dv] or None.
+        Returns (dq, dk, dv, dg, dbeta, ds0); with a per-head gate g
+        [B,T,H] the returned dg is [B,T,H] (summed over the rows it
+        multiplies)."""
+        q, k, v, g, beta, s0, do, dsT = (self._f64(x) for x in
+                                         (q, k, v, g, beta, s0, do, dsT))
+        B, T, H, Dk = q.shape
+        Dv = v.shape[-1]
+        head_gate = g.ndim == 3
+        if head_gate:
+            g = np.ascontiguousarray(np.repeat(g[..., None], Dk, axis=-1))
+        assert k.shape == q.shape and g.shape == q.shape
+        assert v.shape == (B, T, H, Dv) and beta.shape == (B, T, H)
+        assert do.shape == v.shape
+        dq, dk, dg = (np.empty_like(q) for _ in range(3))
+        dv = np.empty_like(v)
+        dbeta = np.empty_like(beta)
+        ds0 = np.empty((B, H, Dk, Dv), np.float64)
+        self.last_threads = self.lib.kda_oracle_backward(
+            B, T, H, Dk, Dv, self._ptr(q), self._ptr(k), self._ptr(v),
+            self._ptr(g), self._ptr(beta), self._ptr(s0), float(scale),
+            self._ptr(do), self._ptr(dsT), self._ptr(dq), self._ptr(dk),
+            self._ptr(dv), self._ptr(dg), self._ptr(dbeta), self._ptr(ds0))
+        if head_gate:
+            dg = dg.sum(axis=-1)
+        return dq, dk, dv, dg, dbeta, ds0
 
     def decode_step(self, q, k, v, g, beta, state, scale=1.0):
         """One recurrent step for N independent sequences: q,k,g [N,H,Dk],

@@ -60,6 +60,17 @@ int kda_oracle_recurrence(int64_t B, int64_t T, int64_t H, int64_t Dk,
                           const double *s0, double scale, double *o,
                           double *s_out);
 
+/* Gradient of kda_oracle_recurrence (reverse-mode through the token loop)
+ * for the loss sum(o * dO) + sum(S_T * dsT): dq, dk, dg [B,T,H,Dk], dv
+ * [B,T,H,Dv], dbeta [B,T,H], ds0 [B,H,Dk,Dv] (may be NULL).  s0 and dsT may
+ * be NULL (zeros).  Returns the number of OpenMP threads that ran it. */
+int kda_oracle_backward(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                        int64_t Dv, const double *q, const double *k,
+                        const double *v, const double *g, const double *beta,
+                        const double *s0, double scale, const double *dO,
+                        const double *dsT, double *dq, double *dk, double *dv,
+                        double *dg, double *dbeta, double *ds0);
+
 /* Causal depthwise conv along time: y[b,t,c] = sum_j w[c,j] x[b,t-W+1+j,c]
  * where x at negative times comes from hist[b,c,W-1+tau] (hist may be NULL:
  * zeros).  If hist_out is not NULL it receives the last W-1 inputs of the

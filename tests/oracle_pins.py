@@ -36,6 +36,12 @@ What each pin fixes (pages: see the header of oracle/kda_oracle.h):
                   left padding W-1), with and without a history.
   conv_identity   taps (0,..,0,1) give the identity; the history update.
   l2_numpy        L2 norm equals x / sqrt(||x||^2 + eps) via numpy.linalg.
+  bwd_fd          the gradient (backward) equals central finite differences
+                  of the forward oracle's loss sum(o*dO) + sum(S_T*dS_T) for
+                  every input (q, k, v, g, beta, S0), per-channel and per-head
+                  gates, over more than one 64-token checkpoint block.
+  bwd_one_token   S0 = 0, T = 1: the closed-form gradient of
+                  o = scale beta (q.k) v.
 """
 from __future__ import annotations
 
@@ -308,7 +314,84 @@ def pin_l2_numpy(orc):
     _close(y, x / np.sqrt(n * n + eps), what="l2")
 
 
+def _fd_check(orc, args, scale, do, dsT, elems, tol, what):
+    """Central differences (h = 1e-6) of the forward loss for the chosen
+    elements of each argument against orc.backward."""
+    names = ("q", "k", "v", "g", "beta", "s0")
+    grads = orc.backward(*args, scale, do, dsT)
+    order = (0, 1, 2, 3, 4, 5)  # backward returns dq, dk, dv, dg, dbeta, ds0
+
+    def loss(a):
+        o, s = orc.recurrence(*a, scale)
+        return float((o * do).sum() + (s * dsT).sum())
+    h = 1e-6
+    for ai, gi in zip(range(6), order):
+        gr = grads[gi]
+        assert gr.shape == args[ai].shape, (names[ai], gr.shape)
+        for ix in elems(args[ai].shape):
+            ap = [x.copy() for x in args]
+            am = [x.copy() for x in args]
+            ap[ai][ix] += h
+            am[ai][ix] -= h
+            fd = (loss(ap) - loss(am)) / (2 * h)
+            den = max(np.max(np.abs(gr)), 1e-12)
+            assert abs(fd - gr[ix]) <= tol * den, \
+                (what, names[ai], ix, fd, gr[ix])
+
+
+def pin_bwd_fd(orc):
+    rng = np.random.default_rng(21)
+    every = lambda shape: list(np.ndindex(shape))
+    # tiny: every element, per-channel gate
+    q, k, v, g, beta, s0 = _rand(rng, 1, 5, 2, 3, 2)
+    do = rng.standard_normal(v.shape)
+    dsT = rng.standard_normal(s0.shape)
+    _fd_check(orc, [q, k, v, g, beta, s0], 0.7, do, dsT, every, 1e-7,
+              "tiny")
+    # per-head gate [B,T,H]
+    a = g[..., 0].copy()
+    _fd_check(orc, [q, k, v, a, beta, s0], 0.7, do, dsT, every, 1e-7,
+              "per-head gate")
+    # beta in (1,2) and a zero start state
+    _fd_check(orc, [q, k, v, g, 1.0 + beta, np.zeros_like(s0)], 1.0, do,
+              dsT, every, 1e-7, "beta > 1")
+    # across checkpoint blocks: 150 tokens, sampled elements
+    q, k, v, g, beta, s0 = _rand(rng, 1, 150, 1, 2, 2, g_scale=0.05)
+    do = rng.standard_normal(v.shape)
+    dsT = rng.standard_normal(s0.shape)
+    pick = np.random.default_rng(5)
+
+    def some(shape):
+        flat = pick.choice(int(np.prod(shape)), size=min(12, int(np.prod(shape))),
+                           replace=False)
+        return [np.unravel_index(f, shape) for f in flat] + \
+            [tuple(d - 1 for d in shape), tuple(0 for _ in shape)]
+    _fd_check(orc, [q, k, v, g, beta, s0], 1.0, do, dsT, some, 1e-6,
+              "150 tokens")
+
+
+def pin_bwd_one_token(orc):
+    rng = np.random.default_rng(22)
+    q, k, v, g, beta, _ = _rand(rng, 1, 1, 1, 4, 3)
+    do = rng.standard_normal(v.shape)
+    sc = 0.6
+    dq, dk, dv, dg, db, ds0 = orc.backward(q, k, v, g, beta, None, sc, do)
+    b = beta[0, 0, 0]
+    qv, kv, vv, dov = q[0, 0, 0], k[0, 0, 0], v[0, 0, 0], do[0, 0, 0]
+    vd, qk = vv @ dov, qv @ kv
+    _close(dq[0, 0, 0], sc * b * vd * kv, tol=1e-14, what="dq")
+    _close(dk[0, 0, 0], sc * b * vd * qv, tol=1e-14, what="dk")
+    _close(dv[0, 0, 0], sc * b * qk * dov, tol=1e-14, what="dv")
+    _close(db[0, 0, 0], sc * qk * vd, tol=1e-14, what="dbeta")
+    assert np.all(dg == 0.0), "dg with S0 = 0"
+    e = np.exp(g[0, 0, 0])
+    want = e[:, None] * (sc * np.outer(qv, dov) - sc * b * qk *
+                         np.outer(kv, dov))
+    _close(ds0[0, 0], want, tol=1e-14, what="dS0")
+
+
 ALL_PINS = [pin_one_token, pin_frozen, pin_pure_decay, pin_forget_restart,
             pin_retrieval, pin_dense_unrolled, pin_contraction,
             pin_scalar_gate, pin_neg_eigen, pin_linearity, pin_column_split, pin_head_perm,
-            pin_conv_torch, pin_conv_identity, pin_l2_numpy]
+            pin_conv_torch, pin_conv_identity, pin_l2_numpy, pin_bwd_fd,
+            pin_bwd_one_token]

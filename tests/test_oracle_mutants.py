@@ -32,7 +32,9 @@ _READ_BEFORE_WRITE = (
 MUTANTS = {
     "decay_on_columns": [("row[j] *= e;", "row[j] *= exp(gt[j % Dk]);")],
     "decay_dropped": [("row[j] *= e;", "(void)e;")],
-    "decay_index_shift": [("exp(gt[i]);", "exp(gt[i > 0 ? i - 1 : 0]);")],
+    "decay_index_shift": [("const double e = exp(gt[i]);\n      double *row",
+                           "const double e = exp(gt[i > 0 ? i - 1 : 0]);\n"
+                           "      double *row")],
     "decay_after_prediction": [("row[j] *= e;", "(void)e; (void)row;"),
                                ("    /* 3. write the beta-scaled correction "
                                 "along k */", _DECAY_AFTER_READ)],
@@ -58,6 +60,19 @@ MUTANTS = {
     "l2_eps_outside_sqrt": [("1.0 / sqrt(ss + eps)",
                              "1.0 / (sqrt(ss) + eps)")],
     "l2_eps_dropped": [("1.0 / sqrt(ss + eps)", "1.0 / sqrt(ss)")],
+    # the gradient
+    "bwd_prediction_term_dropped": [("        dkt[i] += a;\n", "        (void)a;\n")],
+    "bwd_du_sign": [("du[j] = -bt * ddel[j];", "du[j] = bt * ddel[j];")],
+    "bwd_dg_undecayed_state": [("a += dS[i * Dv + j] * Sp[i * Dv + j];",
+                                "a += dS[i * Dv + j] * P[i * Dv + j];")],
+    "bwd_decay_not_propagated": [("          dS[i * Dv + j] *= e;\n",
+                                  "          (void)e;\n")],
+    "bwd_dq_from_decayed_state": [("a += (Sp[i * Dv + j] + kt[i] * del[j]) * dot[j];",
+                                   "a += Sp[i * Dv + j] * dot[j];")],
+    "bwd_block_recompute_short": [("for (int64_t t = t0; t + 1 < t1; ++t)",
+                                   "for (int64_t t = t0; t + 2 < t1; ++t)")],
+    "bwd_dbeta_residual_sign": [("db += ddel[j] * (vt[j] - u[j]);",
+                                 "db += ddel[j] * (vt[j] + u[j]);")],
 }
 
 
