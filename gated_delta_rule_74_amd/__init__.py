@@ -64,6 +64,10 @@ _decode = _sig("kda_decode_step", _i,
 _decode_tokens = _sig("kda_decode_tokens", _i,
                       [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp, _vp] +
                       [_i] * 5 + [_f, ctypes.POINTER(KdaConvDesc), _vp, _vp])
+_bwd = _sig("kda_prefill_backward", _i,
+            [_vp, _vp, _vp, _i, _vp, _vp, _i] + [_vp] * 9 + [_i] * 6 +
+            [_f, _vp, _sz, _vp])
+_bwd_ws_size = _sig("kda_prefill_backward_workspace_size", _sz, [_i] * 7)
 _conv = _sig("kda_conv_prologue", _i,
              [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp] +
              [_i] * 5 + [_i, _f, _vp])
@@ -203,6 +207,41 @@ def kda_prefill_state_pass(workspace, o, *, s0=None, s_out=None, B, T, H,
     st = _state(_dt(o), _ptr(s0), _ptr(s_out), _ptr(o), B, T, H, Dk, Dv,
                 chunk, _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "kda_prefill_state_pass")
+
+
+def kda_prefill_backward_workspace_size(B, T, H, Dk, Dv, chunk,
+                                        qkv_dtype) -> int:
+    dt = qkv_dtype if isinstance(qkv_dtype, int) else (
+        KDA_BF16 if qkv_dtype == torch.bfloat16 else KDA_F32)
+    return int(_bwd_ws_size(B, T, H, Dk, Dv, chunk, dt))
+
+
+def kda_prefill_backward(q, k, v, g, beta, do, *, s0=None, dsT=None,
+                         chunk=64, scale=1.0, workspace=None, want_ds0=True,
+                         stream=None):
+    """Gradient of kda_prefill (no conv) for the loss sum(o*do) +
+    sum(S_T*dsT).  q,k,g [B,T,H,Dk] (g may be [B,T,H]), v, do [B,T,H,Dv],
+    beta [B,T,H].  Returns (dq, dk, dv, dg, dbeta, ds0 or None) with dg
+    shaped like g."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    dq, dk = torch.empty_like(q), torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dg, dbeta = torch.empty_like(g), torch.empty_like(beta)
+    ds0 = (torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+           if want_ds0 else None)
+    need = kda_prefill_backward_workspace_size(B, T, H, Dk, Dv, chunk,
+                                               _dt(q))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    st = _bwd(_ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(g), _ptr(beta),
+              _gate_dt(g, 4), _ptr(s0), _ptr(do), _ptr(dsT), _ptr(dq),
+              _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(ds0), B, T, H,
+              Dk, Dv, chunk, scale, _ptr(workspace), workspace.numel(),
+              _stream(stream))
+    _check(st, "kda_prefill_backward")
+    return dq, dk, dv, dg, dbeta, ds0
 
 
 def kda_decode_step(q, k, v, g, beta, state, *, scale=1.0, o=None,

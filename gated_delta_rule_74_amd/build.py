@@ -20,6 +20,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 SOURCES = ["kda_api.hip", "kda_prep_f32.hip", "kda_prep_bf16_f32.hip",
            "kda_prep_bf16_bf16.hip", "kda_state.hip", "kda_decode.hip",
+           "kda_backward.hip",
            "kda_conv.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -90,6 +90,31 @@ size_t ws_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
   return (size_t)B * H * nc * L.bytes;
 }
 
+// backward workspace: [forward factors | state at every chunk start |
+// gradient at every chunk end | dDelta | per-chunk intermediates | the
+// forward's output o, which the backward does not use]
+struct BwdWs {
+  size_t sc, dsc, dd, gs, o, total;
+};
+BwdWs bwd_ws(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype io) {
+  auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t nc = ((size_t)T + chunk - 1) / chunk, BH = (size_t)B * H;
+  BwdWs w;
+  size_t off = al(ws_bytes(B, T, H, Dk, Dv, chunk, io));
+  w.sc = off;
+  off = al(off + BH * nc * Dk * Dv * 4);
+  w.dsc = off;
+  off = al(off + BH * nc * Dk * Dv * 4);
+  w.dd = off;
+  off = al(off + (size_t)B * T * H * Dv * 4);
+  w.gs = off;
+  off = al(off + BH * nc * kda::backward_chunk_floats(chunk, Dk, Dv) * 4);
+  w.o = off;
+  off = al(off + (size_t)B * T * H * Dv * (io == KDA_BF16 ? 2 : 4));
+  w.total = off;
+  return w;
+}
+
 }  // namespace
 
 namespace kda {
@@ -192,6 +217,71 @@ kda_status kda_prefill(const void *q, const void *k, const void *v,
   hipError_t e = kda::launch_prefill_prep(p, bf, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e);
   return hip_status(kda::launch_state_pass(p, bf, (hipStream_t)stream));
+}
+
+size_t kda_prefill_backward_workspace_size(int B, int T, int H, int Dk,
+                                           int Dv, int chunk,
+                                           kda_dtype qkv_dtype) {
+  if (kda_prefill_workspace_size(B, T, H, Dk, Dv, chunk, qkv_dtype) == 0)
+    return 0;
+  return bwd_ws(B, T, H, Dk, Dv, chunk, qkv_dtype).total;
+}
+
+kda_status kda_prefill_backward(
+    const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
+    const void *g, const void *beta, kda_dtype gate_dtype, const float *s0,
+    const void *dO, const float *dsT, void *dq, void *dk, void *dv, void *dg,
+    void *dbeta, float *ds0, int B, int T, int H, int Dk, int Dv, int chunk,
+    float scale, void *workspace, size_t workspace_bytes, void *stream) {
+  kda::PrefillParams p;
+  kda_status st = prefill_check(q, k, v, qkv_dtype, g, beta, gate_dtype, B, T,
+                                H, Dk, Dv, chunk, scale, nullptr, true, p);
+  if (st != KDA_OK) return st;
+  const void *outs[] = {dq, dk, dv, dg, dbeta};
+  for (const void *o : outs)
+    if (!o || !aligned16(o)) return KDA_EINVAL;
+  if (!dO || !workspace || !aligned16(dO) || !aligned16(workspace))
+    return KDA_EINVAL;
+  const void *opt[] = {s0, dsT, ds0};
+  for (const void *o : opt)
+    if (o && !aligned16(o)) return KDA_EINVAL;
+  // no output may alias an input or another output
+  const void *ins[] = {q, k, v, g, beta, s0, dO, dsT};
+  const void *all_out[] = {dq, dk, dv, dg, dbeta, ds0};
+  for (int i = 0; i < 6; ++i) {
+    if (!all_out[i]) continue;
+    for (const void *x : ins)
+      if (x && x == all_out[i]) return KDA_EINVAL;
+    for (int j = i + 1; j < 6; ++j)
+      if (all_out[j] == all_out[i]) return KDA_EINVAL;
+  }
+  const BwdWs L = bwd_ws(B, T, H, Dk, Dv, chunk, qkv_dtype);
+  if (workspace_bytes < L.total) return KDA_EINVAL;
+  char *wsb = (char *)workspace;
+  const int bf = qkv_dtype == KDA_BF16;
+  hipStream_t s = (hipStream_t)stream;
+  // recompute the forward, keeping the state at every chunk start
+  p.s0 = s0;
+  p.s_out = nullptr;
+  p.o = wsb + L.o;
+  p.ws = wsb;
+  p.wsb = kda::ws_layout(Dk, Dv, chunk, bf ? 2 : 4).bytes;
+  p.ckpt = (float *)(wsb + L.sc);
+  hipError_t e = kda::launch_prefill_prep(p, bf, s);
+  if (e == hipSuccess) e = kda::launch_state_pass(p, bf, s);
+  if (e != hipSuccess) return hip_status(e);
+  kda::BwdParams bp{};
+  bp.f = p;
+  bp.f.ckpt = nullptr;
+  bp.dO = dO;
+  bp.dsT = dsT;
+  bp.ds0 = ds0;
+  bp.dD = (float *)(wsb + L.dd);
+  bp.dSc = (float *)(wsb + L.dsc);
+  bp.Sc = (const float *)(wsb + L.sc);
+  bp.gs = (float *)(wsb + L.gs);
+  bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dg = dg; bp.dbeta = dbeta;
+  return hip_status(kda::launch_backward(bp, bf, s));
 }
 
 kda_status kda_decode_step(const void *q, const void *k, const void *v,

@@ -1,0 +1,854 @@
+// kda_backward.hip -- gradient of the chunked KDA prefill (gfx950).
+//
+// With the chunk factors of the forward (kda_prep_impl.h: P, Qtil = scale
+// Q*Gam, Ktil = K*gam/Gam, W, U, gam per (batch*head, chunk)) and the state
+// S_n at the start of every chunk (saved by the forward state pass), the
+// loss gradient flows back through each chunk n as
+//   dDelta = P^T dO + Ktil dS'                  (dS' = gradient at the end)
+//   dS     = diag(gam) dS' + Qtil^T dO - W^T dDelta   (gradient at the start)
+// which is sequential over chunks (this file's first kernel, last chunk
+// first), and then, for every chunk independently, through the UT transform
+// and the decayed Gram products of that chunk into dq, dk, dv, dg, dbeta
+// (the second and third kernels).  The algebra is the reverse mode of the
+// token rule (see include/kda.h for the sources); each step below names the
+// forward product it differentiates.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+constexpr int BWD_THREADS = 256;
+constexpr int DVMAX_BWD = 128;
+
+// ---------------------------------------------------------------------------
+// helpers: fragment units <-> LDS
+// ---------------------------------------------------------------------------
+
+// Write the A-operand units of a matrix X (row tile a, k unit u at
+// sec[(a * nku + u) * 64 + lane]) transposed into LDS: XT[k][16a + m].
+// Units with u > a / TPU are taken as zero when `lower` (the never-written
+// units above the diagonal of P).
+template <typename IO>
+__device__ __forceinline__ void units_to_lds_t(const char *sec, int nrt,
+                                               int nku, int kmax, bool lower,
+                                               IO *XT, int ldt, int tid) {
+  using M = Mma<IO>;
+  typedef typename M::frag frag;
+  constexpr int KU = 16 * M::TPU;
+  for (int w = tid; w < nrt * nku * 64; w += BWD_THREADS) {
+    const int lane = w & 63, unit = w >> 6;
+    const int a = unit / nku, u = unit % nku;
+    const int m = lane & 15, g = lane >> 4;
+    frag f;
+    if (lower && u > a / M::TPU) {
+      f = frag{};
+    } else {
+      f = *(const frag *)(sec + (size_t)w * 16);
+    }
+#pragma unroll
+    for (int e = 0; e < M::NE; ++e) {
+      const int k = KU * u + M::koff(g, e);
+      if (k < kmax) XT[k * ldt + 16 * a + m] = (IO)M::elem(f, e);
+    }
+  }
+}
+
+// same, not transposed: X[16a + m][k]
+template <typename IO>
+__device__ __forceinline__ void units_to_lds(const char *sec, int nrt, int nku,
+                                             int kmax, IO *X, int ld, int tid) {
+  using M = Mma<IO>;
+  typedef typename M::frag frag;
+  constexpr int KU = 16 * M::TPU;
+  for (int w = tid; w < nrt * nku * 64; w += BWD_THREADS) {
+    const int lane = w & 63, unit = w >> 6;
+    const int a = unit / nku, u = unit % nku;
+    const int m = lane & 15, g = lane >> 4;
+    const frag f = *(const frag *)(sec + (size_t)w * 16);
+#pragma unroll
+    for (int e = 0; e < M::NE; ++e) {
+      const int k = KU * u + M::koff(g, e);
+      if (k < kmax) X[(16 * a + m) * ld + k] = (IO)M::elem(f, e);
+    }
+  }
+}
+
+// B-operand unit from a LDS array whose rows are the product's columns n
+// and are contiguous in k (as load_k); k beyond kmax reads zero
+template <typename IO>
+__device__ __forceinline__ typename Mma<IO>::frag lds_unit(const IO *row,
+                                                           int u, int g,
+                                                           int kmax) {
+  using M = Mma<IO>;
+  constexpr int KU = 16 * M::TPU;
+  return M::load_k(row + KU * u, g, KU * u + 16 < kmax || M::TPU == 1);
+}
+
+// ---------------------------------------------------------------------------
+// kernel 1: reverse state pass
+// ---------------------------------------------------------------------------
+
+template <typename IO, int DK, int C> struct BL {  // reverse-pass LDS layout
+  static constexpr int PE = 16 / (int)sizeof(IO);
+  static constexpr int LDC = C + PE, LDK = DK + PE;
+  static constexpr int TPU = Mma<IO>::TPU;
+  static constexpr int NB = C / 16, NKT = DK / 16;
+  static constexpr int NTU = (NB + TPU - 1) / TPU, NKU = (NKT + TPU - 1) / TPU;
+  static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
+  static constexpr size_t oPT = 0;                                  // [C][LDC]
+  static constexpr size_t oKK = al(oPT + (size_t)C * LDC * sizeof(IO));   // [C][LDK]
+  static constexpr size_t oQT = al(oKK + (size_t)C * LDK * sizeof(IO));   // [DK][LDC]
+  static constexpr size_t oWT = al(oQT + (size_t)DK * LDC * sizeof(IO));  // [DK][LDC]
+  static constexpr size_t oOT = al(oWT + (size_t)DK * LDC * sizeof(IO));  // [16][LDC]
+  static constexpr size_t oSU = al(oOT + (size_t)16 * LDC * sizeof(IO));  // dS units
+  static constexpr size_t oDU = al(oSU + (size_t)NKU * 1024);             // dDelta units
+  static constexpr size_t oGm = al(oDU + (size_t)NTU * 1024);             // gam [DK]
+  static constexpr size_t total = oGm + DK * 4;
+};
+
+template <typename IO, int DK, int C>
+__global__ __launch_bounds__(BWD_THREADS) void kda_bwd_state(BwdParams bp) {
+  using M = Mma<IO>;
+  using L = BL<IO, DK, C>;
+  typedef typename M::frag frag;
+  constexpr int NB = L::NB, NKT = L::NKT, TPU = L::TPU, NTU = L::NTU,
+                NKU = L::NKU, LDC = L::LDC, LDK = L::LDK;
+  constexpr int KT = (NKT + 3) / 4;  // key tiles per wave
+  const PrefillParams &p = bp.f;
+  __shared__ __attribute__((aligned(16))) char sm[L::total];
+  IO *PT = (IO *)(sm + L::oPT), *KK = (IO *)(sm + L::oKK);
+  IO *QT = (IO *)(sm + L::oQT), *WT = (IO *)(sm + L::oWT);
+  IO *OT = (IO *)(sm + L::oOT);
+  frag *SU = (frag *)(sm + L::oSU), *DU = (frag *)(sm + L::oDU);
+  float *Gm = (float *)(sm + L::oGm);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m16 = lane & 15, g4 = lane >> 4;
+  const int Dv = p.Dv, H = p.H, T = p.T, NC = p.NC;
+  const int nvt = Dv / 16;
+  const int bh = blockIdx.x / nvt, vt = blockIdx.x % nvt;
+  const int b = bh / H, h = bh % H;
+  const WsLayout W = ws_layout(DK, Dv, C, (int)sizeof(IO));
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  const size_t orow = (size_t)H * Dv;  // elements between tokens
+
+  // dS key tiles owned by this wave: t = wave + 4 j (accumulator layout:
+  // lane 16 g + n holds column n, rows 4g..4g+3 of the tile)
+  f32x4 dS[KT];
+#pragma unroll
+  for (int j = 0; j < KT; ++j) {
+    dS[j] = zero;
+    const int t = wave + 4 * j;
+    if (bp.dsT && t < NKT) {
+      const float *src = bp.dsT + ((size_t)bh * DK + 16 * t + 4 * g4) * Dv +
+                         16 * vt + m16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dS[j][e] = src[(size_t)e * Dv];
+    }
+  }
+  auto publish_ds = [&]() {
+    // B units of dS (k = key channel, n = value column)
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      const int t = wave + 4 * j;
+      if (t < NKT) {
+        frag *dst = SU + (t / TPU) * 64 + lane;
+        if (TPU == 2) {
+          bf16x4 v4 = {(bf16)dS[j][0], (bf16)dS[j][1], (bf16)dS[j][2],
+                       (bf16)dS[j][3]};
+          *(bf16x4 *)((char *)dst + 8 * (t & 1)) = v4;
+        } else {
+          *(f32x4 *)dst = dS[j];
+        }
+      }
+    }
+  };
+  // zero the units once (an odd tile count leaves a half that is never
+  // written)
+  for (int i = tid; i < (NKU + NTU) * 256; i += BWD_THREADS)
+    ((float *)SU)[i] = 0.f;
+  __syncthreads();
+  publish_ds();
+
+  for (int n = NC - 1; n >= 0; --n) {
+    const char *blk = p.ws + ((size_t)bh * NC + n) * p.wsb;
+    const int t0 = n * C;
+    // ---- stage the chunk's factors, transposed where the products need it
+    units_to_lds_t<IO>(blk + W.off_p, NB, NTU, C, true, PT, LDC, tid);
+    units_to_lds_t<IO>(blk + W.off_ktt, NKT, NTU, C, false, KK, LDK, tid);
+    units_to_lds_t<IO>(blk + W.off_qt, NB, NKU, DK, false, QT, LDC, tid);
+    units_to_lds_t<IO>(blk + W.off_negw, NB, NKU, DK, false, WT, LDC, tid);
+    for (int i = tid; i < 16 * C; i += BWD_THREADS) {
+      const int r = i % C, j = i / C;
+      const int t = t0 + r;
+      OT[j * LDC + r] =
+          t < T ? ((const IO *)bp.dO)[((size_t)b * T + t) * orow + (size_t)h * Dv +
+                                      16 * vt + j]
+                : (IO)0.f;
+    }
+    for (int i = tid; i < DK; i += BWD_THREADS)
+      Gm[i] = ((const float *)(blk + W.off_gam))[i];
+    __syncthreads();
+
+    // ---- the gradient at this chunk's end, for the per-chunk kernels
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      const int t = wave + 4 * j;
+      if (t < NKT) {
+        float *dst = bp.dSc + (((size_t)bh * NC + n) * DK + 16 * t + 4 * g4) * Dv +
+                     16 * vt + m16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(size_t)e * Dv] = dS[j][e];
+      }
+    }
+
+    // ---- dDelta = P^T dO + Ktil dS'   (token tile rt = wave)
+    if (wave < NB) {
+      const int rt = wave;
+      f32x4 acc = zero;
+#pragma unroll
+      for (int u = 0; u < NTU; ++u)
+        acc = M::mma(lds_unit<IO>(PT + (16 * rt + m16) * LDC, u, g4, C),
+                     lds_unit<IO>(OT + m16 * LDC, u, g4, C), acc);
+#pragma unroll
+      for (int u = 0; u < NKU; ++u)
+        acc = M::mma(lds_unit<IO>(KK + (16 * rt + m16) * LDK, u, g4, DK),
+                     SU[u * 64 + lane], acc);
+      // lane holds dDelta[16 rt + 4 g4 + e][16 vt + m16]
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = t0 + 16 * rt + 4 * g4 + e;
+        if (t < T)
+          bp.dD[((size_t)b * T + t) * orow + (size_t)h * Dv + 16 * vt + m16] =
+              acc[e];
+      }
+      frag *dst = DU + (rt / TPU) * 64 + lane;
+      if (TPU == 2) {
+        bf16x4 v4 = {(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
+        *(bf16x4 *)((char *)dst + 8 * (rt & 1)) = v4;
+      } else {
+        *(f32x4 *)dst = acc;
+      }
+    }
+    __syncthreads();
+
+    // ---- dS <- diag(gam) dS' + Qtil^T dO + (-W)^T dDelta
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      const int t = wave + 4 * j;
+      if (t < NKT) {
+        f32x4 acc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = dS[j][e] * Gm[16 * t + 4 * g4 + e];
+#pragma unroll
+        for (int u = 0; u < NTU; ++u) {
+          acc = M::mma(lds_unit<IO>(QT + (16 * t + m16) * LDC, u, g4, C),
+                       lds_unit<IO>(OT + m16 * LDC, u, g4, C), acc);
+          acc = M::mma(lds_unit<IO>(WT + (16 * t + m16) * LDC, u, g4, C),
+                       DU[u * 64 + lane], acc);
+        }
+        dS[j] = acc;
+      }
+    }
+    __syncthreads();  // every read of this chunk's LDS is done
+    publish_ds();
+  }
+  if (bp.ds0) {
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      const int t = wave + 4 * j;
+      if (t < NKT) {
+        float *dst = bp.ds0 + ((size_t)bh * DK + 16 * t + 4 * g4) * Dv +
+                     16 * vt + m16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(size_t)e * Dv] = dS[j][e];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// one 16x16 tile of op(A) op(B) on the matrix cores, operands gathered from
+// LDS (element types TA / TB, fp32 or the q/k/v dtype) and rounded to the
+// product's operand type:
+//   op(A)[m][k] = AT ? A[k * lda + m] : A[m * lda + k]
+//   op(B)[k][n] = BT ? B[n * ldb + k] : B[k * ldb + n]
+// acc is in the accumulator layout: lane 16 g + n holds column n0 + n and
+// rows m0 + 4g .. m0 + 4g + 3.
+// ---------------------------------------------------------------------------
+template <typename IO, bool AT, bool BT, typename TA, typename TB>
+__device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const TA *A, int lda,
+                                          const TB *B, int ldb, int m0, int n0,
+                                          int K, int lane) {
+  using M = Mma<IO>;
+  constexpr int KU = 16 * M::TPU;
+  const int m = lane & 15, g = lane >> 4;
+  for (int u = 0; u * KU < K; ++u) {
+    typename M::frag fa, fb;
+#pragma unroll
+    for (int e = 0; e < M::NE; ++e) {
+      const int k = KU * u + M::koff(g, e);
+      float av = 0.f, bv = 0.f;
+      if (k < K) {
+        av = to_f32(AT ? A[k * lda + m0 + m] : A[(m0 + m) * lda + k]);
+        bv = to_f32(BT ? B[(n0 + m) * ldb + k] : B[k * ldb + n0 + m]);
+      }
+      M::set(fa, e, av);
+      M::set(fb, e, bv);
+    }
+    acc = M::mma(fa, fb, acc);
+  }
+  return acc;
+}
+
+// per-chunk intermediates: the second kernel writes
+// [Delta C x Dv | dQtil C x Dk | dKtil C x Dk | dW C x Dk | dgam Dk], the
+// third adds [Kd = K*Gam C x Dk | dKd C x Dk] for its own later phases; fp32
+__host__ __device__ inline size_t bwd_gs_floats(int C, int Dk, int Dv) {
+  return (size_t)C * (Dv + 5 * Dk) + Dk;
+}
+
+// ---------------------------------------------------------------------------
+// kernel 2: per chunk, the products with the chunk's start state S and the
+// gradient at its end dS' (recomputed Delta = U - W S; dQtil = dO S^T;
+// dW = -dDelta S^T; dKtil = Delta dS'^T; dgam = rowsum(dS' * S)), 32 value
+// columns at a time
+// ---------------------------------------------------------------------------
+template <typename IO, int DK, int C> struct G1L {
+  static constexpr int SV = 32;  // value columns per slab
+  static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
+  static constexpr size_t oW = 0;                                   // [C][DK] IO
+  static constexpr size_t oS = al(oW + (size_t)C * DK * sizeof(IO));  // [DK][SV]
+  static constexpr size_t odS = al(oS + (size_t)DK * SV * 4);        // [DK][SV]
+  static constexpr size_t oO = al(odS + (size_t)DK * SV * 4);        // [C][SV]
+  static constexpr size_t odD = al(oO + (size_t)C * SV * 4);         // [C][SV]
+  static constexpr size_t oD = al(odD + (size_t)C * SV * 4);         // [C][SV]
+  static constexpr size_t total = oD + (size_t)C * SV * 4;
+};
+
+template <typename IO, int DK, int C>
+__global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
+    BwdParams bp) {
+  using L = G1L<IO, DK, C>;
+  constexpr int SV = L::SV, NB = C / 16, NKT = DK / 16;
+  constexpr int NTL = NB * NKT;          // C x DK output tiles
+  constexpr int TW = (NTL + 3) / 4;      // of them per wave
+  constexpr int NKU = (NKT + Mma<IO>::TPU - 1) / Mma<IO>::TPU;
+  const PrefillParams &p = bp.f;
+  __shared__ __attribute__((aligned(16))) char sm[L::total];
+  IO *nW = (IO *)(sm + L::oW);
+  float *Ss = (float *)(sm + L::oS), *dSs = (float *)(sm + L::odS);
+  float *Os = (float *)(sm + L::oO), *dDs = (float *)(sm + L::odD);
+  float *Ds = (float *)(sm + L::oD);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m16 = lane & 15, g4 = lane >> 4;
+  const int Dv = p.Dv, H = p.H, T = p.T, NC = p.NC;
+  const int bh = blockIdx.x / NC, n = blockIdx.x % NC;
+  const int b = bh / H, h = bh % H, t0 = n * C;
+  const WsLayout W = ws_layout(DK, Dv, C, (int)sizeof(IO));
+  const char *blk = p.ws + ((size_t)bh * NC + n) * p.wsb;
+  const float *S = bp.Sc + ((size_t)bh * NC + n) * DK * Dv;
+  const float *dS = bp.dSc + ((size_t)bh * NC + n) * DK * Dv;
+  float *gs = bp.gs + ((size_t)bh * NC + n) * bwd_gs_floats(C, DK, Dv);
+  const size_t orow = (size_t)H * Dv;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+  units_to_lds<IO>(blk + W.off_negw, NB, NKU, DK, nW, DK, tid);  // -W[r][i]
+
+  f32x4 aQ[TW], aK[TW], aW[TW];
+#pragma unroll
+  for (int j = 0; j < TW; ++j) aQ[j] = aK[j] = aW[j] = zero;
+  float dgam = 0.f;
+
+  for (int c0 = 0; c0 < Dv; c0 += SV) {
+    const int sv = min(SV, Dv - c0);
+    for (int i = tid; i < DK * SV; i += BWD_THREADS) {
+      const int r = i / SV, c = i % SV;
+      const bool ok = c < sv;
+      Ss[i] = ok ? S[(size_t)r * Dv + c0 + c] : 0.f;
+      dSs[i] = ok ? dS[(size_t)r * Dv + c0 + c] : 0.f;
+    }
+    for (int i = tid; i < C * SV; i += BWD_THREADS) {
+      const int r = i / SV, c = i % SV, t = t0 + r;
+      const bool ok = c < sv && t < T;
+      const size_t gi = ((size_t)b * T + t) * orow + (size_t)h * Dv + c0 + c;
+      Os[i] = ok ? to_f32(((const IO *)bp.dO)[gi]) : 0.f;
+      dDs[i] = ok ? bp.dD[gi] : 0.f;
+    }
+    __syncthreads();
+    // Delta = U - W S on this slab (U in accumulator tiles [vt][rt])
+    for (int tl = wave; tl < NB * (SV / 16); tl += 4) {
+      const int rt = tl % NB, ct = tl / NB;
+      const int vt = (c0 >> 4) + ct;
+      f32x4 acc = zero;
+      if (16 * ct < sv) {
+        const IO *us = (const IO *)(blk + W.off_u) +
+                       ((size_t)(vt * NB + rt) * 64 + lane) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = to_f32(us[e]);
+        acc = tile_mma<IO, false, false>(acc, nW, DK, Ss, SV, 16 * rt, 16 * ct,
+                                         DK, lane);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + 4 * g4 + e;
+        Ds[r * SV + 16 * ct + m16] = acc[e];
+        if (16 * ct < sv)
+          gs[(size_t)r * Dv + c0 + 16 * ct + m16] = t0 + r < T ? acc[e] : 0.f;
+      }
+    }
+    __syncthreads();
+    // dQtil += dO S^T, dW += -dDelta S^T, dKtil += Delta dS'^T
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+      const int tl = wave + 4 * j;
+      if (tl < NTL) {
+        const int rt = tl % NB, it = tl / NB;
+        aQ[j] = tile_mma<IO, false, true>(aQ[j], Os, SV, Ss, SV, 16 * rt,
+                                          16 * it, SV, lane);
+        aW[j] = tile_mma<IO, false, true>(aW[j], dDs, SV, Ss, SV, 16 * rt,
+                                          16 * it, SV, lane);
+        aK[j] = tile_mma<IO, false, true>(aK[j], Ds, SV, dSs, SV, 16 * rt,
+                                          16 * it, SV, lane);
+      }
+    }
+    if (tid < DK)
+      for (int c = 0; c < SV; ++c) dgam += dSs[tid * SV + c] * Ss[tid * SV + c];
+    __syncthreads();
+  }
+  float *gQ = gs + (size_t)C * Dv, *gK = gQ + (size_t)C * DK;
+  float *gW = gK + (size_t)C * DK, *gG = gW + (size_t)C * DK;
+#pragma unroll
+  for (int j = 0; j < TW; ++j) {
+    const int tl = wave + 4 * j;
+    if (tl < NTL) {
+      const int rt = tl % NB, it = tl / NB;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const size_t o = (size_t)(16 * rt + 4 * g4 + e) * DK + 16 * it + m16;
+        gQ[o] = aQ[j][e];
+        gK[o] = aK[j][e];
+        gW[o] = -aW[j][e];
+      }
+    }
+  }
+  if (tid < DK) gG[tid] = dgam;
+}
+
+// ---------------------------------------------------------------------------
+// kernel 3: per chunk, everything else -- the UT transform T = (I + A)^-1
+// with A = diag(beta) M, M[r,s] = sum_i k_ri k_si D_rsi (D_rs = Gam_r/Gam_s
+// as a product of e over (s, r], never a ratio), and the gradients
+//   dT = dDelta (beta V)^T + dW (beta Kd)^T,  dv = beta T^T dDelta,
+//   dKd = beta T^T dW,  dA = -T^T dT T^T (strictly lower),  dM = beta dA,
+//   dP = tril(dO Delta^T),  dbeta = rowsum(V*T^T dDelta + Kd*T^T dW + dA*M)
+// then, per key channel i and token r (one owner thread per pair), the
+// decayed products
+//   rowK_r = sum_{s<r} dM_rs k_s D_rs,    rowQ_r = sum_{s<=r} dPm_rs k_s D_rs
+//   colK_r = sum_{s>r} dM_sr k_s D_sr,    colQ_r = sum_{s>=r} dPm_sr q_s D_sr
+// (dPm = scale dP) and the elementwise terms of Kd = K*Gam, Qtil = scale
+// Q*Gam, Ktil = K*gam/Gam, gam:
+//   dk = rowK + colK + colQ + dKd*Gam + dKtil*gam/Gam
+//   dq = rowQ + scale dQtil*Gam
+//   dG = k rowK + q rowQ - k (colK + colQ) + dKd*Kd + dQtil*Qtil - dKtil*Ktil
+//   dG_last += sum_r dKtil*Ktil + dgam*gam,   dg_u = sum_{r>=u} dG_r
+// ---------------------------------------------------------------------------
+template <typename IO, int DK, int C> struct G2L {
+  static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
+  static constexpr size_t CC = (size_t)C * C * 4;
+  static constexpr size_t oM = 0, oT = CC, odP = 2 * CC, odM = 3 * CC,
+                          oX = 4 * CC;
+  static constexpr size_t oSm = 5 * CC;  // small arrays
+  static constexpr int RG = BWD_THREADS / DK;  // row groups of owner threads
+  static constexpr size_t oBeta = oSm, odB = oBeta + C * 4,
+                          odGl = odB + C * 4, oTail = odGl + DK * 4,
+                          odgh = oTail + (size_t)RG * DK * 4;
+  static constexpr size_t oR = al(odgh + C * 4);  // phase region
+  // largest phase: k, q (q/k/v dtype) and e (fp32), or two C x Dv arrays
+  static constexpr size_t RK = (size_t)C * DK * (2 * sizeof(IO) + 4);
+  static constexpr size_t RV = 2 * (size_t)C * DVMAX_BWD * sizeof(IO);
+  static constexpr size_t total = oR + (RK > RV ? RK : RV);
+};
+template <typename IO, int DK, int C> struct BwdFits {
+  static constexpr bool value = G2L<IO, DK, C>::total <= 160 * 1024 &&
+                                BL<IO, DK, C>::total <= 160 * 1024 &&
+                                G1L<IO, DK, C>::total <= 160 * 1024;
+};
+
+template <typename IO, typename GT, int DK, int C>
+__global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
+    BwdParams bp) {
+  using L = G2L<IO, DK, C>;
+  constexpr int NB = C / 16, NKT = DK / 16;
+  constexpr int RG = L::RG, RP = C / RG;  // owner rows per thread
+  static_assert(RG * DK == BWD_THREADS && RP * RG == C, "owner mapping");
+  constexpr bool GB = sizeof(GT) == 2;
+  const PrefillParams &p = bp.f;
+  __shared__ __attribute__((aligned(16))) char sm[L::total];
+  float *Mm = (float *)(sm + L::oM), *Tm = (float *)(sm + L::oT);
+  float *dPm = (float *)(sm + L::odP), *dMm = (float *)(sm + L::odM);
+  float *Xm = (float *)(sm + L::oX);
+  float *bet = (float *)(sm + L::oBeta), *dB = (float *)(sm + L::odB);
+  float *dGl = (float *)(sm + L::odGl), *tail = (float *)(sm + L::oTail);
+  float *dgh = (float *)(sm + L::odgh);
+  char *R = sm + L::oR;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m16 = lane & 15, g4 = lane >> 4;
+  const int Dv = p.Dv, H = p.H, T = p.T, NC = p.NC, nvt = Dv / 16;
+  const int bh = blockIdx.x / NC, n = blockIdx.x % NC;
+  const int b = bh / H, h = bh % H, t0 = n * C;
+  const float scale = p.scale;
+  float *gs = bp.gs + ((size_t)bh * NC + n) * bwd_gs_floats(C, DK, Dv);
+  float *gD = gs, *gQ = gs + (size_t)C * Dv, *gK = gQ + (size_t)C * DK;
+  float *gW = gK + (size_t)C * DK, *gG = gW + (size_t)C * DK;
+  float *gKd = gG + DK, *gdKd = gKd + (size_t)C * DK;
+  const size_t krow = (size_t)H * DK, vrow = (size_t)H * Dv;
+  const size_t kb = ((size_t)b * T * H + h) * DK;  // token 0 of (b, h), q/k/g
+  const size_t vb = ((size_t)b * T * H + h) * Dv;  // token 0, v / dO / dv
+  const size_t bb0 = (size_t)b * T * H + h;        // token 0, beta
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  const int oi = tid % DK, orh = tid / DK;  // owner: channel, row group
+
+  auto gate_at = [&](int t, int i) -> float {
+    const size_t gi = p.gate_head ? bb0 + (size_t)t * H
+                                  : kb + (size_t)t * krow + i;
+    return GB ? (float)((const bf16 *)p.g)[gi] : ((const float *)p.g)[gi];
+  };
+  // e for rows beyond the sequence is 1 (as in the forward)
+  auto load_ke = [&](IO *ks, IO *qs, float *es) {
+    for (int x = tid; x < C * DK; x += BWD_THREADS) {
+      const int r = x / DK, i = x % DK, t = t0 + r;
+      const bool ok = t < T;
+      ks[x] = ok ? ((const IO *)p.k)[kb + (size_t)t * krow + i] : (IO)0.f;
+      if (qs) qs[x] = ok ? ((const IO *)p.q)[kb + (size_t)t * krow + i] : (IO)0.f;
+      es[x] = ok ? __expf(gate_at(t, i)) : 1.f;
+    }
+  };
+
+  // ---- phase 1: beta, zeroed accumulators, M by running products ----------
+  for (int x = tid; x < C; x += BWD_THREADS) {
+    const int t = t0 + x;
+    bet[x] = t < T ? (GB ? (float)((const bf16 *)p.beta)[bb0 + (size_t)t * H]
+                         : ((const float *)p.beta)[bb0 + (size_t)t * H])
+                   : 0.f;
+    dB[x] = 0.f;
+    dgh[x] = 0.f;
+  }
+  for (int x = tid; x < C * C; x += BWD_THREADS) Mm[x] = 0.f;
+  for (int x = tid; x < DK; x += BWD_THREADS) dGl[x] = 0.f;
+  IO *ks = (IO *)R;
+  float *es = (float *)(R + (size_t)C * DK * sizeof(IO));
+  load_ke(ks, nullptr, es);
+  __syncthreads();
+  {
+    // item (s, 16-channel group): running D along r, partial M[r][s]
+    constexpr int NG = DK / 16;
+    for (int w = tid; w < C * NG; w += BWD_THREADS) {
+      const int s = w / NG, cg = w % NG;
+      float D[16], kss[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        D[c] = 1.f;
+        kss[c] = to_f32(ks[s * DK + 16 * cg + c]);
+      }
+      for (int r = s + 1; r < C; ++r) {
+        float part = 0.f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          D[c] *= es[r * DK + 16 * cg + c];
+          part += to_f32(ks[r * DK + 16 * cg + c]) * kss[c] * D[c];
+        }
+        atomicAdd(&Mm[r * C + s], part);
+      }
+    }
+    // Kd = K*Gam for the later phases (owner threads: prefix products)
+    float G = 1.f;
+    for (int r = 0; r < orh * RP; ++r) G *= es[r * DK + oi];
+    for (int j = 0; j < RP; ++j) {
+      const int r = orh * RP + j;
+      G *= es[r * DK + oi];
+      gKd[(size_t)r * DK + oi] = to_f32(ks[r * DK + oi]) * G;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: T = (I + diag(beta) M)^-1, one column per thread ----------
+  for (int s = tid; s < C; s += BWD_THREADS) {
+    for (int r = 0; r < s; ++r) Tm[r * C + s] = 0.f;
+    Tm[s * C + s] = 1.f;
+    for (int r = s + 1; r < C; ++r) {
+      float a = 0.f;
+      for (int u = s; u < r; ++u) a += Mm[r * C + u] * Tm[u * C + s];
+      Tm[r * C + s] = -bet[r] * a;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 3: value side: dT = dDelta (beta V)^T, dv = beta T^T dDelta --
+  {
+    IO *dDs = (IO *)R, *bVs = dDs + C * Dv;
+    for (int x = tid; x < C * Dv; x += BWD_THREADS) {
+      const int r = x / Dv, j = x % Dv, t = t0 + r;
+      const bool ok = t < T;
+      const float vv = ok ? to_f32(((const IO *)p.v)[vb + (size_t)t * vrow + j]) : 0.f;
+      dDs[x] = (IO)(ok ? bp.dD[vb + (size_t)t * vrow + j] : 0.f);
+      bVs[x] = (IO)(bet[r] * vv);
+    }
+    __syncthreads();
+    for (int tl = wave; tl < NB * NB; tl += 4) {
+      const int rt = tl % NB, st = tl / NB;
+      f32x4 acc = tile_mma<IO, false, true>(zero, dDs, Dv, bVs, Dv, 16 * rt,
+                                            16 * st, Dv, lane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dMm[(16 * rt + 4 * g4 + e) * C + 16 * st + m16] = acc[e];  // dT
+    }
+    for (int tl = wave; tl < NB * nvt; tl += 4) {
+      const int rt = tl % NB, ct = tl / NB;
+      f32x4 acc = tile_mma<IO, true, false>(zero, Tm, C, dDs, Dv, 16 * rt,
+                                            16 * ct, C, lane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + 4 * g4 + e, j = 16 * ct + m16, t = t0 + r;
+        if (t < T) {
+          ((IO *)bp.dv)[vb + (size_t)t * vrow + j] = from_f32<IO>(bet[r] * acc[e]);
+          atomicAdd(&dB[r],
+                    to_f32(((const IO *)p.v)[vb + (size_t)t * vrow + j]) * acc[e]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- phase 4: key side: dT += dW (beta Kd)^T, dKd = beta T^T dW ---------
+  {
+    IO *dWs = (IO *)R, *bKs = dWs + C * DK;
+    for (int x = tid; x < C * DK; x += BWD_THREADS) {
+      const int r = x / DK;
+      dWs[x] = (IO)gW[x];
+      bKs[x] = (IO)(bet[r] * gKd[x]);
+    }
+    __syncthreads();
+    for (int tl = wave; tl < NB * NB; tl += 4) {
+      const int rt = tl % NB, st = tl / NB;
+      f32x4 acc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc[e] = dMm[(16 * rt + 4 * g4 + e) * C + 16 * st + m16];
+      acc = tile_mma<IO, false, true>(acc, dWs, DK, bKs, DK, 16 * rt, 16 * st,
+                                      DK, lane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dMm[(16 * rt + 4 * g4 + e) * C + 16 * st + m16] = acc[e];
+    }
+    for (int tl = wave; tl < NB * NKT; tl += 4) {
+      const int rt = tl % NB, it = tl / NB;
+      f32x4 acc = tile_mma<IO, true, false>(zero, Tm, C, dWs, DK, 16 * rt,
+                                            16 * it, C, lane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + 4 * g4 + e, i = 16 * it + m16;
+        gdKd[(size_t)r * DK + i] = bet[r] * acc[e];
+        atomicAdd(&dB[r], gKd[(size_t)r * DK + i] * acc[e]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- phase 5: dA = -T^T dT T^T (strictly lower); dM = beta dA ------------
+  for (int tl = wave; tl < NB * NB; tl += 4) {
+    const int rt = tl % NB, st = tl / NB;
+    f32x4 acc = tile_mma<float, false, true>(zero, dMm, C, Tm, C, 16 * rt,
+                                             16 * st, C, lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      Xm[(16 * rt + 4 * g4 + e) * C + 16 * st + m16] = acc[e];
+  }
+  __syncthreads();
+  for (int tl = wave; tl < NB * NB; tl += 4) {
+    const int rt = tl % NB, st = tl / NB;
+    f32x4 acc = tile_mma<float, true, false>(zero, Tm, C, Xm, C, 16 * rt,
+                                             16 * st, C, lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * rt + 4 * g4 + e, s = 16 * st + m16;
+      const float dA = s < r ? -acc[e] : 0.f;
+      atomicAdd(&dB[r], dA * Mm[r * C + s]);
+      dMm[r * C + s] = bet[r] * dA;  // read only after the next barrier
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 6: dPm = scale tril(dO Delta^T) --------------------------------
+  {
+    IO *Os = (IO *)R, *Ds = Os + C * Dv;
+    for (int x = tid; x < C * Dv; x += BWD_THREADS) {
+      const int r = x / Dv, j = x % Dv, t = t0 + r;
+      const bool ok = t < T;
+      Os[x] = ok ? ((const IO *)bp.dO)[vb + (size_t)t * vrow + j] : (IO)0.f;
+      Ds[x] = (IO)gD[x];
+    }
+    __syncthreads();
+    for (int tl = wave; tl < NB * NB; tl += 4) {
+      const int rt = tl % NB, st = tl / NB;
+      f32x4 acc = tile_mma<IO, false, true>(zero, Os, Dv, Ds, Dv, 16 * rt,
+                                            16 * st, Dv, lane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + 4 * g4 + e, s = 16 * st + m16;
+        dPm[r * C + s] = s <= r ? scale * acc[e] : 0.f;
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- phase 7: decayed products and elementwise terms, per owner ---------
+  IO *qs = ks + C * DK;
+  es = (float *)(R + (size_t)2 * C * DK * sizeof(IO));
+  load_ke(ks, qs, es);
+  __syncthreads();
+  float dk_[RP], dq_[RP], dG_[RP];
+  {
+    const int i = oi;
+    // Gam before the owner's rows, and gam / Gam after them
+    float G = 1.f, Sf = 1.f;
+    for (int r = 0; r < orh * RP; ++r) G *= es[r * DK + i];
+    for (int r = (orh + 1) * RP; r < C; ++r) Sf *= es[r * DK + i];
+    float suf[RP];
+    {
+      float x = Sf;
+#pragma unroll
+      for (int j = RP - 1; j >= 0; --j) {
+        suf[j] = x;
+        x *= es[(orh * RP + j) * DK + i];
+      }
+    }
+    float kil = 0.f;  // this owner's part of sum_r dKtil*Ktil
+#pragma unroll
+    for (int j = 0; j < RP; ++j) {
+      const int r = orh * RP + j;
+      G *= es[r * DK + i];
+      const float kr = to_f32(ks[r * DK + i]), qr = to_f32(qs[r * DK + i]);
+      // row role
+      float rK = 0.f, rQ = dPm[r * C + r] * kr, D = 1.f;
+      for (int s2 = r - 1; s2 >= 0; --s2) {
+        D *= es[(s2 + 1) * DK + i];
+        const float tt = to_f32(ks[s2 * DK + i]) * D;
+        rK += dMm[r * C + s2] * tt;
+        rQ += dPm[r * C + s2] * tt;
+      }
+      // column role
+      float cK = 0.f, cQ = dPm[r * C + r] * qr;
+      D = 1.f;
+      for (int r2 = r + 1; r2 < C; ++r2) {
+        D *= es[r2 * DK + i];
+        cK += dMm[r2 * C + r] * to_f32(ks[r2 * DK + i]) * D;
+        cQ += dPm[r2 * C + r] * to_f32(qs[r2 * DK + i]) * D;
+      }
+      const size_t o = (size_t)r * DK + i;
+      const float kd = kr * G, qd = scale * qr * G, ki = kr * suf[j];
+      const float dkd = gdKd[o], dqd = gQ[o], dki = gK[o];
+      dk_[j] = rK + cK + cQ + dkd * G + dki * suf[j];
+      dq_[j] = rQ + scale * dqd * G;
+      dG_[j] = kr * rK + qr * rQ - kr * (cK + cQ) + dkd * kd + dqd * qd -
+               dki * ki;
+      kil += dki * ki;
+      if (r == C - 1) dG_[j] += gG[i] * G;  // dgam * gam (G = gam here)
+    }
+    atomicAdd(&dGl[i], kil);
+  }
+  __syncthreads();
+  // ---- phase 8: dg = reverse cumulative sum of dG, outputs ----------------
+  {
+    const int i = oi;
+    if (orh * RP + RP - 1 == C - 1) dG_[RP - 1] += dGl[i];
+    float own = 0.f;
+#pragma unroll
+    for (int j = 0; j < RP; ++j) own += dG_[j];
+    tail[orh * DK + i] = own;
+    __syncthreads();
+    float acc = 0.f;
+    for (int rr = orh + 1; rr < RG; ++rr) acc += tail[rr * DK + i];
+#pragma unroll
+    for (int j = RP - 1; j >= 0; --j) {
+      acc += dG_[j];
+      const int r = orh * RP + j, t = t0 + r;
+      if (t < T) {
+        const size_t o = kb + (size_t)t * krow + i;
+        ((IO *)bp.dq)[o] = from_f32<IO>(dq_[j]);
+        ((IO *)bp.dk)[o] = from_f32<IO>(dk_[j]);
+        if (p.gate_head)
+          atomicAdd(&dgh[r], acc);
+        else
+          ((GT *)bp.dg)[o] = (GT)acc;
+      }
+    }
+    __syncthreads();
+    for (int r = tid; r < C; r += BWD_THREADS) {
+      const int t = t0 + r;
+      if (t < T) {
+        ((GT *)bp.dbeta)[bb0 + (size_t)t * H] = (GT)dB[r];
+        if (p.gate_head) ((GT *)bp.dg)[bb0 + (size_t)t * H] = (GT)dgh[r];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <typename IO, typename GT, int DK, int C>
+static hipError_t bwd_one(const BwdParams &bp, hipStream_t s) {
+  if constexpr (!BwdFits<IO, DK, C>::value) {
+    return hipErrorInvalidValue;
+  } else {
+    const PrefillParams &p = bp.f;
+    const unsigned heads = (unsigned)(p.B * p.H);
+    hipLaunchKernelGGL((kda_bwd_state<IO, DK, C>), dim3(heads * (p.Dv / 16)),
+                       dim3(BWD_THREADS), 0, s, bp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((kda_bwd_chunk_state<IO, DK, C>), dim3(heads * p.NC),
+                       dim3(BWD_THREADS), 0, s, bp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((kda_bwd_chunk_grad<IO, GT, DK, C>), dim3(heads * p.NC),
+                       dim3(BWD_THREADS), 0, s, bp);
+    return hipGetLastError();
+  }
+}
+
+template <typename IO, typename GT>
+static hipError_t bwd_dk(const BwdParams &bp, hipStream_t s) {
+  switch (bp.f.Dk * 1000 + bp.f.C) {
+    case 16016: return bwd_one<IO, GT, 16, 16>(bp, s);
+    case 16032: return bwd_one<IO, GT, 16, 32>(bp, s);
+    case 16064: return bwd_one<IO, GT, 16, 64>(bp, s);
+    case 32016: return bwd_one<IO, GT, 32, 16>(bp, s);
+    case 32032: return bwd_one<IO, GT, 32, 32>(bp, s);
+    case 32064: return bwd_one<IO, GT, 32, 64>(bp, s);
+    case 64016: return bwd_one<IO, GT, 64, 16>(bp, s);
+    case 64032: return bwd_one<IO, GT, 64, 32>(bp, s);
+    case 64064: return bwd_one<IO, GT, 64, 64>(bp, s);
+    case 128016: return bwd_one<IO, GT, 128, 16>(bp, s);
+    case 128032: return bwd_one<IO, GT, 128, 32>(bp, s);
+    case 128064: return bwd_one<IO, GT, 128, 64>(bp, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_backward(const BwdParams &bp, int io_bf16, hipStream_t s) {
+  if (!io_bf16) return bwd_dk<float, float>(bp, s);
+  return bp.f.gate_bf16 ? bwd_dk<bf16, bf16>(bp, s) : bwd_dk<bf16, float>(bp, s);
+}
+
+size_t backward_chunk_floats(int C, int Dk, int Dv) {
+  return bwd_gs_floats(C, Dk, Dv);
+}
+
+}  // namespace kda

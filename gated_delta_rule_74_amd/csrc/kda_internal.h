@@ -22,7 +22,23 @@ struct PrefillParams {
   const float *wq, *wk, *wv;
   char *ws;                   // workspace base
   size_t wsb;                 // bytes per (bh, chunk) block
+  float *ckpt;                // state pass: if set, the state at the start
+                              // of every chunk, [B,H,NC,Dk,Dv] fp32
 };
+
+// gradient of the chunked prefill (kda_backward.hip)
+struct BwdParams {
+  PrefillParams f;       // forward sizes, inputs and its workspace (ws, wsb)
+  const void *dO;        // [B,T,H,Dv] in the q/k/v dtype
+  const float *dsT;      // [B,H,Dk,Dv] or null
+  float *ds0;            // [B,H,Dk,Dv] or null
+  float *dD;             // dDelta, [B,T,H,Dv] fp32 (scratch)
+  float *dSc;            // gradient at the end of every chunk [B,H,NC,Dk,Dv]
+  const float *Sc;       // forward state at the start of every chunk
+  float *gs;             // per-chunk intermediates (second kernel -> third)
+  void *dq, *dk, *dv, *dg, *dbeta;
+};
+
 
 struct DecodeParams {
   const void *q, *k, *v, *g, *beta;  // [N,L,H,*], beta [N,L,H]
@@ -64,6 +80,11 @@ hipError_t launch_prefill_prep_bf16_bf16(const PrefillParams &p,
 hipError_t launch_state_pass(const PrefillParams &p, int io_bf16,
                              hipStream_t s);
 hipError_t launch_decode(const DecodeParams &p, int io_bf16, hipStream_t s);
+// the three backward kernels (the forward's prep and state pass, with state
+// checkpoints, must have filled bp.f.ws and bp.Sc first)
+hipError_t launch_backward(const BwdParams &bp, int io_bf16, hipStream_t s);
+// floats of per-chunk backward intermediates
+size_t backward_chunk_floats(int C, int Dk, int Dv);
 hipError_t launch_conv(const ConvParams &p, hipStream_t s);
 // the history update alone (after a consumer of the old history has run)
 hipError_t launch_conv_cache(const ConvParams &p, hipStream_t s);

@@ -254,7 +254,27 @@ __global__ __launch_bounds__(STATE_THREADS, 1) void kda_state_pass(
     publish_s();
     lds_barrier();
 
+    // the state at the start of chunk n, for the backward pass
+    auto save_state = [&](int n) {
+#pragma unroll
+      for (int j = 0; j < KUW; ++j)
+#pragma unroll
+        for (int hh = 0; hh < TPU; ++hh) {
+          const int t = TPU * (w4 + SW * j) + hh;
+          if (kv[j] && t < NKT) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+              float *so = p.ckpt +
+                          (((size_t)bh * NC + n) * DK + 16 * t + 4 * g4) * Dv +
+                          16 * (vt0 + s) + m16;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) so[(size_t)e * Dv] = S[j][hh][s][e];
+            }
+          }
+        }
+    };
     auto sstep = [&](int n, const SF &f, SF &nx) {
+      if (p.ckpt) save_state(n);
       const char *nblk = ws0 + (size_t)min(n + 1, NC - 1) * p.wsb;
       load_state<0, IO, DK, C, NS>(nx, nblk, W, rtc, w4, lane, g4, vt0);
       frag sb[NS][NKU];

@@ -106,7 +106,7 @@ typedef struct kda_conv_desc {
 } kda_conv_desc;
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 int kda_abi_version(void);
 
 /* Static text for a status code (never NULL). */
@@ -159,6 +159,40 @@ kda_status kda_prefill_state_pass(kda_dtype qkv_dtype, const float *s0,
                                   int Dk, int Dv, int chunk,
                                   const void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace kda_prefill_backward needs (0 if the sizes are
+ * invalid or unsupported): the forward's factors, the state at every chunk
+ * start and the gradient at every chunk end (fp32, Dk*Dv per chunk-head),
+ * and per-chunk intermediates; about 2.6x the forward's input bytes plus
+ * 8*Dk*Dv bytes per chunk-head. */
+size_t kda_prefill_backward_workspace_size(int B, int T, int H, int Dk,
+                                           int Dv, int chunk,
+                                           kda_dtype qkv_dtype);
+
+/* Gradient of kda_prefill (without the conv prologue) for training: the
+ * layer is trained end to end ([SARNAS] "What exactly changed", the
+ * pretraining comparison of KDA against Gated DeltaNet).  Reverse mode of
+ * the token rule, evaluated in chunks: the forward is recomputed (chunk
+ * prep, then the state pass keeping the state at every chunk start), the
+ * gradient of the state is carried back over the chunks, and every chunk's
+ * inputs get their gradients in parallel.  Loss-gradient inputs:
+ *   dO    [B,T,H,Dv] in qkv_dtype (gradient of o)
+ *   dsT   [B,H,Dk,Dv] fp32 gradient of the final state, or NULL (zero)
+ * Outputs (each written in full; none may alias an input or each other):
+ *   dq, dk [B,T,H,Dk] and dv [B,T,H,Dv] in qkv_dtype
+ *   dg     [B,T,H,Dk] in gate_dtype ([B,T,H] with KDA_GATE_HEAD: the sum
+ *          over the key channels the gate multiplies)
+ *   dbeta  [B,T,H] in gate_dtype
+ *   ds0    [B,H,Dk,Dv] fp32 gradient of s0, or NULL
+ * Other arguments, sizes and errors as for kda_prefill (q, k, v must be
+ * given; s0 may be NULL for zeros).  workspace: at least
+ * kda_prefill_backward_workspace_size() bytes. */
+kda_status kda_prefill_backward(
+    const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
+    const void *g, const void *beta, kda_dtype gate_dtype, const float *s0,
+    const void *dO, const float *dsT, void *dq, void *dk, void *dv, void *dg,
+    void *dbeta, float *ds0, int B, int T, int H, int Dk, int Dv, int chunk,
+    float scale, void *workspace, size_t workspace_bytes, void *stream);
 
 /* One recurrent decode step for N independent sequences ([LQNN-A]: the
  * fused recurrent GPU kernel used for generation).
