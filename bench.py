@@ -1,7 +1,7 @@
 """Benchmark of the KDA forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
-                    [--no-cpu] [--only prefill,decode,tokens,conv,long,gdn,copy]
+                    [--no-cpu] [--only prefill,decode,tokens,conv,long,gdn,bwd,copy]
                     [--decode-steps N]
 
 Headline (`value`): chunked prefill tokens/s on the model-shaped workload
@@ -95,6 +95,7 @@ def main():
                          "gdn, copy (tokens = the verify step and the "
                          "generation step with the fused conv; gdn = the "
                          "headline prefill with one gate per token-head; "
+                         "bwd = the gradient of the headline prefill; "
                          "copy = a plain 1 GiB device copy, the reference "
                          "for scaling HBM byte counters)")
     ap.add_argument("--decode-steps", type=int, default=None,
@@ -103,7 +104,7 @@ def main():
     args = ap.parse_args()
     only = None if args.only is None else set(args.only.split(","))
     bad = (only or set()) - {"prefill", "decode", "tokens", "conv", "long",
-                           "gdn", "copy"}
+                           "gdn", "bwd", "copy"}
     if bad:
         ap.error(f"unknown --only part(s): {sorted(bad)}")
     sel = lambda part: (only is None and part != "copy") or \
@@ -373,6 +374,46 @@ def main():
                                 algo_gbs=gbs, hbm_frac=gbs / HBM_PEAK_GBS)
         log(f"{tag}: {ms:.3f} ms/call, {gbs:.0f} GB/s algorithmic")
         del x, ws, o, s
+        torch.cuda.empty_cache()
+
+    # ---------------- backward of the headline prefill ---------------------
+    if sel("bwd") and not args.no_extra:
+        c = ki.CONFIGS[1]
+        Bc, Tc, Hc, Dc, Cc = c["B"], c["T"], c["H"], c["Dk"], c["chunk"]
+        log("bwd: generating inputs")
+        x = ki.config_prefill_inputs(1, device=dev)
+        gen = torch.Generator(device=dev).manual_seed(7)
+        do = torch.randn((Bc, Tc, Hc, Dc), generator=gen,
+                         device=dev).to(torch.bfloat16)
+        ws = torch.empty(kda.kda_prefill_backward_workspace_size(
+            Bc, Tc, Hc, Dc, Dc, Cc, torch.bfloat16), dtype=torch.uint8,
+            device=dev)
+        fb = lambda: kda.kda_prefill_backward(x["q"], x["k"], x["v"], x["g"],
+                                              x["beta"], do, chunk=Cc,
+                                              workspace=ws)
+        fb()
+        torch.cuda.synchronize()
+        reps = 5
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(reps):
+            fb()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tok = Bc * Tc * Hc
+        # inputs q,k,v,dO (bf16), g (fp32), beta read once; dq,dk,dv (bf16),
+        # dg (fp32), dbeta written once; ds0 written
+        byts = tok * (4 * Dc * 2 + Dc * 4 + 4 + 3 * Dc * 2 + Dc * 4 + 4) + \
+            Bc * Hc * Dc * Dc * 4
+        gbs = byts / (ms * 1e-3) / 1e9
+        extra[c["name"] + "_backward"] = dict(
+            ms_per_call=ms, tokens_per_s=Bc * Tc / (ms * 1e-3), algo_gbs=gbs,
+            hbm_frac=gbs / HBM_PEAK_GBS,
+            vs_forward=ms / out["prefill"]["ms_per_step"]
+            if "prefill" in out else None)
+        log(f"bwd: {ms:.3f} ms/call, {gbs:.0f} GB/s algorithmic")
+        del x, do, ws
         torch.cuda.empty_cache()
 
     # ---------------- copy reference for the byte counters -----------------

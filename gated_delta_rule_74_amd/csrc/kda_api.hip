@@ -91,10 +91,11 @@ size_t ws_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
 }
 
 // backward workspace: [forward factors | state at every chunk start |
-// gradient at every chunk end | dDelta | per-chunk intermediates | the
-// forward's output o, which the backward does not use]
+// gradient at every chunk end | dDelta | per-chunk intermediates | A and
+// T^T of every chunk | the forward's output o, which the backward does not
+// use]
 struct BwdWs {
-  size_t sc, dsc, dd, gs, o, total;
+  size_t sc, dsc, dd, gs, at, o, total;
 };
 BwdWs bwd_ws(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype io) {
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
@@ -109,6 +110,8 @@ BwdWs bwd_ws(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype io) {
   off = al(off + (size_t)B * T * H * Dv * 4);
   w.gs = off;
   off = al(off + BH * nc * kda::backward_chunk_floats(chunk, Dk, Dv) * 4);
+  w.at = off;
+  off = al(off + BH * nc * 2 * (size_t)chunk * chunk * 4);
   w.o = off;
   off = al(off + (size_t)B * T * H * Dv * (io == KDA_BF16 ? 2 : 4));
   w.total = off;
@@ -267,6 +270,7 @@ kda_status kda_prefill_backward(
   p.ws = wsb;
   p.wsb = kda::ws_layout(Dk, Dv, chunk, bf ? 2 : 4).bytes;
   p.ckpt = (float *)(wsb + L.sc);
+  p.train_at = (float *)(wsb + L.at);
   hipError_t e = kda::launch_prefill_prep(p, bf, s);
   if (e == hipSuccess) e = kda::launch_state_pass(p, bf, s);
   if (e != hipSuccess) return hip_status(e);

@@ -304,9 +304,10 @@ __device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const TA *A, int lda,
 
 // per-chunk intermediates: the second kernel writes
 // [Delta C x Dv | dQtil C x Dk | dKtil C x Dk | dW C x Dk | dgam Dk], the
-// third adds [Kd = K*Gam C x Dk | dKd C x Dk] for its own later phases; fp32
+// third adds [Kd = K*Gam | dKd | dk, dq, dG accumulators] (C x Dk each)
+// for its own later phases; fp32
 __host__ __device__ inline size_t bwd_gs_floats(int C, int Dk, int Dv) {
-  return (size_t)C * (Dv + 5 * Dk) + Dk;
+  return (size_t)C * (Dv + 8 * Dk) + Dk;
 }
 
 // ---------------------------------------------------------------------------
@@ -439,9 +440,10 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
 }
 
 // ---------------------------------------------------------------------------
-// kernel 3: per chunk, everything else -- the UT transform T = (I + A)^-1
-// with A = diag(beta) M, M[r,s] = sum_i k_ri k_si D_rsi (D_rs = Gam_r/Gam_s
-// as a product of e over (s, r], never a ratio), and the gradients
+// kernel 3: per chunk, everything else.  The UT transform T = (I + A)^-1
+// and A = diag(beta) M, M[r,s] = sum_i k_ri k_si D_rsi (D_rs = Gam_r/Gam_s,
+// a product of e over (s, r]) come from the forward's chunk prep, which
+// saves them when it runs for the backward; the gradients are
 //   dT = dDelta (beta V)^T + dW (beta Kd)^T,  dv = beta T^T dDelta,
 //   dKd = beta T^T dW,  dA = -T^T dT T^T (strictly lower),  dM = beta dA,
 //   dP = tril(dO Delta^T),  dbeta = rowsum(V*T^T dDelta + Kd*T^T dW + dA*M)
@@ -507,6 +509,8 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   float *gD = gs, *gQ = gs + (size_t)C * Dv, *gK = gQ + (size_t)C * DK;
   float *gW = gK + (size_t)C * DK, *gG = gW + (size_t)C * DK;
   float *gKd = gG + DK, *gdKd = gKd + (size_t)C * DK;
+  float *aDk = gdKd + (size_t)C * DK, *aDq = aDk + (size_t)C * DK;
+  float *aDG = aDq + (size_t)C * DK;
   const size_t krow = (size_t)H * DK, vrow = (size_t)H * Dv;
   const size_t kb = ((size_t)b * T * H + h) * DK;  // token 0 of (b, h), q/k/g
   const size_t vb = ((size_t)b * T * H + h) * Dv;  // token 0, v / dO / dv
@@ -530,7 +534,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
     }
   };
 
-  // ---- phase 1: beta, zeroed accumulators, M by running products ----------
+  // ---- phase 1: beta, accumulators, M and T from the forward, Kd -----------
   for (int x = tid; x < C; x += BWD_THREADS) {
     const int t = t0 + x;
     bet[x] = t < T ? (GB ? (float)((const bf16 *)p.beta)[bb0 + (size_t)t * H]
@@ -539,31 +543,33 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
     dB[x] = 0.f;
     dgh[x] = 0.f;
   }
-  for (int x = tid; x < C * C; x += BWD_THREADS) Mm[x] = 0.f;
   for (int x = tid; x < DK; x += BWD_THREADS) dGl[x] = 0.f;
   IO *ks = (IO *)R;
   float *es = (float *)(R + (size_t)C * DK * sizeof(IO));
   load_ke(ks, nullptr, es);
   __syncthreads();
   {
-    // item (s, 16-channel group): running D along r, partial M[r][s]
-    constexpr int NG = DK / 16;
-    for (int w = tid; w < C * NG; w += BWD_THREADS) {
-      const int s = w / NG, cg = w % NG;
-      float D[16], kss[16];
-#pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        D[c] = 1.f;
-        kss[c] = to_f32(ks[s * DK + 16 * cg + c]);
-      }
-      for (int r = s + 1; r < C; ++r) {
-        float part = 0.f;
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-          D[c] *= es[r * DK + 16 * cg + c];
-          part += to_f32(ks[r * DK + 16 * cg + c]) * kss[c] * D[c];
+    // A = diag(beta) M and T^T as the forward's chunk prep left them (only
+    // the lower triangles are meaningful)
+    const float *at = p.train_at + ((size_t)bh * NC + n) * 2 * C * C;
+    for (int x = tid; x < C * C; x += BWD_THREADS) {
+      const int r = x / C, c = x % C;
+      const float br = bet[r];
+      Mm[x] = (c < r && br != 0.f) ? at[x] / br : 0.f;
+      Tm[x] = c <= r ? at[C * C + c * C + r] : 0.f;
+    }
+    // rows with beta = 0 (A carries no M there): M directly, with running
+    // products of e over (s, r] -- exact, and rare
+    for (int r = 1; r < C; ++r) {
+      if (bet[r] != 0.f || t0 + r >= T) continue;
+      for (int s2 = tid; s2 < r; s2 += BWD_THREADS) {
+        float m = 0.f;
+        for (int i = 0; i < DK; ++i) {
+          float D = 1.f;
+          for (int u = s2 + 1; u <= r; ++u) D *= es[u * DK + i];
+          m += to_f32(ks[r * DK + i]) * to_f32(ks[s2 * DK + i]) * D;
         }
-        atomicAdd(&Mm[r * C + s], part);
+        Mm[r * C + s2] = m;
       }
     }
     // Kd = K*Gam for the later phases (owner threads: prefix products)
@@ -573,18 +579,6 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
       const int r = orh * RP + j;
       G *= es[r * DK + oi];
       gKd[(size_t)r * DK + oi] = to_f32(ks[r * DK + oi]) * G;
-    }
-  }
-  __syncthreads();
-
-  // ---- phase 2: T = (I + diag(beta) M)^-1, one column per thread ----------
-  for (int s = tid; s < C; s += BWD_THREADS) {
-    for (int r = 0; r < s; ++r) Tm[r * C + s] = 0.f;
-    Tm[s * C + s] = 1.f;
-    for (int r = s + 1; r < C; ++r) {
-      float a = 0.f;
-      for (int u = s; u < r; ++u) a += Mm[r * C + u] * Tm[u * C + s];
-      Tm[r * C + s] = -bet[r] * a;
     }
   }
   __syncthreads();
@@ -708,80 +702,131 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   }
 
   // ---- phase 7: decayed products and elementwise terms, per owner ---------
+  // Each owner (channel i, rows R0 .. R0+RP-1) sweeps the chunk once per
+  // role with a register vector, so every step is C independent products:
+  //   row role, r upward:    Y[s] = k_s D_rs  (s <= r; D_rr = 1)
+  //   column role, s downward: V[r] = x_r D_rs (r >= s), x = k or q
+  // and D is only ever multiplied by one more e (no ratios).
   IO *qs = ks + C * DK;
   es = (float *)(R + (size_t)2 * C * DK * sizeof(IO));
   load_ke(ks, qs, es);
+  float *dMT = Mm, *dPT = Tm;  // transposed copies (Mm, Tm are free now)
+  for (int x = tid; x < C * C; x += BWD_THREADS) {
+    const int r = x / C, c = x % C;
+    dMT[c * C + r] = dMm[x];
+    dPT[c * C + r] = dPm[x];
+  }
   __syncthreads();
-  float dk_[RP], dq_[RP], dG_[RP];
   {
-    const int i = oi;
-    // Gam before the owner's rows, and gam / Gam after them
-    float G = 1.f, Sf = 1.f;
-    for (int r = 0; r < orh * RP; ++r) G *= es[r * DK + i];
-    for (int r = (orh + 1) * RP; r < C; ++r) Sf *= es[r * DK + i];
-    float suf[RP];
+    // owner (r, i)'s accumulators live in aDk / aDq / aDG (this workgroup's
+    // scratch), so the row loops need no register arrays
+    const int i = oi, R0 = orh * RP, R1 = R0 + RP - 1;
+    const float *ec = es + i;           // e of this channel, row stride DK
+    const IO *kc = ks + i, *qc = qs + i;
+    // row role: Y[s] for the step before row R0
+    float Y[C];
     {
-      float x = Sf;
+      float P = 1.f;
 #pragma unroll
-      for (int j = RP - 1; j >= 0; --j) {
-        suf[j] = x;
-        x *= es[(orh * RP + j) * DK + i];
+      for (int s2 = C - 1; s2 >= 0; --s2) {
+        const bool on = s2 < R0;
+        Y[s2] = on ? to_f32(kc[s2 * DK]) * P : 0.f;
+        if (on) P *= ec[s2 * DK];
       }
     }
-    float kil = 0.f;  // this owner's part of sum_r dKtil*Ktil
-#pragma unroll
+#pragma unroll 1
     for (int j = 0; j < RP; ++j) {
-      const int r = orh * RP + j;
-      G *= es[r * DK + i];
-      const float kr = to_f32(ks[r * DK + i]), qr = to_f32(qs[r * DK + i]);
-      // row role
-      float rK = 0.f, rQ = dPm[r * C + r] * kr, D = 1.f;
-      for (int s2 = r - 1; s2 >= 0; --s2) {
-        D *= es[(s2 + 1) * DK + i];
-        const float tt = to_f32(ks[s2 * DK + i]) * D;
-        rK += dMm[r * C + s2] * tt;
-        rQ += dPm[r * C + s2] * tt;
-      }
-      // column role
-      float cK = 0.f, cQ = dPm[r * C + r] * qr;
-      D = 1.f;
-      for (int r2 = r + 1; r2 < C; ++r2) {
-        D *= es[r2 * DK + i];
-        cK += dMm[r2 * C + r] * to_f32(ks[r2 * DK + i]) * D;
-        cQ += dPm[r2 * C + r] * to_f32(qs[r2 * DK + i]) * D;
+      const int r = R0 + j;
+      const float er = ec[r * DK], kr = to_f32(kc[r * DK]);
+      float aK = 0.f, aQ = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < C; ++s2) {
+        Y[s2] = (s2 == r) ? kr : Y[s2] * er;
+        aK += dMm[r * C + s2] * Y[s2];
+        aQ += dPm[r * C + s2] * Y[s2];
       }
       const size_t o = (size_t)r * DK + i;
-      const float kd = kr * G, qd = scale * qr * G, ki = kr * suf[j];
-      const float dkd = gdKd[o], dqd = gQ[o], dki = gK[o];
-      dk_[j] = rK + cK + cQ + dkd * G + dki * suf[j];
-      dq_[j] = rQ + scale * dqd * G;
-      dG_[j] = kr * rK + qr * rQ - kr * (cK + cQ) + dkd * kd + dqd * qd -
-               dki * ki;
+      aDk[o] = aK;
+      aDq[o] = aQ;
+      aDG[o] = kr * aK + to_f32(qc[r * DK]) * aQ;
+    }
+    // column role, once for k (dM) and once for q (dPm)
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+      const IO *xc = pass == 0 ? kc : qc;
+      const float *cm = pass == 0 ? dMT : dPT;
+      float V[C];
+      {
+        float P = 1.f;
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
+          if (r > R1) P *= ec[r * DK];
+          V[r] = r >= R1 ? to_f32(xc[r * DK]) * P : 0.f;
+        }
+      }
+#pragma unroll 1
+      for (int jj = RP - 1; jj >= 0; --jj) {
+        const int s2 = R0 + jj;
+        if (jj < RP - 1) {
+          const float en = ec[(s2 + 1) * DK], xv = to_f32(xc[s2 * DK]);
+#pragma unroll
+          for (int r = 0; r < C; ++r) V[r] = (r == s2) ? xv : V[r] * en;
+        }
+        float a = 0.f;
+#pragma unroll
+        for (int r = 0; r < C; ++r) a += cm[s2 * C + r] * V[r];
+        const size_t o = (size_t)s2 * DK + i;
+        aDk[o] += a;
+        aDG[o] -= to_f32(kc[s2 * DK]) * a;
+      }
+    }
+    // elementwise terms: Gam upward, gam / Gam downward
+    float G = 1.f;
+    for (int r = 0; r < R0; ++r) G *= ec[r * DK];
+    for (int j = 0; j < RP; ++j) {
+      const int r = R0 + j;
+      G *= ec[r * DK];
+      const float kr = to_f32(kc[r * DK]), qr = to_f32(qc[r * DK]);
+      const size_t o = (size_t)r * DK + i;
+      const float dkd = gdKd[o], dqd = gQ[o];
+      aDk[o] += dkd * G;
+      aDq[o] += scale * dqd * G;
+      float dg = dkd * kr * G + dqd * scale * qr * G;
+      if (r == C - 1) dg += gG[i] * G;  // dgam * gam (G = gam here)
+      aDG[o] += dg;
+    }
+    float Sf = 1.f, kil = 0.f;  // kil: this owner's part of sum dKtil*Ktil
+    for (int r = C - 1; r > R1; --r) Sf *= ec[r * DK];
+    for (int j = RP - 1; j >= 0; --j) {
+      const int r = R0 + j;
+      const size_t o = (size_t)r * DK + i;
+      const float dki = gK[o], ki = to_f32(kc[r * DK]) * Sf;
+      aDk[o] += dki * Sf;
+      aDG[o] -= dki * ki;
       kil += dki * ki;
-      if (r == C - 1) dG_[j] += gG[i] * G;  // dgam * gam (G = gam here)
+      Sf *= ec[r * DK];
     }
     atomicAdd(&dGl[i], kil);
   }
   __syncthreads();
   // ---- phase 8: dg = reverse cumulative sum of dG, outputs ----------------
   {
-    const int i = oi;
-    if (orh * RP + RP - 1 == C - 1) dG_[RP - 1] += dGl[i];
+    const int i = oi, R0 = orh * RP;
+    if (R0 + RP - 1 == C - 1) aDG[(size_t)(C - 1) * DK + i] += dGl[i];
     float own = 0.f;
-#pragma unroll
-    for (int j = 0; j < RP; ++j) own += dG_[j];
+    for (int j = 0; j < RP; ++j) own += aDG[(size_t)(R0 + j) * DK + i];
     tail[orh * DK + i] = own;
     __syncthreads();
     float acc = 0.f;
     for (int rr = orh + 1; rr < RG; ++rr) acc += tail[rr * DK + i];
-#pragma unroll
     for (int j = RP - 1; j >= 0; --j) {
-      acc += dG_[j];
-      const int r = orh * RP + j, t = t0 + r;
+      const int r = R0 + j, t = t0 + r;
+      const size_t oa = (size_t)r * DK + i;
+      acc += aDG[oa];
       if (t < T) {
         const size_t o = kb + (size_t)t * krow + i;
-        ((IO *)bp.dq)[o] = from_f32<IO>(dq_[j]);
-        ((IO *)bp.dk)[o] = from_f32<IO>(dk_[j]);
+        ((IO *)bp.dq)[o] = from_f32<IO>(aDq[oa]);
+        ((IO *)bp.dk)[o] = from_f32<IO>(aDk[oa]);
         if (p.gate_head)
           atomicAdd(&dgh[r], acc);
         else

@@ -24,6 +24,8 @@ struct PrefillParams {
   size_t wsb;                 // bytes per (bh, chunk) block
   float *ckpt;                // state pass: if set, the state at the start
                               // of every chunk, [B,H,NC,Dk,Dv] fp32
+  float *train_at;            // chunk prep: if set, per (bh, chunk) the
+                              // matrix A then T^T, C x C fp32 each
 };
 
 // gradient of the chunked prefill (kda_backward.hip)

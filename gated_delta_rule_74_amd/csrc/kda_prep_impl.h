@@ -849,6 +849,15 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     }
 
     if (more) prep_load<8, IO, GT, DK, C, CONV>(p, task + gridDim.x, st, tid);
+    if (p.train_at) {
+      // for the backward pass: A = diag(beta) M and T^T, fp32
+      float *dst = p.train_at + ((size_t)bh * p.NC + n) * 2 * C * C;
+      for (int i = tid; i < C * C; i += PREP_THREADS) {
+        const int r = i / C, c = i % C;
+        dst[i] = Af[r * LDA + c];
+        dst[C * C + i] = Tt[r * LDA + c];
+      }
+    }
     // ---- WU: -W (A-operand units) and U (accumulator tiles) ----------------
     // wave rt takes token tile rt: its rows of T are read once and serve
     // every key unit of W and every value slab of U

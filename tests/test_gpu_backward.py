@@ -74,3 +74,26 @@ def test_backward_beta_to_two_and_forgetting(orc, kda, qkv):
     x["g"][:, 10] = -float("inf")
     x["g"][:, 40, :, 5] = -float("inf")
     _check(orc, kda, x, qkv, 32)
+
+
+def test_backward_model_shaped_t8192(orc, kda):
+    """The headline shape (B1 T8192 H32 D128 C64, bf16 q/k/v, fp32 g/beta)
+    in one launch; the oracle's gradient on four sampled heads."""
+    c = ki.CONFIGS[1]
+    say("backward B1 T8192 H32 D128 (sampled heads)")
+    x = ki.config_prefill_inputs(1, device="cuda")
+    B, T, H, D = c["B"], c["T"], c["H"], c["Dk"]
+    gen = torch.Generator(device="cuda").manual_seed(99)
+    do = torch.randn((B, T, H, D), generator=gen, device="cuda").to(torch.bfloat16)
+    got = kda.kda_prefill_backward(x["q"], x["k"], x["v"], x["g"], x["beta"],
+                                   do, chunk=c["chunk"])
+    torch.cuda.synchronize()
+    heads = [0, 9, 22, 31]
+    sub = lambda t: t[:, :, heads].contiguous()
+    ref = orc.backward(sub(x["q"]), sub(x["k"]), sub(x["v"]), sub(x["g"]),
+                       sub(x["beta"]), None, 1.0, sub(do))
+    for n, a, r in zip(NAMES, got, ref):
+        a = a[:, :, heads] if n != "ds0" else a[:, heads]
+        e = rel_err(a, r)
+        say(f"  {n} err {e:.2e}")
+        assert e <= TOL["bf16"], (n, e)
