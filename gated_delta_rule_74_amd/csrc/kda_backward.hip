@@ -461,18 +461,20 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
 template <typename IO, int DK, int C> struct G2L {
   static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
   static constexpr size_t CC = (size_t)C * C * 4;
-  static constexpr size_t oM = 0, oT = CC, odP = 2 * CC, odM = 3 * CC,
-                          oX = 4 * CC;
-  static constexpr size_t oSm = 5 * CC;  // small arrays
+  static constexpr size_t oM = 0, oT = CC, odP = 2 * CC, odM = 3 * CC;
+  static constexpr size_t oSm = 4 * CC;  // small arrays
   static constexpr int RG = BWD_THREADS / DK;  // row groups of owner threads
   static constexpr size_t oBeta = oSm, odB = oBeta + C * 4,
                           odGl = odB + C * 4, oTail = odGl + DK * 4,
-                          odgh = oTail + (size_t)RG * DK * 4;
-  static constexpr size_t oR = al(odgh + C * 4);  // phase region
-  // largest phase: k, q (q/k/v dtype) and e (fp32), or two C x Dv arrays
-  static constexpr size_t RK = (size_t)C * DK * (2 * sizeof(IO) + 4);
+                          odgh = oTail + (size_t)RG * DK * 4,
+                          oVote = odgh + C * 4;
+  static constexpr size_t oR = al(oVote + 16);  // phase region
+  // largest phase: k, q, sigma (q/k/v dtype) and e / rho (fp32); two C x Dv
+  // arrays; or the C x C product of phase 5
+  static constexpr size_t RK = (size_t)C * DK * (3 * sizeof(IO) + 4);
   static constexpr size_t RV = 2 * (size_t)C * DVMAX_BWD * sizeof(IO);
-  static constexpr size_t total = oR + (RK > RV ? RK : RV);
+  static constexpr size_t RR = RK > RV ? (RK > CC ? RK : CC) : (RV > CC ? RV : CC);
+  static constexpr size_t total = oR + RR;
 };
 template <typename IO, int DK, int C> struct BwdFits {
   static constexpr bool value = G2L<IO, DK, C>::total <= 160 * 1024 &&
@@ -492,11 +494,12 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   __shared__ __attribute__((aligned(16))) char sm[L::total];
   float *Mm = (float *)(sm + L::oM), *Tm = (float *)(sm + L::oT);
   float *dPm = (float *)(sm + L::odP), *dMm = (float *)(sm + L::odM);
-  float *Xm = (float *)(sm + L::oX);
+  int *vote = (int *)(sm + L::oVote);
   float *bet = (float *)(sm + L::oBeta), *dB = (float *)(sm + L::odB);
   float *dGl = (float *)(sm + L::odGl), *tail = (float *)(sm + L::oTail);
   float *dgh = (float *)(sm + L::odgh);
   char *R = sm + L::oR;
+  float *Xm = (float *)R;  // phase 5 only
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -701,86 +704,19 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
     __syncthreads();
   }
 
-  // ---- phase 7: decayed products and elementwise terms, per owner ---------
-  // Each owner (channel i, rows R0 .. R0+RP-1) sweeps the chunk once per
-  // role with a register vector, so every step is C independent products:
-  //   row role, r upward:    Y[s] = k_s D_rs  (s <= r; D_rr = 1)
-  //   column role, s downward: V[r] = x_r D_rs (r >= s), x = k or q
-  // and D is only ever multiplied by one more e (no ratios).
+  // ---- phase 7: elementwise terms, then the decayed products -------------
   IO *qs = ks + C * DK;
-  es = (float *)(R + (size_t)2 * C * DK * sizeof(IO));
+  es = (float *)(R + (size_t)2 * C * DK * sizeof(IO));  // e, later rho
+  IO *sg = (IO *)(R + (size_t)2 * C * DK * sizeof(IO) + (size_t)C * DK * 4);
   load_ke(ks, qs, es);
-  float *dMT = Mm, *dPT = Tm;  // transposed copies (Mm, Tm are free now)
-  for (int x = tid; x < C * C; x += BWD_THREADS) {
-    const int r = x / C, c = x % C;
-    dMT[c * C + r] = dMm[x];
-    dPT[c * C + r] = dPm[x];
-  }
+  if (tid == 0) *vote = 0;
   __syncthreads();
   {
-    // owner (r, i)'s accumulators live in aDk / aDq / aDG (this workgroup's
-    // scratch), so the row loops need no register arrays
+    // owner (r, i): Kd = K*Gam, Qtil = scale Q*Gam, Ktil = K*gam/Gam terms
+    // (these start the accumulators aDk / aDq / aDG)
     const int i = oi, R0 = orh * RP, R1 = R0 + RP - 1;
-    const float *ec = es + i;           // e of this channel, row stride DK
+    const float *ec = es + i;
     const IO *kc = ks + i, *qc = qs + i;
-    // row role: Y[s] for the step before row R0
-    float Y[C];
-    {
-      float P = 1.f;
-#pragma unroll
-      for (int s2 = C - 1; s2 >= 0; --s2) {
-        const bool on = s2 < R0;
-        Y[s2] = on ? to_f32(kc[s2 * DK]) * P : 0.f;
-        if (on) P *= ec[s2 * DK];
-      }
-    }
-#pragma unroll 1
-    for (int j = 0; j < RP; ++j) {
-      const int r = R0 + j;
-      const float er = ec[r * DK], kr = to_f32(kc[r * DK]);
-      float aK = 0.f, aQ = 0.f;
-#pragma unroll
-      for (int s2 = 0; s2 < C; ++s2) {
-        Y[s2] = (s2 == r) ? kr : Y[s2] * er;
-        aK += dMm[r * C + s2] * Y[s2];
-        aQ += dPm[r * C + s2] * Y[s2];
-      }
-      const size_t o = (size_t)r * DK + i;
-      aDk[o] = aK;
-      aDq[o] = aQ;
-      aDG[o] = kr * aK + to_f32(qc[r * DK]) * aQ;
-    }
-    // column role, once for k (dM) and once for q (dPm)
-#pragma unroll 1
-    for (int pass = 0; pass < 2; ++pass) {
-      const IO *xc = pass == 0 ? kc : qc;
-      const float *cm = pass == 0 ? dMT : dPT;
-      float V[C];
-      {
-        float P = 1.f;
-#pragma unroll
-        for (int r = 0; r < C; ++r) {
-          if (r > R1) P *= ec[r * DK];
-          V[r] = r >= R1 ? to_f32(xc[r * DK]) * P : 0.f;
-        }
-      }
-#pragma unroll 1
-      for (int jj = RP - 1; jj >= 0; --jj) {
-        const int s2 = R0 + jj;
-        if (jj < RP - 1) {
-          const float en = ec[(s2 + 1) * DK], xv = to_f32(xc[s2 * DK]);
-#pragma unroll
-          for (int r = 0; r < C; ++r) V[r] = (r == s2) ? xv : V[r] * en;
-        }
-        float a = 0.f;
-#pragma unroll
-        for (int r = 0; r < C; ++r) a += cm[s2 * C + r] * V[r];
-        const size_t o = (size_t)s2 * DK + i;
-        aDk[o] += a;
-        aDG[o] -= to_f32(kc[s2 * DK]) * a;
-      }
-    }
-    // elementwise terms: Gam upward, gam / Gam downward
     float G = 1.f;
     for (int r = 0; r < R0; ++r) G *= ec[r * DK];
     for (int j = 0; j < RP; ++j) {
@@ -789,11 +725,11 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
       const float kr = to_f32(kc[r * DK]), qr = to_f32(qc[r * DK]);
       const size_t o = (size_t)r * DK + i;
       const float dkd = gdKd[o], dqd = gQ[o];
-      aDk[o] += dkd * G;
-      aDq[o] += scale * dqd * G;
+      aDk[o] = dkd * G;
+      aDq[o] = scale * dqd * G;
       float dg = dkd * kr * G + dqd * scale * qr * G;
       if (r == C - 1) dg += gG[i] * G;  // dgam * gam (G = gam here)
-      aDG[o] += dg;
+      aDG[o] = dg;
     }
     float Sf = 1.f, kil = 0.f;  // kil: this owner's part of sum dKtil*Ktil
     for (int r = C - 1; r > R1; --r) Sf *= ec[r * DK];
@@ -807,6 +743,168 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
       Sf *= ec[r * DK];
     }
     atomicAdd(&dGl[i], kil);
+  }
+  __syncthreads();
+  // per 16-token sub-chunk and channel: sigma (exclusive suffix product),
+  // rho (inclusive prefix, over e in place) and the sub-chunk product F;
+  // a vote records any rho below 2^-64 (diagonal ratios then unsafe)
+  float *Fs = Mm, *Mid = Tm;  // [NB][DK], [pairs a-b >= 2][DK]
+  for (int w = tid; w < NB * DK; w += BWD_THREADS) {
+    const int a = w / DK, i = w % DK;
+    float P = 1.f;
+    for (int j = 15; j >= 0; --j) {
+      const int r = 16 * a + j;
+      sg[r * DK + i] = (IO)P;
+      P *= es[r * DK + i];
+    }
+    P = 1.f;
+    int bad = 0;
+    for (int j = 0; j < 16; ++j) {
+      const int r = 16 * a + j;
+      P *= es[r * DK + i];
+      es[r * DK + i] = P;
+      if (!(P >= 5.42101086242752217e-20f)) bad = 1;
+    }
+    Fs[a * DK + i] = P;
+    if (bad) *vote = 1;
+  }
+  __syncthreads();
+  constexpr int NP2 = NB >= 3 ? (NB - 1) * (NB - 2) / 2 : 0;
+  for (int w = tid; w < NP2 * DK; w += BWD_THREADS) {
+    const int pi = w / DK, i = w % DK;
+    int aa = 2, bb = pi;
+    while (bb >= aa - 1) { bb -= aa - 1; ++aa; }
+    float mp = 1.f;
+    for (int d = bb + 1; d < aa; ++d) mp *= Fs[d * DK + i];
+    Mid[pi * DK + i] = mp;
+  }
+  __syncthreads();
+  {
+    // D_rs = rho_r Mid_ba sigma_s for s in sub-chunk b < a (r in a), and
+    // rho_r / rho_s inside one sub-chunk.  One wave per 16-channel tile;
+    // output tiles are 16 tokens x 16 channels in the accumulator layout.
+    using MM = Mma<IO>;
+    typedef typename MM::frag frag;
+    const bool dok = *vote == 0;
+    const float *rho = es;
+    auto mid = [&](int a, int b, int i) -> float {
+      return a - b >= 2 ? Mid[((a - 2) * (a - 1) / 2 + b) * DK + i] : 1.f;
+    };
+    // exact diagonal-block sums with running products (vote fallback)
+    auto diag_exact = [&](int r, int i, bool row, const IO *xv, const float *cm,
+                          bool strict) -> float {
+      const int lo = r & ~15, hi = lo + 15;
+      float acc = 0.f, D = 1.f;
+      if (row) {  // sum_{s<=r in the sub-chunk} c[r][s] x_s prod_{s<u<=r} e_u
+        for (int s2 = r; s2 >= lo; --s2) {
+          if (s2 < r) {
+            const int tu = t0 + s2 + 1;
+            D *= tu < T ? __expf(gate_at(tu, i)) : 1.f;
+          }
+          if (!(strict && s2 == r))
+            acc += cm[r * C + s2] * to_f32(xv[s2 * DK + i]) * D;
+        }
+      } else {    // sum_{r2>=r in the sub-chunk} c[r2][r] x_r2 prod_{r<u<=r2} e_u
+        for (int r2 = r; r2 <= hi; ++r2) {
+          if (r2 > r) D *= t0 + r2 < T ? __expf(gate_at(t0 + r2, i)) : 1.f;
+          if (!(strict && r2 == r))
+            acc += cm[r2 * C + r] * to_f32(xv[r2 * DK + i]) * D;
+        }
+      }
+      return acc;
+    };
+    for (int it = wave; it < NKT; it += 4) {
+      const int ib = 16 * it + m16;  // B-operand / output column (channel)
+      // ---- row role: rowK, rowQ of sub-chunk a
+      for (int a = 0; a < NB; ++a) {
+        f32x4 zk = zero, zq = zero;
+        for (int b = 0; b <= a; ++b) {
+          if (b == a && !dok) continue;
+          frag fk, fq, fb;
+#pragma unroll
+          for (int e = 0; e < MM::NE; ++e) {
+            const int k = MM::koff(g4, e);
+            float vk = 0.f, vq = 0.f, vb = 0.f;
+            if (k < 16) {
+              const int ra = 16 * a + m16, sb = 16 * b + k;
+              vk = dMm[ra * C + sb];
+              vq = dPm[ra * C + sb];
+              const float x = to_f32(ks[sb * DK + ib]);
+              vb = b < a ? x * to_f32(sg[sb * DK + ib]) * mid(a, b, ib)
+                         : x / rho[sb * DK + ib];
+            }
+            MM::set(fk, e, vk);
+            MM::set(fq, e, vq);
+            MM::set(fb, e, vb);
+          }
+          zk = MM::mma(fk, fb, zk);
+          zq = MM::mma(fq, fb, zq);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * a + 4 * g4 + e;
+          const float rr = rho[r * DK + ib];
+          float rK = rr * zk[e], rQ = rr * zq[e];
+          if (!dok) {
+            rK += diag_exact(r, ib, true, ks, dMm, true);
+            rQ += diag_exact(r, ib, true, ks, dPm, false);
+          }
+          const size_t o = (size_t)r * DK + ib;
+          aDk[o] += rK;
+          aDq[o] += rQ;
+          aDG[o] += to_f32(ks[r * DK + ib]) * rK + to_f32(qs[r * DK + ib]) * rQ;
+        }
+      }
+      // ---- column role: colK, colQ of sub-chunk b
+      for (int b = 0; b < NB; ++b) {
+        f32x4 ok_ = zero, oq = zero, dk2 = zero, dq2 = zero;
+        for (int a = b; a < NB; ++a) {
+          if (a == b && !dok) continue;
+          frag fk, fq, bk, bq;
+#pragma unroll
+          for (int e = 0; e < MM::NE; ++e) {
+            const int k = MM::koff(g4, e);
+            float vk = 0.f, vq = 0.f, xk = 0.f, xq = 0.f;
+            if (k < 16) {
+              const int sb = 16 * b + m16, ra = 16 * a + k;
+              vk = dMm[ra * C + sb];
+              vq = dPm[ra * C + sb];
+              const float f = rho[ra * DK + ib] * (a > b ? mid(a, b, ib) : 1.f);
+              xk = to_f32(ks[ra * DK + ib]) * f;
+              xq = to_f32(qs[ra * DK + ib]) * f;
+            }
+            MM::set(fk, e, vk);
+            MM::set(fq, e, vq);
+            MM::set(bk, e, xk);
+            MM::set(bq, e, xq);
+          }
+          if (a > b) {
+            ok_ = MM::mma(fk, bk, ok_);
+            oq = MM::mma(fq, bq, oq);
+          } else {
+            dk2 = MM::mma(fk, bk, dk2);
+            dq2 = MM::mma(fq, bq, dq2);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s2 = 16 * b + 4 * g4 + e;
+          const float sgv = to_f32(sg[s2 * DK + ib]);
+          float cK = sgv * ok_[e], cQ = sgv * oq[e];
+          if (dok) {
+            const float ir = 1.f / rho[s2 * DK + ib];
+            cK += dk2[e] * ir;
+            cQ += dq2[e] * ir;
+          } else {
+            cK += diag_exact(s2, ib, false, ks, dMm, true);
+            cQ += diag_exact(s2, ib, false, qs, dPm, false);
+          }
+          const size_t o = (size_t)s2 * DK + ib;
+          aDk[o] += cK + cQ;
+          aDG[o] -= to_f32(ks[s2 * DK + ib]) * (cK + cQ);
+        }
+      }
+    }
   }
   __syncthreads();
   // ---- phase 8: dg = reverse cumulative sum of dG, outputs ----------------
