@@ -53,6 +53,47 @@ __device__ __forceinline__ void units_to_lds_t(const char *sec, int nrt,
   }
 }
 
+// the same, split in two steps so the global loads of the next chunk can be
+// in flight while the current one is computed: each thread holds its NU
+// units' raw bytes (slots w = tid + 256 j) between fetch and store
+template <typename IO, int NU>
+struct UnitStage {
+  uint4 raw[NU];
+  __device__ __forceinline__ void fetch(const char *sec, int nrt, int nku,
+                                        bool lower, int tid) {
+    using M = Mma<IO>;
+#pragma unroll
+    for (int j = 0; j < NU; ++j) {
+      const int w = tid + BWD_THREADS * j;
+      const int unit = w >> 6, a = unit / nku, u = unit % nku;
+      if (w < nrt * nku * 64 && !(lower && u > a / M::TPU))
+        raw[j] = *(const uint4 *)(sec + (size_t)w * 16);
+      else
+        raw[j] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  __device__ __forceinline__ void store_t(int nrt, int nku, int kmax, IO *XT,
+                                          int ldt, int tid) const {
+    using M = Mma<IO>;
+    typedef typename M::frag frag;
+    constexpr int KU = 16 * M::TPU;
+#pragma unroll
+    for (int j = 0; j < NU; ++j) {
+      const int w = tid + BWD_THREADS * j;
+      if (w >= nrt * nku * 64) break;
+      const int lane = w & 63, unit = w >> 6;
+      const int a = unit / nku, u = unit % nku;
+      const int m = lane & 15, g = lane >> 4;
+      const frag f = __builtin_bit_cast(frag, raw[j]);
+#pragma unroll
+      for (int e = 0; e < M::NE; ++e) {
+        const int k = KU * u + M::koff(g, e);
+        if (k < kmax) XT[k * ldt + 16 * a + m] = (IO)M::elem(f, e);
+      }
+    }
+  }
+};
+
 // same, not transposed: X[16a + m][k]
 template <typename IO>
 __device__ __forceinline__ void units_to_lds(const char *sec, int nrt, int nku,
@@ -171,25 +212,50 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_state(BwdParams bp) {
   __syncthreads();
   publish_ds();
 
-  for (int n = NC - 1; n >= 0; --n) {
+  // the next chunk's factors, dO slab and gam wait in registers
+  constexpr int NUP = (NB * NTU * 64 + BWD_THREADS - 1) / BWD_THREADS;
+  constexpr int NUK = (NKT * NTU * 64 + BWD_THREADS - 1) / BWD_THREADS;
+  constexpr int NUQ = (NB * NKU * 64 + BWD_THREADS - 1) / BWD_THREADS;
+  constexpr int NOV = (16 * C + BWD_THREADS - 1) / BWD_THREADS;
+  UnitStage<IO, NUP> stP;
+  UnitStage<IO, NUK> stK;
+  UnitStage<IO, NUQ> stQ, stW;
+  IO ov[NOV];
+  float gv = 0.f;
+  auto fetch = [&](int n) {
     const char *blk = p.ws + ((size_t)bh * NC + n) * p.wsb;
+    stP.fetch(blk + W.off_p, NB, NTU, true, tid);
+    stK.fetch(blk + W.off_ktt, NKT, NTU, false, tid);
+    stQ.fetch(blk + W.off_qt, NB, NKU, false, tid);
+    stW.fetch(blk + W.off_negw, NB, NKU, false, tid);
+#pragma unroll
+    for (int j = 0; j < NOV; ++j) {
+      const int i = tid + BWD_THREADS * j;
+      const int r = i % C, t = n * C + r;
+      ov[j] = (i < 16 * C && t < T)
+                  ? ((const IO *)bp.dO)[((size_t)b * T + t) * orow +
+                                        (size_t)h * Dv + 16 * vt + i / C]
+                  : (IO)0.f;
+    }
+    if (tid < DK) gv = ((const float *)(blk + W.off_gam))[tid];
+  };
+  fetch(NC - 1);
+
+  for (int n = NC - 1; n >= 0; --n) {
     const int t0 = n * C;
     // ---- stage the chunk's factors, transposed where the products need it
-    units_to_lds_t<IO>(blk + W.off_p, NB, NTU, C, true, PT, LDC, tid);
-    units_to_lds_t<IO>(blk + W.off_ktt, NKT, NTU, C, false, KK, LDK, tid);
-    units_to_lds_t<IO>(blk + W.off_qt, NB, NKU, DK, false, QT, LDC, tid);
-    units_to_lds_t<IO>(blk + W.off_negw, NB, NKU, DK, false, WT, LDC, tid);
-    for (int i = tid; i < 16 * C; i += BWD_THREADS) {
-      const int r = i % C, j = i / C;
-      const int t = t0 + r;
-      OT[j * LDC + r] =
-          t < T ? ((const IO *)bp.dO)[((size_t)b * T + t) * orow + (size_t)h * Dv +
-                                      16 * vt + j]
-                : (IO)0.f;
+    stP.store_t(NB, NTU, C, PT, LDC, tid);
+    stK.store_t(NKT, NTU, C, KK, LDK, tid);
+    stQ.store_t(NB, NKU, DK, QT, LDC, tid);
+    stW.store_t(NB, NKU, DK, WT, LDC, tid);
+#pragma unroll
+    for (int j = 0; j < NOV; ++j) {
+      const int i = tid + BWD_THREADS * j;
+      if (i < 16 * C) OT[(i / C) * LDC + i % C] = ov[j];
     }
-    for (int i = tid; i < DK; i += BWD_THREADS)
-      Gm[i] = ((const float *)(blk + W.off_gam))[i];
+    if (tid < DK) Gm[tid] = gv;
     __syncthreads();
+    if (n > 0) fetch(n - 1);
 
     // ---- the gradient at this chunk's end, for the per-chunk kernels
 #pragma unroll
