@@ -258,6 +258,8 @@ kda_status kda_prefill_backward(
     for (int j = i + 1; j < 6; ++j)
       if (all_out[j] == all_out[i]) return KDA_EINVAL;
   }
+  if (!kda::backward_fits(qkv_dtype == KDA_BF16, Dk, chunk))
+    return KDA_EUNSUPPORTED;
   const BwdWs L = bwd_ws(B, T, H, Dk, Dv, chunk, qkv_dtype);
   if (workspace_bytes < L.total) return KDA_EINVAL;
   char *wsb = (char *)workspace;

@@ -370,10 +370,10 @@ __device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const TA *A, int lda,
 
 // per-chunk intermediates: the second kernel writes
 // [Delta C x Dv | dQtil C x Dk | dKtil C x Dk | dW C x Dk | dgam Dk], the
-// third adds [Kd = K*Gam | dKd | dk, dq, dG accumulators] (C x Dk each)
-// for its own later phases; fp32
+// third adds [Kd = K*Gam | dKd] (C x Dk each) for its own later phases;
+// fp32
 __host__ __device__ inline size_t bwd_gs_floats(int C, int Dk, int Dv) {
-  return (size_t)C * (Dv + 8 * Dk) + Dk;
+  return (size_t)C * (Dv + 5 * Dk) + Dk;
 }
 
 // ---------------------------------------------------------------------------
@@ -432,13 +432,19 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
 
   for (int c0 = 0; c0 < Dv; c0 += SV) {
     const int sv = min(SV, Dv - c0);
-    for (int i = tid; i < DK * SV; i += BWD_THREADS) {
+    #pragma unroll
+    for (int i_ = 0; i_ < (DK * SV + BWD_THREADS - 1) / BWD_THREADS; ++i_) {
+      const int i = tid + BWD_THREADS * i_;
+      if (i >= DK * SV) break;
       const int r = i / SV, c = i % SV;
       const bool ok = c < sv;
       Ss[i] = ok ? S[(size_t)r * Dv + c0 + c] : 0.f;
       dSs[i] = ok ? dS[(size_t)r * Dv + c0 + c] : 0.f;
     }
-    for (int i = tid; i < C * SV; i += BWD_THREADS) {
+    #pragma unroll
+    for (int i_ = 0; i_ < (C * SV + BWD_THREADS - 1) / BWD_THREADS; ++i_) {
+      const int i = tid + BWD_THREADS * i_;
+      if (i >= C * SV) break;
       const int r = i / SV, c = i % SV, t = t0 + r;
       const bool ok = c < sv && t < T;
       const size_t gi = ((size_t)b * T + t) * orow + (size_t)h * Dv + c0 + c;
@@ -578,8 +584,6 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   float *gD = gs, *gQ = gs + (size_t)C * Dv, *gK = gQ + (size_t)C * DK;
   float *gW = gK + (size_t)C * DK, *gG = gW + (size_t)C * DK;
   float *gKd = gG + DK, *gdKd = gKd + (size_t)C * DK;
-  float *aDk = gdKd + (size_t)C * DK, *aDq = aDk + (size_t)C * DK;
-  float *aDG = aDq + (size_t)C * DK;
   const size_t krow = (size_t)H * DK, vrow = (size_t)H * Dv;
   const size_t kb = ((size_t)b * T * H + h) * DK;  // token 0 of (b, h), q/k/g
   const size_t vb = ((size_t)b * T * H + h) * Dv;  // token 0, v / dO / dv
@@ -594,7 +598,10 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   };
   // e for rows beyond the sequence is 1 (as in the forward)
   auto load_ke = [&](IO *ks, IO *qs, float *es) {
-    for (int x = tid; x < C * DK; x += BWD_THREADS) {
+    #pragma unroll
+    for (int x_ = 0; x_ < (C * DK + BWD_THREADS - 1) / BWD_THREADS; ++x_) {
+      const int x = tid + BWD_THREADS * x_;
+      if (x >= C * DK) break;
       const int r = x / DK, i = x % DK, t = t0 + r;
       const bool ok = t < T;
       ks[x] = ok ? ((const IO *)p.k)[kb + (size_t)t * krow + i] : (IO)0.f;
@@ -621,7 +628,10 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
     // A = diag(beta) M and T^T as the forward's chunk prep left them (only
     // the lower triangles are meaningful)
     const float *at = p.train_at + ((size_t)bh * NC + n) * 2 * C * C;
-    for (int x = tid; x < C * C; x += BWD_THREADS) {
+    #pragma unroll
+    for (int x_ = 0; x_ < (C * C + BWD_THREADS - 1) / BWD_THREADS; ++x_) {
+      const int x = tid + BWD_THREADS * x_;
+      if (x >= C * C) break;
       const int r = x / C, c = x % C;
       const float br = bet[r];
       Mm[x] = (c < r && br != 0.f) ? at[x] / br : 0.f;
@@ -654,22 +664,26 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
 
   // ---- phase 3: value side: dT = dDelta (beta V)^T, dv = beta T^T dDelta --
   {
-    IO *dDs = (IO *)R, *bVs = dDs + C * Dv;
-    for (int x = tid; x < C * Dv; x += BWD_THREADS) {
+    IO *dDs = (IO *)R, *vS = dDs + C * Dv;
+    #pragma unroll
+    for (int x_ = 0; x_ < (C * DVMAX_BWD + BWD_THREADS - 1) / BWD_THREADS; ++x_) {
+      const int x = tid + BWD_THREADS * x_;
+      if (x >= C * Dv) break;
       const int r = x / Dv, j = x % Dv, t = t0 + r;
       const bool ok = t < T;
       const float vv = ok ? to_f32(((const IO *)p.v)[vb + (size_t)t * vrow + j]) : 0.f;
       dDs[x] = (IO)(ok ? bp.dD[vb + (size_t)t * vrow + j] : 0.f);
-      bVs[x] = (IO)(bet[r] * vv);
+      vS[x] = (IO)vv;
     }
     __syncthreads();
     for (int tl = wave; tl < NB * NB; tl += 4) {
       const int rt = tl % NB, st = tl / NB;
-      f32x4 acc = tile_mma<IO, false, true>(zero, dDs, Dv, bVs, Dv, 16 * rt,
+      f32x4 acc = tile_mma<IO, false, true>(zero, dDs, Dv, vS, Dv, 16 * rt,
                                             16 * st, Dv, lane);
+      const float bs = bet[16 * st + m16];  // (beta V)^T: beta of column s
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        dMm[(16 * rt + 4 * g4 + e) * C + 16 * st + m16] = acc[e];  // dT
+        dMm[(16 * rt + 4 * g4 + e) * C + 16 * st + m16] = bs * acc[e];  // dT
     }
     for (int tl = wave; tl < NB * nvt; tl += 4) {
       const int rt = tl % NB, ct = tl / NB;
@@ -678,11 +692,9 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rt + 4 * g4 + e, j = 16 * ct + m16, t = t0 + r;
-        if (t < T) {
+        if (t < T)
           ((IO *)bp.dv)[vb + (size_t)t * vrow + j] = from_f32<IO>(bet[r] * acc[e]);
-          atomicAdd(&dB[r],
-                    to_f32(((const IO *)p.v)[vb + (size_t)t * vrow + j]) * acc[e]);
-        }
+        atomicAdd(&dB[r], to_f32(vS[r * Dv + j]) * acc[e]);
       }
     }
     __syncthreads();
@@ -690,24 +702,23 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
 
   // ---- phase 4: key side: dT += dW (beta Kd)^T, dKd = beta T^T dW ---------
   {
-    IO *dWs = (IO *)R, *bKs = dWs + C * DK;
-    for (int x = tid; x < C * DK; x += BWD_THREADS) {
-      const int r = x / DK;
+    IO *dWs = (IO *)R, *KdS = dWs + C * DK;
+    #pragma unroll
+    for (int x_ = 0; x_ < (C * DK + BWD_THREADS - 1) / BWD_THREADS; ++x_) {
+      const int x = tid + BWD_THREADS * x_;
+      if (x >= C * DK) break;
       dWs[x] = (IO)gW[x];
-      bKs[x] = (IO)(bet[r] * gKd[x]);
+      KdS[x] = (IO)gKd[x];
     }
     __syncthreads();
     for (int tl = wave; tl < NB * NB; tl += 4) {
       const int rt = tl % NB, st = tl / NB;
-      f32x4 acc;
+      f32x4 acc = tile_mma<IO, false, true>(zero, dWs, DK, KdS, DK, 16 * rt,
+                                            16 * st, DK, lane);
+      const float bs = bet[16 * st + m16];  // (beta Kd)^T: beta of column s
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        acc[e] = dMm[(16 * rt + 4 * g4 + e) * C + 16 * st + m16];
-      acc = tile_mma<IO, false, true>(acc, dWs, DK, bKs, DK, 16 * rt, 16 * st,
-                                      DK, lane);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        dMm[(16 * rt + 4 * g4 + e) * C + 16 * st + m16] = acc[e];
+        dMm[(16 * rt + 4 * g4 + e) * C + 16 * st + m16] += bs * acc[e];
     }
     for (int tl = wave; tl < NB * NKT; tl += 4) {
       const int rt = tl % NB, it = tl / NB;
@@ -717,7 +728,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rt + 4 * g4 + e, i = 16 * it + m16;
         gdKd[(size_t)r * DK + i] = bet[r] * acc[e];
-        atomicAdd(&dB[r], gKd[(size_t)r * DK + i] * acc[e]);
+        atomicAdd(&dB[r], to_f32(KdS[r * DK + i]) * acc[e]);
       }
     }
     __syncthreads();
@@ -750,7 +761,10 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   // ---- phase 6: dPm = scale tril(dO Delta^T) --------------------------------
   {
     IO *Os = (IO *)R, *Ds = Os + C * Dv;
-    for (int x = tid; x < C * Dv; x += BWD_THREADS) {
+    #pragma unroll
+    for (int x_ = 0; x_ < (C * DVMAX_BWD + BWD_THREADS - 1) / BWD_THREADS; ++x_) {
+      const int x = tid + BWD_THREADS * x_;
+      if (x >= C * Dv) break;
       const int r = x / Dv, j = x % Dv, t = t0 + r;
       const bool ok = t < T;
       Os[x] = ok ? ((const IO *)bp.dO)[vb + (size_t)t * vrow + j] : (IO)0.f;
@@ -776,40 +790,6 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   IO *sg = (IO *)(R + (size_t)2 * C * DK * sizeof(IO) + (size_t)C * DK * 4);
   load_ke(ks, qs, es);
   if (tid == 0) *vote = 0;
-  __syncthreads();
-  {
-    // owner (r, i): Kd = K*Gam, Qtil = scale Q*Gam, Ktil = K*gam/Gam terms
-    // (these start the accumulators aDk / aDq / aDG)
-    const int i = oi, R0 = orh * RP, R1 = R0 + RP - 1;
-    const float *ec = es + i;
-    const IO *kc = ks + i, *qc = qs + i;
-    float G = 1.f;
-    for (int r = 0; r < R0; ++r) G *= ec[r * DK];
-    for (int j = 0; j < RP; ++j) {
-      const int r = R0 + j;
-      G *= ec[r * DK];
-      const float kr = to_f32(kc[r * DK]), qr = to_f32(qc[r * DK]);
-      const size_t o = (size_t)r * DK + i;
-      const float dkd = gdKd[o], dqd = gQ[o];
-      aDk[o] = dkd * G;
-      aDq[o] = scale * dqd * G;
-      float dg = dkd * kr * G + dqd * scale * qr * G;
-      if (r == C - 1) dg += gG[i] * G;  // dgam * gam (G = gam here)
-      aDG[o] = dg;
-    }
-    float Sf = 1.f, kil = 0.f;  // kil: this owner's part of sum dKtil*Ktil
-    for (int r = C - 1; r > R1; --r) Sf *= ec[r * DK];
-    for (int j = RP - 1; j >= 0; --j) {
-      const int r = R0 + j;
-      const size_t o = (size_t)r * DK + i;
-      const float dki = gK[o], ki = to_f32(kc[r * DK]) * Sf;
-      aDk[o] += dki * Sf;
-      aDG[o] -= dki * ki;
-      kil += dki * ki;
-      Sf *= ec[r * DK];
-    }
-    atomicAdd(&dGl[i], kil);
-  }
   __syncthreads();
   // per 16-token sub-chunk and channel: sigma (exclusive suffix product),
   // rho (inclusive prefix, over e in place) and the sub-chunk product F;
@@ -845,10 +825,13 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
     Mid[pi * DK + i] = mp;
   }
   __syncthreads();
+  // One wave per 16-channel tile; each lane owns, in the accumulator
+  // layout, rows 16a + 4g + e of every sub-chunk a for channel 16 it + m16
+  // and keeps dk, dq, dG of those (r, i) in registers.  D_rs = rho_r Mid_ba
+  // sigma_s for s in sub-chunk b < a (r in a), rho_r / rho_s inside one.
+  constexpr int JT = (NKT + 3) / 4;
+  f32x4 aK_[JT][NB], aQ_[JT][NB], aG_[JT][NB];
   {
-    // D_rs = rho_r Mid_ba sigma_s for s in sub-chunk b < a (r in a), and
-    // rho_r / rho_s inside one sub-chunk.  One wave per 16-channel tile;
-    // output tiles are 16 tokens x 16 channels in the accumulator layout.
     using MM = Mma<IO>;
     typedef typename MM::frag frag;
     const bool dok = *vote == 0;
@@ -879,9 +862,43 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
       }
       return acc;
     };
-    for (int it = wave; it < NKT; it += 4) {
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) {
+      const int it = wave + 4 * jt;
+      if (it >= NKT) continue;
       const int ib = 16 * it + m16;  // B-operand / output column (channel)
+      // ---- elementwise terms of Kd = K*Gam, Qtil, Ktil = K*gam/Gam, gam
+      float Fb[NB];
+#pragma unroll
+      for (int a = 0; a < NB; ++a) Fb[a] = Fs[a * DK + ib];
+      float kil = 0.f;
+#pragma unroll
+      for (int a = 0; a < NB; ++a) {
+        float pre = 1.f, post = 1.f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          if (b < a) pre *= Fb[b];
+          if (b > a) post *= Fb[b];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * a + 4 * g4 + e;
+          const size_t o = (size_t)r * DK + ib;
+          const float G = rho[r * DK + ib] * pre;              // Gam_r
+          const float sf = to_f32(sg[r * DK + ib]) * post;      // gam / Gam_r
+          const float kr = to_f32(ks[r * DK + ib]), qr = to_f32(qs[r * DK + ib]);
+          const float dkd = gdKd[o], dqd = gQ[o], dki = gK[o];
+          aK_[jt][a][e] = dkd * G + dki * sf;
+          aQ_[jt][a][e] = scale * dqd * G;
+          float dg = dkd * kr * G + dqd * scale * qr * G - dki * kr * sf;
+          if (r == C - 1) dg += gG[ib] * G;  // dgam * gam (G = gam here)
+          aG_[jt][a][e] = dg;
+          kil += dki * kr * sf;
+        }
+      }
+      atomicAdd(&dGl[ib], kil);
       // ---- row role: rowK, rowQ of sub-chunk a
+#pragma unroll
       for (int a = 0; a < NB; ++a) {
         f32x4 zk = zero, zq = zero;
         for (int b = 0; b <= a; ++b) {
@@ -915,13 +932,14 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
             rK += diag_exact(r, ib, true, ks, dMm, true);
             rQ += diag_exact(r, ib, true, ks, dPm, false);
           }
-          const size_t o = (size_t)r * DK + ib;
-          aDk[o] += rK;
-          aDq[o] += rQ;
-          aDG[o] += to_f32(ks[r * DK + ib]) * rK + to_f32(qs[r * DK + ib]) * rQ;
+          aK_[jt][a][e] += rK;
+          aQ_[jt][a][e] += rQ;
+          aG_[jt][a][e] += to_f32(ks[r * DK + ib]) * rK +
+                           to_f32(qs[r * DK + ib]) * rQ;
         }
       }
       // ---- column role: colK, colQ of sub-chunk b
+#pragma unroll
       for (int b = 0; b < NB; ++b) {
         f32x4 ok_ = zero, oq = zero, dk2 = zero, dq2 = zero;
         for (int a = b; a < NB; ++a) {
@@ -965,36 +983,52 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
             cK += diag_exact(s2, ib, false, ks, dMm, true);
             cQ += diag_exact(s2, ib, false, qs, dPm, false);
           }
-          const size_t o = (size_t)s2 * DK + ib;
-          aDk[o] += cK + cQ;
-          aDG[o] -= to_f32(ks[s2 * DK + ib]) * (cK + cQ);
+          aK_[jt][b][e] += cK + cQ;
+          aG_[jt][b][e] -= to_f32(ks[s2 * DK + ib]) * (cK + cQ);
         }
       }
     }
   }
+  __syncthreads();  // dGl complete; rho no longer read
+  // ---- phase 8: dk, dq out; dg = reverse cumulative sum of dG ------------
+  float *dGs = es;  // [C][DK] fp32, in place of rho
+#pragma unroll
+  for (int jt = 0; jt < JT; ++jt) {
+    const int it = wave + 4 * jt;
+    if (it >= NKT) continue;
+    const int ib = 16 * it + m16;
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * a + 4 * g4 + e, t = t0 + r;
+        float dgv = aG_[jt][a][e];
+        if (r == C - 1) dgv += dGl[ib];  // sum_r dKtil*Ktil (d log gam)
+        dGs[r * DK + ib] = dgv;
+        if (t < T) {
+          const size_t o = kb + (size_t)t * krow + ib;
+          ((IO *)bp.dq)[o] = from_f32<IO>(aQ_[jt][a][e]);
+          ((IO *)bp.dk)[o] = from_f32<IO>(aK_[jt][a][e]);
+        }
+      }
+  }
   __syncthreads();
-  // ---- phase 8: dg = reverse cumulative sum of dG, outputs ----------------
   {
     const int i = oi, R0 = orh * RP;
-    if (R0 + RP - 1 == C - 1) aDG[(size_t)(C - 1) * DK + i] += dGl[i];
     float own = 0.f;
-    for (int j = 0; j < RP; ++j) own += aDG[(size_t)(R0 + j) * DK + i];
+    for (int j = 0; j < RP; ++j) own += dGs[(R0 + j) * DK + i];
     tail[orh * DK + i] = own;
     __syncthreads();
     float acc = 0.f;
     for (int rr = orh + 1; rr < RG; ++rr) acc += tail[rr * DK + i];
     for (int j = RP - 1; j >= 0; --j) {
       const int r = R0 + j, t = t0 + r;
-      const size_t oa = (size_t)r * DK + i;
-      acc += aDG[oa];
+      acc += dGs[r * DK + i];
       if (t < T) {
-        const size_t o = kb + (size_t)t * krow + i;
-        ((IO *)bp.dq)[o] = from_f32<IO>(aDq[oa]);
-        ((IO *)bp.dk)[o] = from_f32<IO>(aDk[oa]);
         if (p.gate_head)
           atomicAdd(&dgh[r], acc);
         else
-          ((GT *)bp.dg)[o] = (GT)acc;
+          ((GT *)bp.dg)[kb + (size_t)t * krow + i] = (GT)acc;
       }
     }
     __syncthreads();
@@ -1054,6 +1088,24 @@ static hipError_t bwd_dk(const BwdParams &bp, hipStream_t s) {
 hipError_t launch_backward(const BwdParams &bp, int io_bf16, hipStream_t s) {
   if (!io_bf16) return bwd_dk<float, float>(bp, s);
   return bp.f.gate_bf16 ? bwd_dk<bf16, bf16>(bp, s) : bwd_dk<bf16, float>(bp, s);
+}
+
+template <typename IO>
+static bool fits_io(int Dk, int C) {
+  switch (Dk * 1000 + C) {
+#define KDA_FIT(D, CC) \
+  case D * 1000 + CC: return BwdFits<IO, D, CC>::value;
+    KDA_FIT(16, 16) KDA_FIT(16, 32) KDA_FIT(16, 64)
+    KDA_FIT(32, 16) KDA_FIT(32, 32) KDA_FIT(32, 64)
+    KDA_FIT(64, 16) KDA_FIT(64, 32) KDA_FIT(64, 64)
+    KDA_FIT(128, 16) KDA_FIT(128, 32) KDA_FIT(128, 64)
+#undef KDA_FIT
+  }
+  return false;
+}
+
+bool backward_fits(int io_bf16, int Dk, int C) {
+  return io_bf16 ? fits_io<bf16>(Dk, C) : fits_io<float>(Dk, C);
 }
 
 size_t backward_chunk_floats(int C, int Dk, int Dv) {

@@ -85,6 +85,8 @@ hipError_t launch_decode(const DecodeParams &p, int io_bf16, hipStream_t s);
 // the three backward kernels (the forward's prep and state pass, with state
 // checkpoints, must have filled bp.f.ws and bp.Sc first)
 hipError_t launch_backward(const BwdParams &bp, int io_bf16, hipStream_t s);
+// whether the backward kernels' LDS fits for these sizes
+bool backward_fits(int io_bf16, int Dk, int C);
 // floats of per-chunk backward intermediates
 size_t backward_chunk_floats(int C, int Dk, int Dv);
 hipError_t launch_conv(const ConvParams &p, hipStream_t s);
