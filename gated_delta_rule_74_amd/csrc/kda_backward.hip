@@ -432,24 +432,36 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
 
   for (int c0 = 0; c0 < Dv; c0 += SV) {
     const int sv = min(SV, Dv - c0);
-    #pragma unroll
-    for (int i_ = 0; i_ < (DK * SV + BWD_THREADS - 1) / BWD_THREADS; ++i_) {
-      const int i = tid + BWD_THREADS * i_;
-      if (i >= DK * SV) break;
-      const int r = i / SV, c = i % SV;
-      const bool ok = c < sv;
-      Ss[i] = ok ? S[(size_t)r * Dv + c0 + c] : 0.f;
-      dSs[i] = ok ? dS[(size_t)r * Dv + c0 + c] : 0.f;
+    // all loads first (clamped addresses, branch-free), then the LDS stores
+    constexpr int NA = DK * SV / BWD_THREADS, NO = C * SV / BWD_THREADS;
+    float la[NA], lb[NA], lo[NO], ld[NO];
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const int i = tid + BWD_THREADS * j, r = i / SV, c = min(i % SV, sv - 1);
+      la[j] = S[(size_t)r * Dv + c0 + c];
+      lb[j] = dS[(size_t)r * Dv + c0 + c];
     }
-    #pragma unroll
-    for (int i_ = 0; i_ < (C * SV + BWD_THREADS - 1) / BWD_THREADS; ++i_) {
-      const int i = tid + BWD_THREADS * i_;
-      if (i >= C * SV) break;
-      const int r = i / SV, c = i % SV, t = t0 + r;
-      const bool ok = c < sv && t < T;
+#pragma unroll
+    for (int j = 0; j < NO; ++j) {
+      const int i = tid + BWD_THREADS * j, r = i / SV, c = min(i % SV, sv - 1);
+      const int t = min(t0 + r, T - 1);
       const size_t gi = ((size_t)b * T + t) * orow + (size_t)h * Dv + c0 + c;
-      Os[i] = ok ? to_f32(((const IO *)bp.dO)[gi]) : 0.f;
-      dDs[i] = ok ? bp.dD[gi] : 0.f;
+      lo[j] = to_f32(((const IO *)bp.dO)[gi]);
+      ld[j] = bp.dD[gi];
+    }
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const int i = tid + BWD_THREADS * j;
+      const bool ok = i % SV < sv;
+      Ss[i] = ok ? la[j] : 0.f;
+      dSs[i] = ok ? lb[j] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < NO; ++j) {
+      const int i = tid + BWD_THREADS * j;
+      const bool ok = i % SV < sv && t0 + i / SV < T;
+      Os[i] = ok ? lo[j] : 0.f;
+      dDs[i] = ok ? ld[j] : 0.f;
     }
     __syncthreads();
     // Delta = U - W S on this slab (U in accumulator tiles [vt][rt])
@@ -598,15 +610,24 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   };
   // e for rows beyond the sequence is 1 (as in the forward)
   auto load_ke = [&](IO *ks, IO *qs, float *es) {
-    #pragma unroll
-    for (int x_ = 0; x_ < (C * DK + BWD_THREADS - 1) / BWD_THREADS; ++x_) {
-      const int x = tid + BWD_THREADS * x_;
-      if (x >= C * DK) break;
-      const int r = x / DK, i = x % DK, t = t0 + r;
-      const bool ok = t < T;
-      ks[x] = ok ? ((const IO *)p.k)[kb + (size_t)t * krow + i] : (IO)0.f;
-      if (qs) qs[x] = ok ? ((const IO *)p.q)[kb + (size_t)t * krow + i] : (IO)0.f;
-      es[x] = ok ? __expf(gate_at(t, i)) : 1.f;
+    constexpr int NL = C * DK / BWD_THREADS;
+    IO lk[NL], lq[NL];
+    float lg[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int x = tid + BWD_THREADS * j, r = x / DK, i = x % DK;
+      const int t = min(t0 + r, T - 1);
+      lk[j] = ((const IO *)p.k)[kb + (size_t)t * krow + i];
+      lq[j] = qs ? ((const IO *)p.q)[kb + (size_t)t * krow + i] : (IO)0.f;
+      lg[j] = gate_at(t, i);
+    }
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int x = tid + BWD_THREADS * j;
+      const bool ok = t0 + x / DK < T;
+      ks[x] = ok ? lk[j] : (IO)0.f;
+      if (qs) qs[x] = ok ? lq[j] : (IO)0.f;
+      es[x] = ok ? __expf(lg[j]) : 1.f;
     }
   };
 
@@ -628,14 +649,20 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
     // A = diag(beta) M and T^T as the forward's chunk prep left them (only
     // the lower triangles are meaningful)
     const float *at = p.train_at + ((size_t)bh * NC + n) * 2 * C * C;
-    #pragma unroll
-    for (int x_ = 0; x_ < (C * C + BWD_THREADS - 1) / BWD_THREADS; ++x_) {
-      const int x = tid + BWD_THREADS * x_;
-      if (x >= C * C) break;
-      const int r = x / C, c = x % C;
+    constexpr int NC2 = C * C / BWD_THREADS;
+    float la[NC2], lt[NC2];
+#pragma unroll
+    for (int j = 0; j < NC2; ++j) {
+      const int x = tid + BWD_THREADS * j, r = x / C, c = x % C;
+      la[j] = at[x];
+      lt[j] = at[C * C + c * C + r];
+    }
+#pragma unroll
+    for (int j = 0; j < NC2; ++j) {
+      const int x = tid + BWD_THREADS * j, r = x / C, c = x % C;
       const float br = bet[r];
-      Mm[x] = (c < r && br != 0.f) ? at[x] / br : 0.f;
-      Tm[x] = c <= r ? at[C * C + c * C + r] : 0.f;
+      Mm[x] = (c < r && br != 0.f) ? la[j] / br : 0.f;
+      Tm[x] = c <= r ? lt[j] : 0.f;
     }
     // rows with beta = 0 (A carries no M there): M directly, with running
     // products of e over (s, r] -- exact, and rare
@@ -665,15 +692,23 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   // ---- phase 3: value side: dT = dDelta (beta V)^T, dv = beta T^T dDelta --
   {
     IO *dDs = (IO *)R, *vS = dDs + C * Dv;
-    #pragma unroll
-    for (int x_ = 0; x_ < (C * DVMAX_BWD + BWD_THREADS - 1) / BWD_THREADS; ++x_) {
-      const int x = tid + BWD_THREADS * x_;
-      if (x >= C * Dv) break;
-      const int r = x / Dv, j = x % Dv, t = t0 + r;
-      const bool ok = t < T;
-      const float vv = ok ? to_f32(((const IO *)p.v)[vb + (size_t)t * vrow + j]) : 0.f;
-      dDs[x] = (IO)(ok ? bp.dD[vb + (size_t)t * vrow + j] : 0.f);
-      vS[x] = (IO)vv;
+    constexpr int NV = (C * DVMAX_BWD + BWD_THREADS - 1) / BWD_THREADS;
+    float lv[NV], ld[NV];
+#pragma unroll
+    for (int jj = 0; jj < NV; ++jj) {
+      const int x = min(tid + BWD_THREADS * jj, C * Dv - 1);
+      const int r = x / Dv, j = x % Dv, t = min(t0 + r, T - 1);
+      lv[jj] = to_f32(((const IO *)p.v)[vb + (size_t)t * vrow + j]);
+      ld[jj] = bp.dD[vb + (size_t)t * vrow + j];
+    }
+#pragma unroll
+    for (int jj = 0; jj < NV; ++jj) {
+      const int x = tid + BWD_THREADS * jj;
+      if (x < C * Dv) {
+        const bool ok = t0 + x / Dv < T;
+        dDs[x] = (IO)(ok ? ld[jj] : 0.f);
+        vS[x] = (IO)(ok ? lv[jj] : 0.f);
+      }
     }
     __syncthreads();
     for (int tl = wave; tl < NB * NB; tl += 4) {
@@ -703,12 +738,19 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   // ---- phase 4: key side: dT += dW (beta Kd)^T, dKd = beta T^T dW ---------
   {
     IO *dWs = (IO *)R, *KdS = dWs + C * DK;
-    #pragma unroll
-    for (int x_ = 0; x_ < (C * DK + BWD_THREADS - 1) / BWD_THREADS; ++x_) {
-      const int x = tid + BWD_THREADS * x_;
-      if (x >= C * DK) break;
-      dWs[x] = (IO)gW[x];
-      KdS[x] = (IO)gKd[x];
+    constexpr int NK = C * DK / BWD_THREADS;
+    float lw[NK], lk[NK];
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+      const int x = tid + BWD_THREADS * j;
+      lw[j] = gW[x];
+      lk[j] = gKd[x];
+    }
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+      const int x = tid + BWD_THREADS * j;
+      dWs[x] = (IO)lw[j];
+      KdS[x] = (IO)lk[j];
     }
     __syncthreads();
     for (int tl = wave; tl < NB * NB; tl += 4) {
@@ -761,14 +803,23 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   // ---- phase 6: dPm = scale tril(dO Delta^T) --------------------------------
   {
     IO *Os = (IO *)R, *Ds = Os + C * Dv;
-    #pragma unroll
-    for (int x_ = 0; x_ < (C * DVMAX_BWD + BWD_THREADS - 1) / BWD_THREADS; ++x_) {
-      const int x = tid + BWD_THREADS * x_;
-      if (x >= C * Dv) break;
-      const int r = x / Dv, j = x % Dv, t = t0 + r;
-      const bool ok = t < T;
-      Os[x] = ok ? ((const IO *)bp.dO)[vb + (size_t)t * vrow + j] : (IO)0.f;
-      Ds[x] = (IO)gD[x];
+    constexpr int NV = (C * DVMAX_BWD + BWD_THREADS - 1) / BWD_THREADS;
+    IO lo[NV];
+    float ld[NV];
+#pragma unroll
+    for (int jj = 0; jj < NV; ++jj) {
+      const int x = min(tid + BWD_THREADS * jj, C * Dv - 1);
+      const int r = x / Dv, j = x % Dv, t = min(t0 + r, T - 1);
+      lo[jj] = ((const IO *)bp.dO)[vb + (size_t)t * vrow + j];
+      ld[jj] = gD[x];
+    }
+#pragma unroll
+    for (int jj = 0; jj < NV; ++jj) {
+      const int x = tid + BWD_THREADS * jj;
+      if (x < C * Dv) {
+        Os[x] = t0 + x / Dv < T ? lo[jj] : (IO)0.f;
+        Ds[x] = (IO)ld[jj];
+      }
     }
     __syncthreads();
     for (int tl = wave; tl < NB * NB; tl += 4) {
