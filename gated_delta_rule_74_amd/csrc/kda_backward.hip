@@ -368,6 +368,23 @@ __device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const TA *A, int lda,
   return acc;
 }
 
+// the same for A and B both given as k-contiguous rows of the q/k/v dtype
+// (op(A) = A, op(B) = B^T): whole fragment units per load, no gathers
+template <typename IO>
+__device__ __forceinline__ f32x4 tile_mma_rows(f32x4 acc, const IO *A, int lda,
+                                               const IO *B, int ldb, int m0,
+                                               int n0, int K, int lane) {
+  using M = Mma<IO>;
+  constexpr int KU = 16 * M::TPU;
+  const int m = lane & 15, g = lane >> 4;
+  for (int u = 0; u * KU < K; ++u) {
+    const bool full = KU * u + 16 < K || M::TPU == 1;
+    acc = M::mma(M::load_k(A + (m0 + m) * lda + KU * u, g, full),
+                 M::load_k(B + (n0 + m) * ldb + KU * u, g, full), acc);
+  }
+  return acc;
+}
+
 // per-chunk intermediates: the second kernel writes
 // [Delta C x Dv | dQtil C x Dk | dKtil C x Dk | dW C x Dk | dgam Dk], the
 // third adds [Kd = K*Gam | dKd] (C x Dk each) for its own later phases;
@@ -384,30 +401,36 @@ __host__ __device__ inline size_t bwd_gs_floats(int C, int Dk, int Dv) {
 // ---------------------------------------------------------------------------
 template <typename IO, int DK, int C> struct G1L {
   static constexpr int SV = 32;  // value columns per slab
+  static constexpr int PE = 16 / (int)sizeof(IO);  // row padding
+  static constexpr int LK = DK + PE, LS = SV + PE;
   static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
-  static constexpr size_t oW = 0;                                   // [C][DK] IO
-  static constexpr size_t oS = al(oW + (size_t)C * DK * sizeof(IO));  // [DK][SV]
-  static constexpr size_t odS = al(oS + (size_t)DK * SV * 4);        // [DK][SV]
-  static constexpr size_t oO = al(odS + (size_t)DK * SV * 4);        // [C][SV]
-  static constexpr size_t odD = al(oO + (size_t)C * SV * 4);         // [C][SV]
-  static constexpr size_t oD = al(odD + (size_t)C * SV * 4);         // [C][SV]
-  static constexpr size_t total = oD + (size_t)C * SV * 4;
+  // every array in the q/k/v dtype, rows contiguous in the contracted index
+  static constexpr size_t oW = 0;                                    // -W [C][LK]
+  static constexpr size_t oST = al(oW + (size_t)C * LK * sizeof(IO));  // S^T [SV][LK]
+  static constexpr size_t oS = al(oST + (size_t)SV * LK * sizeof(IO)); // S [DK][LS]
+  static constexpr size_t odS = al(oS + (size_t)DK * LS * sizeof(IO)); // dS' [DK][LS]
+  static constexpr size_t oO = al(odS + (size_t)DK * LS * sizeof(IO)); // dO [C][LS]
+  static constexpr size_t odD = al(oO + (size_t)C * LS * sizeof(IO));  // dDelta
+  static constexpr size_t oD = al(odD + (size_t)C * LS * sizeof(IO));  // Delta
+  static constexpr size_t oG = al(oD + (size_t)C * LS * sizeof(IO));   // dgam [DK]
+  static constexpr size_t total = oG + DK * 4;
 };
 
 template <typename IO, int DK, int C>
 __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
     BwdParams bp) {
   using L = G1L<IO, DK, C>;
-  constexpr int SV = L::SV, NB = C / 16, NKT = DK / 16;
+  constexpr int SV = L::SV, NB = C / 16, NKT = DK / 16, LK = L::LK, LS = L::LS;
   constexpr int NTL = NB * NKT;          // C x DK output tiles
   constexpr int TW = (NTL + 3) / 4;      // of them per wave
   constexpr int NKU = (NKT + Mma<IO>::TPU - 1) / Mma<IO>::TPU;
   const PrefillParams &p = bp.f;
   __shared__ __attribute__((aligned(16))) char sm[L::total];
-  IO *nW = (IO *)(sm + L::oW);
-  float *Ss = (float *)(sm + L::oS), *dSs = (float *)(sm + L::odS);
-  float *Os = (float *)(sm + L::oO), *dDs = (float *)(sm + L::odD);
-  float *Ds = (float *)(sm + L::oD);
+  IO *nW = (IO *)(sm + L::oW), *STs = (IO *)(sm + L::oST);
+  IO *Ss = (IO *)(sm + L::oS), *dSs = (IO *)(sm + L::odS);
+  IO *Os = (IO *)(sm + L::oO), *dDs = (IO *)(sm + L::odD);
+  IO *Ds = (IO *)(sm + L::oD);
+  float *dgs = (float *)(sm + L::oG);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -423,12 +446,13 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
   const size_t orow = (size_t)H * Dv;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-  units_to_lds<IO>(blk + W.off_negw, NB, NKU, DK, nW, DK, tid);  // -W[r][i]
+  units_to_lds<IO>(blk + W.off_negw, NB, NKU, DK, nW, LK, tid);  // -W[r][i]
+  for (int i = tid; i < DK; i += BWD_THREADS) dgs[i] = 0.f;
+  __syncthreads();
 
   f32x4 aQ[TW], aK[TW], aW[TW];
 #pragma unroll
   for (int j = 0; j < TW; ++j) aQ[j] = aK[j] = aW[j] = zero;
-  float dgam = 0.f;
 
   for (int c0 = 0; c0 < Dv; c0 += SV) {
     const int sv = min(SV, Dv - c0);
@@ -451,17 +475,20 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
     }
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
-      const int i = tid + BWD_THREADS * j;
-      const bool ok = i % SV < sv;
-      Ss[i] = ok ? la[j] : 0.f;
-      dSs[i] = ok ? lb[j] : 0.f;
+      const int i = tid + BWD_THREADS * j, r = i / SV, c = i % SV;
+      const bool ok = c < sv;
+      const float sv_ = ok ? la[j] : 0.f, dv_ = ok ? lb[j] : 0.f;
+      Ss[r * LS + c] = (IO)sv_;
+      STs[c * LK + r] = (IO)sv_;
+      dSs[r * LS + c] = (IO)dv_;
+      atomicAdd(&dgs[r], sv_ * dv_);  // dgam = rowsum(dS' * S), fp32
     }
 #pragma unroll
     for (int j = 0; j < NO; ++j) {
-      const int i = tid + BWD_THREADS * j;
-      const bool ok = i % SV < sv && t0 + i / SV < T;
-      Os[i] = ok ? lo[j] : 0.f;
-      dDs[i] = ok ? ld[j] : 0.f;
+      const int i = tid + BWD_THREADS * j, r = i / SV, c = i % SV;
+      const bool ok = c < sv && t0 + r < T;
+      Os[r * LS + c] = (IO)(ok ? lo[j] : 0.f);
+      dDs[r * LS + c] = (IO)(ok ? ld[j] : 0.f);
     }
     __syncthreads();
     // Delta = U - W S on this slab (U in accumulator tiles [vt][rt])
@@ -474,13 +501,13 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
                        ((size_t)(vt * NB + rt) * 64 + lane) * 4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] = to_f32(us[e]);
-        acc = tile_mma<IO, false, false>(acc, nW, DK, Ss, SV, 16 * rt, 16 * ct,
-                                         DK, lane);
+        acc = tile_mma_rows<IO>(acc, nW, LK, STs, LK, 16 * rt, 16 * ct, DK,
+                                lane);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rt + 4 * g4 + e;
-        Ds[r * SV + 16 * ct + m16] = acc[e];
+        Ds[r * LS + 16 * ct + m16] = (IO)acc[e];
         if (16 * ct < sv)
           gs[(size_t)r * Dv + c0 + 16 * ct + m16] = t0 + r < T ? acc[e] : 0.f;
       }
@@ -492,16 +519,14 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
       const int tl = wave + 4 * j;
       if (tl < NTL) {
         const int rt = tl % NB, it = tl / NB;
-        aQ[j] = tile_mma<IO, false, true>(aQ[j], Os, SV, Ss, SV, 16 * rt,
-                                          16 * it, SV, lane);
-        aW[j] = tile_mma<IO, false, true>(aW[j], dDs, SV, Ss, SV, 16 * rt,
-                                          16 * it, SV, lane);
-        aK[j] = tile_mma<IO, false, true>(aK[j], Ds, SV, dSs, SV, 16 * rt,
-                                          16 * it, SV, lane);
+        aQ[j] = tile_mma_rows<IO>(aQ[j], Os, LS, Ss, LS, 16 * rt, 16 * it, SV,
+                                  lane);
+        aW[j] = tile_mma_rows<IO>(aW[j], dDs, LS, Ss, LS, 16 * rt, 16 * it, SV,
+                                  lane);
+        aK[j] = tile_mma_rows<IO>(aK[j], Ds, LS, dSs, LS, 16 * rt, 16 * it, SV,
+                                  lane);
       }
     }
-    if (tid < DK)
-      for (int c = 0; c < SV; ++c) dgam += dSs[tid * SV + c] * Ss[tid * SV + c];
     __syncthreads();
   }
   float *gQ = gs + (size_t)C * Dv, *gK = gQ + (size_t)C * DK;
@@ -520,7 +545,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
       }
     }
   }
-  if (tid < DK) gG[tid] = dgam;
+  if (tid < DK) gG[tid] = dgs[tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -713,8 +738,8 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
     __syncthreads();
     for (int tl = wave; tl < NB * NB; tl += 4) {
       const int rt = tl % NB, st = tl / NB;
-      f32x4 acc = tile_mma<IO, false, true>(zero, dDs, Dv, vS, Dv, 16 * rt,
-                                            16 * st, Dv, lane);
+      f32x4 acc = tile_mma_rows<IO>(zero, dDs, Dv, vS, Dv, 16 * rt, 16 * st,
+                                    Dv, lane);
       const float bs = bet[16 * st + m16];  // (beta V)^T: beta of column s
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -755,8 +780,8 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
     __syncthreads();
     for (int tl = wave; tl < NB * NB; tl += 4) {
       const int rt = tl % NB, st = tl / NB;
-      f32x4 acc = tile_mma<IO, false, true>(zero, dWs, DK, KdS, DK, 16 * rt,
-                                            16 * st, DK, lane);
+      f32x4 acc = tile_mma_rows<IO>(zero, dWs, DK, KdS, DK, 16 * rt, 16 * st,
+                                    DK, lane);
       const float bs = bet[16 * st + m16];  // (beta Kd)^T: beta of column s
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -824,8 +849,8 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
     __syncthreads();
     for (int tl = wave; tl < NB * NB; tl += 4) {
       const int rt = tl % NB, st = tl / NB;
-      f32x4 acc = tile_mma<IO, false, true>(zero, Os, Dv, Ds, Dv, 16 * rt,
-                                            16 * st, Dv, lane);
+      f32x4 acc = tile_mma_rows<IO>(zero, Os, Dv, Ds, Dv, 16 * rt, 16 * st,
+                                    Dv, lane);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rt + 4 * g4 + e, s = 16 * st + m16;
