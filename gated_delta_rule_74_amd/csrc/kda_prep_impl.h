@@ -103,8 +103,11 @@ template <typename IO, int DK, int C> struct PL {  // prep LDS layout
   // channel-major copy of the k*sigma operand (bf16 only: the Ktil^T units
   // are assembled from it 16 bytes per lane)
   static constexpr size_t oKST = al(oVote + 64);
-  static constexpr size_t total =
-      oKST + (TPU == 2 ? (size_t)DK * LDC * sizeof(IO) : 0);
+  // beta of the chunk's tokens (fp32), written at the end of the previous
+  // task from one coalesced load
+  static constexpr size_t oBeta =
+      al(oKST + (TPU == 2 ? (size_t)DK * LDC * sizeof(IO) : 0));
+  static constexpr size_t total = oBeta + 64 * 4;
   __device__ static int p2(int a, int b) { return (a - 2) * (a - 1) / 2 + b; }
 };
 
@@ -112,12 +115,13 @@ template <typename IO, bool CONV> struct Stage {
   static constexpr int XR = CONV ? 11 : 8;  // rows of q/k/v (conv: +3 halo)
   typename Vec4<IO>::raw xq[XR], xk[XR], xv[XR];
   uint4 g[8];
-  uint32_t beta[8], betav[8];
+  uint32_t beta;  // wave 0: beta of token lane of the chunk (raw bits)
 };
 
-// PART selects what to fetch: 1 = g and beta, 2 = q, 4 = k, 8 = v (and the
-// V side's beta); the parts are issued in different phases of the previous
-// task so the vector memory queue drains between them
+// PART selects what to fetch: 1 = g and beta, 2 = q, 4 = k, 8 = v; the parts
+// are issued in different phases of the previous task so the vector memory
+// queue drains between them.  beta is one coalesced load by wave 0 (token =
+// lane), later written to LDS for both the K and the V side.
 template <int PART, typename IO, typename GT, int DK, int C, bool CONV>
 __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
                                           Stage<IO, CONV> &st, int tid) {
@@ -134,12 +138,15 @@ __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
   // 64-bit bases of (batch b, head h); in-batch offsets fit in 32 bits
   const size_t kb = (tok0 * H + h) * DK;
   const unsigned rowK = (unsigned)(H * DK);
+  if ((PART & 1) && tid < 64) {
+    const size_t bi = (tok0 + (unsigned)min(t0 + tid, tlast)) * H + h;
+    st.beta = GB ? (uint32_t)((const unsigned short *)p.beta)[bi]
+                 : ((const unsigned *)p.beta)[bi];
+  }
   if (tid < NQ * NTG) {
     const int cq = tid % NQ, tg = tid / NQ;
     const float *gf = (const float *)p.g + kb + 4 * cq;
     const bf16 *gh = (const bf16 *)p.g + kb + 4 * cq;
-    const float *bf = (const float *)p.beta + tok0 * H + h;
-    const unsigned short *bh16 = (const unsigned short *)p.beta + tok0 * H + h;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (!(PART & 1)) break;
@@ -149,14 +156,11 @@ __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
         const size_t gi = (tok0 + t) * H + h;
         st.g[i].x = GB ? (unsigned)((const unsigned short *)p.g)[gi]
                        : ((const unsigned *)p.g)[gi];
-        st.beta[i] = GB ? (uint32_t)bh16[t * H] : __float_as_uint(bf[t * H]);
       } else if (GB) {
         const uint2 v = *(const uint2 *)(gh + t * rowK);
         st.g[i] = make_uint4(v.x, v.y, 0u, 0u);
-        st.beta[i] = bh16[t * H];
       } else {
         st.g[i] = *(const uint4 *)(gf + t * rowK);
-        st.beta[i] = __float_as_uint(bf[t * H]);
       }
     }
     const IO *xq = (const IO *)(CONV ? p.xq : p.q) + kb + 4 * cq;
@@ -175,19 +179,11 @@ __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
     const unsigned rowV = (unsigned)(H * Dv);
     const IO *xv = (const IO *)(CONV ? p.xv : p.v) + (tok0 * H + h) * Dv +
                    4 * cv;
-    const float *bf = (const float *)p.beta + tok0 * H + h;
-    const unsigned short *bh16 = (const unsigned short *)p.beta + tok0 * H + h;
 #pragma unroll
     for (int i = 0; i < Stage<IO, CONV>::XR; ++i) {
       const unsigned t =
           (unsigned)min(max(t0 + 8 * tg + i - (CONV ? 3 : 0), 0), tlast);
       st.xv[i] = *(const R *)(xv + t * rowV);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const unsigned t = (unsigned)min(t0 + 8 * tg + i, tlast);
-      st.betav[i] = GB ? (uint32_t)bh16[t * H]
-                                : __float_as_uint(bf[t * H]);
     }
   }
 }
@@ -258,6 +254,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
   float *FbA = (float *)(sm + L::oFb), *FbP = FbA + NB * 256;
   int *votes = (int *)(sm + L::oVote);
   IO *XksT = (IO *)(sm + L::oKST);  // [DK][LDC], bf16 only
+  float *betas = (float *)(sm + L::oBeta);  // [64], token of the chunk
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -276,6 +273,14 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
   Stage<IO, CONV> st;
   int task = blockIdx.x;
   if (task < ntask) prep_load<15, IO, GT, DK, C, CONV>(p, task, st, tid);
+  // wave 0 moves the staged betas of a task into LDS
+  auto put_beta = [&]() {
+    if (wave == 0)
+      betas[lane] = GB ? __uint_as_float(st.beta << 16)
+                       : __uint_as_float(st.beta);
+  };
+  if (task < ntask) put_beta();
+  __syncthreads();
 
   for (; task < ntask; task += gridDim.x) {
     const int bh = task % BH, n = p.NC - 1 - task / BH;
@@ -295,13 +300,11 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
       for (int i = 0; i < 8; ++i) {
         const bool ok = t0 + r0 + i < T;
         float gv[4];
-        if (GB) {
+        if (GB)
           Vec4<bf16>::get(make_uint2(st.g[i].x, st.g[i].y), gv);
-          bt[i] = ok ? __uint_as_float(st.beta[i] << 16) : 0.f;
-        } else {
+        else
           Vec4<float>::get(st.g[i], gv);
-          bt[i] = ok ? __uint_as_float(st.beta[i]) : 0.f;
-        }
+        bt[i] = ok ? betas[r0 + i] : 0.f;
         if (p.gate_head) {
           // the head's one gate, shared by the 4 channels: one exp
           const float e0 =
@@ -444,9 +447,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const bool ok = t0 + 8 * tgv + i < T;
-        const float bb = GB ? __uint_as_float(st.betav[i] << 16)
-                                     : __uint_as_float(st.betav[i]);
-        bvt[i] = ok ? bb : 0.f;
+        bvt[i] = ok ? betas[8 * tgv + i] : 0.f;
       }
       if (CONV) {
         float tv[4][4];
@@ -911,6 +912,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
         *(typename V4::raw *)dst = V4::put(a4);
       }
     }
+    if (more) put_beta();  // the current task's betas were last read in E1
     __syncthreads();  // B5: LDS free for the next task
   }
 }

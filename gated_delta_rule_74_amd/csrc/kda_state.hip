@@ -144,16 +144,12 @@ __device__ __forceinline__ void load_out(OFrag<IO, DK, C, NS> &f,
 #pragma unroll
     for (int u = 0; u < G::NKU; ++u) f.q[u] = Lq[(rtc * G::NKU + u) * 64];
   } else {
-    // P units above the diagonal are never written by the prep: their bits
-    // are cleared so the product can run unconditionally
+    // P units above the diagonal are never written by the prep: they are
+    // neither loaded nor multiplied (the test is uniform over the wave)
     const frag *Lp = (const frag *)(blk + W.off_p) + lane;
 #pragma unroll
-    for (int u = 0; u < G::NTU; ++u) {
-      const unsigned keep = (G::NTU == 1 || u <= rtc / G::TPU) ? ~0u : 0u;
-      uint4 r = __builtin_bit_cast(uint4, Lp[(rtc * G::NTU + u) * 64]);
-      r.x &= keep; r.y &= keep; r.z &= keep; r.w &= keep;
-      f.p[u] = __builtin_bit_cast(frag, r);
-    }
+    for (int u = 0; u < G::NTU; ++u)
+      if (G::NTU == 1 || u <= rtc / G::TPU) f.p[u] = Lp[(rtc * G::NTU + u) * 64];
   }
 }
 
@@ -184,7 +180,8 @@ __global__ __launch_bounds__(STATE_THREADS, 1) void kda_state_pass(
   frag *SU = (frag *)(sm + G::oSU);  // S as second operand, [NS][NKU] units
   frag *DU = (frag *)(sm + G::oDU);  // Delta as second operand, [NS][NTU]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // role: uniform
   const int m16 = lane & 15, g4 = lane >> 4;
   const int Dv = p.Dv, H = p.H, T = p.T, BH = p.B * p.H, NC = p.NC;
   const int ng = Dv / (16 * NS);  // workgroups per head
@@ -386,9 +383,11 @@ __global__ __launch_bounds__(STATE_THREADS, 1) void kda_state_pass(
 #pragma unroll
         for (int u = 0; u < NTU; ++u) db[s][u] = DU[(s * NTU + u) * 64 + lane];
 #pragma unroll
-      for (int u = 0; u < NTU; ++u)
+      for (int u = 0; u < NTU; ++u) {
+        if (NTU > 1 && u > rtc / TPU) continue;  // P is zero there
 #pragma unroll
         for (int s = 0; s < NS; ++s) ot[s] = M::mma(db[s][u], f.p[u], ot[s]);
+      }
       // lane (g4, m16) holds token 16 rtc + m16, value columns 4 g4 .. 4 g4 + 3
       const int tok = n * C + 16 * rtc + m16;
       if (rv && tok < T) {
