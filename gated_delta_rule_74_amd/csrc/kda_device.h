@@ -27,6 +27,33 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
+// Streaming (nontemporal) 8- or 16-byte accesses, for data touched once in
+// a kernel: read-once inputs and write-once workspace blocks.  They keep the
+// L2 from filling with dirty lines that a following kernel has to write
+// back while it runs.
+template <typename R>
+__device__ __forceinline__ R ld_stream(const void *q) {
+  static_assert(sizeof(R) == 8 || sizeof(R) == 16, "8 or 16 bytes");
+  if constexpr (sizeof(R) == 16) {
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(R, __builtin_nontemporal_load((const u4 *)q));
+  } else {
+    typedef unsigned u2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(R, __builtin_nontemporal_load((const u2 *)q));
+  }
+}
+template <typename T>
+__device__ __forceinline__ void st_stream(void *q, T v) {
+  static_assert(sizeof(T) == 8 || sizeof(T) == 16, "8 or 16 bytes");
+  if constexpr (sizeof(T) == 16) {
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(__builtin_bit_cast(u4, v), (u4 *)q);
+  } else {
+    typedef unsigned u2 __attribute__((ext_vector_type(2)));
+    __builtin_nontemporal_store(__builtin_bit_cast(u2, v), (u2 *)q);
+  }
+}
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 template <typename T> __device__ __forceinline__ T from_f32(float x);

@@ -157,10 +157,10 @@ __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
         st.g[i].x = GB ? (unsigned)((const unsigned short *)p.g)[gi]
                        : ((const unsigned *)p.g)[gi];
       } else if (GB) {
-        const uint2 v = *(const uint2 *)(gh + t * rowK);
+        const uint2 v = ld_stream<uint2>(gh + t * rowK);
         st.g[i] = make_uint4(v.x, v.y, 0u, 0u);
       } else {
-        st.g[i] = *(const uint4 *)(gf + t * rowK);
+        st.g[i] = ld_stream<uint4>(gf + t * rowK);
       }
     }
     const IO *xq = (const IO *)(CONV ? p.xq : p.q) + kb + 4 * cq;
@@ -169,8 +169,8 @@ __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
     for (int i = 0; i < Stage<IO, CONV>::XR; ++i) {
       const unsigned t =
           (unsigned)min(max(t0 + 8 * tg + i - (CONV ? 3 : 0), 0), tlast);
-      if (PART & 2) st.xq[i] = *(const R *)(xq + t * rowK);
-      if (PART & 4) st.xk[i] = *(const R *)(xk + t * rowK);
+      if (PART & 2) st.xq[i] = ld_stream<R>(xq + t * rowK);
+      if (PART & 4) st.xk[i] = ld_stream<R>(xk + t * rowK);
     }
   }
   const int NQV = Dv / 4;
@@ -183,7 +183,7 @@ __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
     for (int i = 0; i < Stage<IO, CONV>::XR; ++i) {
       const unsigned t =
           (unsigned)min(max(t0 + 8 * tg + i - (CONV ? 3 : 0), 0), tlast);
-      st.xv[i] = *(const R *)(xv + t * rowV);
+      st.xv[i] = ld_stream<R>(xv + t * rowV);
     }
   }
 }
@@ -530,9 +530,8 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
           }
           const int u = c0 / KU, gq = (c0 % KU) / 4;
           const int ln = (r & 15) + 16 * gq;
-          *(typename V4::raw *)(blk + W.off_qt +
-                                ((size_t)(a * NKU + u) * 64 + ln) * 16) =
-              V4::put(qt);
+          st_stream(blk + W.off_qt + ((size_t)(a * NKU + u) * 64 + ln) * 16,
+                    V4::put(qt));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -544,9 +543,8 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
             const int ln = (c & 15) + 16 * gq;
             float v4[4] = {kt[4 * hh + 0][j], kt[4 * hh + 1][j],
                            kt[4 * hh + 2][j], kt[4 * hh + 3][j]};
-            *(typename V4::raw *)(blk + W.off_ktt +
-                                  ((size_t)(ct * NTU + u) * 64 + ln) * 16) =
-                V4::put(v4);
+            st_stream(blk + W.off_ktt + ((size_t)(ct * NTU + u) * 64 + ln) * 16,
+                      V4::put(v4));
           }
         }
       }
@@ -596,8 +594,8 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
           y1[j] = QHI ? x1[j] * f1[j] : 0.f;
         }
         const typename V4::raw lo = V4::put(y0), up = V4::put(y1);
-        *(uint4 *)(blk + W.off_qt + ((size_t)(aa * NKU + u) * 64 + lane) * 16) =
-            make_uint4(lo.x, lo.y, up.x, up.y);
+        st_stream(blk + W.off_qt + ((size_t)(aa * NKU + u) * 64 + lane) * 16,
+                  make_uint4(lo.x, lo.y, up.x, up.y));
       }
 #pragma unroll
       for (int it = 0; it < (NKT * NTU + NW4 - 1) / NW4; ++it) {
@@ -628,8 +626,8 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
           y1[j] = KHI ? x1[j] * s1 : 0.f;
         }
         const typename V4::raw lo = V4::put(y0), up = V4::put(y1);
-        *(uint4 *)(blk + W.off_ktt + ((size_t)(ct * NTU + u) * 64 + lane) * 16) =
-            make_uint4(lo.x, lo.y, up.x, up.y);
+        st_stream(blk + W.off_ktt + ((size_t)(ct * NTU + u) * 64 + lane) * 16,
+                  make_uint4(lo.x, lo.y, up.x, up.y));
       }
     }
     // mid products M_{b->a} = prod_{b<d<a} F_d for sub-chunk pairs a-b >= 2
@@ -751,7 +749,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
           char *dst = blk + W.off_p + ((size_t)(aa * NTU + u) * 64 + lane) * 16 +
                       hf * 4 * sizeof(IO);
           const float a4[4] = {accP[0], accP[1], accP[2], accP[3]};
-          *(typename V4::raw *)dst = V4::put(a4);
+          st_stream(dst, V4::put(a4));
           if (TPU == 2 && diag && (aa % 2) == 0) {
             const float z[4] = {0.f, 0.f, 0.f, 0.f};
             *(typename V4::raw *)(dst + 4 * sizeof(IO)) = V4::put(z);
@@ -892,8 +890,8 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
             for (int hh = 0; hh < TPU; ++hh)
               if (TPU * u + hh < NKT) acc[hh] = M::mma(xa[uu][hh], tb[uu], acc[hh]);
         const frag out = M::pack(-acc[0], -acc[1]);
-        *(frag *)(blk + W.off_negw + ((size_t)(rt * NKU + u) * 64 + lane) *
-                                         16) = out;
+        st_stream(blk + W.off_negw + ((size_t)(rt * NKU + u) * 64 + lane) * 16,
+                  out);
       }
       for (int vt = 0; vt < nvt; ++vt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -909,7 +907,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
         IO *dst = (IO *)(blk + W.off_u) +
                   ((size_t)(vt * NB + rt) * 64 + lane) * 4;
         float a4[4] = {acc[0], acc[1], acc[2], acc[3]};
-        *(typename V4::raw *)dst = V4::put(a4);
+        st_stream(dst, V4::put(a4));
       }
     }
     if (more) put_beta();  // the current task's betas were last read in E1
