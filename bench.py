@@ -130,6 +130,16 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
+    def settle(fn, seconds=0.25):
+        # untimed, before a part's own warm-up steps: the GPU's clocks ramp
+        # over the first ~10-20 ms of sustained work, and a timed region that
+        # starts cold reports part of that ramp instead of the steady rate
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(4):
+                fn()
+            torch.cuda.synchronize()
+
     # ---------------- prefill, model-shaped (headline) ----------------------
     c1 = ki.CONFIGS[1]
     B, T, H, Dk, Dv, C = (c1[n] for n in ("B", "T", "H", "Dk", "Dv", "chunk"))
@@ -145,6 +155,7 @@ def main():
             kda.kda_prefill(x["q"], x["k"], x["v"], x["g"], x["beta"],
                             chunk=C, o=o, s_out=s, workspace=ws)
 
+        settle(step)
         for _ in range(W):
             step()
         torch.cuda.synchronize()
@@ -226,6 +237,9 @@ def main():
         xs = [ki.decode_step_inputs(N, H3, D3, D3, i, device=dev)
               for i in range(steps)]
         od = torch.empty((N, H3, D3), dtype=torch.bfloat16, device=dev)
+        d0 = xs[0]
+        settle(lambda: kda.kda_decode_step(d0["q"], d0["k"], d0["v"], d0["g"],
+                                           d0["beta"], st, o=od))
         for i in range(10):
             d = xs[i]
             kda.kda_decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], st,
@@ -268,6 +282,7 @@ def main():
         callt = lambda: kda.kda_decode_tokens(xt["q"], xt["k"], xt["v"],
                                               xt["g"], xt["beta"], st,
                                               state_out=st, o=ot)
+        settle(callt)
         for _ in range(5):
             callt()
         torch.cuda.synchronize()
@@ -288,18 +303,19 @@ def main():
             f"{N * L / (mt * 1e-3) / 1e6:.2f} M tokens/s")
         # the generation step with the conv prologue fused: raw projections
         # in, width-4 conv over the rolling history, history rolled forward
-        W = 4
+        CW = 4
         xc = ki.prefill_inputs(N, 1, H3, D3, D3, qkv="bf16", gate="bf16",
-                               conv_width=W, seed=6, device=dev)
-        cache = torch.zeros((N, 3, H3 * D3, W - 1), device=dev)
+                               conv_width=CW, seed=6, device=dev)
+        cache = torch.zeros((N, 3, H3 * D3, CW - 1), device=dev)
         oc = torch.empty((N, 1, H3, D3), dtype=torch.bfloat16, device=dev)
         conv = dict(xq=xc["xq"], xk=xc["xk"], xv=xc["xv"], wq=xc["wq"],
-                    wk=xc["wk"], wv=xc["wv"], width=W, l2norm_qk=True,
+                    wk=xc["wk"], wv=xc["wv"], width=CW, l2norm_qk=True,
                     eps=1e-6)
         callc = lambda: kda.kda_decode_tokens(None, None, None, xc["g"],
                                               xc["beta"], st, state_out=st,
                                               o=oc, conv=conv,
                                               conv_state=cache)
+        settle(callc)
         for _ in range(5):
             callc()
         torch.cuda.synchronize()
@@ -314,7 +330,7 @@ def main():
         byc = (N * H3 * (2 * D3 * D3 * 4 + (3 * D3 + 2 * D3 + 1) * 2)
                + 2 * cache.numel() * 4)
         dtok["conv_step"] = dict(
-            conv_width=W, calls=reps, us_per_call=mc * 1e3,
+            conv_width=CW, calls=reps, us_per_call=mc * 1e3,
             tokens_per_s=N / (mc * 1e-3),
             achieved_gbs=byc / (mc * 1e-3) / 1e9,
             hbm_frac=byc / (mc * 1e-3) / 1e9 / HBM_PEAK_GBS)
@@ -350,6 +366,7 @@ def main():
         f = lambda: kda.kda_prefill(x.get("q"), x.get("k"), x.get("v"),
                                     x["g"], x["beta"], chunk=Cc, conv=conv,
                                     o=o, s_out=s, workspace=ws)
+        settle(f)
         f()
         torch.cuda.synchronize()
         reps = 5 if cid == 2 else 3
@@ -391,6 +408,7 @@ def main():
         fb = lambda: kda.kda_prefill_backward(x["q"], x["k"], x["v"], x["g"],
                                               x["beta"], do, chunk=Cc,
                                               workspace=ws)
+        settle(fb)
         fb()
         torch.cuda.synchronize()
         reps = 5
