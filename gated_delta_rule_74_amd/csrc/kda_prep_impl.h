@@ -188,6 +188,36 @@ __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
   }
 }
 
+// Channel-major operand rows ([channel][token], LDC elements per row): the
+// 4-element blocks of row r are stored XOR-swizzled by r / 4.  The
+// transposed writes of phases E1 and T0 (a wave's lanes write the same block
+// of rows 4 apart) then spread over the LDS banks instead of piling onto a
+// few, and the k-contiguous unit reads stay conflict-free.
+template <int C>
+__device__ __forceinline__ int cm_off(int row, int col) {
+  constexpr int M = C / 4 - 1;  // blocks per row - 1, a power of two
+  return (((col >> 2) ^ ((row >> 2) & M)) << 2) | (col & 3);
+}
+// operand unit (k = k0 ...) from swizzled channel-major row `row`
+template <typename IO, int C>
+__device__ __forceinline__ typename Mma<IO>::frag load_k_cm(const IO *rowp,
+                                                            int row, int k0,
+                                                            int g,
+                                                            bool full) {
+  if constexpr (sizeof(IO) == 2) {
+    const bf16x4 lo = *(const bf16x4 *)(rowp + cm_off<C>(row, k0 + 4 * g));
+    const bf16x4 hi =
+        full ? *(const bf16x4 *)(rowp + cm_off<C>(row, k0 + 16 + 4 * g))
+             : bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    bf16x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+  } else {
+    return *(const f32x4 *)(rowp + cm_off<C>(row, k0 + 4 * g));
+  }
+}
+
 // block j of the A/P sub-block list: (aa, bb), bb <= aa.  With four
 // sub-chunks the order spreads the four costly blocks (the three that need
 // mid products, and the last row) over the four waves.
@@ -430,11 +460,13 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
         if constexpr (TPU == 2) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            *(typename V4::raw *)(XksT + (c0 + j) * LDC + r0) =
+            *(typename V4::raw *)(XksT + (c0 + j) * LDC +
+                                  cm_off<C>(c0 + j, r0)) =
                 V4::put(&xkc[j][0]);
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            *(typename V4::raw *)(XksT + (c0 + j) * LDC + r0 + 4) =
+            *(typename V4::raw *)(XksT + (c0 + j) * LDC +
+                                  cm_off<C>(c0 + j, r0 + 4)) =
                 V4::put(&xkc[j][4]);
         }
       }
@@ -618,8 +650,10 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
           if (bb > a0 + 1) s1 *= fl[bb];
         }
         float x0[4], x1[4], y0[4], y1[4];
-        V4::get(*(const typename V4::raw *)(XksT + ch * LDC + tk0), x0);
-        V4::get(*(const typename V4::raw *)(XksT + ch * LDC + tk1), x1);
+        V4::get(*(const typename V4::raw *)(XksT + ch * LDC +
+                                            cm_off<C>(ch, tk0)), x0);
+        V4::get(*(const typename V4::raw *)(XksT + ch * LDC +
+                                            cm_off<C>(ch, tk1)), x1);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           y0[j] = x0[j] * s0;
@@ -769,9 +803,9 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
       for (int j = 0; j < 4; ++j) {
         float lo[4] = {kgb[0][j], kgb[1][j], kgb[2][j], kgb[3][j]};
         float hi[4] = {kgb[4][j], kgb[5][j], kgb[6][j], kgb[7][j]};
-        IO *row = XkgT + (c0 + j) * LDC + r0;
-        *(typename V4::raw *)row = V4::put(lo);
-        *(typename V4::raw *)(row + 4) = V4::put(hi);
+        IO *row = XkgT + (c0 + j) * LDC;
+        *(typename V4::raw *)(row + cm_off<C>(c0 + j, r0)) = V4::put(lo);
+        *(typename V4::raw *)(row + cm_off<C>(c0 + j, r0 + 4)) = V4::put(hi);
       }
     }
     if (vthr) {
@@ -779,9 +813,11 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
       for (int j = 0; j < 4; ++j) {
         float lo[4] = {bv[0][j], bv[1][j], bv[2][j], bv[3][j]};
         float hi[4] = {bv[4][j], bv[5][j], bv[6][j], bv[7][j]};
-        IO *row = XvT + (4 * cv + j) * LDC + 8 * tgv;
-        *(typename V4::raw *)row = V4::put(lo);
-        *(typename V4::raw *)(row + 4) = V4::put(hi);
+        IO *row = XvT + (4 * cv + j) * LDC;
+        *(typename V4::raw *)(row + cm_off<C>(4 * cv + j, 8 * tgv)) =
+            V4::put(lo);
+        *(typename V4::raw *)(row + cm_off<C>(4 * cv + j, 8 * tgv + 4)) =
+            V4::put(hi);
       }
     }
     __syncthreads();  // B4
@@ -879,8 +915,8 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
 #pragma unroll
           for (int hh = 0; hh < TPU; ++hh) {
             const int ct = (TPU * u + hh) % NKT;
-            xa[uu][hh] = M::load_k(XkgT + (16 * ct + m16) * LDC + KU * uu, g4,
-                                   fullT);
+            xa[uu][hh] = load_k_cm<IO, C>(XkgT + (16 * ct + m16) * LDC,
+                                          16 * ct + m16, KU * uu, g4, fullT);
           }
         }
 #pragma unroll
@@ -899,7 +935,8 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
 #pragma unroll
         for (int uu = 0; uu < NTU; ++uu) {
           const bool fullT = (TPU == 1) || (TPU * uu + 1 < NB);
-          vb[uu] = M::load_k(XvT + (16 * vt + m16) * LDC + KU * uu, g4, fullT);
+          vb[uu] = load_k_cm<IO, C>(XvT + (16 * vt + m16) * LDC, 16 * vt + m16,
+                                    KU * uu, g4, fullT);
         }
 #pragma unroll
         for (int uu = 0; uu < NTU; ++uu)
