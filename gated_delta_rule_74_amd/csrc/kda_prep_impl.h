@@ -68,7 +68,8 @@ template <> struct Vec4<float> {
   }
 };
 
-template <typename IO, int DK, int C> struct PL {  // prep LDS layout
+template <typename IO, int DK, int C, bool CONV = false>
+struct PL {  // prep LDS layout
   static constexpr int NB = C / 16, NKT = DK / 16, TPU = Mma<IO>::TPU;
   static constexpr int NKU = (NKT + TPU - 1) / TPU;
   static constexpr int NTU = (NB + TPU - 1) / TPU;
@@ -107,7 +108,11 @@ template <typename IO, int DK, int C> struct PL {  // prep LDS layout
   // task from one coalesced load
   static constexpr size_t oBeta =
       al(oKST + (TPU == 2 ? (size_t)DK * LDC * sizeof(IO) : 0));
-  static constexpr size_t total = oBeta + 64 * 4;
+  // conv taps of the chunk's head, right-aligned, one float4 per channel:
+  // q channels, then k, then v (conv only); written like the betas
+  static constexpr size_t oTap = al(oBeta + 64 * 4);
+  static constexpr size_t total =
+      oTap + (CONV ? (size_t)(2 * DK + DVMAX) * 16 : 0);
   __device__ static int p2(int a, int b) { return (a - 2) * (a - 1) / 2 + b; }
 };
 
@@ -116,6 +121,7 @@ template <typename IO, bool CONV> struct Stage {
   typename Vec4<IO>::raw xq[XR], xk[XR], xv[XR];
   uint4 g[8];
   uint32_t beta;  // wave 0: beta of token lane of the chunk (raw bits)
+  f32x4 tap[CONV ? 2 : 1];  // conv: taps of channel items tid, tid + 256
 };
 
 // PART selects what to fetch: 1 = g and beta, 2 = q, 4 = k, 8 = v; the parts
@@ -142,6 +148,29 @@ __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
     const size_t bi = (tok0 + (unsigned)min(t0 + tid, tlast)) * H + h;
     st.beta = GB ? (uint32_t)((const unsigned short *)p.beta)[bi]
                  : ((const unsigned *)p.beta)[bi];
+  }
+  if constexpr (CONV) {
+    // the head's taps: item = q channel, DK + k channel, 2 DK + v channel
+    // (fetched with the last part: they are live only until the task ends)
+    if (PART & 8) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int it = tid + PREP_THREADS * r;
+        if (it >= 2 * DK + Dv) break;
+        const float *w = it < DK ? p.wq + ((size_t)h * DK + it) * p.cw
+                       : it < 2 * DK ? p.wk + ((size_t)h * DK + it - DK) * p.cw
+                                     : p.wv + ((size_t)h * Dv + it - 2 * DK) * p.cw;
+        if (p.cw == 4) {
+          st.tap[r] = *(const f32x4 *)w;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int jj = i - (4 - p.cw);
+            st.tap[r][i] = (jj >= 0) ? w[jj] : 0.f;
+          }
+        }
+      }
+    }
   }
   if (tid < NQ * NTG) {
     const int cq = tid % NQ, tg = tid / NQ;
@@ -246,21 +275,33 @@ __device__ __forceinline__ void ap_block(int j, int &aa, int &bb) {
   }
 }
 
-// 4 taps right-aligned (w4[3] multiplies the newest input) for 4 channels
-__device__ __forceinline__ void load_taps(const float *w, int W, float t[4][4]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int jj = i - (4 - W);
-      t[j][i] = (jj >= 0) ? w[j * W + jj] : 0.f;
-    }
+// sum over aligned groups of G lanes (G a power of two, at most 32), every
+// lane of a group getting the total: DPP moves within a 16-lane row (quad
+// swaps, then rotations by 4 and 8 or the half-row mirror), one shuffle
+// across the two rows of a 32-lane group
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (G >= 2) x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+  if constexpr (G >= 4) x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+  if constexpr (G == 8) x += dpp_mov<0x141>(x);  // row_half_mirror
+  if constexpr (G >= 16) {
+    x += dpp_mov<0x124>(x);  // row_ror:4
+    x += dpp_mov<0x128>(x);  // row_ror:8
+  }
+  if constexpr (G >= 32) x += __shfl_xor(x, 16, 64);
+  static_assert(G <= 32, "groups of at most 32 lanes");
+  return x;
 }
 
 template <typename IO, typename GT, int DK, int C, bool CONV>
 __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     PrefillParams p) {
-  using L = PL<IO, DK, C>;
+  using L = PL<IO, DK, C, CONV>;
   using M = Mma<IO>;
   using V4 = Vec4<IO>;
   typedef typename M::frag frag;
@@ -285,6 +326,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
   int *votes = (int *)(sm + L::oVote);
   IO *XksT = (IO *)(sm + L::oKST);  // [DK][LDC], bf16 only
   float *betas = (float *)(sm + L::oBeta);  // [64], token of the chunk
+  f32x4 *taps = (f32x4 *)(sm + (CONV ? L::oTap : 0));  // conv only
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -308,6 +350,12 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     if (wave == 0)
       betas[lane] = GB ? __uint_as_float(st.beta << 16)
                        : __uint_as_float(st.beta);
+    if constexpr (CONV) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        if (tid + PREP_THREADS * r < 2 * DK + Dv)
+          taps[tid + PREP_THREADS * r] = st.tap[r];
+    }
   };
   if (task < ntask) put_beta();
   __syncthreads();
@@ -348,9 +396,12 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
         }
       }
       if (CONV) {
-        float tq[4][4], tk[4][4];
-        load_taps(p.wq + ((size_t)h * DK + c0) * p.cw, p.cw, tq);
-        load_taps(p.wk + ((size_t)h * DK + c0) * p.cw, p.cw, tk);
+        f32x4 tq[4], tk[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          tq[j] = taps[c0 + j];
+          tk[j] = taps[DK + c0 + j];
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           float sq = 0.f, sk = 0.f;
@@ -376,11 +427,8 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
           }
           if (p.l2) {
             // per-token sum over the head: the NQ lanes sharing this token
-#pragma unroll
-            for (int off = NQ / 2; off >= 1; off >>= 1) {
-              sq += __shfl_xor(sq, off, 64);
-              sk += __shfl_xor(sk, off, 64);
-            }
+            sq = group_sum<NQ>(sq);
+            sk = group_sum<NQ>(sk);
             const float iq = 1.f / sqrtf(sq + p.eps);
             const float ik = 1.f / sqrtf(sk + p.eps);
 #pragma unroll
@@ -482,8 +530,9 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
         bvt[i] = ok ? betas[8 * tgv + i] : 0.f;
       }
       if (CONV) {
-        float tv[4][4];
-        load_taps(p.wv + ((size_t)h * Dv + 4 * cv) * p.cw, p.cw, tv);
+        f32x4 tv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tv[j] = taps[2 * DK + 4 * cv + j];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
 #pragma unroll
@@ -955,7 +1004,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
 // ---------------------------------------------------------------------------
 template <typename IO, int DK, int C>
 struct Fits {
-  static constexpr bool value = PL<IO, DK, C>::total <= 160 * 1024;
+  static constexpr bool value = PL<IO, DK, C, true>::total <= 160 * 1024;
 };
 
 static int cu_count() {
