@@ -453,6 +453,12 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
   f32x4 aQ[TW], aK[TW], aW[TW];
 #pragma unroll
   for (int j = 0; j < TW; ++j) aQ[j] = aK[j] = aW[j] = zero;
+  // dgam = rowsum(dS' * S): this thread's share of key row (tid + 256 j) / SV,
+  // summed over the value slabs here and over the SV lanes of a row at the end
+  constexpr int NGA = DK * SV / BWD_THREADS;
+  float dga[NGA];
+#pragma unroll
+  for (int j = 0; j < NGA; ++j) dga[j] = 0.f;
 
   for (int c0 = 0; c0 < Dv; c0 += SV) {
     const int sv = min(SV, Dv - c0);
@@ -481,7 +487,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
       Ss[r * LS + c] = (IO)sv_;
       STs[c * LK + r] = (IO)sv_;
       dSs[r * LS + c] = (IO)dv_;
-      atomicAdd(&dgs[r], sv_ * dv_);  // dgam = rowsum(dS' * S), fp32
+      dga[j] += sv_ * dv_;
     }
 #pragma unroll
     for (int j = 0; j < NO; ++j) {
@@ -529,6 +535,13 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
     }
     __syncthreads();
   }
+  static_assert(SV <= 32 && 64 % SV == 0, "a key row's lanes form a group");
+#pragma unroll
+  for (int j = 0; j < NGA; ++j) {
+    const float x = group_sum<SV>(dga[j]);
+    if (lane % SV == 0) atomicAdd(&dgs[(tid + BWD_THREADS * j) / SV], x);
+  }
+  __syncthreads();
   float *gQ = gs + (size_t)C * Dv, *gK = gQ + (size_t)C * DK;
   float *gW = gK + (size_t)C * DK, *gG = gW + (size_t)C * DK;
 #pragma unroll
@@ -546,6 +559,20 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
     }
   }
   if (tid < DK) gG[tid] = dgs[tid];
+}
+
+// rows r0 .. r0+3 (lane group g of an accumulator tile) += the sums of x[e]
+// over the 16 columns of the tile: reduced across the tile's 16 lanes first,
+// then one LDS atomic per row instead of one per element
+__device__ __forceinline__ void add_rows(float *dst, int r0, const float x[4],
+                                         int m16) {
+  float sum[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) sum[e] = group_sum<16>(x[e]);
+  if (m16 == 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) atomicAdd(&dst[r0 + e], sum[e]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -749,13 +776,15 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
       const int rt = tl % NB, ct = tl / NB;
       f32x4 acc = tile_mma<IO, true, false>(zero, Tm, C, dDs, Dv, 16 * rt,
                                             16 * ct, C, lane);
+      float x[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rt + 4 * g4 + e, j = 16 * ct + m16, t = t0 + r;
         if (t < T)
           ((IO *)bp.dv)[vb + (size_t)t * vrow + j] = from_f32<IO>(bet[r] * acc[e]);
-        atomicAdd(&dB[r], to_f32(vS[r * Dv + j]) * acc[e]);
+        x[e] = to_f32(vS[r * Dv + j]) * acc[e];
       }
+      add_rows(dB, 16 * rt + 4 * g4, x, m16);
     }
     __syncthreads();
   }
@@ -791,12 +820,14 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
       const int rt = tl % NB, it = tl / NB;
       f32x4 acc = tile_mma<IO, true, false>(zero, Tm, C, dWs, DK, 16 * rt,
                                             16 * it, C, lane);
+      float x[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rt + 4 * g4 + e, i = 16 * it + m16;
         gdKd[(size_t)r * DK + i] = bet[r] * acc[e];
-        atomicAdd(&dB[r], to_f32(KdS[r * DK + i]) * acc[e]);
+        x[e] = to_f32(KdS[r * DK + i]) * acc[e];
       }
+      add_rows(dB, 16 * rt + 4 * g4, x, m16);
     }
     __syncthreads();
   }
@@ -815,13 +846,15 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
     const int rt = tl % NB, st = tl / NB;
     f32x4 acc = tile_mma<float, true, false>(zero, Tm, C, Xm, C, 16 * rt,
                                              16 * st, C, lane);
+    float x[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * rt + 4 * g4 + e, s = 16 * st + m16;
       const float dA = s < r ? -acc[e] : 0.f;
-      atomicAdd(&dB[r], dA * Mm[r * C + s]);
+      x[e] = dA * Mm[r * C + s];
       dMm[r * C + s] = bet[r] * dA;  // read only after the next barrier
     }
+    add_rows(dB, 16 * rt + 4 * g4, x, m16);
   }
   __syncthreads();
 

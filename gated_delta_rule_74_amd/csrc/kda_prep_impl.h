@@ -275,28 +275,6 @@ __device__ __forceinline__ void ap_block(int j, int &aa, int &bb) {
   }
 }
 
-// sum over aligned groups of G lanes (G a power of two, at most 32), every
-// lane of a group getting the total: DPP moves within a 16-lane row (quad
-// swaps, then rotations by 4 and 8 or the half-row mirror), one shuffle
-// across the two rows of a 32-lane group
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __int_as_float(
-      __builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-template <int G>
-__device__ __forceinline__ float group_sum(float x) {
-  if constexpr (G >= 2) x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
-  if constexpr (G >= 4) x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
-  if constexpr (G == 8) x += dpp_mov<0x141>(x);  // row_half_mirror
-  if constexpr (G >= 16) {
-    x += dpp_mov<0x124>(x);  // row_ror:4
-    x += dpp_mov<0x128>(x);  // row_ror:8
-  }
-  if constexpr (G >= 32) x += __shfl_xor(x, 16, 64);
-  static_assert(G <= 32, "groups of at most 32 lanes");
-  return x;
-}
 
 template <typename IO, typename GT, int DK, int C, bool CONV>
 __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
