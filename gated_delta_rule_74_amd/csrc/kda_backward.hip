@@ -20,6 +20,45 @@ namespace kda {
 constexpr int BWD_THREADS = 256;
 constexpr int DVMAX_BWD = 128;
 
+// 8 consecutive elements of a row as one 16-byte (bf16) or two 16-byte
+// (fp32) accesses: raw copies between global memory and LDS, and
+// conversions to and from fp32
+template <typename T> struct Row8 {
+  static_assert(sizeof(T) == 2 || sizeof(T) == 4, "bf16 or fp32");
+  static constexpr int NQ = sizeof(T) / 2;  // 16-byte quads per 8 elements
+  uint4 q[NQ];
+  __device__ __forceinline__ void load(const T *p) {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) q[i] = ((const uint4 *)p)[i];
+  }
+  __device__ __forceinline__ void store(T *p) const {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) ((uint4 *)p)[i] = q[i];
+  }
+  __device__ __forceinline__ float get(int e) const {
+    const unsigned w = ((const unsigned *)q)[NQ == 1 ? e / 2 : e];
+    return NQ == 1 ? __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16))
+                   : __uint_as_float(w);
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) q[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+};
+// 8 floats to 8 elements of type T at p (LDS), rounding to nearest even
+template <typename T>
+__device__ __forceinline__ void put8(T *p, const float v[8]) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (bf16)v[e];
+    *(bf16x8 *)p = r;
+  } else {
+    *(f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
+    *(f32x4 *)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  }
+}
+
 // ---------------------------------------------------------------------------
 // helpers: fragment units <-> LDS
 // ---------------------------------------------------------------------------
@@ -628,7 +667,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   constexpr bool GB = sizeof(GT) == 2;
   const PrefillParams &p = bp.f;
   __shared__ __attribute__((aligned(16))) char sm[L::total];
-  float *Mm = (float *)(sm + L::oM), *Tm = (float *)(sm + L::oT);
+  float *Mm = (float *)(sm + L::oM), *TTm = (float *)(sm + L::oT);  // M, T^T
   float *dPm = (float *)(sm + L::odP), *dMm = (float *)(sm + L::odM);
   int *vote = (int *)(sm + L::oVote);
   float *bet = (float *)(sm + L::oBeta), *dB = (float *)(sm + L::odB);
@@ -661,25 +700,42 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
     return GB ? (float)((const bf16 *)p.g)[gi] : ((const float *)p.g)[gi];
   };
   // e for rows beyond the sequence is 1 (as in the forward)
+  // k, q and e = exp(g) of the chunk as [C][DK] rows, 8 channels per lane
   auto load_ke = [&](IO *ks, IO *qs, float *es) {
-    constexpr int NL = C * DK / BWD_THREADS;
-    IO lk[NL], lq[NL];
-    float lg[NL];
+    constexpr int N8 = (C * DK / 8 + BWD_THREADS - 1) / BWD_THREADS;
+    Row8<IO> lk[N8], lq[N8];
+    Row8<GT> lg[N8];
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const int x = tid + BWD_THREADS * j, r = x / DK, i = x % DK;
-      const int t = min(t0 + r, T - 1);
-      lk[j] = ((const IO *)p.k)[kb + (size_t)t * krow + i];
-      lq[j] = qs ? ((const IO *)p.q)[kb + (size_t)t * krow + i] : (IO)0.f;
-      lg[j] = gate_at(t, i);
+    for (int j = 0; j < N8; ++j) {
+      const int x = min(8 * (tid + BWD_THREADS * j), C * DK - 8);
+      const int r = x / DK, i = x % DK, t = min(t0 + r, T - 1);
+      lk[j].load((const IO *)p.k + kb + (size_t)t * krow + i);
+      if (qs) lq[j].load((const IO *)p.q + kb + (size_t)t * krow + i);
+      if (p.gate_head) {
+        // one gate per token: element 0 carries it
+        lg[j].zero();
+        ((GT *)lg[j].q)[0] = ((const GT *)p.g)[bb0 + (size_t)t * H];
+      } else {
+        lg[j].load((const GT *)p.g + kb + (size_t)t * krow + i);
+      }
     }
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const int x = tid + BWD_THREADS * j;
-      const bool ok = t0 + x / DK < T;
-      ks[x] = ok ? lk[j] : (IO)0.f;
-      if (qs) qs[x] = ok ? lq[j] : (IO)0.f;
-      es[x] = ok ? __expf(lg[j]) : 1.f;
+    for (int j = 0; j < N8; ++j) {
+      const int x = 8 * (tid + BWD_THREADS * j);
+      if (x < C * DK) {
+        const bool ok = t0 + x / DK < T;
+        if (!ok) {
+          lk[j].zero();
+          lq[j].zero();
+        }
+        lk[j].store(ks + x);
+        if (qs) lq[j].store(qs + x);
+        float ev[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          ev[e] = ok ? __expf(lg[j].get(p.gate_head ? 0 : e)) : 1.f;
+        put8(es + x, ev);
+      }
     }
   };
 
@@ -701,20 +757,26 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
     // A = diag(beta) M and T^T as the forward's chunk prep left them (only
     // the lower triangles are meaningful)
     const float *at = p.train_at + ((size_t)bh * NC + n) * 2 * C * C;
-    constexpr int NC2 = C * C / BWD_THREADS;
-    float la[NC2], lt[NC2];
+    constexpr int N4 = (C * C / 4 + BWD_THREADS - 1) / BWD_THREADS;
+    f32x4 la[N4], lt[N4];
 #pragma unroll
-    for (int j = 0; j < NC2; ++j) {
-      const int x = tid + BWD_THREADS * j, r = x / C, c = x % C;
-      la[j] = at[x];
-      lt[j] = at[C * C + c * C + r];
+    for (int j = 0; j < N4; ++j) {
+      const int x = min(4 * (tid + BWD_THREADS * j), C * C - 4);
+      la[j] = *(const f32x4 *)(at + x);
+      lt[j] = *(const f32x4 *)(at + C * C + x);
     }
 #pragma unroll
-    for (int j = 0; j < NC2; ++j) {
-      const int x = tid + BWD_THREADS * j, r = x / C, c = x % C;
-      const float br = bet[r];
-      Mm[x] = (c < r && br != 0.f) ? la[j] / br : 0.f;
-      Tm[x] = c <= r ? lt[j] : 0.f;
+    for (int j = 0; j < N4; ++j) {
+      const int x4 = 4 * (tid + BWD_THREADS * j);
+      if (x4 < C * C) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int x = x4 + e, r = x / C, c = x % C;
+          const float br = bet[r];
+          Mm[x] = (c < r && br != 0.f) ? la[j][e] / br : 0.f;
+          TTm[x] = r <= c ? lt[j][e] : 0.f;  // T^T: upper triangle
+        }
+      }
     }
     // rows with beta = 0 (A carries no M there): M directly, with running
     // products of e over (s, r] -- exact, and rare
@@ -744,22 +806,29 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   // ---- phase 3: value side: dT = dDelta (beta V)^T, dv = beta T^T dDelta --
   {
     IO *dDs = (IO *)R, *vS = dDs + C * Dv;
-    constexpr int NV = (C * DVMAX_BWD + BWD_THREADS - 1) / BWD_THREADS;
-    float lv[NV], ld[NV];
+    constexpr int N8 = (C * DVMAX_BWD / 8 + BWD_THREADS - 1) / BWD_THREADS;
+    Row8<IO> lv[N8];
+    Row8<float> ld[N8];
 #pragma unroll
-    for (int jj = 0; jj < NV; ++jj) {
-      const int x = min(tid + BWD_THREADS * jj, C * Dv - 1);
+    for (int jj = 0; jj < N8; ++jj) {
+      const int x = min(8 * (tid + BWD_THREADS * jj), C * Dv - 8);
       const int r = x / Dv, j = x % Dv, t = min(t0 + r, T - 1);
-      lv[jj] = to_f32(((const IO *)p.v)[vb + (size_t)t * vrow + j]);
-      ld[jj] = bp.dD[vb + (size_t)t * vrow + j];
+      lv[jj].load((const IO *)p.v + vb + (size_t)t * vrow + j);
+      ld[jj].load(bp.dD + vb + (size_t)t * vrow + j);
     }
 #pragma unroll
-    for (int jj = 0; jj < NV; ++jj) {
-      const int x = tid + BWD_THREADS * jj;
+    for (int jj = 0; jj < N8; ++jj) {
+      const int x = 8 * (tid + BWD_THREADS * jj);
       if (x < C * Dv) {
-        const bool ok = t0 + x / Dv < T;
-        dDs[x] = (IO)(ok ? ld[jj] : 0.f);
-        vS[x] = (IO)(ok ? lv[jj] : 0.f);
+        if (t0 + x / Dv >= T) {
+          lv[jj].zero();
+          ld[jj].zero();
+        }
+        float d8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d8[e] = ld[jj].get(e);
+        put8(dDs + x, d8);
+        lv[jj].store(vS + x);
       }
     }
     __syncthreads();
@@ -774,7 +843,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
     }
     for (int tl = wave; tl < NB * nvt; tl += 4) {
       const int rt = tl % NB, ct = tl / NB;
-      f32x4 acc = tile_mma<IO, true, false>(zero, Tm, C, dDs, Dv, 16 * rt,
+      f32x4 acc = tile_mma<IO, false, false>(zero, TTm, C, dDs, Dv, 16 * rt,
                                             16 * ct, C, lane);
       float x[4];
 #pragma unroll
@@ -792,19 +861,27 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   // ---- phase 4: key side: dT += dW (beta Kd)^T, dKd = beta T^T dW ---------
   {
     IO *dWs = (IO *)R, *KdS = dWs + C * DK;
-    constexpr int NK = C * DK / BWD_THREADS;
-    float lw[NK], lk[NK];
+    constexpr int N8 = (C * DK / 8 + BWD_THREADS - 1) / BWD_THREADS;
+    Row8<float> lw[N8], lk[N8];
 #pragma unroll
-    for (int j = 0; j < NK; ++j) {
-      const int x = tid + BWD_THREADS * j;
-      lw[j] = gW[x];
-      lk[j] = gKd[x];
+    for (int j = 0; j < N8; ++j) {
+      const int x = min(8 * (tid + BWD_THREADS * j), C * DK - 8);
+      lw[j].load(gW + x);
+      lk[j].load(gKd + x);
     }
 #pragma unroll
-    for (int j = 0; j < NK; ++j) {
-      const int x = tid + BWD_THREADS * j;
-      dWs[x] = (IO)lw[j];
-      KdS[x] = (IO)lk[j];
+    for (int j = 0; j < N8; ++j) {
+      const int x = 8 * (tid + BWD_THREADS * j);
+      if (x < C * DK) {
+        float w8[8], k8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          w8[e] = lw[j].get(e);
+          k8[e] = lk[j].get(e);
+        }
+        put8(dWs + x, w8);
+        put8(KdS + x, k8);
+      }
     }
     __syncthreads();
     for (int tl = wave; tl < NB * NB; tl += 4) {
@@ -818,7 +895,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
     }
     for (int tl = wave; tl < NB * NKT; tl += 4) {
       const int rt = tl % NB, it = tl / NB;
-      f32x4 acc = tile_mma<IO, true, false>(zero, Tm, C, dWs, DK, 16 * rt,
+      f32x4 acc = tile_mma<IO, false, false>(zero, TTm, C, dWs, DK, 16 * rt,
                                             16 * it, C, lane);
       float x[4];
 #pragma unroll
@@ -835,7 +912,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   // ---- phase 5: dA = -T^T dT T^T (strictly lower); dM = beta dA ------------
   for (int tl = wave; tl < NB * NB; tl += 4) {
     const int rt = tl % NB, st = tl / NB;
-    f32x4 acc = tile_mma<float, false, true>(zero, dMm, C, Tm, C, 16 * rt,
+    f32x4 acc = tile_mma<float, false, false>(zero, dMm, C, TTm, C, 16 * rt,
                                              16 * st, C, lane);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -844,7 +921,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   __syncthreads();
   for (int tl = wave; tl < NB * NB; tl += 4) {
     const int rt = tl % NB, st = tl / NB;
-    f32x4 acc = tile_mma<float, true, false>(zero, Tm, C, Xm, C, 16 * rt,
+    f32x4 acc = tile_mma<float, false, false>(zero, TTm, C, Xm, C, 16 * rt,
                                              16 * st, C, lane);
     float x[4];
 #pragma unroll
@@ -861,22 +938,26 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   // ---- phase 6: dPm = scale tril(dO Delta^T) --------------------------------
   {
     IO *Os = (IO *)R, *Ds = Os + C * Dv;
-    constexpr int NV = (C * DVMAX_BWD + BWD_THREADS - 1) / BWD_THREADS;
-    IO lo[NV];
-    float ld[NV];
+    constexpr int N8 = (C * DVMAX_BWD / 8 + BWD_THREADS - 1) / BWD_THREADS;
+    Row8<IO> lo[N8];
+    Row8<float> ld[N8];
 #pragma unroll
-    for (int jj = 0; jj < NV; ++jj) {
-      const int x = min(tid + BWD_THREADS * jj, C * Dv - 1);
+    for (int jj = 0; jj < N8; ++jj) {
+      const int x = min(8 * (tid + BWD_THREADS * jj), C * Dv - 8);
       const int r = x / Dv, j = x % Dv, t = min(t0 + r, T - 1);
-      lo[jj] = ((const IO *)bp.dO)[vb + (size_t)t * vrow + j];
-      ld[jj] = gD[x];
+      lo[jj].load((const IO *)bp.dO + vb + (size_t)t * vrow + j);
+      ld[jj].load(gD + x);
     }
 #pragma unroll
-    for (int jj = 0; jj < NV; ++jj) {
-      const int x = tid + BWD_THREADS * jj;
+    for (int jj = 0; jj < N8; ++jj) {
+      const int x = 8 * (tid + BWD_THREADS * jj);
       if (x < C * Dv) {
-        Os[x] = t0 + x / Dv < T ? lo[jj] : (IO)0.f;
-        Ds[x] = (IO)ld[jj];
+        if (t0 + x / Dv >= T) lo[jj].zero();
+        lo[jj].store(Os + x);
+        float d8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d8[e] = ld[jj].get(e);
+        put8(Ds + x, d8);
       }
     }
     __syncthreads();
@@ -903,7 +984,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   // per 16-token sub-chunk and channel: sigma (exclusive suffix product),
   // rho (inclusive prefix, over e in place) and the sub-chunk product F;
   // a vote records any rho below 2^-64 (diagonal ratios then unsafe)
-  float *Fs = Mm, *Mid = Tm;  // [NB][DK], [pairs a-b >= 2][DK]
+  float *Fs = Mm, *Mid = TTm;  // [NB][DK], [pairs a-b >= 2][DK]
   for (int w = tid; w < NB * DK; w += BWD_THREADS) {
     const int a = w / DK, i = w % DK;
     float P = 1.f;
