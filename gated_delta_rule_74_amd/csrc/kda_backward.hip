@@ -492,48 +492,67 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
   f32x4 aQ[TW], aK[TW], aW[TW];
 #pragma unroll
   for (int j = 0; j < TW; ++j) aQ[j] = aK[j] = aW[j] = zero;
-  // dgam = rowsum(dS' * S): this thread's share of key row (tid + 256 j) / SV,
-  // summed over the value slabs here and over the SV lanes of a row at the end
-  constexpr int NGA = DK * SV / BWD_THREADS;
+  // dgam = rowsum(dS' * S): this thread's 8 columns of key row
+  // 8 (tid + 256 j) / SV, summed over the value slabs here and over the SV / 8
+  // lanes of a row at the end
+  constexpr int NGA = (DK * SV / 8 + BWD_THREADS - 1) / BWD_THREADS;
   float dga[NGA];
 #pragma unroll
   for (int j = 0; j < NGA; ++j) dga[j] = 0.f;
 
   for (int c0 = 0; c0 < Dv; c0 += SV) {
     const int sv = min(SV, Dv - c0);
-    // all loads first (clamped addresses, branch-free), then the LDS stores
-    constexpr int NA = DK * SV / BWD_THREADS, NO = C * SV / BWD_THREADS;
-    float la[NA], lb[NA], lo[NO], ld[NO];
+    // all loads first (clamped addresses, branch-free), then the LDS
+    // stores; 8 columns of a row per lane (sv is a multiple of 16)
+    constexpr int NO8 = (C * SV / 8 + BWD_THREADS - 1) / BWD_THREADS;
+    Row8<float> la[NGA], lb[NGA], ld[NO8];
+    Row8<IO> lo[NO8];
 #pragma unroll
-    for (int j = 0; j < NA; ++j) {
-      const int i = tid + BWD_THREADS * j, r = i / SV, c = min(i % SV, sv - 1);
-      la[j] = S[(size_t)r * Dv + c0 + c];
-      lb[j] = dS[(size_t)r * Dv + c0 + c];
+    for (int j = 0; j < NGA; ++j) {
+      const int i = min(8 * (tid + BWD_THREADS * j), DK * SV - 8);
+      const int r = i / SV, c = min(i % SV, sv - 8);
+      la[j].load(S + (size_t)r * Dv + c0 + c);
+      lb[j].load(dS + (size_t)r * Dv + c0 + c);
     }
 #pragma unroll
-    for (int j = 0; j < NO; ++j) {
-      const int i = tid + BWD_THREADS * j, r = i / SV, c = min(i % SV, sv - 1);
-      const int t = min(t0 + r, T - 1);
+    for (int j = 0; j < NO8; ++j) {
+      const int i = min(8 * (tid + BWD_THREADS * j), C * SV - 8);
+      const int r = i / SV, c = min(i % SV, sv - 8), t = min(t0 + r, T - 1);
       const size_t gi = ((size_t)b * T + t) * orow + (size_t)h * Dv + c0 + c;
-      lo[j] = to_f32(((const IO *)bp.dO)[gi]);
-      ld[j] = bp.dD[gi];
+      lo[j].load((const IO *)bp.dO + gi);
+      ld[j].load(bp.dD + gi);
     }
 #pragma unroll
-    for (int j = 0; j < NA; ++j) {
-      const int i = tid + BWD_THREADS * j, r = i / SV, c = i % SV;
-      const bool ok = c < sv;
-      const float sv_ = ok ? la[j] : 0.f, dv_ = ok ? lb[j] : 0.f;
-      Ss[r * LS + c] = (IO)sv_;
-      STs[c * LK + r] = (IO)sv_;
-      dSs[r * LS + c] = (IO)dv_;
-      dga[j] += sv_ * dv_;
+    for (int j = 0; j < NGA; ++j) {
+      const int i = 8 * (tid + BWD_THREADS * j), r = i / SV, c = i % SV;
+      if (i < DK * SV) {
+        const bool ok = c < sv;
+        float s8[8], d8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          s8[e] = ok ? la[j].get(e) : 0.f;
+          d8[e] = ok ? lb[j].get(e) : 0.f;
+          dga[j] += s8[e] * d8[e];
+          STs[(c + e) * LK + r] = (IO)s8[e];
+        }
+        put8(Ss + r * LS + c, s8);
+        put8(dSs + r * LS + c, d8);
+      }
     }
 #pragma unroll
-    for (int j = 0; j < NO; ++j) {
-      const int i = tid + BWD_THREADS * j, r = i / SV, c = i % SV;
-      const bool ok = c < sv && t0 + r < T;
-      Os[r * LS + c] = (IO)(ok ? lo[j] : 0.f);
-      dDs[r * LS + c] = (IO)(ok ? ld[j] : 0.f);
+    for (int j = 0; j < NO8; ++j) {
+      const int i = 8 * (tid + BWD_THREADS * j), r = i / SV, c = i % SV;
+      if (i < C * SV) {
+        const bool ok = c < sv && t0 + r < T;
+        float o8[8], d8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          o8[e] = ok ? lo[j].get(e) : 0.f;
+          d8[e] = ok ? ld[j].get(e) : 0.f;
+        }
+        put8(Os + r * LS + c, o8);
+        put8(dDs + r * LS + c, d8);
+      }
     }
     __syncthreads();
     // Delta = U - W S on this slab (U in accumulator tiles [vt][rt])
@@ -574,11 +593,13 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
     }
     __syncthreads();
   }
-  static_assert(SV <= 32 && 64 % SV == 0, "a key row's lanes form a group");
+  static_assert(SV % 8 == 0 && SV / 8 <= 32 && 64 % (SV / 8) == 0,
+                "a key row's lanes form a group");
 #pragma unroll
   for (int j = 0; j < NGA; ++j) {
-    const float x = group_sum<SV>(dga[j]);
-    if (lane % SV == 0) atomicAdd(&dgs[(tid + BWD_THREADS * j) / SV], x);
+    const float x = group_sum<SV / 8>(dga[j]);
+    const int i = 8 * (tid + BWD_THREADS * j);
+    if (lane % (SV / 8) == 0 && i < DK * SV) atomicAdd(&dgs[i / SV], x);
   }
   __syncthreads();
   float *gQ = gs + (size_t)C * Dv, *gK = gQ + (size_t)C * DK;
