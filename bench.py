@@ -453,6 +453,23 @@ def main():
         log(f"copy: 1 GiB in {ms:.3f} ms, {2 * n / (ms * 1e-3) / 1e9:.0f} "
             "GB/s read+write")
         del a, b2
+        # the decode state's traffic shape with next to no arithmetic: 512 MiB
+        # fp32 scaled in place by torch's elementwise kernel (a practical
+        # ceiling for a streaming read-modify-write on this part)
+        sref = torch.ones(1 << 27, dtype=torch.float32, device=dev)
+        settle(lambda: sref.mul_(0.999))
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(20):
+            sref.mul_(0.999)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms2 = e0.elapsed_time(e1) / 20
+        out["copy"]["inplace_scale_512mib"] = dict(
+            ms=ms2, gbs=2 * sref.numel() * 4 / (ms2 * 1e-3) / 1e9)
+        log(f"in-place scale of 512 MiB fp32: {ms2:.3f} ms, "
+            f"{2 * sref.numel() * 4 / (ms2 * 1e-3) / 1e9:.0f} GB/s read+write")
+        del sref
 
     pf = out.get("prefill")
     line = {
