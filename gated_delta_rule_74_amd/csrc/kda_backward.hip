@@ -1216,14 +1216,27 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
         float dgv = aG_[jt][a][e];
         if (r == C - 1) dgv += dGl[ib];  // sum_r dKtil*Ktil (d log gam)
         dGs[r * DK + ib] = dgv;
-        if (t < T) {
-          const size_t o = kb + (size_t)t * krow + ib;
-          ((IO *)bp.dq)[o] = from_f32<IO>(aQ_[jt][a][e]);
-          ((IO *)bp.dk)[o] = from_f32<IO>(aK_[jt][a][e]);
-        }
+        // dq, dk staged as [C][DK] rows where k and q were (read no more)
+        ks[r * DK + ib] = from_f32<IO>(aQ_[jt][a][e]);
+        qs[r * DK + ib] = from_f32<IO>(aK_[jt][a][e]);
+        (void)t;
       }
   }
   __syncthreads();
+  // rows of dq and dk out, 8 channels per lane
+  constexpr int NO8 = (C * DK / 8 + BWD_THREADS - 1) / BWD_THREADS;
+#pragma unroll
+  for (int j = 0; j < NO8; ++j) {
+    const int x = 8 * (tid + BWD_THREADS * j), r = x / DK, i = x % DK;
+    if (x < C * DK && t0 + r < T) {
+      const size_t o = kb + (size_t)(t0 + r) * krow + i;
+      Row8<IO> a8, b8;
+      a8.load(ks + x);
+      b8.load(qs + x);
+      a8.store((IO *)bp.dq + o);
+      b8.store((IO *)bp.dk + o);
+    }
+  }
   {
     const int i = oi, R0 = orh * RP;
     float own = 0.f;
@@ -1235,14 +1248,32 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
     for (int j = RP - 1; j >= 0; --j) {
       const int r = R0 + j, t = t0 + r;
       acc += dGs[r * DK + i];
-      if (t < T) {
-        if (p.gate_head)
-          atomicAdd(&dgh[r], acc);
-        else
-          ((GT *)bp.dg)[kb + (size_t)t * krow + i] = (GT)acc;
-      }
+      dGs[r * DK + i] = acc;  // this thread's own (r, i): read just above
+      if (t < T && p.gate_head) atomicAdd(&dgh[r], acc);
     }
     __syncthreads();
+    if (!p.gate_head) {
+      // rows of dg out, 8 channels per lane
+#pragma unroll
+      for (int j = 0; j < NO8; ++j) {
+        const int x = 8 * (tid + BWD_THREADS * j), r = x / DK, ii = x % DK;
+        if (x < C * DK && t0 + r < T) {
+          float v8[8];
+          *(f32x4 *)v8 = *(const f32x4 *)(dGs + x);
+          *(f32x4 *)(v8 + 4) = *(const f32x4 *)(dGs + x + 4);
+          GT *dst = (GT *)bp.dg + kb + (size_t)(t0 + r) * krow + ii;
+          if constexpr (sizeof(GT) == 2) {
+            bf16x8 h8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h8[e] = (bf16)v8[e];
+            *(bf16x8 *)dst = h8;
+          } else {
+            *(f32x4 *)dst = *(const f32x4 *)v8;
+            *(f32x4 *)(dst + 4) = *(const f32x4 *)(v8 + 4);
+          }
+        }
+      }
+    }
     for (int r = tid; r < C; r += BWD_THREADS) {
       const int t = t0 + r;
       if (t < T) {
