@@ -255,11 +255,11 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_state(BwdParams bp) {
   constexpr int NUP = (NB * NTU * 64 + BWD_THREADS - 1) / BWD_THREADS;
   constexpr int NUK = (NKT * NTU * 64 + BWD_THREADS - 1) / BWD_THREADS;
   constexpr int NUQ = (NB * NKU * 64 + BWD_THREADS - 1) / BWD_THREADS;
-  constexpr int NOV = (16 * C + BWD_THREADS - 1) / BWD_THREADS;
+  static_assert(2 * C <= BWD_THREADS, "two lanes per token of the chunk");
   UnitStage<IO, NUP> stP;
   UnitStage<IO, NUK> stK;
   UnitStage<IO, NUQ> stQ, stW;
-  IO ov[NOV];
+  Row8<IO> ov;  // lanes 2r, 2r + 1: token r, value columns 8 (tid & 1) + 0..7
   float gv = 0.f;
   auto fetch = [&](int n) {
     const char *blk = p.ws + ((size_t)bh * NC + n) * p.wsb;
@@ -267,14 +267,11 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_state(BwdParams bp) {
     stK.fetch(blk + W.off_ktt, NKT, NTU, false, tid);
     stQ.fetch(blk + W.off_qt, NB, NKU, false, tid);
     stW.fetch(blk + W.off_negw, NB, NKU, false, tid);
-#pragma unroll
-    for (int j = 0; j < NOV; ++j) {
-      const int i = tid + BWD_THREADS * j;
-      const int r = i % C, t = n * C + r;
-      ov[j] = (i < 16 * C && t < T)
-                  ? ((const IO *)bp.dO)[((size_t)b * T + t) * orow +
-                                        (size_t)h * Dv + 16 * vt + i / C]
-                  : (IO)0.f;
+    if (tid < 2 * C) {
+      const int r = tid >> 1, t = min(n * C + r, T - 1);
+      ov.load((const IO *)bp.dO + ((size_t)b * T + t) * orow + (size_t)h * Dv +
+              16 * vt + 8 * (tid & 1));
+      if (n * C + r >= T) ov.zero();
     }
     if (tid < DK) gv = ((const float *)(blk + W.off_gam))[tid];
   };
@@ -287,10 +284,12 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_state(BwdParams bp) {
     stK.store_t(NKT, NTU, C, KK, LDK, tid);
     stQ.store_t(NB, NKU, DK, QT, LDC, tid);
     stW.store_t(NB, NKU, DK, WT, LDC, tid);
+    if (tid < 2 * C) {
+      // dO slab transposed: OT[value column][token]
+      const int r = tid >> 1, c0 = 8 * (tid & 1);
 #pragma unroll
-    for (int j = 0; j < NOV; ++j) {
-      const int i = tid + BWD_THREADS * j;
-      if (i < 16 * C) OT[(i / C) * LDC + i % C] = ov[j];
+      for (int e = 0; e < 8; ++e)
+        OT[(c0 + e) * LDC + r] = from_f32<IO>(ov.get(e));
     }
     if (tid < DK) Gm[tid] = gv;
     __syncthreads();
