@@ -1,4 +1,5 @@
-// kda_prep.hip -- chunk-local factors of the chunked KDA prefill (gfx950).
+// kda_prep_impl.h -- chunk-local factors of the chunked KDA prefill (gfx950),
+// instantiated per dtype pair by the kda_prep_*.hip files.
 //
 // Method (per head; see include/kda.h for the sources).  The token rule
 //   S' = diag(e_t) S,  e_t = exp(g_t);  S_t = S' + k_t (beta_t (v_t - S'^T k_t))^T;
@@ -25,11 +26,15 @@
 //
 // Execution: a persistent grid (one workgroup of 256 threads per CU) walks
 // the (batch*head, chunk) tasks, last chunk first: the state pass reads the
-// chunks in order right afterwards, so its early chunks are the most recently
-// written ones and tend to still sit in the memory-side cache.  Thread t owns 4 consecutive key channels x
-// 8 consecutive tokens of a task; its raw inputs are fetched with 8/16-byte
-// vector loads into registers one task ahead, so the fetch of task i+1
-// overlaps the matrix-core phases of task i.
+// chunks in order right afterwards, so its early chunks are the most
+// recently written ones and tend to still sit in the memory-side cache.
+// Thread t owns 4 consecutive key channels x 8 consecutive tokens of a task;
+// its raw inputs are fetched with 8/16-byte vector loads into registers one
+// task ahead, so the fetch of task i+1 overlaps the matrix-core phases of
+// task i.  The chunk's betas (and, with the conv, the head's taps) are
+// fetched the same way by a few lanes and handed to every thread through
+// LDS.  Inputs (read once) and the workspace (written once) use streaming
+// accesses, which keeps the L2 free of dirty lines for the state pass.
 #pragma once
 #include "kda_device.h"
 #include "kda_internal.h"
