@@ -185,6 +185,48 @@ def test_conv_prefill_b8_t4096(orc, kda):
         assert eo <= 2e-2 and es <= 2e-2
 
 
+CONV_CASES = [("bf16", 128, 128, 2, 64), ("bf16", 64, 128, 3, 64),
+              ("bf16", 128, 32, 4, 32), ("bf16", 32, 32, 3, 16),
+              ("f32", 32, 16, 2, 32), ("f32", 16, 64, 3, 16),
+              ("f32", 64, 64, 4, 64)]
+
+
+@pytest.mark.parametrize("qkv,Dk,Dv,W,C", CONV_CASES)
+def test_conv_prefill_widths(orc, kda, qkv, Dk, Dv, W, C):
+    """Fused conv prologue at every supported width, with d_k != d_v (the
+    value taps then cover a different channel range than the key taps)."""
+    say(f"conv prefill qkv={qkv} Dk={Dk} Dv={Dv} W={W} C={C}")
+    x = ki.prefill_inputs(2, 3 * C + 11, 3, Dk, Dv, qkv=qkv, conv_width=W,
+                          seed=23 + W + Dk + C, device="cuda")
+    conv = dict(xq=x["xq"], xk=x["xk"], xv=x["xv"], wq=x["wq"], wk=x["wk"],
+                wv=x["wv"], width=W, l2norm_qk=True, eps=1e-6)
+    o, s = _run(kda, x, C, conv=conv)
+    sub = dict(xq=x["xq"], xk=x["xk"], xv=x["xv"], wq=x["wq"], wk=x["wk"],
+               wv=x["wv"], eps=1e-6, l2norm_qk=True)
+    ro, rs = orc.prefill(None, None, None, x["g"], x["beta"], conv=sub)
+    eo, es = rel_err(o, ro), rel_err(s, rs)
+    say(f"  err o={eo:.2e} S={es:.2e}")
+    assert eo <= TOL[qkv] and es <= TOL[qkv]
+
+
+@pytest.mark.parametrize("qkv,D,C", [("bf16", 128, 64), ("f32", 32, 32),
+                                     ("bf16", 64, 16)])
+@pytest.mark.parametrize("tk", ["1", "5", "C-1", "C", "C+1"])
+def test_prefill_short_sequences(orc, kda, qkv, D, C, tk):
+    """Sequences shorter than, equal to and one past a chunk: one partly
+    filled chunk, one full chunk, a full chunk and a one-token tail."""
+    T = {"1": 1, "5": 5, "C-1": C - 1, "C": C, "C+1": C + 1}[tk]
+    say(f"prefill short qkv={qkv} D={D} C={C} T={T}")
+    x = ki.prefill_inputs(2, T, 3, D, D, qkv=qkv, seed=31 + T + D,
+                          device="cuda", with_s0=True)
+    o, s = _run(kda, x, C, scale=0.8, s0=x["s0"])
+    ro, rs = orc.recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"],
+                            x["s0"], 0.8)
+    eo, es = rel_err(o, ro), rel_err(s, rs)
+    say(f"  err o={eo:.2e} S={es:.2e}")
+    assert eo <= TOL[qkv] and es <= TOL[qkv]
+
+
 def test_long_context_prefill_t262144(orc, kda):
     c = ki.CONFIGS[4]
     say("long-context prefill B1 T262144 H32 D128 C64 (sampled heads)")
