@@ -110,9 +110,9 @@ def main():
     sel = lambda part: (only is None and part != "copy") or \
         (only is not None and part in only)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for "
-              f"--gpus {args.gpus}); the multi-GPU design is described in "
-              "DESIGN.md but not built.", file=sys.stderr)
+        print(f"bench.py: the KDA library runs on one GPU (asked for "
+              f"--gpus {args.gpus}); a head-split multi-GPU path is not "
+              "implemented.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -141,12 +141,12 @@ def main():
             torch.cuda.synchronize()
 
     # ---------------- prefill, model-shaped (headline) ----------------------
-    c1 = ki.CONFIGS[1]
+    c1 = ki.workload(ki.PREFILL)
     B, T, H, Dk, Dv, C = (c1[n] for n in ("B", "T", "H", "Dk", "Dv", "chunk"))
     run_prefill = sel("prefill")
     if run_prefill:
         log("prefill: generating inputs")
-        x = ki.config_prefill_inputs(1, device=dev)
+        x = ki.workload_prefill_inputs(ki.PREFILL, device=dev)
         ws = kda.alloc_workspace(B, T, H, Dk, Dv, C, torch.bfloat16, dev)
         o = torch.empty((B, T, H, Dv), dtype=torch.bfloat16, device=dev)
         s = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
@@ -227,7 +227,7 @@ def main():
         torch.cuda.empty_cache()
 
     # ---------------- decode workload ---------------------------------------
-    c3 = ki.CONFIGS[3]
+    c3 = ki.workload(ki.DECODE)
     N, H3, D3, steps = c3["N"], c3["H"], c3["Dk"], c3["steps"]
     if args.decode_steps:
         steps = max(1, min(steps, args.decode_steps))
@@ -340,10 +340,11 @@ def main():
 
     # ---------------- fused-conv prefill and long context -------------------
     extra = {}
-    for cid, tag in ((2, "conv"), (4, "long"), (1, "gdn")):
+    for wl, tag in ((ki.CONV_PREFILL, "conv"), (ki.LONG, "long"),
+                    (ki.PREFILL, "gdn")):
         if args.no_extra or not sel(tag):
             continue
-        c = ki.CONFIGS[cid]
+        c = ki.workload(wl)
         log(f"{tag}: generating inputs")
         if tag == "gdn":
             # the headline shape with one gate per token-head (the Gated
@@ -353,7 +354,7 @@ def main():
                                   seed=ki.SEED_BASE + 11, device=dev,
                                   gate_per_head=True)
         else:
-            x = ki.config_prefill_inputs(cid, device=dev)
+            x = ki.workload_prefill_inputs(wl, device=dev)
         Bc, Tc, Hc, Dc, Cc = c["B"], c["T"], c["H"], c["Dk"], c["chunk"]
         conv = None
         if c["conv_width"]:
@@ -369,7 +370,7 @@ def main():
         settle(f)
         f()
         torch.cuda.synchronize()
-        reps = 5 if cid == 2 else 3
+        reps = 5 if wl == ki.CONV_PREFILL else 3
         e0, e1 = ev(), ev()
         e0.record(stream)
         for _ in range(reps):
@@ -395,10 +396,10 @@ def main():
 
     # ---------------- backward of the headline prefill ---------------------
     if sel("bwd") and not args.no_extra:
-        c = ki.CONFIGS[1]
+        c = ki.workload(ki.PREFILL)
         Bc, Tc, Hc, Dc, Cc = c["B"], c["T"], c["H"], c["Dk"], c["chunk"]
         log("bwd: generating inputs")
-        x = ki.config_prefill_inputs(1, device=dev)
+        x = ki.workload_prefill_inputs(ki.PREFILL, device=dev)
         gen = torch.Generator(device=dev).manual_seed(7)
         do = torch.randn((Bc, Tc, Hc, Dc), generator=gen,
                          device=dev).to(torch.bfloat16)
@@ -486,7 +487,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; shapes and distributions of the "
                 "KDA workloads)",
-        "config": {"workload": ki.CONFIGS[1]["name"], "B": B, "T": T, "H": H,
+        "config": {"workload": ki.PREFILL, "B": B, "T": T, "H": H,
                    "d_k": Dk, "d_v": Dv, "chunk": C, "qkv": "bf16",
                    "gate": "f32", "state": "f32"},
         "roofline": pf["roofline"] if pf else None,

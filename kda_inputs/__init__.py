@@ -13,15 +13,19 @@ re-drawn on its own.  Values are drawn in fp32, shaped, then rounded
 (round-to-nearest-even) to the stored dtype; consumers that need the oracle's
 view upcast those stored values exactly.
 
-Workloads (shapes from the KDA deployment the pages describe: 32 linear-
-attention heads, head dim 128, kernel-4 conv, 8K pretraining context, 262,144
-served context; decode batch 256):
+Workloads, by name (shapes from the KDA deployment the pages describe: 32
+linear-attention heads, head dim 128, kernel-4 conv, 8K pretraining context,
+262,144 served context; decode batch 256):
 
-  0  tiny fp32 prefill      B1 T64 H2 D16 C16, all fp32
-  1  model-shaped prefill   B1 T8192 H32 D128 C64, bf16 q/k/v, fp32 g/beta
-  2  prefill + conv prologue B8 T4096 H32 D128 C64, raw x over 4096 channels
-  3  decode step            N256 H32 D128, fp32 state, bf16 inputs, 1000 steps
-  4  long-context prefill   B1 T262144 H32 D128 C64, slow forgetting
+  TINY          tiny fp32 prefill       B1 T64 H2 D16 C16, all fp32
+  PREFILL       model-shaped prefill    B1 T8192 H32 D128 C64, bf16 q/k/v,
+                                        fp32 g/beta
+  CONV_PREFILL  prefill + conv prologue B8 T4096 H32 D128 C64, raw x over
+                                        4096 channels
+  DECODE        decode step             N256 H32 D128, fp32 state, bf16
+                                        inputs, 1000 steps
+  LONG          long-context prefill    B1 T262144 H32 D128 C64, slow
+                                        forgetting
 """
 from __future__ import annotations
 
@@ -32,25 +36,37 @@ import torch.nn.functional as F
 
 BLOCK = 4096  # tokens per independently seeded block
 
-CONFIGS = {
-    0: dict(name="kda_prefill_tiny_fp32", kind="prefill", B=1, T=64, H=2,
-            Dk=16, Dv=16, chunk=16, qkv="f32", gate="f32", gate_kind="softplus",
-            conv_width=0),
-    1: dict(name="kda_prefill_b1_t8192_h32_d128", kind="prefill", B=1,
-            T=8192, H=32, Dk=128, Dv=128, chunk=64, qkv="bf16", gate="f32",
-            gate_kind="softplus", conv_width=0),
-    2: dict(name="kda_prefill_conv4_b8_t4096_h32_d128", kind="prefill", B=8,
-            T=4096, H=32, Dk=128, Dv=128, chunk=64, qkv="bf16", gate="f32",
-            gate_kind="softplus", conv_width=4),
-    3: dict(name="kda_decode_n256_h32_d128_x1000", kind="decode", N=256,
-            H=32, Dk=128, Dv=128, steps=1000, qkv="bf16", gate="bf16",
-            state_std=0.1),
-    4: dict(name="kda_prefill_b1_t262144_h32_d128", kind="prefill", B=1,
-            T=262144, H=32, Dk=128, Dv=128, chunk=64, qkv="bf16", gate="f32",
-            gate_kind="slow", conv_width=0),
+SEED_BASE = 7400
+
+TINY = "kda_prefill_tiny_fp32"
+PREFILL = "kda_prefill_b1_t8192_h32_d128"
+CONV_PREFILL = "kda_prefill_conv4_b8_t4096_h32_d128"
+DECODE = "kda_decode_n256_h32_d128_x1000"
+LONG = "kda_prefill_b1_t262144_h32_d128"
+
+# each workload draws from its own seed
+WORKLOADS = {
+    TINY: dict(kind="prefill", seed=SEED_BASE + 0, B=1, T=64, H=2, Dk=16,
+               Dv=16, chunk=16, qkv="f32", gate="f32", gate_kind="softplus",
+               conv_width=0),
+    PREFILL: dict(kind="prefill", seed=SEED_BASE + 1, B=1, T=8192, H=32,
+                  Dk=128, Dv=128, chunk=64, qkv="bf16", gate="f32",
+                  gate_kind="softplus", conv_width=0),
+    CONV_PREFILL: dict(kind="prefill", seed=SEED_BASE + 2, B=8, T=4096, H=32,
+                       Dk=128, Dv=128, chunk=64, qkv="bf16", gate="f32",
+                       gate_kind="softplus", conv_width=4),
+    DECODE: dict(kind="decode", seed=SEED_BASE + 3, N=256, H=32, Dk=128,
+                 Dv=128, steps=1000, qkv="bf16", gate="bf16", state_std=0.1),
+    LONG: dict(kind="prefill", seed=SEED_BASE + 4, B=1, T=262144, H=32,
+               Dk=128, Dv=128, chunk=64, qkv="bf16", gate="f32",
+               gate_kind="slow", conv_width=0),
 }
 
-SEED_BASE = 7400
+
+def workload(name: str) -> dict:
+    """The workload's parameters (a copy), with its name."""
+    return dict(WORKLOADS[name], name=name)
+
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -134,25 +150,28 @@ def prefill_inputs(B, T, H, Dk, Dv, qkv="bf16", gate="f32",
     return out
 
 
-def config_prefill_inputs(cfg_id: int, device="cpu", seed=None, **over):
-    c = dict(CONFIGS[cfg_id])
+def workload_prefill_inputs(name: str, device="cpu", seed=None, **over):
+    """The named prefill workload's inputs (fields in `over` replace the
+    workload's own)."""
+    c = workload(name)
     c.update(over)
     return prefill_inputs(c["B"], c["T"], c["H"], c["Dk"], c["Dv"],
                           qkv=c["qkv"], gate=c["gate"],
                           gate_kind=c["gate_kind"],
                           conv_width=c["conv_width"],
-                          seed=SEED_BASE + cfg_id if seed is None else seed,
+                          seed=c["seed"] if seed is None else seed,
                           device=device)
 
 
-def decode_state(N, H, Dk, Dv, std=0.1, seed=SEED_BASE + 3, device="cpu"):
+def decode_state(N, H, Dk, Dv, std=0.1, seed=WORKLOADS[DECODE]["seed"], device="cpu"):
     """Initial decode state, fp32 N(0, std^2) ('N(0,0.01)' read as variance
     0.01, std 0.1), layout [N,H,Dk,Dv]."""
     return std * _randn((N, H, Dk, Dv), device, seed, _ID["state"])
 
 
 def decode_step_inputs(N, H, Dk, Dv, step, qkv="bf16", gate="bf16",
-                       seed=SEED_BASE + 3, device="cpu", gate_per_head=False,
+                       seed=WORKLOADS[DECODE]["seed"], device="cpu",
+                       gate_per_head=False,
                        beta_max=1.0):
     """Fresh single-token inputs for decode step `step`, distributed as the
     tiny workload: q,k unit per head, v ~ N(0,1), g = -softplus(N(0,1)),

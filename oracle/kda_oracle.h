@@ -27,7 +27,7 @@
  *            check these three places before fine-tuning" (Chinese) -- the
  *            config-validation list: conv kernel >= 2, chunk size positive.
  *
- * Readings where the pages are silent (each also listed in the design doc):
+ * Readings where the pages are silent:
  *  - the prediction is read from the already-decayed state;
  *  - the output is read from the updated state, o_t = scale * S_t^T q_t;
  *  - "row" of the state = key channel, so g_t in R^{Dk} scales rows;

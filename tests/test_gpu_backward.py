@@ -79,9 +79,9 @@ def test_backward_beta_to_two_and_forgetting(orc, kda, qkv):
 def test_backward_model_shaped_t8192(orc, kda):
     """The headline shape (B1 T8192 H32 D128 C64, bf16 q/k/v, fp32 g/beta)
     in one launch; the oracle's gradient on four sampled heads."""
-    c = ki.CONFIGS[1]
+    c = ki.workload(ki.PREFILL)
     say("backward B1 T8192 H32 D128 (sampled heads)")
-    x = ki.config_prefill_inputs(1, device="cuda")
+    x = ki.workload_prefill_inputs(ki.PREFILL, device="cuda")
     B, T, H, D = c["B"], c["T"], c["H"], c["Dk"]
     gen = torch.Generator(device="cuda").manual_seed(99)
     do = torch.randn((B, T, H, D), generator=gen, device="cuda").to(torch.bfloat16)

@@ -41,7 +41,7 @@ def test_decode_steps(orc, kda, qkv, gate, Dk, Dv):
 
 
 def test_decode_workload_1000_steps(orc, kda):
-    c = ki.CONFIGS[3]
+    c = ki.workload(ki.DECODE)
     N, H, Dk, Dv, steps = c["N"], c["H"], c["Dk"], c["Dv"], c["steps"]
     say(f"decode workload N{N} H{H} D{Dk} x{steps} steps (sampled heads)")
     st = ki.decode_state(N, H, Dk, Dv, std=c["state_std"], device="cuda")

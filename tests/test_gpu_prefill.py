@@ -54,8 +54,8 @@ def test_prefill_small(orc, kda, qkv, gate, Dk, Dv, C):
 
 
 def test_tiny_fp32_workload(orc, kda):
-    c = ki.CONFIGS[0]
-    x = ki.config_prefill_inputs(0, device="cuda")
+    c = ki.workload(ki.TINY)
+    x = ki.workload_prefill_inputs(ki.TINY, device="cuda")
     o, s = _run(kda, x, c["chunk"])
     ro, rs = orc.recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"])
     eo, es = rel_err(o, ro), rel_err(s, rs)
@@ -151,9 +151,9 @@ def test_poisoned_outputs_fully_written(kda):
 # full-size workloads, checked on sampled heads
 
 def test_model_shaped_prefill_t8192(orc, kda):
-    c = ki.CONFIGS[1]
+    c = ki.workload(ki.PREFILL)
     say("model-shaped prefill B1 T8192 H32 D128 C64")
-    x = ki.config_prefill_inputs(1, device="cuda")
+    x = ki.workload_prefill_inputs(ki.PREFILL, device="cuda")
     o, s = _run(kda, x, c["chunk"])
     for h in (0, 13, 31):
         sl = lambda t: t[:, :, h:h + 1]
@@ -165,9 +165,9 @@ def test_model_shaped_prefill_t8192(orc, kda):
 
 
 def test_conv_prefill_b8_t4096(orc, kda):
-    c = ki.CONFIGS[2]
+    c = ki.workload(ki.CONV_PREFILL)
     say("conv prefill B8 T4096 H32 D128 C64 (fused prologue)")
-    x = ki.config_prefill_inputs(2, device="cuda")
+    x = ki.workload_prefill_inputs(ki.CONV_PREFILL, device="cuda")
     conv = dict(xq=x["xq"], xk=x["xk"], xv=x["xv"], wq=x["wq"], wk=x["wk"],
                 wv=x["wv"], width=4, l2norm_qk=True, eps=1e-6)
     o, s = _run(kda, x, c["chunk"], conv=conv)
@@ -228,9 +228,9 @@ def test_prefill_short_sequences(orc, kda, qkv, D, C, tk):
 
 
 def test_long_context_prefill_t262144(orc, kda):
-    c = ki.CONFIGS[4]
+    c = ki.workload(ki.LONG)
     say("long-context prefill B1 T262144 H32 D128 C64 (sampled heads)")
-    x = ki.config_prefill_inputs(4, device="cuda")
+    x = ki.workload_prefill_inputs(ki.LONG, device="cuda")
     o, s = _run(kda, x, c["chunk"])
     n = 4096
     for h in (3, 28):
