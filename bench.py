@@ -335,7 +335,38 @@ def main():
             achieved_gbs=byc / (mc * 1e-3) / 1e9,
             hbm_frac=byc / (mc * 1e-3) / 1e9 / HBM_PEAK_GBS)
         log(f"decode step with fused conv: {mc*1e3:.1f} us/call")
-        del st, xt, xc, cache
+        # the same step with two history buffers used in turn: the decode
+        # kernel writes the rolled history into the other buffer itself
+        cache2 = torch.zeros_like(cache)
+        bufs = [cache, cache2]
+        turn = [0]
+
+        def callp():
+            a = turn[0]
+            turn[0] ^= 1
+            kda.kda_decode_tokens(None, None, None, xc["g"], xc["beta"], st,
+                                  state_out=st, o=oc, conv=conv,
+                                  conv_state=bufs[a],
+                                  conv_state_out=bufs[a ^ 1])
+        settle(callp)
+        for _ in range(6):
+            callp()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(reps):
+            callp()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        mp = e0.elapsed_time(e1) / reps
+        dtok["conv_step_two_buffers"] = dict(
+            conv_width=CW, calls=reps, us_per_call=mp * 1e3,
+            tokens_per_s=N / (mp * 1e-3),
+            achieved_gbs=byc / (mp * 1e-3) / 1e9,
+            hbm_frac=byc / (mp * 1e-3) / 1e9 / HBM_PEAK_GBS)
+        log(f"decode step with fused conv, two history buffers: "
+            f"{mp*1e3:.1f} us/call")
+        del st, xt, xc, cache, cache2, bufs
         torch.cuda.empty_cache()
 
     # ---------------- fused-conv prefill and long context -------------------

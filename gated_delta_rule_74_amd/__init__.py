@@ -63,7 +63,8 @@ _decode = _sig("kda_decode_step", _i,
                [_f, _vp])
 _decode_tokens = _sig("kda_decode_tokens", _i,
                       [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp, _vp] +
-                      [_i] * 5 + [_f, ctypes.POINTER(KdaConvDesc), _vp, _vp])
+                      [_i] * 5 + [_f, ctypes.POINTER(KdaConvDesc), _vp, _vp,
+                                  _vp])
 _bwd = _sig("kda_prefill_backward", _i,
             [_vp, _vp, _vp, _i, _vp, _vp, _i] + [_vp] * 9 + [_i] * 6 +
             [_f, _vp, _sz, _vp])
@@ -261,7 +262,7 @@ def kda_decode_step(q, k, v, g, beta, state, *, scale=1.0, o=None,
 
 def kda_decode_tokens(q, k, v, g, beta, state_in, *, state_out=None,
                       token_states=False, scale=1.0, o=None, conv=None,
-                      conv_state=None, stream=None):
+                      conv_state=None, conv_state_out=None, stream=None):
     """L tokens per sequence in one call (the speculative-decoding verify
     step, or with L = 1 the generation step).  q,k,g [N,L,H,Dk],
     v [N,L,H,Dv], beta [N,L,H]; state_in [N,H,Dk,Dv] fp32.  state_out: a
@@ -271,8 +272,9 @@ def kda_decode_tokens(q, k, v, g, beta, state_in, *, state_out=None,
     or False.  conv: dict(xq, xk, xv [N,L,H*D], wq, wk, wv, width,
     l2norm_qk, eps) to make q, k, v from raw projections (q, k, v may then
     be None), with conv_state the fp32 history [N,3,H*max(Dk,Dv),W-1]
-    (rolled forward in place) or None.  Returns (o, state_out,
-    token_states or None)."""
+    or None (zeros), rolled forward in place unless conv_state_out (a
+    second history tensor, written by the decode kernel itself) is given.
+    Returns (o, state_out, token_states or None)."""
     if g.dim() == 4:
         N, L, H, Dk = g.shape
     else:  # per-head gate [N,L,H]
@@ -298,7 +300,8 @@ def kda_decode_tokens(q, k, v, g, beta, state_in, *, state_out=None,
     st = _decode_tokens(_ptr(q), _ptr(k), _ptr(v), _dt(io), _ptr(g),
                         _ptr(beta), _gate_dt(g, 4), _ptr(state_in), _ptr(state_out),
                         _ptr(ts), _ptr(o), N, L, H, Dk, Dv, scale, cd,
-                        _ptr(conv_state), _stream(stream))
+                        _ptr(conv_state), _ptr(conv_state_out),
+                        _stream(stream))
     _check(st, "kda_decode_tokens")
     return o, state_out, ts
 

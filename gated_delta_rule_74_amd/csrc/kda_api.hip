@@ -324,11 +324,12 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
                              float *token_states, void *o, int N, int L,
                              int H, int Dk, int Dv, float scale,
                              const kda_conv_desc *conv, float *conv_state,
-                             void *stream) {
+                             float *conv_state_out, void *stream) {
   if (N <= 0 || L <= 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_EINVAL;
   if (!g || !beta || !state_in || !state_out || !o) return KDA_EINVAL;
   if (!conv && (!q || !k || !v)) return KDA_EINVAL;
-  if (!conv && conv_state) return KDA_EINVAL;
+  if (!conv && (conv_state || conv_state_out)) return KDA_EINVAL;
+  if (conv_state_out == conv_state) conv_state_out = nullptr;  // in place
   if (conv) {
     if (!conv->xq || !conv->xk || !conv->xv || !conv->wq || !conv->wk ||
         !conv->wv)
@@ -337,7 +338,7 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
     if (conv->l2norm_qk != 0 && conv->l2norm_qk != 1) return KDA_EINVAL;
     if (!(conv->eps >= 0.f) || !isfinite(conv->eps)) return KDA_EINVAL;
     const void *cp[] = {conv->xq, conv->xk, conv->xv, conv->wq, conv->wk,
-                        conv->wv, conv_state};
+                        conv->wv, conv_state, conv_state_out};
     for (const void *ptr : cp)
       if (ptr && !aligned16(ptr)) return KDA_EINVAL;
     if (conv->width > 4) return KDA_EUNSUPPORTED;
@@ -354,7 +355,14 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
     return KDA_EINVAL;
   if (conv && (o == conv->xq || o == conv->xk || o == conv->xv ||
                (conv_state && ((const void *)conv_state == o ||
-                               conv_state == state_out))))
+                               conv_state == state_out)) ||
+               (conv_state_out &&
+                ((const void *)conv_state_out == o ||
+                 conv_state_out == state_out ||
+                 conv_state_out == state_in ||
+                 (const void *)conv_state_out == conv->xq ||
+                 (const void *)conv_state_out == conv->xk ||
+                 (const void *)conv_state_out == conv->xv))))
     return KDA_EINVAL;
   if (!dim_ok(Dk) || !dim_ok(Dv)) return KDA_EUNSUPPORTED;
   if (!pair_ok(qkv_dtype, gate_dtype)) return KDA_EUNSUPPORTED;
@@ -372,13 +380,14 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
     p.xq = conv->xq; p.xk = conv->xk; p.xv = conv->xv;
     p.wq = conv->wq; p.wk = conv->wk; p.wv = conv->wv;
     p.cw = conv->width; p.l2 = conv->l2norm_qk; p.eps = conv->eps;
-    p.cstate = conv_state; p.Dmax = Dmax;
+    p.cstate = conv_state; p.cstate_out = conv_state_out; p.Dmax = Dmax;
   }
   hipError_t e = kda::launch_decode(p, qkv_dtype == KDA_BF16,
                                     (hipStream_t)stream);
-  if (e != hipSuccess || !conv || !conv_state) return hip_status(e);
-  // roll the conv history forward by the L raw inputs (after the decode
-  // kernel has read the old history on the same stream)
+  if (e != hipSuccess || !conv || !conv_state || conv_state_out)
+    return hip_status(e);
+  // in place: roll the conv history forward by the L raw inputs (after the
+  // decode kernel has read the old history on the same stream)
   kda::ConvParams c{};
   c.x[0] = conv->xq; c.x[1] = conv->xk; c.x[2] = conv->xv;
   c.D[0] = Dk; c.D[1] = Dk; c.D[2] = Dv;

@@ -269,6 +269,33 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode(DecodeParams p) {
           s[i], (f32x4 *)(p.state_out + so + (size_t)(rg + RG * i) * DV +
                           4 * q4));
   }
+  // 6. the conv history rolled forward, into a buffer other than the one
+  //    read: every column share of the head holds the whole q/k history, so
+  //    share cg writes q/k channels [cg DK/CS, (cg+1) DK/CS) and each share
+  //    its own value columns
+  if (CONV && p.cstate_out) {
+    const int W = p.cw;
+    const size_t hs = (size_t)H * p.Dmax * (W - 1);
+    float *out = p.cstate_out + n * 3 * hs;
+    // slot m of the 3 kept inputs is history entry m - (4 - W); constant
+    // slot indices keep the inputs in registers
+    if (tid < DK && tid / (DK / CS) == (int)(wid % CS)) {
+      const size_t base = (h * DK + tid) * (W - 1);
+#pragma unroll
+      for (int m = 0; m < 3; ++m)
+        if (m >= 4 - W) {
+          const size_t e = base + (m - (4 - W));
+          out[e] = cq.h[m];
+          out[hs + e] = ck.h[m];
+        }
+    }
+    if (tid < DVB) {
+      const size_t base = 2 * hs + (h * DV + c0 + tid) * (W - 1);
+#pragma unroll
+      for (int m = 0; m < 3; ++m)
+        if (m >= 4 - W) out[base + (m - (4 - W))] = cv.h[m];
+    }
+  }
 }
 
 template <typename IO, int DK, int DV>

@@ -53,12 +53,15 @@ struct DecodeParams {
   int N, L, H, Dk, Dv;
   float scale;
   // optional fused conv prologue (xq != null): raw inputs [N,L,H*D], taps
-  // [H*D,cw], history [N,3,H*Dmax,cw-1] (null: zeros)
+  // [H*D,cw], history [N,3,H*Dmax,cw-1] (null: zeros); cstate_out (or
+  // null) receives the history rolled forward by the L inputs and must not
+  // alias cstate
   const void *xq, *xk, *xv;
   const float *wq, *wk, *wv;
   int cw, l2, Dmax;
   float eps;
   const float *cstate;
+  float *cstate_out;
 };
 
 struct ConvParams {

@@ -230,9 +230,17 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
  *                 taps, width and L2 norm of kda_conv_desc
  *   conv_state    with conv: NULL (zeros before the first token), or the
  *                 fp32 history [N,3,H*D_max,width-1] of kda_conv_prologue,
- *                 read as the inputs before the first token and then
- *                 rolled forward to end with the L new raw inputs
- *                 (conv_state must be NULL without conv)
+ *                 read as the inputs before the first token and then, when
+ *                 conv_state_out is NULL or equal to it, rolled forward in
+ *                 place to end with the L new raw inputs (a second, small
+ *                 kernel on the same stream)
+ *   conv_state_out  NULL, or a second history buffer of the same layout
+ *                 that receives the rolled history instead (conv_state is
+ *                 then only read and may be NULL); written by the decode
+ *                 kernel itself, so a caller that alternates two buffers
+ *                 saves the in-place roll.  Must not alias o, the states or
+ *                 the raw inputs.
+ *                 (conv_state and conv_state_out must be NULL without conv)
  * With conv and L = 1 this is the generation step with its conv cache.
  * Errors as for kda_decode_step; L <= 0 is KDA_EINVAL. */
 kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
@@ -242,7 +250,7 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
                              float *token_states, void *o, int N, int L,
                              int H, int Dk, int Dv, float scale,
                              const kda_conv_desc *conv, float *conv_state,
-                             void *stream);
+                             float *conv_state_out, void *stream);
 
 /* Standalone conv prologue ([LQNN-A]: kernel-4 causal conv with a cache
  * updated incrementally).  Same arithmetic as kda_conv_desc; outputs

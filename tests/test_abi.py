@@ -123,7 +123,7 @@ def _decode_tokens(**kw):
     a = dict(q=A, k=A, v=A, io=kda.KDA_BF16, g=A, beta=A, gt=kda.KDA_BF16,
              s_in=A + 4096, s_out=A + 4096, ts=None, o=A + 8192, N=2, L=2,
              H=2, Dk=16, Dv=16, scale=1.0, conv=None, cstate=None,
-             stream=None)
+             cstate_out=None, stream=None)
     a.update(kw)
     return kda._decode_tokens(*a.values())
 
@@ -137,6 +137,7 @@ def _decode_tokens(**kw):
     (dict(Dk=48), kda.KDA_EUNSUPPORTED),
     (dict(io=kda.KDA_F32, gt=kda.KDA_BF16), kda.KDA_EUNSUPPORTED),
     (dict(cstate=A + 16384), kda.KDA_EINVAL),  # a history without a conv
+    (dict(cstate_out=A + 16384), kda.KDA_EINVAL),
     (dict(io=kda.KDA_BF16 | kda.KDA_GATE_HEAD), kda.KDA_EINVAL),
     (dict(gt=kda.KDA_GATE_HEAD | 5), kda.KDA_EINVAL),
 ])
@@ -158,6 +159,11 @@ def _cdesc(**kw):
     (dict(l2norm_qk=2), {}, kda.KDA_EINVAL),
     ({}, dict(cstate=A + 8192), kda.KDA_EINVAL),    # history aliases o
     ({}, dict(cstate=A + 16386), kda.KDA_EINVAL),   # misaligned history
+    ({}, dict(cstate_out=A + 8192), kda.KDA_EINVAL),   # rolled history = o
+    ({}, dict(cstate_out=A + 4096), kda.KDA_EINVAL),   # ... = the state
+    ({}, dict(cstate_out=A + 16392), kda.KDA_EINVAL),  # misaligned
+    (dict(xk=A + 16384), dict(cstate_out=A + 16384),
+     kda.KDA_EINVAL),                                  # ... = a raw input
     (dict(xq=A + 8192), {}, kda.KDA_EINVAL),        # o aliases a raw input
 ])
 def test_decode_tokens_conv_rejects(ckw, kw, want):

@@ -151,20 +151,29 @@ def _cut(x, a, b):
     return {n: x[n][:, a:b] for n in ("xq", "xk", "xv", "g", "beta")}
 
 
-@pytest.mark.parametrize("qkv,gate,Dk,Dv,W,splits,hist", [
-    ("bf16", "bf16", 128, 128, 4, (1, 1, 1), True),
-    ("bf16", "f32", 64, 128, 3, (3, 1), True),
-    ("f32", "f32", 32, 16, 2, (5,), False),
-    ("f32", "f32", 128, 64, 4, (1, 2), False),
-    ("bf16", "bf16", 128, 32, 4, (2, 1, 4), True),
-    ("f32", "f32", 16, 16, 3, (1, 1), True)])
-def test_decode_tokens_conv(orc, kda, qkv, gate, Dk, Dv, W, splits, hist):
+@pytest.mark.parametrize("qkv,gate,Dk,Dv,W,splits,hist,pingpong", [
+    ("bf16", "bf16", 128, 128, 4, (1, 1, 1), True, False),
+    ("bf16", "f32", 64, 128, 3, (3, 1), True, False),
+    ("f32", "f32", 32, 16, 2, (5,), False, False),
+    ("f32", "f32", 128, 64, 4, (1, 2), False, False),
+    ("bf16", "bf16", 128, 32, 4, (2, 1, 4), True, False),
+    ("f32", "f32", 16, 16, 3, (1, 1), True, False),
+    ("bf16", "bf16", 128, 128, 4, (1, 1, 1), True, True),
+    ("bf16", "f32", 64, 128, 3, (3, 1, 1), False, True),
+    ("bf16", "bf16", 128, 64, 2, (1, 2, 1), True, True),
+    ("f32", "f32", 32, 128, 4, (2, 1), False, True),
+    ("f32", "f32", 16, 16, 3, (1, 1, 1), True, True)])
+def test_decode_tokens_conv(orc, kda, qkv, gate, Dk, Dv, W, splits, hist,
+                            pingpong):
     """Decode calls with the conv prologue fused (raw projections in), the
     conv history and the recurrent state carried from call to call, against
     the oracle's conv + recurrence over the whole token run: outputs, final
-    state and the rolled conv history."""
+    state and the rolled conv history.  pingpong: each call writes the
+    rolled history into the other of two buffers (conv_state_out) instead
+    of rolling it in place; without a starting history the first call reads
+    zeros and still writes one."""
     say(f"decode tokens + conv qkv={qkv} gate={gate} Dk={Dk} Dv={Dv} W={W} "
-        f"splits={splits} hist={hist}")
+        f"splits={splits} hist={hist} pingpong={pingpong}")
     N, H, T = 4, 3, sum(splits)
     Dm = max(Dk, Dv)
     x = ki.prefill_inputs(N, T, H, Dk, Dv, qkv=qkv, gate=gate, conv_width=W,
@@ -175,6 +184,8 @@ def test_decode_tokens_conv(orc, kda, qkv, gate, Dk, Dv, W, splits, hist):
         cache = torch.randn((N, 3, H * Dm, W - 1), device="cuda")
         old = to_cpu64(cache)
         hist_in = tuple(old[:, i, :H * D] for i, D in enumerate((Dk, Dk, Dv)))
+    spare = (torch.full((N, 3, H * Dm, W - 1), float("nan"), device="cuda")
+             if pingpong else None)
     st = x["s0"].clone()
     outs, t0 = [], 0
     for L in splits:
@@ -186,9 +197,16 @@ def test_decode_tokens_conv(orc, kda, qkv, gate, Dk, Dv, W, splits, hist):
                                         c["g"].contiguous(),
                                         c["beta"].contiguous(), st,
                                         state_out=st, scale=0.6, conv=conv,
-                                        conv_state=cache)
+                                        conv_state=cache,
+                                        conv_state_out=spare)
         outs.append(o)
         t0 += L
+        if pingpong:
+            cache, spare = spare, cache
+            if spare is None:
+                spare = torch.full_like(cache, float("nan"))
+            else:
+                spare.fill_(float("nan"))
         if cache is None:
             break   # without a history only one call continues correctly
     torch.cuda.synchronize()
@@ -201,6 +219,6 @@ def test_decode_tokens_conv(orc, kda, qkv, gate, Dk, Dv, W, splits, hist):
     eo, es = rel_err(torch.cat(outs, 1), ro), rel_err(st, rs)
     say(f"  err o={eo:.2e} S={es:.2e}")
     assert eo <= TOL[qkv] and es <= TOL[qkv]
-    if hist:
+    if cache is not None:
         for i, D in enumerate((Dk, Dk, Dv)):
             assert rel_err(cache[:, i, :H * D], rh[i]) <= 1e-6, i
