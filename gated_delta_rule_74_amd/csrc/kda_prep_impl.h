@@ -863,6 +863,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     // two matrices given in operand form yields the second-operand form of
     // the result; the first-operand form of X equals the second-operand form
     // of X^T, so both forms of L^2 and L^4 come from products of L and L^T.
+    f32x4 Tcol[NB];  // Tcol[j] = T_{w+j, w} of this wave's column w (B form)
     if (wave < NB) {
       const int aa = wave;
       const float *ab = Af + (16 * aa) * LDA + 16 * aa;
@@ -883,6 +884,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
       Y = mma16_f32(L4A, Y, Y);
       Y = mma16_f32(L8A, Y, Y);
       // lane (g4, m16) holds T_aa[4 g4 + j][m16]
+      Tcol[0] = Y;
       *(f32x4 *)(Tt + (16 * aa + m16) * LDA + 16 * aa + 4 * g4) = Y;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -891,29 +893,35 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
       }
     }
     __syncthreads();
-    // ---- T2: off-diagonal blocks, one block-diagonal at a time -------------
+    // ---- T2: off-diagonal blocks, one block column per wave ---------------
     //   T_ab = -T_aa * sum_{c=b}^{a-1} A_ac T_cb   (fp32 matrix cores)
-    for (int d = 1; d < NB; ++d) {
-      for (int tk = wave; tk < NB - d; tk += PREP_THREADS / 64) {
-        const int aa = d + tk, bb = tk;
+    // Column b needs only its own earlier blocks T_cb, which the wave keeps
+    // in registers (a product's result is the next product's B operand),
+    // and the diagonal inverses of T1: one barrier for the whole phase.
+    if (wave < NB) {
+      const int bb = wave;
+#pragma unroll
+      for (int k = 1; k < NB; ++k) {
+        if (bb + k >= NB) break;
+        const int aa = bb + k;
         f32x4 X = {0.f, 0.f, 0.f, 0.f};
-        for (int cc = bb; cc < aa; ++cc) {
+#pragma unroll
+        for (int j = 0; j < k; ++j) {
           const f32x4 af = *(const f32x4 *)(Af + (16 * aa + m16) * LDA +
-                                            16 * cc + 4 * g4);
-          const f32x4 tf = *(const f32x4 *)(Tt + (16 * bb + m16) * LDA +
-                                            16 * cc + 4 * g4);
-          X = mma16_f32(af, tf, X);
+                                            16 * (bb + j) + 4 * g4);
+          X = mma16_f32(af, Tcol[j], X);
         }
         const f32x4 ta = *(const f32x4 *)(Taa + (aa * 16 + m16) * 16 + 4 * g4);
         const f32x4 Tn = -mma16_f32(ta, X, f32x4{0.f, 0.f, 0.f, 0.f});
+        Tcol[k] = Tn;
         // lane (n = m16, g4) holds T_ab[4g4 + j][m16]
         *(f32x4 *)(Tt + (16 * bb + m16) * LDA + 16 * aa + 4 * g4) = Tn;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           Tb[(16 * aa + 4 * g4 + j) * LDC + 16 * bb + m16] = from_f32<IO>(Tn[j]);
       }
-      __syncthreads();
     }
+    __syncthreads();
 
     if (more) prep_load<8, IO, GT, DK, C, CONV>(p, task + gridDim.x, st, tid);
     if (p.train_at) {
