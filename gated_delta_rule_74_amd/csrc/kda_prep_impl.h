@@ -935,16 +935,40 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     }
     // ---- WU: -W (A-operand units) and U (accumulator tiles) ----------------
     // wave rt takes token tile rt: its rows of T are read once and serve
-    // every key unit of W and every value slab of U
-    for (int rt = wave; rt < NB; rt += PREP_THREADS / 64) {
+    // every key unit of W and its value slabs of U
+    auto load_t = [&](int rt, frag *tb) {
       const int umax = (16 * rt + 15) / KU;  // last token unit T row rt uses
-      frag tb[NTU];
 #pragma unroll
       for (int uu = 0; uu < NTU; ++uu) {
         const bool fullT = (TPU == 1) || (TPU * uu + 1 < NB);
         tb[uu] = M::load_k(Tb + (16 * rt + m16) * LDC + KU * min(uu, umax), g4,
                            fullT);
       }
+    };
+    auto u_tiles = [&](int rt, const frag *tb, int v0, int v1) {
+      const int umax = (16 * rt + 15) / KU;
+      for (int vt = v0; vt < v1; ++vt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        frag vb[NTU];
+#pragma unroll
+        for (int uu = 0; uu < NTU; ++uu) {
+          const bool fullT = (TPU == 1) || (TPU * uu + 1 < NB);
+          vb[uu] = load_k_cm<IO, C>(XvT + (16 * vt + m16) * LDC, 16 * vt + m16,
+                                    KU * uu, g4, fullT);
+        }
+#pragma unroll
+        for (int uu = 0; uu < NTU; ++uu)
+          if (uu <= umax) acc = M::mma(tb[uu], vb[uu], acc);
+        IO *dst = (IO *)(blk + W.off_u) +
+                  ((size_t)(vt * NB + rt) * 64 + lane) * 4;
+        float a4[4] = {acc[0], acc[1], acc[2], acc[3]};
+        st_stream(dst, V4::put(a4));
+      }
+    };
+    for (int rt = wave; rt < NB; rt += PREP_THREADS / 64) {
+      const int umax = (16 * rt + 15) / KU;  // last token unit T row rt uses
+      frag tb[NTU];
+      load_t(rt, tb);
 #pragma unroll
       for (int u = 0; u < NKU; ++u) {
         f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -969,22 +993,20 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
         st_stream(blk + W.off_negw + ((size_t)(rt * NKU + u) * 64 + lane) * 16,
                   out);
       }
-      for (int vt = 0; vt < nvt; ++vt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        frag vb[NTU];
-#pragma unroll
-        for (int uu = 0; uu < NTU; ++uu) {
-          const bool fullT = (TPU == 1) || (TPU * uu + 1 < NB);
-          vb[uu] = load_k_cm<IO, C>(XvT + (16 * vt + m16) * LDC, 16 * vt + m16,
-                                    KU * uu, g4, fullT);
+      if constexpr (TPU == 2 && NB == 4) {
+        // token tiles 2 and 3 use two units of T against one for tiles 0
+        // and 1, so waves 0 and 1 also take the first half of tiles 2 and
+        // 3's value slabs: every wave then does the same number of products
+        if (rt < 2) {
+          u_tiles(rt, tb, 0, nvt);
+          frag tb2[NTU];
+          load_t(rt + 2, tb2);
+          u_tiles(rt + 2, tb2, 0, nvt / 2);
+        } else {
+          u_tiles(rt, tb, nvt / 2, nvt);
         }
-#pragma unroll
-        for (int uu = 0; uu < NTU; ++uu)
-          if (uu <= umax) acc = M::mma(tb[uu], vb[uu], acc);
-        IO *dst = (IO *)(blk + W.off_u) +
-                  ((size_t)(vt * NB + rt) * 64 + lane) * 4;
-        float a4[4] = {acc[0], acc[1], acc[2], acc[3]};
-        st_stream(dst, V4::put(a4));
+      } else {
+        u_tiles(rt, tb, 0, nvt);
       }
     }
     if (more) put_beta();  // the current task's betas were last read in E1
