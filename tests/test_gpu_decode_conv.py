@@ -222,3 +222,23 @@ def test_decode_tokens_conv(orc, kda, qkv, gate, Dk, Dv, W, splits, hist,
     if cache is not None:
         for i, D in enumerate((Dk, Dk, Dv)):
             assert rel_err(cache[:, i, :H * D], rh[i]) <= 1e-6, i
+
+
+def test_conv_state_out_same_buffer_is_in_place(kda):
+    """conv_state_out naming the conv_state buffer itself means in place:
+    the same outputs, state and rolled history as leaving it out."""
+    N, H, L, D, W = 3, 2, 2, 64, 4
+    x = ki.prefill_inputs(N, L, H, D, D, qkv="bf16", gate="bf16",
+                          conv_width=W, seed=77, device="cuda", with_s0=True)
+    conv = dict(xq=x["xq"], xk=x["xk"], xv=x["xv"], wq=x["wq"], wk=x["wk"],
+                wv=x["wv"], width=W, l2norm_qk=True, eps=1e-6)
+    h0 = torch.randn((N, 3, H * D, W - 1), device="cuda")
+    ha, hb = h0.clone(), h0.clone()
+    oa, sa, _ = kda.kda_decode_tokens(None, None, None, x["g"], x["beta"],
+                                      x["s0"], conv=conv, conv_state=ha)
+    ob, sb, _ = kda.kda_decode_tokens(None, None, None, x["g"], x["beta"],
+                                      x["s0"], conv=conv, conv_state=hb,
+                                      conv_state_out=hb)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob) and torch.equal(sa, sb)
+    assert torch.equal(ha, hb) and not torch.equal(ha, h0)
