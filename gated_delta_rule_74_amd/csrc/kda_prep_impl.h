@@ -355,6 +355,9 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     // sigma are running products written out as they are formed.
     int vote = 0;
     float F[4] = {1.f, 1.f, 1.f, 1.f};
+    // raw k and q rows (packed as stored): only the exact fallback reads
+    // them, so they go to LDS after B1 and only when the vote asks for it
+    typename V4::raw kraw[8], qraw[8];
     if (kthr) {
       float e[8][4], kk[8][4], qq[8][4], bt[8];
 #pragma unroll
@@ -434,8 +437,8 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
         if (t0 + r >= T)
 #pragma unroll
           for (int j = 0; j < 4; ++j) qq[i][j] = kk[i][j] = 0.f;
-        *(typename V4::raw *)(Kraw + r * LDK + c0) = V4::put(kk[i]);
-        *(typename V4::raw *)(Aq + r * LDK + c0) = V4::put(qq[i]);
+        kraw[i] = V4::put(kk[i]);
+        qraw[i] = V4::put(qq[i]);
       }
       // this thread's 8-token product, then the other half of the 16-token
       // sub-chunk (lane ^ NQ) for the cross terms
@@ -551,6 +554,13 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     // ---- E2: Qtil and Ktil^T units, gamma_C, beta K Gam for W ------------
     const bool fallback =
         (votes[0] | votes[1] | votes[2] | votes[3]) != 0;
+    if (fallback && kthr) {  // read after B2 by the exact diagonal sums
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        *(typename V4::raw *)(Kraw + (r0 + i) * LDK + c0) = kraw[i];
+        *(typename V4::raw *)(Aq + (r0 + i) * LDK + c0) = qraw[i];
+      }
+    }
     float kgb[8][4];
     if (kthr) {
       float fpre[4], fsuf[4];
