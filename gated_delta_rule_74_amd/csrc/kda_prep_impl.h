@@ -348,7 +348,6 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     const int b = bh / H, h = bh % H;
     const int t0 = n * C;
     char *blk = p.ws + ((size_t)bh * p.NC + n) * p.wsb;
-    for (int i = tid; i < 2 * NB * 256; i += PREP_THREADS) FbA[i] = 0.f;
 
     // ---- E1: decay, running products within the sub-chunk, conv + L2 -----
     // Writes the A/P operands (region A), raw k/q rows and F_a; rho and
@@ -554,11 +553,15 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     // ---- E2: Qtil and Ktil^T units, gamma_C, beta K Gam for W ------------
     const bool fallback =
         (votes[0] | votes[1] | votes[2] | votes[3]) != 0;
-    if (fallback && kthr) {  // read after B2 by the exact diagonal sums
+    if (fallback) {  // read after B2 by the exact diagonal sums
+      for (int i = tid; i < 2 * NB * 64; i += PREP_THREADS)
+        ((f32x4 *)FbA)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (kthr) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        *(typename V4::raw *)(Kraw + (r0 + i) * LDK + c0) = kraw[i];
-        *(typename V4::raw *)(Aq + (r0 + i) * LDK + c0) = qraw[i];
+        for (int i = 0; i < 8; ++i) {
+          *(typename V4::raw *)(Kraw + (r0 + i) * LDK + c0) = kraw[i];
+          *(typename V4::raw *)(Aq + (r0 + i) * LDK + c0) = qraw[i];
+        }
       }
     }
     float kgb[8][4];
