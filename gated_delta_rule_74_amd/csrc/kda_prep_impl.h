@@ -551,6 +551,10 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     __syncthreads();  // B1: region A, Fs, votes
 
     // ---- E2: Qtil and Ktil^T units, gamma_C, beta K Gam for W ------------
+    // the next task's g and beta (this task's were last read in E1) go out
+    // first, ahead of this phase's workspace stores
+    const bool more = task + (int)gridDim.x < ntask;
+    if (more) prep_load<1, IO, GT, DK, C, CONV>(p, task + gridDim.x, st, tid);
     const bool fallback =
         (votes[0] | votes[1] | votes[2] | votes[3]) != 0;
     if (fallback) {  // read after B2 by the exact diagonal sums
@@ -722,10 +726,8 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     }
     __syncthreads();  // B2: region A complete
 
-    // stage the next task while this one runs on the matrix cores, a part
-    // per phase
-    const bool more = task + (int)gridDim.x < ntask;
-    if (more) prep_load<1, IO, GT, DK, C, CONV>(p, task + gridDim.x, st, tid);
+    // the next task's q, k and v follow while this one runs on the matrix
+    // cores, a part per phase
 
     if (fallback) {
       // exact diagonal-block sums: task (sub-chunk a, column s, 16 channels)
