@@ -727,7 +727,10 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     __syncthreads();  // B2: region A complete
 
     // the next task's q, k and v follow while this one runs on the matrix
-    // cores, a part per phase
+    // cores, a part per phase (one phase later with the conv, whose staged
+    // rows hold three more tokens and so more registers)
+    if constexpr (!CONV)
+      if (more) prep_load<2, IO, GT, DK, C, CONV>(p, task + gridDim.x, st, tid);
 
     if (fallback) {
       // exact diagonal-block sums: task (sub-chunk a, column s, 16 channels)
@@ -839,7 +842,12 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
       }
     }
     __syncthreads();  // B3: region A no longer read
-    if (more) prep_load<2, IO, GT, DK, C, CONV>(p, task + gridDim.x, st, tid);
+    if (more) {
+      if constexpr (CONV)
+        prep_load<2, IO, GT, DK, C, CONV>(p, task + gridDim.x, st, tid);
+      else
+        prep_load<4, IO, GT, DK, C, CONV>(p, task + gridDim.x, st, tid);
+    }
 
     // ---- T0: W/U inputs into the freed region, T zero-filled --------------
     static_assert((C * LDC * sizeof(IO)) % 16 == 0, "Tb rows");
@@ -868,7 +876,8 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
       }
     }
     __syncthreads();  // B4
-    if (more) prep_load<4, IO, GT, DK, C, CONV>(p, task + gridDim.x, st, tid);
+    if constexpr (CONV)
+      if (more) prep_load<4, IO, GT, DK, C, CONV>(p, task + gridDim.x, st, tid);
 
     // ---- T1: inverse of each unit-lower 16x16 diagonal block (fp32) ------
     // With L the strictly lower block (L^16 = 0),
