@@ -774,17 +774,24 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     // the NB(NB+1)/2 blocks (aa, bb <= aa) are dealt to the waves in an
     // order that evens out their cost (blocks two or more sub-chunks apart
     // also scale an operand by the mid products)
+    // consecutive blocks of a wave often share their row sub-chunk: its
+    // k and q operands are then kept rather than read again (not with the
+    // conv, whose build has no registers to spare for them)
+    frag kf[NKU], qf[NKU];
+    int row_aa = -1;
     for (int j = wave; j < NB * (NB + 1) / 2; j += PREP_THREADS / 64) {
       int aa, bb;
       ap_block<NB>(j, aa, bb);
-      const IO *kb = Xkr + (16 * aa + m16) * LDK;
-      const IO *qb = Xqr + (16 * aa + m16) * LDK;
-      frag kf[NKU], qf[NKU];
+      if (CONV || aa != row_aa) {
+        row_aa = aa;
+        const IO *kb = Xkr + (16 * aa + m16) * LDK;
+        const IO *qb = Xqr + (16 * aa + m16) * LDK;
 #pragma unroll
-      for (int u = 0; u < NKU; ++u) {
-        const bool full = (TPU == 1) || (TPU * u + 1 < NKT);
-        kf[u] = M::load_k(kb + KU * u, g4, full);
-        qf[u] = M::load_k(qb + KU * u, g4, full);
+        for (int u = 0; u < NKU; ++u) {
+          const bool full = (TPU == 1) || (TPU * u + 1 < NKT);
+          kf[u] = M::load_k(kb + KU * u, g4, full);
+          qf[u] = M::load_k(qb + KU * u, g4, full);
+        }
       }
       {
         const bool diag = (aa == bb);
