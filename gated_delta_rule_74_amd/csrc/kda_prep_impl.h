@@ -436,8 +436,10 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
         if (t0 + r >= T)
 #pragma unroll
           for (int j = 0; j < 4; ++j) qq[i][j] = kk[i][j] = 0.f;
-        kraw[i] = V4::put(kk[i]);
-        qraw[i] = V4::put(qq[i]);
+        if constexpr (CONV) {
+          kraw[i] = V4::put(kk[i]);
+          qraw[i] = V4::put(qq[i]);
+        }
       }
       // this thread's 8-token product, then the other half of the 16-token
       // sub-chunk (lane ^ NQ) for the cross terms
@@ -560,7 +562,7 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     if (fallback) {  // read after B2 by the exact diagonal sums
       for (int i = tid; i < 2 * NB * 64; i += PREP_THREADS)
         ((f32x4 *)FbA)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (kthr) {
+      if (CONV && kthr) {  // without the conv they are read from q and k
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           *(typename V4::raw *)(Kraw + (r0 + i) * LDK + c0) = kraw[i];
@@ -755,9 +757,21 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
                                            : ((const float *)p.g)[gi];
               pr[c] *= (tr < T) ? __expf(gv) : 1.f;
             }
-            const float ks = to_f32(Kraw[(16 * aa + s) * LDK + ch]);
-            sa += to_f32(Kraw[(16 * aa + r) * LDK + ch]) * ks * pr[c];
-            sp += to_f32(Aq[(16 * aa + r) * LDK + ch]) * ks * pr[c];
+            float ks, kr, qr;
+            if constexpr (CONV) {
+              ks = to_f32(Kraw[(16 * aa + s) * LDK + ch]);
+              kr = to_f32(Kraw[(16 * aa + r) * LDK + ch]);
+              qr = to_f32(Aq[(16 * aa + r) * LDK + ch]);
+            } else {  // raw k, q of the input rows, zero beyond the sequence
+              const int ts = t0 + 16 * aa + s;
+              const size_t ob = ((tokb + min(ts, T - 1)) * H + h) * DK + ch;
+              const size_t orr = ((tokb + trc) * H + h) * DK + ch;
+              ks = ts < T ? to_f32(((const IO *)p.k)[ob]) : 0.f;
+              kr = tr < T ? to_f32(((const IO *)p.k)[orr]) : 0.f;
+              qr = tr < T ? to_f32(((const IO *)p.q)[orr]) : 0.f;
+            }
+            sa += kr * ks * pr[c];
+            sp += qr * ks * pr[c];
           }
           const float br = (tr < T)
               ? (GB ? (float)((const bf16 *)p.beta)[(tokb + trc) * H + h]
