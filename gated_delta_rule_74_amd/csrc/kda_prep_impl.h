@@ -871,9 +871,17 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
     }
 
     // ---- T0: W/U inputs into the freed region, T zero-filled --------------
-    static_assert((C * LDC * sizeof(IO)) % 16 == 0, "Tb rows");
-    for (int i = tid; i < (int)(C * LDC * sizeof(IO) / 16); i += PREP_THREADS)
-      ((uint4 *)Tb)[i] = make_uint4(0u, 0u, 0u, 0u);
+    // W/U read T in whole token units: with 32-token (bf16) units the upper
+    // block (r, r+1) of every even token tile r is read and must be zero;
+    // every other block they read is written by T1/T2
+    if constexpr (TPU == 2) {
+      static_assert((LDC * sizeof(IO)) % 16 == 0, "Tb rows");
+      for (int i = tid; i < (NB / 2) * 32; i += PREP_THREADS) {
+        const int rt = 2 * (i / 32), row = (i % 32) / 2, hv = i % 2;
+        *(uint4 *)(Tb + (16 * rt + row) * LDC + 16 * (rt + 1) + 8 * hv) =
+            make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
     if (kthr) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
