@@ -435,6 +435,77 @@ def main():
         del x, ws, o, s
         torch.cuda.empty_cache()
 
+    # ---------------- the oracle on the other workloads (CPU) ---------------
+    # bounded samples of each workload (a few seconds of host time each),
+    # the same fp64 token loop as cpu_baseline, on the host's cores
+    if not args.no_cpu and not args.no_extra and only is None:
+        import oracle
+        orc = oracle.get()
+        ocpu = extra["oracle_cpu"] = {}
+
+        def t_oracle(fn):
+            t0 = time.perf_counter()
+            fn()
+            return time.perf_counter() - t0
+
+        c = ki.workload(ki.CONV_PREFILL)
+        log("oracle: conv prefill sample")
+        Bs = 2  # two of the eight sequences, every token and head
+        xc = ki.prefill_inputs(Bs, c["T"], c["H"], c["Dk"], c["Dv"],
+                               qkv=c["qkv"], gate=c["gate"],
+                               conv_width=c["conv_width"], seed=c["seed"],
+                               device=dev)
+        xc = {n: t.detach().cpu() for n, t in xc.items()}
+        conv = dict(xq=xc["xq"], xk=xc["xk"], xv=xc["xv"], wq=xc["wq"],
+                    wk=xc["wk"], wv=xc["wv"], eps=1e-6, l2norm_qk=True)
+        dt = t_oracle(lambda: orc.prefill(None, None, None, xc["g"],
+                                          xc["beta"], conv=conv))
+        ocpu[c["name"]] = dict(
+            value=Bs * c["T"] / dt, unit="tokens/s", cores=orc.last_threads,
+            kind="oracle", seconds=dt,
+            sample=f"batch rows 0-{Bs - 1} of B{c['B']} (T{c['T']}, all "
+                   f"{c['H']} heads): fp64 conv, L2 and token loop")
+        del xc, conv
+        c = ki.workload(ki.DECODE)
+        nst = 50
+        log(f"oracle: decode sample ({nst} steps)")
+        st0 = ki.decode_state(c["N"], c["H"], c["Dk"], c["Dv"],
+                              std=c["state_std"], device=dev).cpu()
+        xs = [ki.decode_step_inputs(c["N"], c["H"], c["Dk"], c["Dv"], i,
+                                    device=dev) for i in range(nst)]
+        seq = {n: torch.stack([x[n] for x in xs], 1).cpu()
+               for n in ("q", "k", "v", "g", "beta")}
+        del xs
+        dt = t_oracle(lambda: orc.recurrence(seq["q"], seq["k"], seq["v"],
+                                             seq["g"], seq["beta"], st0))
+        ocpu[c["name"]] = dict(
+            value=c["N"] * nst / dt, unit="tokens/s", cores=orc.last_threads,
+            kind="oracle", seconds=dt,
+            sample=f"the first {nst} of {c['steps']} steps, all {c['N']} "
+                   f"sequences x {c['H']} heads (fp64 state per head kept "
+                   "across the steps)")
+        del seq, st0
+        c = ki.workload(ki.LONG)
+        Ts = 16384
+        log(f"oracle: long-context sample ({Ts} tokens)")
+        xl = ki.prefill_inputs(c["B"], Ts, c["H"], c["Dk"], c["Dv"],
+                               qkv=c["qkv"], gate=c["gate"],
+                               gate_kind=c["gate_kind"], seed=c["seed"],
+                               device=dev)
+        xl = {n: t.detach().cpu() for n, t in xl.items()}
+        dt = t_oracle(lambda: orc.recurrence(xl["q"], xl["k"], xl["v"],
+                                             xl["g"], xl["beta"]))
+        ocpu[c["name"]] = dict(
+            value=Ts / dt, unit="tokens/s", cores=orc.last_threads,
+            kind="oracle", seconds=dt,
+            sample=f"the first {Ts} of {c['T']} tokens, all {c['H']} heads "
+                   "(the token loop's cost per token does not depend on "
+                   "the position)")
+        del xl
+        for name, r in ocpu.items():
+            log(f"oracle {name}: {r['value']:.0f} {r['unit']} on "
+                f"{r['cores']} threads ({r['seconds']:.1f} s)")
+
     # ---------------- backward of the headline prefill ---------------------
     if sel("bwd") and not args.no_extra:
         c = ki.workload(ki.PREFILL)

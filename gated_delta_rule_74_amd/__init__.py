@@ -116,6 +116,57 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _need(t, shape, dtype, name):
+    """Raise ValueError unless tensor t (skipped when None) has exactly this
+    shape and dtype: the C ABI takes bare pointers and derives every extent
+    from the sizes passed with them, so a mismatch would read or write past
+    a buffer."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(int(d) for d in shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected "
+                         f"{tuple(int(d) for d in shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+
+
+def _io_dtype(t, name):
+    if t.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"{name}: dtype {t.dtype}, expected float32 or "
+                         "bfloat16")
+    return t.dtype
+
+
+def _check_gates(g, beta, lead, Dk):
+    """g [*lead, Dk] (per channel) or [*lead] (per head); beta [*lead] in
+    g's dtype."""
+    gd = _io_dtype(g, "g")
+    if g.dim() == len(lead) + 1:
+        _need(g, (*lead, Dk), gd, "g")
+    else:
+        _need(g, lead, gd, "g (per-head gate)")
+    _need(beta, lead, gd, "beta (must have g's dtype)")
+
+
+def _check_conv(conv, B, T, H, Dk, Dv, io):
+    W = int(conv.get("width", conv["wq"].shape[-1]))
+    for n, D in (("xq", Dk), ("xk", Dk), ("xv", Dv)):
+        _need(conv[n], (B, T, H * D), io, n)
+    for n, D in (("wq", Dk), ("wk", Dk), ("wv", Dv)):
+        _need(conv[n], (H * D, W), torch.float32, n)
+    return W
+
+
+def _check_prefill(q, k, v, g, beta, conv, B, T, H, Dk, Dv, io):
+    if conv is None:
+        _need(q, (B, T, H, Dk), io, "q")
+        _need(k, (B, T, H, Dk), io, "k (must have q's dtype)")
+        _need(v, (B, T, H, Dv), io, "v (must have q's dtype)")
+    else:
+        _check_conv(conv, B, T, H, Dk, Dv, io)
+    _check_gates(g, beta, (B, T, H), Dk)
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -145,6 +196,9 @@ def _conv_desc(conv):
 
 
 def _prefill_shapes(q, v, g, conv):
+    if g.dim() not in (3, 4):
+        raise ValueError(f"g has {g.dim()} dimensions (expected 4, or 3 "
+                         "for a per-head gate)")
     if g.dim() == 4:
         B, T, H, Dk = g.shape
     else:  # per-head gate [B,T,H]
@@ -154,8 +208,11 @@ def _prefill_shapes(q, v, g, conv):
         Dv = conv["xv"].shape[-1] // H
         io = conv["xq"]
     else:
+        if q is None or v is None:
+            raise ValueError("q, k and v are required without a conv")
         Dv = v.shape[-1]
         io = q
+    _io_dtype(io, "q" if conv is None else "xq")
     return B, T, H, Dk, Dv, io
 
 
@@ -174,6 +231,10 @@ def kda_prefill(q, k, v, g, beta, *, s0=None, chunk=64, scale=1.0,
     be [B,T,H], one log-decay per token-head shared by the key channels).
     Returns (o [B,T,H,Dv], final state [B,H,Dk,Dv] fp32 or None)."""
     B, T, H, Dk, Dv, io = _prefill_shapes(q, v, g, conv)
+    _check_prefill(q, k, v, g, beta, conv, B, T, H, Dk, Dv, io.dtype)
+    _need(s0, (B, H, Dk, Dv), torch.float32, "s0")
+    _need(s_out, (B, H, Dk, Dv), torch.float32, "s_out")
+    _need(o, (B, T, H, Dv), io.dtype, "o")
     if o is None:
         o = torch.empty((B, T, H, Dv), dtype=io.dtype, device=g.device)
     if s_out is None and want_state:
@@ -195,9 +256,13 @@ def kda_prefill_chunk_prep(q, k, v, g, beta, workspace, *, chunk=64,
                            scale=1.0, conv=None, Dv=None, stream=None):
     """First prefill phase alone (chunk-local factors -> workspace)."""
     B, T, H, Dk, Dv_, io = _prefill_shapes(q, v, g, conv)
+    if Dv is not None and conv is None and int(Dv) != Dv_:
+        raise ValueError(f"Dv={Dv} but v has {Dv_} columns")
+    Dv_ = Dv_ if Dv is None else int(Dv)
+    _check_prefill(q, k, v, g, beta, conv, B, T, H, Dk, Dv_, io.dtype)
     cd, _keep = _conv_desc(conv)
     st = _prep(_ptr(q), _ptr(k), _ptr(v), _dt(io), _ptr(g), _ptr(beta),
-               _gate_dt(g, 4), B, T, H, Dk, Dv_ if Dv is None else Dv, chunk, scale,
+               _gate_dt(g, 4), B, T, H, Dk, Dv_, chunk, scale,
                cd, _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "kda_prefill_chunk_prep")
 
@@ -205,6 +270,10 @@ def kda_prefill_chunk_prep(q, k, v, g, beta, workspace, *, chunk=64,
 def kda_prefill_state_pass(workspace, o, *, s0=None, s_out=None, B, T, H,
                            Dk, Dv, chunk=64, stream=None):
     """Second prefill phase alone (sequential state pass -> o, s_out)."""
+    io = _io_dtype(o, "o")
+    _need(o, (B, T, H, Dv), io, "o")
+    _need(s0, (B, H, Dk, Dv), torch.float32, "s0")
+    _need(s_out, (B, H, Dk, Dv), torch.float32, "s_out")
     st = _state(_dt(o), _ptr(s0), _ptr(s_out), _ptr(o), B, T, H, Dk, Dv,
                 chunk, _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "kda_prefill_state_pass")
@@ -226,6 +295,11 @@ def kda_prefill_backward(q, k, v, g, beta, do, *, s0=None, dsT=None,
     shaped like g."""
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
+    io = _io_dtype(q, "q")
+    _check_prefill(q, k, v, g, beta, None, B, T, H, Dk, Dv, io)
+    _need(do, (B, T, H, Dv), io, "do (must have q's dtype)")
+    _need(s0, (B, H, Dk, Dv), torch.float32, "s0")
+    _need(dsT, (B, H, Dk, Dv), torch.float32, "dsT")
     dev = q.device
     dq, dk = torch.empty_like(q), torch.empty_like(k)
     dv = torch.empty_like(v)
@@ -251,6 +325,12 @@ def kda_decode_step(q, k, v, g, beta, state, *, scale=1.0, o=None,
     Returns o [N,H,Dv]."""
     N, H, Dk = q.shape
     Dv = v.shape[-1]
+    io = _io_dtype(q, "q")
+    _need(k, (N, H, Dk), io, "k (must have q's dtype)")
+    _need(v, (N, H, Dv), io, "v (must have q's dtype)")
+    _check_gates(g, beta, (N, H), Dk)
+    _need(state, (N, H, Dk, Dv), torch.float32, "state")
+    _need(o, (N, H, Dv), io, "o")
     if o is None:
         o = torch.empty((N, H, Dv), dtype=q.dtype, device=q.device)
     st = _decode(_ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(g), _ptr(beta),
@@ -286,6 +366,18 @@ def kda_decode_tokens(q, k, v, g, beta, state_in, *, state_out=None,
     else:
         Dv = v.shape[-1]
         io = q
+    iod = _io_dtype(io, "q" if conv is None else "xq")
+    _check_prefill(q, k, v, g, beta, conv, N, L, H, Dk, Dv, iod)
+    _need(state_in, (N, H, Dk, Dv), torch.float32, "state_in")
+    _need(state_out, (N, H, Dk, Dv), torch.float32, "state_out")
+    _need(o, (N, L, H, Dv), iod, "o")
+    if conv is not None:
+        W = _check_conv(conv, N, L, H, Dk, Dv, iod)
+        for n, c in (("conv_state", conv_state),
+                     ("conv_state_out", conv_state_out)):
+            _need(c, (N, 3, H * max(Dk, Dv), W - 1), torch.float32, n)
+    elif conv_state is not None or conv_state_out is not None:
+        raise ValueError("conv_state without conv")
     if o is None:
         o = torch.empty((N, L, H, Dv), dtype=io.dtype, device=g.device)
     if state_out is None:
@@ -296,6 +388,7 @@ def kda_decode_tokens(q, k, v, g, beta, state_in, *, state_out=None,
                          device=g.device)
     elif token_states is not False and token_states is not None:
         ts = token_states
+        _need(ts, (N, L, H, Dk, Dv), torch.float32, "token_states")
     cd, _keep = _conv_desc(conv)
     st = _decode_tokens(_ptr(q), _ptr(k), _ptr(v), _dt(io), _ptr(g),
                         _ptr(beta), _gate_dt(g, 4), _ptr(state_in), _ptr(state_out),
@@ -314,6 +407,13 @@ def kda_conv_prologue(xq, xk, xv, wq, wk, wv, *, H, Dk, Dv, conv_state=None,
     is fp32 [B,3,H*max(Dk,Dv),W-1], read then updated in place."""
     B, T, _ = xq.shape
     W = wq.shape[-1]
+    io = _io_dtype(xq, "xq")
+    _check_conv(dict(xq=xq, xk=xk, xv=xv, wq=wq, wk=wk, wv=wv), B, T, H, Dk,
+                Dv, io)
+    _need(conv_state, (B, 3, H * max(Dk, Dv), W - 1), torch.float32,
+          "conv_state")
+    for n, t, D in (("q", q, Dk), ("k", k, Dk), ("v", v, Dv)):
+        _need(t, (B, T, H, D), io, n)
     if q is None:
         q = torch.empty((B, T, H, Dk), dtype=xq.dtype, device=xq.device)
     if k is None:

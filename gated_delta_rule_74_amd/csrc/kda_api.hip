@@ -25,6 +25,15 @@ bool pair_ok(kda_dtype io, kda_dtype gt) {
   return (io == KDA_F32 && gt == KDA_F32) ||
          (io == KDA_BF16 && (gt == KDA_F32 || gt == KDA_BF16));
 }
+// Chunk length the kernels run for a requested chunk.  The chunked form is
+// exact algebra for any chunk length, so this changes only rounding: fp32
+// q/k/v with d_k = 128 runs a requested 64-token chunk as two 32-token
+// chunks, because the chunk prep's LDS for a 64-token fp32 chunk at
+// d_k = 128 exceeds the 160 KiB of one CU.
+int run_chunk(kda_dtype io, int Dk, int chunk) {
+  return (io == KDA_F32 && Dk == 128 && chunk == 64) ? 32 : chunk;
+}
+
 kda_status hip_status(hipError_t e) {
   if (e == hipSuccess) return KDA_OK;
   (void)hipGetLastError();
@@ -62,8 +71,8 @@ kda_status prefill_check(const void *q, const void *k, const void *v,
   }
   if (!dim_ok(Dk) || !dim_ok(Dv) || !chunk_ok(chunk)) return KDA_EUNSUPPORTED;
   if (!pair_ok(io, gt)) return KDA_EUNSUPPORTED;
-  if (io == KDA_F32 && Dk == 128 && chunk == 64) return KDA_EUNSUPPORTED;
   if (need_inputs && conv && conv->width > 4) return KDA_EUNSUPPORTED;
+  chunk = run_chunk(io, Dk, chunk);
   const long long nc = ((long long)T + chunk - 1) / chunk;
   if ((long long)B * H * nc > 0x7fffffffLL) return KDA_EUNSUPPORTED;
   if ((long long)B * H * (Dv / 16) > 0x7fffffffLL) return KDA_EUNSUPPORTED;
@@ -85,6 +94,7 @@ kda_status prefill_check(const void *q, const void *k, const void *v,
 
 size_t ws_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
                 kda_dtype io) {
+  chunk = run_chunk(io, Dk, chunk);
   const size_t nc = ((size_t)T + chunk - 1) / chunk;
   const kda::WsLayout L = kda::ws_layout(Dk, Dv, chunk, io == KDA_BF16 ? 2 : 4);
   return (size_t)B * H * nc * L.bytes;
@@ -99,9 +109,11 @@ struct BwdWs {
 };
 BwdWs bwd_ws(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype io) {
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const int requested = chunk;
+  chunk = run_chunk(io, Dk, chunk);
   const size_t nc = ((size_t)T + chunk - 1) / chunk, BH = (size_t)B * H;
   BwdWs w;
-  size_t off = al(ws_bytes(B, T, H, Dk, Dv, chunk, io));
+  size_t off = al(ws_bytes(B, T, H, Dk, Dv, requested, io));
   w.sc = off;
   off = al(off + BH * nc * Dk * Dv * 4);
   w.dsc = off;
@@ -116,6 +128,25 @@ BwdWs bwd_ws(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype io) {
   off = al(off + (size_t)B * T * H * Dv * (io == KDA_BF16 ? 2 : 4));
   w.total = off;
   return w;
+}
+
+// validation of kda_prefill's arguments (everything but
+// the workspace); fills p without it
+kda_status prefill_args(const void *q, const void *k, const void *v,
+                        kda_dtype io, const void *g, const void *beta,
+                        kda_dtype gt, const float *s0, float *s_out, void *o,
+                        int B, int T, int H, int Dk, int Dv, int chunk,
+                        float scale, const kda_conv_desc *conv,
+                        kda::PrefillParams &p) {
+  kda_status st = prefill_check(q, k, v, io, g, beta, gt, B, T, H, Dk, Dv,
+                                chunk, scale, conv, true, p);
+  if (st != KDA_OK) return st;
+  if (!o) return KDA_EINVAL;
+  if (!aligned16(o) || (s0 && !aligned16(s0)) || (s_out && !aligned16(s_out)))
+    return KDA_EINVAL;
+  if (o == q || o == k || o == v || o == g || o == beta) return KDA_EINVAL;
+  p.s0 = s0; p.s_out = s_out; p.o = o;
+  return KDA_OK;
 }
 
 }  // namespace
@@ -148,7 +179,6 @@ size_t kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv,
   if (B <= 0 || T <= 0 || H <= 0 || !dim_ok(Dk) || !dim_ok(Dv) ||
       !chunk_ok(chunk) || !dtype_valid(qkv_dtype))
     return 0;
-  if (qkv_dtype == KDA_F32 && Dk == 128 && chunk == 64) return 0;
   return ws_bytes(B, T, H, Dk, Dv, chunk, qkv_dtype);
 }
 
@@ -167,7 +197,7 @@ kda_status kda_prefill_chunk_prep(const void *q, const void *k, const void *v,
   if (workspace_bytes < ws_bytes(B, T, H, Dk, Dv, chunk, qkv_dtype))
     return KDA_EINVAL;
   p.ws = (char *)workspace;
-  p.wsb = kda::ws_layout(Dk, Dv, chunk, qkv_dtype == KDA_BF16 ? 2 : 4).bytes;
+  p.wsb = kda::ws_layout(Dk, Dv, p.C, qkv_dtype == KDA_BF16 ? 2 : 4).bytes;
   return hip_status(kda::launch_prefill_prep(p, qkv_dtype == KDA_BF16,
                                              (hipStream_t)stream));
 }
@@ -190,7 +220,7 @@ kda_status kda_prefill_state_pass(kda_dtype qkv_dtype, const float *s0,
     return KDA_EINVAL;
   p.s0 = s0; p.s_out = s_out; p.o = o;
   p.ws = (char *)workspace;
-  p.wsb = kda::ws_layout(Dk, Dv, chunk, qkv_dtype == KDA_BF16 ? 2 : 4).bytes;
+  p.wsb = kda::ws_layout(Dk, Dv, p.C, qkv_dtype == KDA_BF16 ? 2 : 4).bytes;
   return hip_status(kda::launch_state_pass(p, qkv_dtype == KDA_BF16,
                                            (hipStream_t)stream));
 }
@@ -203,19 +233,15 @@ kda_status kda_prefill(const void *q, const void *k, const void *v,
                        void *workspace, size_t workspace_bytes,
                        void *stream) {
   kda::PrefillParams p;
-  kda_status st = prefill_check(q, k, v, qkv_dtype, g, beta, gate_dtype, B, T,
-                                H, Dk, Dv, chunk, scale, conv, true, p);
+  kda_status st = prefill_args(q, k, v, qkv_dtype, g, beta, gate_dtype, s0,
+                               s_out, o, B, T, H, Dk, Dv, chunk, scale, conv,
+                               p);
   if (st != KDA_OK) return st;
-  if (!o || !workspace) return KDA_EINVAL;
-  if (!aligned16(o) || !aligned16(workspace) || (s0 && !aligned16(s0)) ||
-      (s_out && !aligned16(s_out)))
-    return KDA_EINVAL;
-  if (o == q || o == k || o == v || o == g || o == beta) return KDA_EINVAL;
+  if (!workspace || !aligned16(workspace)) return KDA_EINVAL;
   if (workspace_bytes < ws_bytes(B, T, H, Dk, Dv, chunk, qkv_dtype))
     return KDA_EINVAL;
-  p.s0 = s0; p.s_out = s_out; p.o = o;
   p.ws = (char *)workspace;
-  p.wsb = kda::ws_layout(Dk, Dv, chunk, qkv_dtype == KDA_BF16 ? 2 : 4).bytes;
+  p.wsb = kda::ws_layout(Dk, Dv, p.C, qkv_dtype == KDA_BF16 ? 2 : 4).bytes;
   const int bf = qkv_dtype == KDA_BF16;
   hipError_t e = kda::launch_prefill_prep(p, bf, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e);
@@ -258,7 +284,7 @@ kda_status kda_prefill_backward(
     for (int j = i + 1; j < 6; ++j)
       if (all_out[j] == all_out[i]) return KDA_EINVAL;
   }
-  if (!kda::backward_fits(qkv_dtype == KDA_BF16, Dk, chunk))
+  if (!kda::backward_fits(qkv_dtype == KDA_BF16, Dk, p.C))
     return KDA_EUNSUPPORTED;
   const BwdWs L = bwd_ws(B, T, H, Dk, Dv, chunk, qkv_dtype);
   if (workspace_bytes < L.total) return KDA_EINVAL;
@@ -270,7 +296,7 @@ kda_status kda_prefill_backward(
   p.s_out = nullptr;
   p.o = wsb + L.o;
   p.ws = wsb;
-  p.wsb = kda::ws_layout(Dk, Dv, chunk, bf ? 2 : 4).bytes;
+  p.wsb = kda::ws_layout(Dk, Dv, p.C, bf ? 2 : 4).bytes;
   p.ckpt = (float *)(wsb + L.sc);
   p.train_at = (float *)(wsb + L.at);
   hipError_t e = kda::launch_prefill_prep(p, bf, s);

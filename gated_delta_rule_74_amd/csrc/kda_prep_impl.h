@@ -146,9 +146,10 @@ __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
   const int t0 = n * C;
   const int tlast = T - 1;
   const size_t tok0 = (size_t)b * T;  // first token row of batch b
-  // 64-bit bases of (batch b, head h); in-batch offsets fit in 32 bits
+  // 64-bit bases of (batch b, head h) and 64-bit row offsets (a batch
+  // may hold more than 2^32 elements)
   const size_t kb = (tok0 * H + h) * DK;
-  const unsigned rowK = (unsigned)(H * DK);
+  const size_t rowK = (size_t)H * DK;
   if ((PART & 1) && tid < 64) {
     const size_t bi = (tok0 + (unsigned)min(t0 + tid, tlast)) * H + h;
     st.beta = GB ? (uint32_t)((const unsigned short *)p.beta)[bi]
@@ -191,10 +192,10 @@ __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
         st.g[i].x = GB ? (unsigned)((const unsigned short *)p.g)[gi]
                        : ((const unsigned *)p.g)[gi];
       } else if (GB) {
-        const uint2 v = ld_stream<uint2>(gh + t * rowK);
+        const uint2 v = ld_stream<uint2>(gh + (size_t)t * rowK);
         st.g[i] = make_uint4(v.x, v.y, 0u, 0u);
       } else {
-        st.g[i] = ld_stream<uint4>(gf + t * rowK);
+        st.g[i] = ld_stream<uint4>(gf + (size_t)t * rowK);
       }
     }
     const IO *xq = (const IO *)(CONV ? p.xq : p.q) + kb + 4 * cq;
@@ -203,21 +204,21 @@ __device__ __forceinline__ void prep_load(const PrefillParams &p, int task,
     for (int i = 0; i < Stage<IO, CONV>::XR; ++i) {
       const unsigned t =
           (unsigned)min(max(t0 + 8 * tg + i - (CONV ? 3 : 0), 0), tlast);
-      if (PART & 2) st.xq[i] = ld_stream<R>(xq + t * rowK);
-      if (PART & 4) st.xk[i] = ld_stream<R>(xk + t * rowK);
+      if (PART & 2) st.xq[i] = ld_stream<R>(xq + (size_t)t * rowK);
+      if (PART & 4) st.xk[i] = ld_stream<R>(xk + (size_t)t * rowK);
     }
   }
   const int NQV = Dv / 4;
   if ((PART & 8) && tid < NQV * NTG) {
     const int cv = tid % NQV, tg = tid / NQV;
-    const unsigned rowV = (unsigned)(H * Dv);
+    const size_t rowV = (size_t)H * Dv;
     const IO *xv = (const IO *)(CONV ? p.xv : p.v) + (tok0 * H + h) * Dv +
                    4 * cv;
 #pragma unroll
     for (int i = 0; i < Stage<IO, CONV>::XR; ++i) {
       const unsigned t =
           (unsigned)min(max(t0 + 8 * tg + i - (CONV ? 3 : 0), 0), tlast);
-      st.xv[i] = ld_stream<R>(xv + t * rowV);
+      st.xv[i] = ld_stream<R>(xv + (size_t)t * rowV);
     }
   }
 }

@@ -39,8 +39,11 @@
  *    states: [B,H,Dk,Dv] fp32 with row i = key channel i.
  *  - Supported: Dk, Dv in {16,32,64,128}; chunk in {16,32,64}; conv width in
  *    [2,4]; dtype pairs (q/k/v, g/beta) in {(F32,F32), (BF16,F32),
- *    (BF16,BF16)}; fp32 q/k/v with Dk = 128 needs chunk <= 32.  Outputs
- *    o have the q/k/v dtype; states are always fp32.
+ *    (BF16,BF16)}.  fp32 q/k/v with Dk = 128 and chunk 64 run as 32-token
+ *    chunks (the chunked form is exact for any chunk length, so only the
+ *    rounding differs; a 64-token fp32 chunk at Dk = 128 does not fit one
+ *    CU's LDS), and the workspace sizes follow.  Outputs o have the q/k/v
+ *    dtype; states are always fp32.
  *  - Element values are not checked: g > 0 or beta outside (0,2) are the
  *    caller's responsibility (the pages keep beta in (0,1), or (0,2) with
  *    negative eigenvalues allowed); g = -inf is supported and forgets

@@ -176,8 +176,11 @@ class Oracle:
         """Whole layer forward: optional conv prologue, then the recurrence.
         conv: dict(xq, xk, xv, wq, wk, wv, eps, l2norm_qk) or None."""
         if conv is not None:
-            B, T, H, Dk = self._f64(g).shape
-            Dv = self._f64(conv["xv"]).shape[-1] // H
+            # heads from beta [B,T,H], so g may be per channel [B,T,H,Dk]
+            # or per head [B,T,H]; head sizes from the raw channel counts
+            H = beta.shape[2]
+            Dk = conv["xq"].shape[-1] // H
+            Dv = conv["xv"].shape[-1] // H
             q, k, v, _ = self.conv_prologue(
                 conv["xq"], conv["xk"], conv["xv"], conv["wq"], conv["wk"],
                 conv["wv"], H, Dk, Dv, conv.get("eps", 1e-6),

@@ -36,6 +36,13 @@ What each pin fixes (pages: see the header of oracle/kda_oracle.h):
                   left padding W-1), with and without a history.
   conv_identity   taps (0,..,0,1) give the identity; the history update.
   l2_numpy        L2 norm equals x / sqrt(||x||^2 + eps) via numpy.linalg.
+  conv_prologue   the prologue composition (Oracle.conv_prologue and
+                  Oracle.prefill(conv=...)): each stream [B,T,H*D] through
+                  torch conv1d, split into heads as [B,T,H,D] (head h owns
+                  channels h*D .. h*D+D-1), q and k scaled per head to
+                  x / sqrt(||x||^2 + eps) with numpy, v left raw; d_k != d_v,
+                  H = 3, with and without a history, per-channel and per-head
+                  gates through the prefill.
   bwd_fd          the gradient (backward) equals central finite differences
                   of the forward oracle's loss sum(o*dO) + sum(S_T*dS_T) for
                   every input (q, k, v, g, beta, S0), per-channel and per-head
@@ -314,6 +321,74 @@ def pin_l2_numpy(orc):
     _close(y, x / np.sqrt(n * n + eps), what="l2")
 
 
+def _conv_ref(x, w, hist=None):
+    """torch conv1d over [B,T,C] (groups = C, taps newest last), with the
+    history prepended or W-1 zeros of left padding."""
+    xt = torch.from_numpy(np.asarray(x, dtype=np.float64)).permute(0, 2, 1)
+    wt = torch.from_numpy(np.asarray(w, dtype=np.float64))[:, None, :]
+    C, W = w.shape
+    if hist is None:
+        y = torch.nn.functional.conv1d(xt, wt, groups=C,
+                                       padding=W - 1)[..., :xt.shape[-1]]
+    else:
+        xt = torch.cat([torch.from_numpy(hist), xt], dim=-1)
+        y = torch.nn.functional.conv1d(xt, wt, groups=C)
+    return y.permute(0, 2, 1).numpy()
+
+
+def pin_conv_prologue(orc):
+    rng = np.random.default_rng(15)
+    B, T, H, Dk, Dv, W, eps = 2, 9, 3, 4, 6, 4, 1e-6
+    xq = rng.standard_normal((B, T, H * Dk))
+    xk = rng.standard_normal((B, T, H * Dk))
+    xv = rng.standard_normal((B, T, H * Dv))
+    # taps differ per channel so a wrong channel-to-head split shows
+    wq = 0.5 * rng.standard_normal((H * Dk, W))
+    wk = 0.5 * rng.standard_normal((H * Dk, W))
+    wv = 0.5 * rng.standard_normal((H * Dv, W))
+
+    def heads_l2(y, D, norm):
+        y = y.reshape(B, T, H, D)  # head h = channels [h*D, (h+1)*D)
+        if norm:
+            n = np.linalg.norm(y, axis=-1, keepdims=True)
+            y = y / np.sqrt(n * n + eps)
+        return y
+
+    for hist in (None, tuple(rng.standard_normal((B, H * D, W - 1))
+                             for D in (Dk, Dk, Dv))):
+        hq, hk, hv = (None, None, None) if hist is None else hist
+        want = (heads_l2(_conv_ref(xq, wq, hq), Dk, True),
+                heads_l2(_conv_ref(xk, wk, hk), Dk, True),
+                heads_l2(_conv_ref(xv, wv, hv), Dv, False))
+        got = orc.conv_prologue(xq, xk, xv, wq, wk, wv, H, Dk, Dv, eps,
+                                True, hist)
+        for name, a, b in zip("qkv", got[:3], want):
+            _close(a, b, what=f"prologue {name} hist={hist is not None}")
+        # without the norm all three streams are the raw conv
+        got = orc.conv_prologue(xq, xk, xv, wq, wk, wv, H, Dk, Dv, eps,
+                                False, hist)
+        _close(got[0], heads_l2(_conv_ref(xq, wq, hq), Dk, False),
+               what="prologue q, no norm")
+        if hist is not None:
+            for i, (x, hh) in enumerate(((xq, hq), (xk, hk), (xv, hv))):
+                cat = np.concatenate([hh, x.transpose(0, 2, 1)], axis=-1)
+                _close(got[3][i], cat[..., -(W - 1):], what=f"history {i}")
+    # the whole forward with the prologue: the recurrence (pinned above) on
+    # the q, k, v built here, for a per-channel and a per-head gate
+    q, k, v = (heads_l2(_conv_ref(xq, wq), Dk, True),
+               heads_l2(_conv_ref(xk, wk), Dk, True),
+               heads_l2(_conv_ref(xv, wv), Dv, False))
+    g = -np.log1p(np.exp(rng.standard_normal((B, T, H, Dk))))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))
+    conv = dict(xq=xq, xk=xk, xv=xv, wq=wq, wk=wk, wv=wv, eps=eps,
+                l2norm_qk=True)
+    for gate in (g, g[..., 1].copy()):
+        o, s = orc.prefill(None, None, None, gate, beta, None, 0.9, conv=conv)
+        ro, rs = orc.recurrence(q, k, v, gate, beta, None, 0.9)
+        _close(o, ro, what=f"prefill conv o (gate ndim {gate.ndim})")
+        _close(s, rs, what=f"prefill conv S (gate ndim {gate.ndim})")
+
+
 def _fd_check(orc, args, scale, do, dsT, elems, tol, what):
     """Central differences (h = 1e-6) of the forward loss for the chosen
     elements of each argument against orc.backward."""
@@ -393,5 +468,6 @@ def pin_bwd_one_token(orc):
 ALL_PINS = [pin_one_token, pin_frozen, pin_pure_decay, pin_forget_restart,
             pin_retrieval, pin_dense_unrolled, pin_contraction,
             pin_scalar_gate, pin_neg_eigen, pin_linearity, pin_column_split, pin_head_perm,
-            pin_conv_torch, pin_conv_identity, pin_l2_numpy, pin_bwd_fd,
+            pin_conv_torch, pin_conv_identity, pin_l2_numpy,
+            pin_conv_prologue, pin_bwd_fd,
             pin_bwd_one_token]

@@ -49,7 +49,9 @@ def test_workspace_size():
     for bad in [(0, 8, 1, 16, 16, 16), (1, 8, 1, 48, 16, 16),
                 (1, 8, 1, 16, 16, 8), (1, 8, 1, 16, 256, 16)]:
         assert ws(*bad, kda.KDA_BF16) == 0
-    assert ws(1, 64, 1, 128, 128, 64, kda.KDA_F32) == 0  # LDS limit
+    # fp32 at d_k = 128 runs 64-token requests as 32-token chunks
+    assert ws(1, 64, 1, 128, 128, 64, kda.KDA_F32) == \
+        ws(1, 64, 1, 128, 128, 32, kda.KDA_F32) > 0
 
 
 def _prefill(**kw):
@@ -78,7 +80,9 @@ def _prefill(**kw):
     (dict(Dk=48), kda.KDA_EUNSUPPORTED),
     (dict(Dv=256), kda.KDA_EUNSUPPORTED),
     (dict(io=kda.KDA_F32, gt=kda.KDA_BF16), kda.KDA_EUNSUPPORTED),
-    (dict(io=kda.KDA_F32, Dk=128, Dv=128, chunk=64), kda.KDA_EUNSUPPORTED),
+    # fp32 at d_k = 128 runs chunk 64 as 32-token chunks: accepted, and the
+    # workspace it needs is the 32-token chunks' (too small here)
+    (dict(io=kda.KDA_F32, Dk=128, Dv=128, chunk=64, wsb=1024), kda.KDA_EINVAL),
     # the per-head gate flag belongs to the gate dtype only
     (dict(io=kda.KDA_BF16 | kda.KDA_GATE_HEAD), kda.KDA_EINVAL),
     (dict(gt=2 | kda.KDA_GATE_HEAD), kda.KDA_EINVAL),
@@ -188,3 +192,69 @@ def _conv(**kw):
 ])
 def test_conv_rejects(kw, want):
     assert _conv(**kw) == want
+
+
+# ---------------------------------------------------------------------------
+# The Python binding checks shapes and dtypes before it passes any pointer:
+# these raise on the CPU (with CPU tensors) before any launch is attempted,
+# with the mismatch named rather than the device complaint.
+
+def _t(*shape, dt=None):
+    import torch
+    return torch.zeros(shape, dtype=dt or torch.bfloat16)
+
+
+def test_binding_rejects_mismatched_prefill_inputs():
+    import torch
+    B, T, H, D = 1, 8, 2, 16
+    f32 = torch.float32
+    q, k, v = _t(B, T, H, D), _t(B, T, H, D), _t(B, T, H, D)
+    g, beta = _t(B, T, H, D, dt=f32), _t(B, T, H, dt=f32)
+    cases = [
+        (dict(beta=_t(B, T, H)), "beta"),                # bf16 beta, fp32 g
+        (dict(k=_t(B, T, H, D, dt=f32)), "k"),           # k not in q's dtype
+        (dict(v=_t(B, T, H, 2 * D, dt=f32)), "v"),
+        (dict(k=_t(B, T, H, 2 * D)), "k"),               # wrong size
+        (dict(beta=_t(B, T + 1, H, dt=f32)), "beta"),
+        (dict(g=_t(B, T, H, 2 * D, dt=f32)), "q"),       # g says Dk = 32
+        (dict(g=_t(B, T, dt=f32)), "g"),                 # 2-d gate
+    ]
+    for over, what in cases:
+        a = dict(q=q, k=k, v=v, g=g, beta=beta)
+        a.update(over)
+        with pytest.raises(ValueError, match=what):
+            kda.kda_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"])
+    with pytest.raises(ValueError, match="s0"):
+        kda.kda_prefill(q, k, v, g, beta, s0=_t(B, H, D, D))  # bf16 state
+    with pytest.raises(ValueError, match="o"):
+        kda.kda_prefill(q, k, v, g, beta, o=_t(B, T, H, 2 * D))
+    with pytest.raises(ValueError, match="do"):
+        kda.kda_prefill_backward(q, k, v, g, beta, _t(B, T, H, D, dt=f32))
+
+
+def test_binding_rejects_mismatched_decode_and_conv_inputs():
+    import torch
+    N, H, D, W = 3, 2, 16, 4
+    f32 = torch.float32
+    q = _t(N, H, D)
+    st = _t(N, H, D, D, dt=f32)
+    with pytest.raises(ValueError, match="beta"):
+        kda.kda_decode_step(q, q, q, _t(N, H, D, dt=f32), _t(N, H), st)
+    with pytest.raises(ValueError, match="state"):
+        kda.kda_decode_step(q, q, q, _t(N, H, D), _t(N, H), _t(N, H, D, D))
+    x = _t(1, 5, H * D)
+    w = _t(H * D, W, dt=f32)
+    with pytest.raises(ValueError, match="wk"):
+        kda.kda_conv_prologue(x, x, x, w, _t(H * D, W), w, H=H, Dk=D, Dv=D)
+    with pytest.raises(ValueError, match="xv"):
+        kda.kda_conv_prologue(x, x, _t(1, 5, 2 * H * D), w, w, w, H=H, Dk=D,
+                              Dv=D)
+    with pytest.raises(ValueError, match="conv_state"):
+        kda.kda_conv_prologue(x, x, x, w, w, w, H=H, Dk=D, Dv=D,
+                              conv_state=_t(1, 3, H * D, W, dt=f32))
+    xt = _t(N, 2, H * D)
+    conv = dict(xq=xt, xk=xt, xv=xt, wq=w, wk=w, wv=w, width=W)
+    with pytest.raises(ValueError, match="conv_state"):
+        kda.kda_decode_tokens(None, None, None, _t(N, 2, H), _t(N, 2, H), st,
+                              conv=conv, conv_state=_t(N, 3, H * D, W - 2,
+                                                       dt=f32))

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import kda_inputs as ki
-from gpu_common import TOL, rel_err, say, to_cpu64
+from gpu_common import TOL, check, rel_err, say, to_cpu64
 
 pytestmark = pytest.mark.gpu
 
@@ -43,8 +43,7 @@ def _check(orc, kda, x, qkv, C, scale=0.9, head_gate=False, tol=None):
 CASES = []
 for D in (16, 32, 64, 128):
     for C in (16, 32, 64):
-        if not (D == 128 and C == 64):
-            CASES.append(("f32", "f32", D, D, C))
+        CASES.append(("f32", "f32", D, D, C))
         CASES.append(("bf16", "f32", D, D, C))
 CASES += [("bf16", "bf16", 128, 128, 64), ("bf16", "f32", 64, 128, 64),
           ("f32", "f32", 32, 64, 32)]
@@ -78,9 +77,9 @@ def test_backward_beta_to_two_and_forgetting(orc, kda, qkv):
 
 def test_backward_model_shaped_t8192(orc, kda):
     """The headline shape (B1 T8192 H32 D128 C64, bf16 q/k/v, fp32 g/beta)
-    in one launch; the oracle's gradient on four sampled heads."""
+    in one launch; the oracle's gradient on every head."""
     c = ki.workload(ki.PREFILL)
-    say("backward B1 T8192 H32 D128 (sampled heads)")
+    say("backward B1 T8192 H32 D128, all heads")
     x = ki.workload_prefill_inputs(ki.PREFILL, device="cuda")
     B, T, H, D = c["B"], c["T"], c["H"], c["Dk"]
     gen = torch.Generator(device="cuda").manual_seed(99)
@@ -88,12 +87,7 @@ def test_backward_model_shaped_t8192(orc, kda):
     got = kda.kda_prefill_backward(x["q"], x["k"], x["v"], x["g"], x["beta"],
                                    do, chunk=c["chunk"])
     torch.cuda.synchronize()
-    heads = [0, 9, 22, 31]
-    sub = lambda t: t[:, :, heads].contiguous()
-    ref = orc.backward(sub(x["q"]), sub(x["k"]), sub(x["v"]), sub(x["g"]),
-                       sub(x["beta"]), None, 1.0, sub(do))
+    ref = orc.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], None, 1.0,
+                       do)
     for n, a, r in zip(NAMES, got, ref):
-        a = a[:, :, heads] if n != "ds0" else a[:, heads]
-        e = rel_err(a, r)
-        say(f"  {n} err {e:.2e}")
-        assert e <= TOL["bf16"], (n, e)
+        check(n, a, r, TOL["bf16"], (0, 1) if n == "ds0" else (0, 2))

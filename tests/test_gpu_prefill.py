@@ -1,8 +1,9 @@
 """GPU parity of the chunked prefill (kda_prefill through the C ABI) against
 the fp64 oracle: small shapes spanning several chunks and ragged tails for
 every supported head size and chunk size, the tiny fp32 workload, -inf and
-extreme gates (exact fallback path), and the full-size workloads on sampled
-heads.  Plus the invariants that pin the chunked algebra on the device:
+extreme gates (exact fallback path, with and without the fused conv), the
+two-slab build of the state pass, and the full-size workloads on every
+(batch, head).  Plus the invariants that pin the chunked algebra on the device:
 split-sequence state carry, prefill == repeated decode steps, no unwritten
 output (poisoned buffers)."""
 import numpy as np
@@ -10,7 +11,7 @@ import pytest
 import torch
 
 import kda_inputs as ki
-from gpu_common import TOL, rel_err, say, to_cpu64
+from gpu_common import TOL, check, rel_err, say, to_cpu64
 
 pytestmark = pytest.mark.gpu
 
@@ -32,8 +33,7 @@ def _run(kda, x, chunk, scale=1.0, s0=None, conv=None):
 CASES = []
 for D in (16, 32, 64, 128):
     for C in (16, 32, 64):
-        if not (D == 128 and C == 64):
-            CASES.append(("f32", "f32", D, D, C))
+        CASES.append(("f32", "f32", D, D, C))
         CASES.append(("bf16", "f32", D, D, C))
 CASES += [("bf16", "bf16", 128, 128, 64), ("bf16", "bf16", 32, 32, 16),
           ("bf16", "f32", 64, 128, 64), ("bf16", "f32", 128, 32, 32),
@@ -48,9 +48,8 @@ def test_prefill_small(orc, kda, qkv, gate, Dk, Dv, C):
     o, s = _run(kda, x, C, scale=0.9, s0=x["s0"])
     ro, rs = orc.recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"],
                             x["s0"], 0.9)
-    eo, es = rel_err(o, ro), rel_err(s, rs)
-    say(f"  err o={eo:.2e} S={es:.2e}")
-    assert eo <= TOL[qkv] and es <= TOL[qkv]
+    check("o", o, ro, TOL[qkv], (0, 2))
+    check("S", s, rs, TOL[qkv], (0, 1))
 
 
 def test_tiny_fp32_workload(orc, kda):
@@ -148,41 +147,98 @@ def test_poisoned_outputs_fully_written(kda):
 
 
 # ---------------------------------------------------------------------------
-# full-size workloads, checked on sampled heads
+# extreme gates at the headline head size, with and without the fused conv
+
+@pytest.mark.parametrize("conv_w", [0, 4])
+def test_forgetting_extremes_d128(orc, kda, conv_w):
+    """-inf and -60 gates at B = 2, d = 128, chunk 64, bf16 q/k/v and bf16
+    gates, T not a multiple of the chunk: the exact diagonal path with its
+    batch offsets and bf16 gate reads; with conv_w = 4 the raw k/q rows it
+    needs come from the fused prologue."""
+    say(f"prefill extremes d128 conv={conv_w}")
+    B, T, H, D = 2, 200, 3, 128
+    x = ki.prefill_inputs(B, T, H, D, D, qkv="bf16", gate="bf16",
+                          conv_width=conv_w, seed=17 + conv_w, device="cuda",
+                          with_s0=True)
+    g = x["g"]
+    g[1, 5] = -float("inf")              # batch 1 only: batch offsets
+    g[0, 70, :, 3] = -float("inf")       # one channel
+    g[:, 100:108] = -60.0
+    g[1, 191:] = -float("inf")           # in the ragged tail
+    conv = None
+    if conv_w:
+        conv = dict(xq=x["xq"], xk=x["xk"], xv=x["xv"], wq=x["wq"],
+                    wk=x["wk"], wv=x["wv"], width=conv_w, l2norm_qk=True,
+                    eps=1e-6)
+    o, s = _run(kda, x, 64, s0=x["s0"], conv=conv)
+    if conv_w:
+        sub = dict(conv, eps=1e-6, l2norm_qk=True)
+        ro, rs = orc.prefill(None, None, None, g, x["beta"], x["s0"],
+                             conv=sub)
+    else:
+        ro, rs = orc.recurrence(x["q"], x["k"], x["v"], g, x["beta"],
+                                x["s0"])
+    check("o", o, ro, TOL["bf16"], (0, 2))
+    check("S", s, rs, TOL["bf16"], (0, 1))
+
+
+# ---------------------------------------------------------------------------
+# the state pass's two-slab build: taken when there are at least twice as
+# many 16-column value slabs as compute units
+
+TWO_SLAB = [("f32", 64, 32, 8), ("f32", 32, 16, 16), ("bf16", 64, 32, 8),
+            ("bf16", 128, 16, 4), ("bf16", 32, 64, 16), ("bf16", 128, 32, 4)]
+
+
+@pytest.mark.parametrize("qkv,D,C,B", TWO_SLAB)
+def test_two_slab_state_pass(orc, kda, qkv, D, C, B):
+    H = 32
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert B * H * (D // 16) >= 2 * cus, "shape must select two slabs"
+    say(f"two-slab state pass qkv={qkv} D={D} C={C} B={B} H={H}")
+    x = ki.prefill_inputs(B, 2 * C + 9, H, D, D, qkv=qkv, gate="f32",
+                          seed=51 + D + C, device="cuda", with_s0=True)
+    o, s = _run(kda, x, C, scale=0.9, s0=x["s0"])
+    ro, rs = orc.recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"],
+                            x["s0"], 0.9)
+    check("o", o, ro, TOL[qkv], (0, 2))
+    check("S", s, rs, TOL[qkv], (0, 1))
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, every (batch, head) against the oracle
 
 def test_model_shaped_prefill_t8192(orc, kda):
     c = ki.workload(ki.PREFILL)
-    say("model-shaped prefill B1 T8192 H32 D128 C64")
+    say("model-shaped prefill B1 T8192 H32 D128 C64, all heads")
     x = ki.workload_prefill_inputs(ki.PREFILL, device="cuda")
     o, s = _run(kda, x, c["chunk"])
-    for h in (0, 13, 31):
-        sl = lambda t: t[:, :, h:h + 1]
-        ro, rs = orc.recurrence(sl(x["q"]), sl(x["k"]), sl(x["v"]),
-                                sl(x["g"]), sl(x["beta"]))
-        eo, es = rel_err(sl(o), ro), rel_err(s[:, h:h + 1], rs)
-        say(f"  head {h}: err o={eo:.2e} S={es:.2e}")
-        assert eo <= 2e-2 and es <= 2e-2
+    ro, rs = orc.recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"])
+    check("o", o, ro, 2e-2, (0, 2))
+    check("S", s, rs, 2e-2, (0, 1))
 
 
 def test_conv_prefill_b8_t4096(orc, kda):
     c = ki.workload(ki.CONV_PREFILL)
-    say("conv prefill B8 T4096 H32 D128 C64 (fused prologue)")
+    say("conv prefill B8 T4096 H32 D128 C64 (fused prologue), all (b, h)")
     x = ki.workload_prefill_inputs(ki.CONV_PREFILL, device="cuda")
     conv = dict(xq=x["xq"], xk=x["xk"], xv=x["xv"], wq=x["wq"], wk=x["wk"],
                 wv=x["wv"], width=4, l2norm_qk=True, eps=1e-6)
     o, s = _run(kda, x, c["chunk"], conv=conv)
-    D = c["Dk"]
-    for b, h in ((0, 0), (5, 17), (7, 31)):
-        cs = slice(h * D, (h + 1) * D)
-        sub = dict(xq=x["xq"][b:b + 1, :, cs], xk=x["xk"][b:b + 1, :, cs],
-                   xv=x["xv"][b:b + 1, :, cs], wq=x["wq"][cs], wk=x["wk"][cs],
-                   wv=x["wv"][cs], eps=1e-6, l2norm_qk=True)
-        ro, rs = orc.prefill(None, None, None, x["g"][b:b + 1, :, h:h + 1],
-                             x["beta"][b:b + 1, :, h:h + 1], conv=sub)
-        eo = rel_err(o[b:b + 1, :, h:h + 1], ro)
-        es = rel_err(s[b:b + 1, h:h + 1], rs)
-        say(f"  (b={b}, h={h}): err o={eo:.2e} S={es:.2e}")
-        assert eo <= 2e-2 and es <= 2e-2
+    # two batch rows at a time keeps the fp64 copies small
+    worst_o = worst_s = 0.0
+    for b0 in range(0, c["B"], 2):
+        bs = slice(b0, b0 + 2)
+        sub = dict(xq=x["xq"][bs], xk=x["xk"][bs], xv=x["xv"][bs],
+                   wq=x["wq"], wk=x["wk"], wv=x["wv"], eps=1e-6,
+                   l2norm_qk=True)
+        ro, rs = orc.prefill(None, None, None, x["g"][bs], x["beta"][bs],
+                             conv=sub)
+        worst_o = max(worst_o, check(f"o b{b0}-{b0 + 1}", o[bs], ro, 2e-2,
+                                     (0, 2))[1])
+        worst_s = max(worst_s, check(f"S b{b0}-{b0 + 1}", s[bs], rs, 2e-2,
+                                     (0, 1))[1])
+    say(f"  worst (b, h) slab: o {worst_o:.2e}, S {worst_s:.2e}")
 
 
 CONV_CASES = [("bf16", 128, 128, 2, 64), ("bf16", 64, 128, 3, 64),
@@ -228,17 +284,20 @@ def test_prefill_short_sequences(orc, kda, qkv, D, C, tk):
 
 
 def test_long_context_prefill_t262144(orc, kda):
+    """All 32 heads: o on the first and last 4096 tokens and the final state
+    (the oracle runs every token; 16 heads at a time bounds its memory)."""
     c = ki.workload(ki.LONG)
-    say("long-context prefill B1 T262144 H32 D128 C64 (sampled heads)")
+    say("long-context prefill B1 T262144 H32 D128 C64, all heads")
     x = ki.workload_prefill_inputs(ki.LONG, device="cuda")
     o, s = _run(kda, x, c["chunk"])
     n = 4096
-    for h in (3, 28):
-        sl = lambda t: t[:, :, h:h + 1]
+    for h0 in range(0, c["H"], 16):
+        hs = slice(h0, h0 + 16)
+        sl = lambda t: t[:, :, hs]
         ro, rs = orc.recurrence(sl(x["q"]), sl(x["k"]), sl(x["v"]),
                                 sl(x["g"]), sl(x["beta"]))
-        ef = rel_err(sl(o)[:, :n], ro[:, :n])
-        el = rel_err(sl(o)[:, -n:], ro[:, -n:])
-        es = rel_err(s[:, h:h + 1], rs)
-        say(f"  head {h}: err first={ef:.2e} last={el:.2e} S={es:.2e}")
-        assert ef <= 2e-2 and el <= 2e-2 and es <= 2e-2
+        tag = f"heads {h0}-{h0 + 15}"
+        check(f"o first 4096, {tag}", sl(o)[:, :n], ro[:, :n], 2e-2, (0, 2))
+        check(f"o last 4096, {tag}", sl(o)[:, -n:], ro[:, -n:], 2e-2, (0, 2))
+        check(f"S, {tag}", s[:, hs], rs, 2e-2, (0, 1))
+        del ro, rs

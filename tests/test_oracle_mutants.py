@@ -76,6 +76,16 @@ MUTANTS = {
 }
 
 
+# mistakes in the Python composition of the conv prologue (oracle/__init__.py)
+PY_MUTANTS = {
+    "py_l2_on_v": [("if l2norm_qk and i < 2:", "if l2norm_qk:")],
+    "py_heads_as_d_by_h": [("y = y.reshape(B, T, H, D)",
+                            "y = y.reshape(B, T, D, H).transpose(0, 1, 3, 2)")],
+    "py_history_ignored": [("None if hist is None else hist[i]", "None")],
+    "py_l2_only_q": [("if l2norm_qk and i < 2:", "if l2norm_qk and i < 1:")],
+}
+
+
 @pytest.fixture(scope="module")
 def tmpdir_mod():
     d = tempfile.mkdtemp(prefix="kda_mutants_")
@@ -111,4 +121,21 @@ def test_mutant_is_caught(name, tmpdir_mod):
         f.write(text)
     lib = oracle.build(src, os.path.join(d, "lib.so"))
     failed = _failures(oracle.Oracle(lib))
+    assert failed, f"mutant {name} passed every pin"
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_python_mutant_is_caught(name, orc):
+    """The same for the prologue composition in the oracle's Python layer:
+    the mutated module runs on the real compiled library."""
+    import types
+    path = oracle.__file__
+    text = open(path).read()
+    for old, new in PY_MUTANTS[name]:
+        assert text.count(old) == 1, (name, old)
+        text = text.replace(old, new)
+    mod = types.ModuleType("oracle_mutant_" + name)
+    mod.__file__ = path
+    exec(compile(text, path, "exec"), mod.__dict__)
+    failed = _failures(mod.Oracle(oracle._LIB))
     assert failed, f"mutant {name} passed every pin"
