@@ -6,7 +6,8 @@ device memory and the current stream.  There is no fallback of any kind: if
 the library has not been built, importing this package raises.
 
 Functions mirror the C entry points by name:
-  kda_prefill, kda_prefill_chunk_prep, kda_prefill_state_pass,
+  kda_prefill, kda_prefill_noalloc, kda_prefill_chunk_prep,
+  kda_prefill_state_pass,
   kda_decode_step, kda_conv_prologue, kda_prefill_workspace_size,
   kda_status_string, kda_abi_version
 """
@@ -27,7 +28,8 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-KDA_OK, KDA_EINVAL, KDA_EUNSUPPORTED, KDA_EHIP = 0, 1, 2, 3
+KDA_OK, KDA_EINVAL, KDA_EUNSUPPORTED, KDA_EHIP, KDA_ENOSPACE = 0, 1, 2, 3, 4
+KDA_NOALLOC_SCRATCH_BYTES = 64 << 20  # the fixed workspace of kda_prefill_noalloc
 KDA_F32, KDA_BF16 = 0, 1
 KDA_GATE_HEAD = 16  # gate-dtype flag: g holds one log-decay per token-head
 
@@ -53,6 +55,9 @@ _ws_size = _sig("kda_prefill_workspace_size", _sz, [_i] * 6 + [_i])
 _prefill = _sig("kda_prefill", _i,
                 [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp] + [_i] * 6 +
                 [_f, ctypes.POINTER(KdaConvDesc), _vp, _sz, _vp])
+_prefill_noalloc = _sig("kda_prefill_noalloc", _i,
+                        [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp] +
+                        [_i] * 6 + [_f, ctypes.POINTER(KdaConvDesc), _vp])
 _prep = _sig("kda_prefill_chunk_prep", _i,
              [_vp, _vp, _vp, _i, _vp, _vp, _i] + [_i] * 6 +
              [_f, ctypes.POINTER(KdaConvDesc), _vp, _sz, _vp])
@@ -249,6 +254,33 @@ def kda_prefill(q, k, v, g, beta, *, s0=None, chunk=64, scale=1.0,
                   chunk, scale, cd, _ptr(workspace), workspace.numel(),
                   _stream(stream))
     _check(st, "kda_prefill")
+    return o, s_out
+
+
+def kda_prefill_noalloc(q, k, v, g, beta, *, s0=None, chunk=64, scale=1.0,
+                        conv=None, o=None, s_out=None, want_state=True,
+                        stream=None):
+    """kda_prefill on the library's fixed scratch workspace: the C call
+    allocates nothing (pass o and s_out to keep this wrapper from
+    allocating them).  Raises KdaError(KDA_ENOSPACE) when the sizes need
+    more than KDA_NOALLOC_SCRATCH_BYTES of workspace.  Calls that overlap
+    in time on one GPU share the scratch and race."""
+    B, T, H, Dk, Dv, io = _prefill_shapes(q, v, g, conv)
+    _check_prefill(q, k, v, g, beta, conv, B, T, H, Dk, Dv, io.dtype)
+    _need(s0, (B, H, Dk, Dv), torch.float32, "s0")
+    _need(s_out, (B, H, Dk, Dv), torch.float32, "s_out")
+    _need(o, (B, T, H, Dv), io.dtype, "o")
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=io.dtype, device=g.device)
+    if s_out is None and want_state:
+        s_out = torch.empty((B, H, Dk, Dv), dtype=torch.float32,
+                            device=g.device)
+    cd, _keep = _conv_desc(conv)
+    st = _prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _dt(io), _ptr(g),
+                          _ptr(beta), _gate_dt(g, 4), _ptr(s0), _ptr(s_out),
+                          _ptr(o), B, T, H, Dk, Dv, chunk, scale, cd,
+                          _stream(stream))
+    _check(st, "kda_prefill_noalloc")
     return o, s_out
 
 

@@ -5,6 +5,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -130,7 +132,7 @@ BwdWs bwd_ws(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype io) {
   return w;
 }
 
-// validation of kda_prefill's arguments (everything but
+// validation shared by kda_prefill and kda_prefill_noalloc (everything but
 // the workspace); fills p without it
 kda_status prefill_args(const void *q, const void *k, const void *v,
                         kda_dtype io, const void *g, const void *beta,
@@ -146,6 +148,37 @@ kda_status prefill_args(const void *q, const void *k, const void *v,
     return KDA_EINVAL;
   if (o == q || o == k || o == v || o == g || o == beta) return KDA_EINVAL;
   p.s0 = s0; p.s_out = s_out; p.o = o;
+  return KDA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The fixed workspace of kda_prefill_noalloc.  In host code the name
+// `scratch` is only a host-side stand-in: kernels get the device address
+// that hipGetSymbolAddress reports for the current GPU (each GPU holds its
+// own copy of the array at its own address), looked up once per GPU and
+// kept.  It needs no initialisation: the chunk prep writes every byte of
+// the workspace that the state pass reads.
+__device__ __align__(256) char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::once_flag scratch_once[SCRATCH_MAX_DEVICES];
+void *scratch_ptr[SCRATCH_MAX_DEVICES];
+hipError_t scratch_err[SCRATCH_MAX_DEVICES];
+
+kda_status scratch_on_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return hip_status(hipErrorNoDevice);
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return KDA_EUNSUPPORTED;
+  std::call_once(scratch_once[dev], [dev]() {
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    scratch_err[dev] = e;
+    scratch_ptr[dev] = e == hipSuccess ? ptr : nullptr;
+  });
+  if (scratch_err[dev] != hipSuccess || !scratch_ptr[dev])
+    return hip_status(scratch_err[dev] != hipSuccess ? scratch_err[dev]
+                                                     : hipErrorInvalidSymbol);
+  *out = scratch_ptr[dev];
   return KDA_OK;
 }
 
@@ -170,6 +203,9 @@ const char *kda_status_string(kda_status s) {
     case KDA_EINVAL: return "KDA_EINVAL: invalid argument";
     case KDA_EUNSUPPORTED: return "KDA_EUNSUPPORTED: valid but unsupported";
     case KDA_EHIP: return "KDA_EHIP: HIP launch error";
+    case KDA_ENOSPACE:
+      return "KDA_ENOSPACE: larger than the fixed scratch of "
+             "kda_prefill_noalloc";
   }
   return "KDA: unknown status";
 }
@@ -241,6 +277,31 @@ kda_status kda_prefill(const void *q, const void *k, const void *v,
   if (workspace_bytes < ws_bytes(B, T, H, Dk, Dv, chunk, qkv_dtype))
     return KDA_EINVAL;
   p.ws = (char *)workspace;
+  p.wsb = kda::ws_layout(Dk, Dv, p.C, qkv_dtype == KDA_BF16 ? 2 : 4).bytes;
+  const int bf = qkv_dtype == KDA_BF16;
+  hipError_t e = kda::launch_prefill_prep(p, bf, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(kda::launch_state_pass(p, bf, (hipStream_t)stream));
+}
+
+kda_status kda_prefill_noalloc(const void *q, const void *k, const void *v,
+                               kda_dtype qkv_dtype, const void *g,
+                               const void *beta, kda_dtype gate_dtype,
+                               const float *s0, float *s_out, void *o,
+                               int B, int T, int H, int Dk, int Dv, int chunk,
+                               float scale, const kda_conv_desc *conv,
+                               void *stream) {
+  kda::PrefillParams p;
+  kda_status st = prefill_args(q, k, v, qkv_dtype, g, beta, gate_dtype, s0,
+                               s_out, o, B, T, H, Dk, Dv, chunk, scale, conv,
+                               p);
+  if (st != KDA_OK) return st;
+  if (ws_bytes(B, T, H, Dk, Dv, chunk, qkv_dtype) > KDA_NOALLOC_SCRATCH_BYTES)
+    return KDA_ENOSPACE;
+  void *ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != KDA_OK) return st;
+  p.ws = (char *)ws;
   p.wsb = kda::ws_layout(Dk, Dv, p.C, qkv_dtype == KDA_BF16 ? 2 : 4).bytes;
   const int bf = qkv_dtype == KDA_BF16;
   hipError_t e = kda::launch_prefill_prep(p, bf, (hipStream_t)stream);

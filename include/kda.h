@@ -29,9 +29,10 @@
  *     token per step.
  *
  * Conventions shared by every entry point.
- *  - All pointers are DEVICE pointers owned by the caller; the library keeps
- *    no global mutable state and never allocates device memory (the prefill
- *    workspace is passed in).  Calls are thread-safe.
+ *  - All pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates device memory (the prefill workspace is passed in) and
+ *    keeps no global mutable state, with one exception: the fixed scratch
+ *    array of kda_prefill_noalloc (below).  Calls are thread-safe.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream) and never synchronises.
  *  - Tensors are dense, contiguous, row-major.  Pointers must be 16-byte
@@ -72,7 +73,10 @@ typedef enum kda_status {
   KDA_OK = 0,
   KDA_EINVAL = 1,
   KDA_EUNSUPPORTED = 2,
-  KDA_EHIP = 3
+  KDA_EHIP = 3,
+  /* kda_prefill_noalloc only: the request needs more workspace than its
+   * fixed scratch array holds (KDA_NOALLOC_SCRATCH_BYTES) */
+  KDA_ENOSPACE = 4
 } kda_status;
 
 typedef enum kda_dtype {
@@ -109,7 +113,7 @@ typedef struct kda_conv_desc {
 } kda_conv_desc;
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 int kda_abi_version(void);
 
 /* Static text for a status code (never NULL). */
@@ -141,6 +145,31 @@ kda_status kda_prefill(const void *q, const void *k, const void *v,
                        void *o, int B, int T, int H, int Dk, int Dv,
                        int chunk, float scale, const kda_conv_desc *conv,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* kda_prefill for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, arithmetic, results (bit for bit) and errors as
+ * kda_prefill, without the workspace arguments: the workspace is a static
+ * device array of KDA_NOALLOC_SCRATCH_BYTES (64 MiB) inside the library,
+ * one per GPU, held until the process ends.  Its device address is looked
+ * up once per GPU, on the first call made with that GPU current (the
+ * caller's current device must be the one `stream` belongs to).  Requests
+ * whose kda_prefill_workspace_size() exceeds the array return KDA_ENOSPACE
+ * before anything is launched (64 MiB holds 904 chunk-heads at
+ * Dk = Dv = 128, chunk 64, bf16: B*H*ceil(T/64) <= 904, e.g. T <= 1792 at
+ * B = 1, H = 32).  The call allocates nothing, host or device.  Every call
+ * on one GPU shares that GPU's array: calls that overlap in time on one
+ * GPU (on different streams, or from several threads) race and corrupt
+ * each other's results; serialise them (one stream, or events).  The
+ * array needs no initialisation and keeps the last call's contents. */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kda_status kda_prefill_noalloc(const void *q, const void *k, const void *v,
+                               kda_dtype qkv_dtype, const void *g,
+                               const void *beta, kda_dtype gate_dtype,
+                               const float *s0, float *s_out, void *o,
+                               int B, int T, int H, int Dk, int Dv, int chunk,
+                               float scale, const kda_conv_desc *conv,
+                               void *stream);
 
 /* First phase of kda_prefill alone: every (batch, head, chunk) is reduced
  * to its state-independent factors (the UT-transform of the chunk's

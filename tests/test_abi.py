@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
 def test_version_and_strings():
     ver = int(re.search(r"#define KDA_ABI_VERSION (\d+)", open(HDR).read())[1])
     assert kda.kda_abi_version() == ver
-    for s in range(4):
+    for s in range(5):
         assert kda.kda_status_string(s).startswith("KDA_")
     assert "unknown" in kda.kda_status_string(99)
 
@@ -258,3 +258,23 @@ def test_binding_rejects_mismatched_decode_and_conv_inputs():
         kda.kda_decode_tokens(None, None, None, _t(N, 2, H), _t(N, 2, H), st,
                               conv=conv, conv_state=_t(N, 3, H * D, W - 2,
                                                        dt=f32))
+
+
+def test_noalloc_rejects_before_any_launch():
+    """kda_prefill_noalloc validates like kda_prefill and refuses a request
+    larger than its fixed scratch with KDA_ENOSPACE, all before it looks up
+    the scratch or launches (so no GPU is touched here)."""
+    f = kda._prefill_noalloc
+    base = [A, A, A, kda.KDA_BF16, A, A, kda.KDA_F32, None, None, A + 4096]
+    # B=1, T=2048, H=32, d=128, chunk 64: 93 MiB of workspace > 64 MiB
+    assert kda.kda_prefill_workspace_size(1, 2048, 32, 128, 128, 64,
+                                          kda.KDA_BF16) > \
+        kda.KDA_NOALLOC_SCRATCH_BYTES
+    assert f(*base, 1, 2048, 32, 128, 128, 64, 1.0, None, None) == \
+        kda.KDA_ENOSPACE
+    assert f(*base, 1, 2048, 32, 128, 128, 48, 1.0, None, None) == \
+        kda.KDA_EUNSUPPORTED
+    bad = list(base)
+    bad[9] = A  # o aliases q
+    assert f(*bad, 1, 64, 2, 16, 16, 16, 1.0, None, None) == kda.KDA_EINVAL
+    assert f(*base, 0, 64, 2, 16, 16, 16, 1.0, None, None) == kda.KDA_EINVAL
