@@ -82,6 +82,11 @@ hipError_t launch_prefill_prep_f32(const PrefillParams &p, hipStream_t s);
 hipError_t launch_prefill_prep_bf16_f32(const PrefillParams &p, hipStream_t s);
 hipError_t launch_prefill_prep_bf16_bf16(const PrefillParams &p,
                                          hipStream_t s);
+// the chunk prep for one gate per token-head (bf16 q/k/v, d_k = 128,
+// chunk 64, no conv, no backward outputs): whether it serves p, and its
+// launcher
+bool prep_gdn_applies(const PrefillParams &p, int io_bf16);
+hipError_t launch_prefill_prep_gdn(const PrefillParams &p, hipStream_t s);
 hipError_t launch_state_pass(const PrefillParams &p, int io_bf16,
                              hipStream_t s);
 hipError_t launch_decode(const DecodeParams &p, int io_bf16, hipStream_t s);
