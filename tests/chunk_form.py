@@ -67,7 +67,10 @@ def chunk_matrices(q, k, g, beta, scale, bs=16):
         # diagonal block
         idx = range(ra.start, ra.stop)
         rr = rho[ra]
-        if np.all(rr[:-1] >= SAFE_MIN):
+        # every rho of the sub-chunk, the last one too: it divides the last
+        # token's own column (P's diagonal), so a vanished rho there must
+        # take the direct path as well
+        if np.all(rr >= SAFE_MIN):
             col = k[ra] / rr
             Ad = (beta[ra, None] * k[ra] * rr) @ col.T
             Pd = scale * (q[ra] * rr) @ col.T
@@ -122,5 +125,44 @@ def chunked_forward(q, k, v, g, beta, s0=None, scale=1.0, C=64, bs=16):
                 D = U - W @ S
                 o[b, sl, h] = scale * (qc * Gam) @ S + P @ D
                 S = gamC[:, None] * S + Kt.T @ D
+            sT[b, h] = S
+    return o, sT
+
+
+def chunked_forward_scalar_gate(q, k, v, g, beta, s0=None, scale=1.0, C=64):
+    """The chunked form with one log-decay per token-head (g [B,T,H]), in
+    the arrangement of the per-head-gate chunk prep: Gram products of the
+    raw keys and queries times a scalar decay matrix, T applied with its
+    columns scaled, and rows of Q and K scaled for the state products.
+      D[r,s] = prod_{u=s+1..r} e_u    (s <= r; a direct product, no ratio)
+      A = diag(beta) (K K^T * D) (strictly lower), P = scale (Q K^T * D)
+      W = T diag(beta Gam) K,  U = T diag(beta) V,  T = (I + A)^-1
+      Qtil = scale diag(Gam) Q,  Ktil = diag(Gam_C / Gam) K"""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    o = np.zeros((B, T, H, Dv))
+    sT = np.zeros((B, H, Dk, Dv))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((Dk, Dv)) if s0 is None else s0[b, h].copy()
+            for t0 in range(0, T, C):
+                sl = slice(t0, min(T, t0 + C))
+                qc, kc, vc = q[b, sl, h], k[b, sl, h], v[b, sl, h]
+                e, bc = np.exp(g[b, sl, h]), beta[b, sl, h]
+                n = len(e)
+                D = np.zeros((n, n))
+                for r in range(n):
+                    for s in range(r + 1):
+                        D[r, s] = np.prod(e[s + 1:r + 1])
+                gam = np.array([np.prod(e[:r + 1]) for r in range(n)])
+                sfx = np.array([np.prod(e[r + 1:]) for r in range(n)])
+                A = np.tril(bc[:, None] * (kc @ kc.T) * D, -1)
+                P = scale * (qc @ kc.T) * D
+                Tm = np.linalg.inv(np.eye(n) + A)
+                W = (Tm * (bc * gam)[None, :]) @ kc
+                U = (Tm * bc[None, :]) @ vc
+                Dl = U - W @ S
+                o[b, sl, h] = (scale * gam[:, None] * qc) @ S + P @ Dl
+                S = gam[-1] * S + (sfx[:, None] * kc).T @ Dl
             sT[b, h] = S
     return o, sT
