@@ -190,7 +190,7 @@ def main():
         # one kda_prefill call = chunk prep + state pass, back to back
         t_k = ms * 1e-3
         gbs = byts / t_k / 1e9
-        srcs = ["kda_prep_impl.h", "kda_prep_bf16_f32.hip", "kda_state.hip",
+        srcs = ["kda_prep_d128.hip", "kda_prep_impl.h", "kda_state.hip",
                 "kda_device.h"]
         tr_p = traffic_for("kda_chunk_prep", srcs)
         tr_s = traffic_for("kda_state_pass", srcs)

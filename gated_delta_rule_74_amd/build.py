@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libkda.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 SOURCES = ["kda_api.hip", "kda_prep_f32.hip", "kda_prep_bf16_f32.hip",
-           "kda_prep_bf16_bf16.hip", "kda_prep_gdn.hip", "kda_state.hip", "kda_decode.hip",
+           "kda_prep_bf16_bf16.hip", "kda_prep_gdn.hip", "kda_prep_d128.hip", "kda_state.hip", "kda_decode.hip",
            "kda_backward.hip",
            "kda_conv.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")

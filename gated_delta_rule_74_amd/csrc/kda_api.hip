@@ -188,6 +188,7 @@ namespace kda {
 hipError_t launch_prefill_prep(const PrefillParams &p, int io_bf16,
                                hipStream_t s) {
   if (prep_gdn_applies(p, io_bf16)) return launch_prefill_prep_gdn(p, s);
+  if (prep_d128_applies(p, io_bf16)) return launch_prefill_prep_d128(p, s);
   if (!io_bf16) return launch_prefill_prep_f32(p, s);
   return p.gate_bf16 ? launch_prefill_prep_bf16_bf16(p, s)
                      : launch_prefill_prep_bf16_f32(p, s);

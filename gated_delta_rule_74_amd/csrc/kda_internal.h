@@ -87,6 +87,10 @@ hipError_t launch_prefill_prep_bf16_bf16(const PrefillParams &p,
 // launcher
 bool prep_gdn_applies(const PrefillParams &p, int io_bf16);
 hipError_t launch_prefill_prep_gdn(const PrefillParams &p, hipStream_t s);
+// the chunk prep for one gate per key channel at bf16 q/k/v,
+// d_k = d_v = 128, chunk 64, no conv (eight waves per task)
+bool prep_d128_applies(const PrefillParams &p, int io_bf16);
+hipError_t launch_prefill_prep_d128(const PrefillParams &p, hipStream_t s);
 hipError_t launch_state_pass(const PrefillParams &p, int io_bf16,
                              hipStream_t s);
 hipError_t launch_decode(const DecodeParams &p, int io_bf16, hipStream_t s);

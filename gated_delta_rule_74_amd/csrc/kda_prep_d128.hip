@@ -1,0 +1,655 @@
+// kda_prep_d128.hip -- chunk prep of the chunked KDA prefill for one gate per
+// key channel at bf16 q/k/v, d_k = d_v = 128 and 64-token chunks (gfx950),
+// without the fused conv.
+//
+// It computes exactly the factors of kda_prep_impl.h (see there for the
+// method, the decay-ratio splitting and the exact diagonal fallback) and
+// writes them in the same workspace layout, so kda_state_pass consumes
+// either.  What differs is the execution shape:
+//
+//  * Eight waves (512 threads, two waves per SIMD) work on one task instead
+//    of four.  Every phase of a task is a short dependent chain (LDS reads,
+//    matrix-core products, a barrier); with two waves per SIMD one wave's
+//    waits overlap the other's issue.  The register budget that allows it
+//    (at most 256 per lane) comes from giving each thread half the data.
+//  * Wave w holds sub-chunk w / 2 (16 tokens) and key channels
+//    64 (w % 2) .. 64 (w % 2) + 63; lane 32 h + c holds channels
+//    64 (w % 2) + 2c, +1 of tokens 8h .. 8h + 7 of the sub-chunk.  The two
+//    8-token halves of a sub-chunk sit in lanes l and l ^ 32 of one wave, so
+//    the running decay products need no exchange through LDS.
+//  * (beta V)^T and (beta K Gam)^T, the channel-major inputs of W and U,
+//    have their own LDS and are written as soon as they are formed (phase
+//    E1 and E2) instead of in a separate phase after the A/P products.
+//  * A and P blocks are dealt out as 20 half-blocks (A or P of one 16x16
+//    block), three or two per wave, so each SIMD does the same share; the W
+//    and U products follow a fixed table that gives every wave 12 of the 96
+//    matrix-core steps.
+#include "kda_prep_impl.h"
+
+namespace kda {
+namespace pc {
+
+constexpr int NT = 512, NW = NT / 64;
+constexpr int DK = 128, DV = 128, C = 64;
+constexpr int NB = 4, NKT = 8, NKU = 4, NTU = 2, NVT = 8, KU = 32;
+constexpr int LDK = DK + 8;  // token-major bf16 rows [C][LDK]
+constexpr int LDC = C + 8;   // channel-major bf16 rows [*][LDC]
+constexpr int LDA = C + 4;   // fp32 rows [C][LDA]
+
+// LDS layout (bytes).  Region A (E1 -> AP) holds the row and column
+// operands of A and P; region D (T1 -> WU) overlays it.
+constexpr size_t TOK = (size_t)C * LDK * 2;
+constexpr size_t oKR = 0, oQR = TOK, oKS = 2 * TOK, oKIR = 3 * TOK;
+constexpr size_t oTt = 0;                                  // T fp32
+constexpr size_t oTaa = oTt + (size_t)C * LDA * 4;         // diagonal T^T
+constexpr size_t oTb = oTaa + (size_t)NB * 256 * 4;        // T bf16
+static_assert(oTb + (size_t)C * LDC * 2 <= 4 * TOK, "region D inside A");
+constexpr size_t oAf = 4 * TOK;                            // A fp32
+constexpr size_t oFb = oAf + (size_t)C * LDA * 4;          // exact diagonals
+constexpr size_t oKST = oFb + (size_t)2 * NB * 256 * 4;    // (K sigma)^T
+constexpr size_t oKG = oKST + (size_t)DK * LDC * 2;        // (beta K Gam)^T
+constexpr size_t oVT = oKG + (size_t)DK * LDC * 2;         // (beta V)^T
+constexpr size_t oF = oVT + (size_t)DV * LDC * 2;          // F per sub-chunk
+constexpr size_t oM = oF + (size_t)NB * DK * 4;            // mid products
+constexpr size_t oVote = oM + (size_t)3 * DK * 4;
+constexpr size_t oBeta = oVote + 64;
+constexpr size_t LDS = oBeta + 64 * 4;
+static_assert(LDS <= 160 * 1024, "one workgroup per CU");
+
+// two bf16 values as raw bits
+__device__ __forceinline__ void get2(uint32_t r, float &a, float &b) {
+  a = __uint_as_float(r << 16);
+  b = __uint_as_float(r & 0xffff0000u);
+}
+__device__ __forceinline__ uint32_t put2(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const bf16x2 v = {(bf16)a, (bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint32_t ld4_stream(const void *p) {
+  return __builtin_nontemporal_load((const uint32_t *)p);
+}
+
+template <typename GT> struct GRaw;  // two gates as loaded
+template <> struct GRaw<float> {
+  typedef uint2 raw;
+  __device__ static __forceinline__ raw load(const float *p) {
+    return ld_stream<uint2>(p);
+  }
+  __device__ static __forceinline__ void get(raw r, float &a, float &b) {
+    a = __uint_as_float(r.x);
+    b = __uint_as_float(r.y);
+  }
+};
+template <> struct GRaw<bf16> {
+  typedef uint32_t raw;
+  __device__ static __forceinline__ raw load(const bf16 *p) {
+    return ld4_stream(p);
+  }
+  __device__ static __forceinline__ void get(raw r, float &a, float &b) {
+    get2(r, a, b);
+  }
+};
+
+// the next task's inputs, one task ahead in registers: 2 channels x 8 tokens
+// of q, k, v and g per thread, and (wave 0) the chunk's betas, token = lane
+template <typename GT> struct Stage {
+  uint32_t q[8], k[8], v[8];
+  typename GRaw<GT>::raw g[8];
+  uint32_t beta;
+};
+
+// PART: 1 = g and beta, 2 = q, 4 = k, 8 = v
+template <int PART, typename GT>
+__device__ __forceinline__ void load_task(const PrefillParams &p, int task,
+                                          Stage<GT> &st, int tid, int c0,
+                                          int r0) {
+  const int BH = p.B * p.H;
+  const int bh = task % BH, n = p.NC - 1 - task / BH;
+  const int b = bh / p.H, h = bh % p.H, T = p.T, H = p.H;
+  const int t0 = n * C, tlast = T - 1;
+  const size_t tok0 = (size_t)b * T;
+  const size_t kb = (tok0 * H + h) * DK + c0, rowK = (size_t)H * DK;
+  if ((PART & 1) && tid < 64) {
+    const size_t bi = (tok0 + (unsigned)min(t0 + tid, tlast)) * H + h;
+    st.beta = sizeof(GT) == 2 ? (uint32_t)((const unsigned short *)p.beta)[bi]
+                              : ((const unsigned *)p.beta)[bi];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const size_t t = (size_t)min(t0 + r0 + i, tlast);
+    if (PART & 1) st.g[i] = GRaw<GT>::load((const GT *)p.g + kb + t * rowK);
+    if (PART & 2) st.q[i] = ld4_stream((const bf16 *)p.q + kb + t * rowK);
+    if (PART & 4) st.k[i] = ld4_stream((const bf16 *)p.k + kb + t * rowK);
+    if (PART & 8)
+      st.v[i] = ld4_stream((const bf16 *)p.v + (tok0 * H + h) * DV + c0 +
+                           t * (size_t)H * DV);
+  }
+}
+
+template <typename GT>
+__global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
+  using M = Mma<bf16>;
+  typedef M::frag frag;
+  typedef Vec4<bf16>::raw R4;
+
+  __shared__ __attribute__((aligned(16))) char sm[LDS];
+  bf16 *Xkr = (bf16 *)(sm + oKR), *Xqr = (bf16 *)(sm + oQR);
+  bf16 *Xks = (bf16 *)(sm + oKS), *Xkir = (bf16 *)(sm + oKIR);
+  float *Tt = (float *)(sm + oTt), *Taa = (float *)(sm + oTaa);
+  bf16 *Tb = (bf16 *)(sm + oTb);
+  float *Af = (float *)(sm + oAf);
+  float *FbA = (float *)(sm + oFb), *FbP = FbA + NB * 256;
+  bf16 *XksT = (bf16 *)(sm + oKST), *XkgT = (bf16 *)(sm + oKG);
+  bf16 *XvT = (bf16 *)(sm + oVT);
+  float *Fs = (float *)(sm + oF), *Mid = (float *)(sm + oM);
+  int *votes = (int *)(sm + oVote);
+  float *betas = (float *)(sm + oBeta);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4, m16 = lane & 15;
+  const int BH = p.B * p.H, T = p.T, H = p.H;
+  const int ntask = BH * p.NC;
+  const WsLayout W = ws_layout(DK, DV, C, 2);
+  // this thread's share of a task: sub-chunk a, token half hh, 2 channels
+  const int a = wave >> 1, hh = lane >> 5;
+  const int c0 = 64 * (wave & 1) + 2 * (lane & 31);
+  const int r0 = 16 * a + 8 * hh;
+  constexpr bool GB = sizeof(GT) == 2;
+
+  Stage<GT> st;
+  int task = blockIdx.x;
+  if (task < ntask) load_task<15, GT>(p, task, st, tid, c0, r0);
+  auto put_beta = [&]() {
+    if (wave == 0)
+      betas[lane] = GB ? __uint_as_float(st.beta << 16)
+                       : __uint_as_float(st.beta);
+  };
+  if (task < ntask) put_beta();
+  __syncthreads();
+
+  for (; task < ntask; task += gridDim.x) {
+    // per-lane indices are rebuilt from an opaque copy every task: the
+    // compiler would otherwise keep dozens of addresses derived from them
+    // live across the whole loop, past the 256 registers a lane may hold
+    int lid = tid;
+    asm volatile("" : "+v"(lid));
+    const int lane = lid & 63, g4 = lane >> 4, m16 = lane & 15;
+    const int hh = lane >> 5;
+    const int c0 = 64 * (wave & 1) + 2 * (lane & 31);
+    const int r0 = 16 * a + 8 * hh;
+    const int bh = task % BH, n = p.NC - 1 - task / BH;
+    const int b = bh / H, h = bh % H;
+    const int t0 = n * C;
+    char *blk = p.ws + ((size_t)bh * p.NC + n) * p.wsb;
+
+    // ---- E1: decay, running products, A/P operands, (beta V)^T -----------
+    float F[2], xkr[8][2];
+    int vote;
+    {
+      float e[8][2], kk[8][2], qq[8][2], bt[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool ok = t0 + r0 + i < T;
+        float g0, g1;
+        GRaw<GT>::get(st.g[i], g0, g1);
+        bt[i] = ok ? betas[r0 + i] : 0.f;
+        e[i][0] = ok ? __expf(g0) : 1.f;
+        e[i][1] = ok ? __expf(g1) : 1.f;
+        get2(st.k[i], kk[i][0], kk[i][1]);
+        get2(st.q[i], qq[i][0], qq[i][1]);
+        if (!ok) kk[i][0] = kk[i][1] = qq[i][0] = qq[i][1] = 0.f;
+      }
+      // this half's 8-token product, then the other half's (lane ^ 32)
+      float ltp[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float lt = 1.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lt *= e[i][j];
+        ltp[j] = __shfl_xor(lt, 32, 64);
+        F[j] = lt * ltp[j];
+      }
+      // rho is non-increasing within the sub-chunk: its least value is F
+      vote = !(F[0] >= SAFE_MIN) || !(F[1] >= SAFE_MIN);
+      // forward: rho = inclusive prefix within the sub-chunk
+      {
+        float pr0 = hh ? ltp[0] : 1.f, pr1 = hh ? ltp[1] : 1.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = r0 + i;
+          pr0 *= e[i][0];
+          pr1 *= e[i][1];
+          xkr[i][0] = bt[i] * kk[i][0] * pr0;
+          xkr[i][1] = bt[i] * kk[i][1] * pr1;
+          *(uint32_t *)(Xkr + r * LDK + c0) = put2(xkr[i][0], xkr[i][1]);
+          *(uint32_t *)(Xqr + r * LDK + c0) =
+              put2(p.scale * qq[i][0] * pr0, p.scale * qq[i][1] * pr1);
+          *(uint32_t *)(Xkir + r * LDK + c0) =
+              put2(kk[i][0] * __builtin_amdgcn_rcpf(pr0),
+                   kk[i][1] * __builtin_amdgcn_rcpf(pr1));
+        }
+      }
+      // backward: sigma = exclusive suffix within the sub-chunk
+      {
+        float sf0 = hh ? 1.f : ltp[0], sf1 = hh ? 1.f : ltp[1];
+        float xc0[8], xc1[8];  // the same values by channel
+#pragma unroll
+        for (int i = 7; i >= 0; --i) {
+          xc0[i] = kk[i][0] * sf0;
+          xc1[i] = kk[i][1] * sf1;
+          sf0 *= e[i][0];
+          sf1 *= e[i][1];
+          *(uint32_t *)(Xks + (r0 + i) * LDK + c0) = put2(xc0[i], xc1[i]);
+        }
+        bf16 *row0 = XksT + c0 * LDC, *row1 = row0 + LDC;
+        *(R4 *)(row0 + cm_off<C>(c0, r0)) = Vec4<bf16>::put(&xc0[0]);
+        *(R4 *)(row0 + cm_off<C>(c0, r0 + 4)) = Vec4<bf16>::put(&xc0[4]);
+        *(R4 *)(row1 + cm_off<C>(c0 + 1, r0)) = Vec4<bf16>::put(&xc1[0]);
+        *(R4 *)(row1 + cm_off<C>(c0 + 1, r0 + 4)) = Vec4<bf16>::put(&xc1[4]);
+      }
+      if (!hh) *(float2 *)(Fs + a * DK + c0) = make_float2(F[0], F[1]);
+      // (beta V)^T for U: value channels c0, c0 + 1 (beta is 0 past T)
+      {
+        float bv0[8], bv1[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float v0, v1;
+          get2(st.v[i], v0, v1);
+          bv0[i] = bt[i] * v0;
+          bv1[i] = bt[i] * v1;
+        }
+        bf16 *row0 = XvT + c0 * LDC, *row1 = row0 + LDC;
+        *(R4 *)(row0 + cm_off<C>(c0, r0)) = Vec4<bf16>::put(&bv0[0]);
+        *(R4 *)(row0 + cm_off<C>(c0, r0 + 4)) = Vec4<bf16>::put(&bv0[4]);
+        *(R4 *)(row1 + cm_off<C>(c0 + 1, r0)) = Vec4<bf16>::put(&bv1[0]);
+        *(R4 *)(row1 + cm_off<C>(c0 + 1, r0 + 4)) = Vec4<bf16>::put(&bv1[4]);
+      }
+    }
+    {
+      const unsigned long long bal = __ballot(vote);
+      if (lane == 0) votes[wave] = bal != 0ull;
+    }
+    __syncthreads();  // B1: region A, (K sigma)^T, (beta V)^T, Fs, votes
+
+    // ---- E2: Qtil and Ktil^T units, gamma_C, (beta K Gam)^T, mid products -
+    const bool more = task + (int)gridDim.x < ntask;
+    if (more) load_task<1, GT>(p, task + gridDim.x, st, tid, c0, r0);
+    int anyv = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) anyv |= votes[w];
+    const bool fallback = anyv != 0;
+    if (fallback)  // accumulated by the exact diagonal sums after B2
+      ((f32x4 *)FbA)[tid] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+      // Gam at the sub-chunk start: product of the earlier sub-chunks' F
+      float fp0 = 1.f, fp1 = 1.f;
+#pragma unroll
+      for (int bb = 0; bb < NB - 1; ++bb) {
+        const float2 f = *(const float2 *)(Fs + bb * DK + c0);
+        if (bb < a) { fp0 *= f.x; fp1 *= f.y; }
+      }
+      float k0[8], k1[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        k0[i] = xkr[i][0] * fp0;
+        k1[i] = xkr[i][1] * fp1;
+      }
+      bf16 *row0 = XkgT + c0 * LDC, *row1 = row0 + LDC;
+      *(R4 *)(row0 + cm_off<C>(c0, r0)) = Vec4<bf16>::put(&k0[0]);
+      *(R4 *)(row0 + cm_off<C>(c0, r0 + 4)) = Vec4<bf16>::put(&k0[4]);
+      *(R4 *)(row1 + cm_off<C>(c0 + 1, r0)) = Vec4<bf16>::put(&k1[0]);
+      *(R4 *)(row1 + cm_off<C>(c0 + 1, r0 + 4)) = Vec4<bf16>::put(&k1[4]);
+      if (a == NB - 1 && hh == 1)
+        *(float2 *)((float *)(blk + W.off_gam) + c0) =
+            make_float2(fp0 * F[0], fp1 * F[1]);
+    }
+    // Qtil = scale Q*Gam: 16 units (row tile aa, channel unit u), two per
+    // wave; a lane's 16-byte slot holds channels 32u + 4g4 .. +3 and
+    // 32u + 16 + 4g4 .. +3 of token 16aa + m16
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int w = wave + NW * it;
+      const int aa = w / NKU, u = w % NKU;
+      const int tok = 16 * aa + m16;
+      const int ch0 = KU * u + 4 * g4, ch1 = ch0 + 16;
+      f32x4 f0 = {1.f, 1.f, 1.f, 1.f}, f1 = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+      for (int bb = 0; bb < NB - 1; ++bb) {
+        const f32x4 l0 = *(const f32x4 *)(Fs + bb * DK + ch0);
+        const f32x4 l1 = *(const f32x4 *)(Fs + bb * DK + ch1);
+        if (bb < aa) {
+          f0 *= l0;
+          f1 *= l1;
+        }
+      }
+      float x0[4], x1[4], y0[4], y1[4];
+      Vec4<bf16>::get(*(const R4 *)(Xqr + tok * LDK + ch0), x0);
+      Vec4<bf16>::get(*(const R4 *)(Xqr + tok * LDK + ch1), x1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y0[j] = x0[j] * f0[j];
+        y1[j] = x1[j] * f1[j];
+      }
+      const R4 lo = Vec4<bf16>::put(y0), up = Vec4<bf16>::put(y1);
+      st_stream(blk + W.off_qt + ((size_t)(aa * NKU + u) * 64 + lane) * 16,
+                make_uint4(lo.x, lo.y, up.x, up.y));
+    }
+    // Ktil^T = (K*Gam_C/Gam)^T: 16 units (channel tile ct, token unit u)
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int w = wave + NW * it;
+      const int ct = w / NTU, u = w % NTU;
+      const int ch = 16 * ct + m16;
+      const int tk0 = KU * u + 4 * g4, tk1 = tk0 + 16;
+      const int a0 = 2 * u;  // sub-chunk of tk0; tk1 lies in a0 + 1
+      float fl[NB];
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) fl[bb] = Fs[bb * DK + ch];
+      float s0 = 1.f, s1 = 1.f;
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        if (bb > a0) s0 *= fl[bb];
+        if (bb > a0 + 1) s1 *= fl[bb];
+      }
+      float x0[4], x1[4], y0[4], y1[4];
+      Vec4<bf16>::get(*(const R4 *)(XksT + ch * LDC + cm_off<C>(ch, tk0)), x0);
+      Vec4<bf16>::get(*(const R4 *)(XksT + ch * LDC + cm_off<C>(ch, tk1)), x1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y0[j] = x0[j] * s0;
+        y1[j] = x1[j] * s1;
+      }
+      const R4 lo = Vec4<bf16>::put(y0), up = Vec4<bf16>::put(y1);
+      st_stream(blk + W.off_ktt + ((size_t)(ct * NTU + u) * 64 + lane) * 16,
+                make_uint4(lo.x, lo.y, up.x, up.y));
+    }
+    // mid products M_{b->a} = prod_{b<d<a} F_d for sub-chunk pairs a-b >= 2:
+    // pairs (2,0), (3,0), (3,1) at index 0, 1, 2
+    if (tid < 3 * DK) {
+      const int c = tid % DK, pi = tid / DK;
+      const int aa = pi == 0 ? 2 : 3, bb = pi == 2 ? 1 : 0;
+      float mp = 1.f;
+#pragma unroll
+      for (int d = 1; d < 3; ++d)
+        if (d > bb && d < aa) mp *= Fs[d * DK + c];
+      Mid[pi * DK + c] = mp;
+    }
+    __syncthreads();  // B2
+
+    if (more) load_task<2, GT>(p, task + gridDim.x, st, tid, c0, r0);
+
+    if (fallback) {
+      // exact diagonal-block sums: item (sub-chunk aa, column s, 16
+      // channels), one per thread; raw k and q of the input rows
+      const size_t tokb = (size_t)b * T;
+      const int cg = tid % 8, s = (tid / 8) % 16, aa = tid / 128;
+      float pr[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) pr[c] = 1.f;
+      const int ts = t0 + 16 * aa + s;
+      for (int r = s; r < 16; ++r) {
+        const int tr = t0 + 16 * aa + r;
+        const int trc = min(tr, T - 1);
+        float sa = 0.f, sp = 0.f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          const int ch = cg * 16 + c;
+          if (r > s) {
+            const size_t gi = ((tokb + trc) * H + h) * DK + ch;
+            const float gv = GB ? (float)((const bf16 *)p.g)[gi]
+                                : ((const float *)p.g)[gi];
+            pr[c] *= (tr < T) ? __expf(gv) : 1.f;
+          }
+          const size_t ob = ((tokb + min(ts, T - 1)) * H + h) * DK + ch;
+          const size_t orr = ((tokb + trc) * H + h) * DK + ch;
+          const float ks = ts < T ? (float)((const bf16 *)p.k)[ob] : 0.f;
+          const float kr = tr < T ? (float)((const bf16 *)p.k)[orr] : 0.f;
+          const float qr = tr < T ? (float)((const bf16 *)p.q)[orr] : 0.f;
+          sa += kr * ks * pr[c];
+          sp += qr * ks * pr[c];
+        }
+        const float br =
+            (tr < T) ? (GB ? (float)((const bf16 *)p.beta)[(tokb + trc) * H + h]
+                           : ((const float *)p.beta)[(tokb + trc) * H + h])
+                     : 0.f;
+        if (r > s) atomicAdd(&FbA[(aa * 16 + r) * 16 + s], br * sa);
+        atomicAdd(&FbP[(aa * 16 + r) * 16 + s], p.scale * sp);
+      }
+      __syncthreads();
+    }
+
+    // ---- AP: A^T and P^T blocks as 20 half-blocks --------------------------
+    // item i < 10: A of block i, else P of block i - 10 (blocks in ap_block
+    // order); wave w takes items w, w + 8, w + 16
+    for (int it = wave; it < 20; it += NW) {
+      const bool isP = it >= 10;
+      int aa, bb;
+      ap_block<NB>(isP ? it - 10 : it, aa, bb);
+      const bool diag = aa == bb;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (diag && fallback) {
+        const float *fb = isP ? FbP : FbA;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[j] = fb[(aa * 16 + m16) * 16 + 4 * g4 + j];
+      } else {
+        const bf16 *rb = (isP ? Xqr : Xkr) + (16 * aa + m16) * LDK;
+        const bf16 *cb = (diag ? Xkir : Xks) + (16 * bb + m16) * LDK;
+        frag rf[NKU], cf[NKU];
+#pragma unroll
+        for (int u = 0; u < NKU; ++u) {
+          rf[u] = M::load_k(rb + KU * u, g4);
+          cf[u] = M::load_k(cb + KU * u, g4);
+        }
+        if (aa - bb >= 2) {
+          const float *mid = Mid + (aa == 2 ? 0 : (bb == 0 ? 1 : 2)) * DK;
+#pragma unroll
+          for (int u = 0; u < NKU; ++u)
+#pragma unroll
+            for (int ee = 0; ee < M::NE; ++ee)
+              M::set(cf[u], ee,
+                     M::elem(cf[u], ee) * mid[KU * u + M::koff(g4, ee)]);
+        }
+#pragma unroll
+        for (int u = 0; u < NKU; ++u) acc = M::mma(cf[u], rf[u], acc);
+      }
+      // lane (m16, g4): element j is row 16aa + m16, col 16bb + 4g4 + j
+      if (diag) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int sc = 4 * g4 + j;
+          if (isP ? !(sc <= m16) : !(sc < m16)) acc[j] = 0.f;
+        }
+      }
+      if (!isP) {
+        *(f32x4 *)(Af + (16 * aa + m16) * LDA + 16 * bb + 4 * g4) = acc;
+      } else {
+        char *dst = blk + W.off_p +
+                    ((size_t)(aa * NTU + bb / 2) * 64 + lane) * 16 +
+                    (bb % 2) * 8;
+        const float a4[4] = {acc[0], acc[1], acc[2], acc[3]};
+        st_stream(dst, Vec4<bf16>::put(a4));
+        if (diag && (aa % 2) == 0) {
+          const float z[4] = {0.f, 0.f, 0.f, 0.f};
+          st_stream(dst + 8, Vec4<bf16>::put(z));
+        }
+      }
+    }
+    __syncthreads();  // B3: region A no longer read
+    if (more) load_task<4, GT>(p, task + gridDim.x, st, tid, c0, r0);
+
+    // ---- T1: diagonal inverses (waves 0-3, as in kda_prep_impl.h) while
+    // waves 4-7 zero the upper block (r, r+1) of every even token tile r of
+    // the bf16 T, which the W/U products read as part of whole 32-token units
+    f32x4 Tcol[NB];
+    if (wave < NB) {
+      const int aa = wave;
+      const float *ab = Af + (16 * aa) * LDA + 16 * aa;
+      const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 LA = *(const f32x4 *)(ab + m16 * LDA + 4 * g4);
+      f32x4 LB, Y;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        LB[j] = ab[(4 * g4 + j) * LDA + m16];
+        Y[j] = ((4 * g4 + j) == m16 ? 1.f : 0.f) - LB[j];  // I - L
+      }
+      const f32x4 L2B = mma16_f32(LA, LB, z4);
+      const f32x4 L2A = mma16_f32(LB, LA, z4);
+      const f32x4 L4B = mma16_f32(L2A, L2B, z4);
+      const f32x4 L4A = mma16_f32(L2B, L2A, z4);
+      const f32x4 L8A = mma16_f32(L4B, L4A, z4);
+      Y = mma16_f32(L2A, Y, Y);
+      Y = mma16_f32(L4A, Y, Y);
+      Y = mma16_f32(L8A, Y, Y);
+      Tcol[0] = Y;
+      *(f32x4 *)(Tt + (16 * aa + m16) * LDA + 16 * aa + 4 * g4) = Y;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        Taa[(aa * 16 + 4 * g4 + j) * 16 + m16] = Y[j];
+        Tb[(16 * aa + 4 * g4 + j) * LDC + 16 * aa + m16] = (bf16)Y[j];
+      }
+    } else if (tid - 256 < 64) {
+      // rows 16 rt .. 16 rt + 15 (rt = 0, 2), 16 columns from 16 (rt + 1)
+      const int i = tid - 256;
+      const int rt = 2 * (i / 32), row = (i % 32) / 2, hv = i % 2;
+      *(uint4 *)(Tb + (16 * rt + row) * LDC + 16 * (rt + 1) + 8 * hv) =
+          make_uint4(0u, 0u, 0u, 0u);
+    }
+    __syncthreads();
+    // ---- T2: off-diagonal blocks, one block column per wave ---------------
+    if (wave < NB) {
+      const int bb = wave;
+#pragma unroll
+      for (int k = 1; k < NB; ++k) {
+        if (bb + k >= NB) break;
+        const int aa = bb + k;
+        f32x4 X = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < k; ++j) {
+          const f32x4 af = *(const f32x4 *)(Af + (16 * aa + m16) * LDA +
+                                            16 * (bb + j) + 4 * g4);
+          X = mma16_f32(af, Tcol[j], X);
+        }
+        const f32x4 ta = *(const f32x4 *)(Taa + (aa * 16 + m16) * 16 + 4 * g4);
+        const f32x4 Tn = -mma16_f32(ta, X, f32x4{0.f, 0.f, 0.f, 0.f});
+        Tcol[k] = Tn;
+        *(f32x4 *)(Tt + (16 * bb + m16) * LDA + 16 * aa + 4 * g4) = Tn;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          Tb[(16 * aa + 4 * g4 + j) * LDC + 16 * bb + m16] = (bf16)Tn[j];
+      }
+    } else if (more) {
+      load_task<8, GT>(p, task + gridDim.x, st, tid, c0, r0);
+    }
+    __syncthreads();
+    if (more && wave < NB) load_task<8, GT>(p, task + gridDim.x, st, tid, c0, r0);
+
+    if (p.train_at) {
+      // for the backward pass: A = diag(beta) M and T^T, fp32
+      float *dst = p.train_at + ((size_t)bh * p.NC + n) * 2 * C * C;
+      for (int i = tid; i < C * C; i += NT) {
+        const int r = i / C, c = i % C;
+        dst[i] = Af[r * LDA + c];
+        dst[C * C + i] = Tt[r * LDA + c];
+      }
+    }
+
+    // ---- WU: -W (A-operand units) and U (accumulator tiles) ----------------
+    // token tile rt reads T rows 16 rt .. 16 rt + 15 over token units
+    // 0 .. umax(rt) = rt / 2; W costs 2 (umax + 1) steps per key unit, U
+    // (umax + 1) per value tile.  Waves 0-3 make -W, waves 4-7 U, 12 steps
+    // each.
+    auto load_t = [&](int rt, frag *tb) {
+      const int umax = rt / 2;
+#pragma unroll
+      for (int uu = 0; uu < NTU; ++uu)
+        tb[uu] = M::load_k(Tb + (16 * rt + m16) * LDC + KU * min(uu, umax), g4);
+    };
+    auto w_units = [&](int rt, int u0, int u1) {
+      frag tb[NTU];
+      load_t(rt, tb);
+      const int umax = rt / 2;
+      for (int u = u0; u < u1; ++u) {
+        f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        frag xa[NTU][2];
+#pragma unroll
+        for (int uu = 0; uu < NTU; ++uu)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int ct = 2 * u + h2;
+            xa[uu][h2] = load_k_cm<bf16, C>(XkgT + (16 * ct + m16) * LDC,
+                                            16 * ct + m16, KU * uu, g4, true);
+          }
+#pragma unroll
+        for (int uu = 0; uu < NTU; ++uu)
+          if (uu <= umax)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+              acc[h2] = M::mma(xa[uu][h2], tb[uu], acc[h2]);
+        st_stream(blk + W.off_negw + ((size_t)(rt * NKU + u) * 64 + lane) * 16,
+                  M::pack(-acc[0], -acc[1]));
+      }
+    };
+    auto u_tiles = [&](int rt, int v0, int v1) {
+      frag tb[NTU];
+      load_t(rt, tb);
+      const int umax = rt / 2;
+      for (int vt = v0; vt < v1; ++vt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        frag vb[NTU];
+#pragma unroll
+        for (int uu = 0; uu < NTU; ++uu)
+          vb[uu] = load_k_cm<bf16, C>(XvT + (16 * vt + m16) * LDC,
+                                      16 * vt + m16, KU * uu, g4, true);
+#pragma unroll
+        for (int uu = 0; uu < NTU; ++uu)
+          if (uu <= umax) acc = M::mma(tb[uu], vb[uu], acc);
+        bf16 *dst = (bf16 *)(blk + W.off_u) +
+                    ((size_t)(vt * NB + rt) * 64 + lane) * 4;
+        const float a4[4] = {acc[0], acc[1], acc[2], acc[3]};
+        st_stream(dst, Vec4<bf16>::put(a4));
+      }
+    };
+    if (wave < 4) {
+      const int u0 = 2 * (wave & 1);
+      w_units(2 + (wave >> 1), u0, u0 + 2);
+      w_units(wave >> 1, u0, u0 + 2);
+    } else if (wave == 4) {
+      u_tiles(2, 0, 6);
+    } else if (wave == 5) {
+      u_tiles(3, 0, 6);
+    } else if (wave == 6) {
+      u_tiles(2, 6, 8);
+      u_tiles(3, 6, 8);
+      u_tiles(0, 0, 4);
+    } else {
+      u_tiles(0, 4, 8);
+      u_tiles(1, 0, 8);
+    }
+    if (more) put_beta();  // the current task's betas were last read in E1
+    __syncthreads();       // B5: LDS free for the next task
+  }
+}
+
+}  // namespace pc
+
+bool prep_d128_applies(const PrefillParams &p, int io_bf16) {
+  return io_bf16 && !p.gate_head && !p.use_conv && p.Dk == pc::DK &&
+         p.Dv == pc::DV && p.C == pc::C;
+}
+
+hipError_t launch_prefill_prep_d128(const PrefillParams &p, hipStream_t s) {
+  const long long ntask = (long long)p.B * p.H * p.NC;
+  const unsigned grid = (unsigned)std::min<long long>(ntask, cu_count());
+  if (p.gate_bf16)
+    hipLaunchKernelGGL(pc::kda_chunk_prep_d128<bf16>, dim3(grid), dim3(pc::NT),
+                       0, s, p);
+  else
+    hipLaunchKernelGGL(pc::kda_chunk_prep_d128<float>, dim3(grid),
+                       dim3(pc::NT), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace kda

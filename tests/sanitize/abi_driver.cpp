@@ -18,6 +18,8 @@ hipError_t launch_prefill_prep_bf16_f32(const PrefillParams &, hipStream_t) { ++
 hipError_t launch_prefill_prep_bf16_bf16(const PrefillParams &, hipStream_t) { ++launches; return hipErrorInvalidValue; }
 bool prep_gdn_applies(const PrefillParams &, int) { return false; }
 hipError_t launch_prefill_prep_gdn(const PrefillParams &, hipStream_t) { ++launches; return hipErrorInvalidValue; }
+bool prep_d128_applies(const PrefillParams &, int) { return false; }
+hipError_t launch_prefill_prep_d128(const PrefillParams &, hipStream_t) { ++launches; return hipErrorInvalidValue; }
 hipError_t launch_state_pass(const PrefillParams &, int, hipStream_t) { ++launches; return hipErrorInvalidValue; }
 hipError_t launch_decode(const DecodeParams &, int, hipStream_t) { ++launches; return hipErrorInvalidValue; }
 hipError_t launch_backward(const BwdParams &, int, hipStream_t) { ++launches; return hipErrorInvalidValue; }
