@@ -36,14 +36,15 @@ constexpr int LDK = DK + 8;  // token-major bf16 rows [C][LDK]
 constexpr int LDC = C + 8;   // channel-major bf16 rows [*][LDC]
 constexpr int LDA = C + 4;   // fp32 rows [C][LDA]
 
-// LDS layout (bytes).  Region A (E1 -> AP) holds the row and column
-// operands of A and P; region D (T1 -> WU) overlays it.
+// LDS layout (bytes).  Region A (E1 -> the P products) holds the row and
+// column operands of A and P; region D (T1 -> WU: the diagonal inverses and
+// T in bf16) overlays the rows of beta K rho, which only the A products
+// read, so P and the Qtil / Ktil^T units can still run beside T1 and T2.
 constexpr size_t TOK = (size_t)C * LDK * 2;
-constexpr size_t oKR = 0, oQR = TOK, oKS = 2 * TOK, oKIR = 3 * TOK;
-constexpr size_t oTt = 0;                                  // T fp32
-constexpr size_t oTaa = oTt + (size_t)C * LDA * 4;         // diagonal T^T
+constexpr size_t oKR = 0, oKIR = TOK, oQR = 2 * TOK, oKS = 3 * TOK;
+constexpr size_t oTaa = 0;                                 // diagonal T^T
 constexpr size_t oTb = oTaa + (size_t)NB * 256 * 4;        // T bf16
-static_assert(oTb + (size_t)C * LDC * 2 <= 4 * TOK, "region D inside A");
+static_assert(oTb + (size_t)C * LDC * 2 <= TOK, "region D inside beta K rho");
 constexpr size_t oAf = 4 * TOK;                            // A fp32
 constexpr size_t oFb = oAf + (size_t)C * LDA * 4;          // exact diagonals
 constexpr size_t oKST = oFb + (size_t)2 * NB * 256 * 4;    // (K sigma)^T
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) char sm[LDS];
   bf16 *Xkr = (bf16 *)(sm + oKR), *Xqr = (bf16 *)(sm + oQR);
   bf16 *Xks = (bf16 *)(sm + oKS), *Xkir = (bf16 *)(sm + oKIR);
-  float *Tt = (float *)(sm + oTt), *Taa = (float *)(sm + oTaa);
+  float *Taa = (float *)(sm + oTaa);
   bf16 *Tb = (bf16 *)(sm + oTb);
   float *Af = (float *)(sm + oAf);
   float *FbA = (float *)(sm + oFb), *FbP = FbA + NB * 256;
@@ -305,66 +306,6 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
         *(float2 *)((float *)(blk + W.off_gam) + c0) =
             make_float2(fp0 * F[0], fp1 * F[1]);
     }
-    // Qtil = scale Q*Gam: 16 units (row tile aa, channel unit u), two per
-    // wave; a lane's 16-byte slot holds channels 32u + 4g4 .. +3 and
-    // 32u + 16 + 4g4 .. +3 of token 16aa + m16
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int w = wave + NW * it;
-      const int aa = w / NKU, u = w % NKU;
-      const int tok = 16 * aa + m16;
-      const int ch0 = KU * u + 4 * g4, ch1 = ch0 + 16;
-      f32x4 f0 = {1.f, 1.f, 1.f, 1.f}, f1 = {1.f, 1.f, 1.f, 1.f};
-#pragma unroll
-      for (int bb = 0; bb < NB - 1; ++bb) {
-        const f32x4 l0 = *(const f32x4 *)(Fs + bb * DK + ch0);
-        const f32x4 l1 = *(const f32x4 *)(Fs + bb * DK + ch1);
-        if (bb < aa) {
-          f0 *= l0;
-          f1 *= l1;
-        }
-      }
-      float x0[4], x1[4], y0[4], y1[4];
-      Vec4<bf16>::get(*(const R4 *)(Xqr + tok * LDK + ch0), x0);
-      Vec4<bf16>::get(*(const R4 *)(Xqr + tok * LDK + ch1), x1);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        y0[j] = x0[j] * f0[j];
-        y1[j] = x1[j] * f1[j];
-      }
-      const R4 lo = Vec4<bf16>::put(y0), up = Vec4<bf16>::put(y1);
-      st_stream(blk + W.off_qt + ((size_t)(aa * NKU + u) * 64 + lane) * 16,
-                make_uint4(lo.x, lo.y, up.x, up.y));
-    }
-    // Ktil^T = (K*Gam_C/Gam)^T: 16 units (channel tile ct, token unit u)
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int w = wave + NW * it;
-      const int ct = w / NTU, u = w % NTU;
-      const int ch = 16 * ct + m16;
-      const int tk0 = KU * u + 4 * g4, tk1 = tk0 + 16;
-      const int a0 = 2 * u;  // sub-chunk of tk0; tk1 lies in a0 + 1
-      float fl[NB];
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb) fl[bb] = Fs[bb * DK + ch];
-      float s0 = 1.f, s1 = 1.f;
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb) {
-        if (bb > a0) s0 *= fl[bb];
-        if (bb > a0 + 1) s1 *= fl[bb];
-      }
-      float x0[4], x1[4], y0[4], y1[4];
-      Vec4<bf16>::get(*(const R4 *)(XksT + ch * LDC + cm_off<C>(ch, tk0)), x0);
-      Vec4<bf16>::get(*(const R4 *)(XksT + ch * LDC + cm_off<C>(ch, tk1)), x1);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        y0[j] = x0[j] * s0;
-        y1[j] = x1[j] * s1;
-      }
-      const R4 lo = Vec4<bf16>::put(y0), up = Vec4<bf16>::put(y1);
-      st_stream(blk + W.off_ktt + ((size_t)(ct * NTU + u) * 64 + lane) * 16,
-                make_uint4(lo.x, lo.y, up.x, up.y));
-    }
     // mid products M_{b->a} = prod_{b<d<a} F_d for sub-chunk pairs a-b >= 2:
     // pairs (2,0), (3,0), (3,1) at index 0, 1, 2
     if (tid < 3 * DK) {
@@ -420,69 +361,154 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
       __syncthreads();
     }
 
-    // ---- AP: A^T and P^T blocks as 20 half-blocks --------------------------
-    // item i < 10: A of block i, else P of block i - 10 (blocks in ap_block
-    // order); wave w takes items w, w + 8, w + 16
-    for (int it = wave; it < 20; it += NW) {
-      const bool isP = it >= 10;
-      int aa, bb;
-      ap_block<NB>(isP ? it - 10 : it, aa, bb);
-      const bool diag = aa == bb;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if (diag && fallback) {
-        const float *fb = isP ? FbP : FbA;
+    // Qtil = scale Q*Gam, unit w (row tile w / 4, channel unit w % 4): a
+    // lane's 16-byte slot holds channels 32u + 4g4 .. +3 and 32u + 16 + 4g4
+    // .. +3 of token 16aa + m16
+    auto q_unit = [&](int w) {
+      const int aa = w / NKU, u = w % NKU;
+      const int tok = 16 * aa + m16;
+      const int ch0 = KU * u + 4 * g4, ch1 = ch0 + 16;
+      f32x4 f0 = {1.f, 1.f, 1.f, 1.f}, f1 = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[j] = fb[(aa * 16 + m16) * 16 + 4 * g4 + j];
+      for (int bb = 0; bb < NB - 1; ++bb) {
+        const f32x4 l0 = *(const f32x4 *)(Fs + bb * DK + ch0);
+        const f32x4 l1 = *(const f32x4 *)(Fs + bb * DK + ch1);
+        if (bb < aa) {
+          f0 *= l0;
+          f1 *= l1;
+        }
+      }
+      float x0[4], x1[4], y0[4], y1[4];
+      Vec4<bf16>::get(*(const R4 *)(Xqr + tok * LDK + ch0), x0);
+      Vec4<bf16>::get(*(const R4 *)(Xqr + tok * LDK + ch1), x1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y0[j] = x0[j] * f0[j];
+        y1[j] = x1[j] * f1[j];
+      }
+      const R4 lo = Vec4<bf16>::put(y0), up = Vec4<bf16>::put(y1);
+      st_stream(blk + W.off_qt + ((size_t)(aa * NKU + u) * 64 + lane) * 16,
+                make_uint4(lo.x, lo.y, up.x, up.y));
+    };
+    // Ktil^T = (K*Gam_C/Gam)^T, unit w (channel tile w / 2, token unit w % 2)
+    auto k_unit = [&](int w) {
+      const int ct = w / NTU, u = w % NTU;
+      const int ch = 16 * ct + m16;
+      const int tk0 = KU * u + 4 * g4, tk1 = tk0 + 16;
+      const int a0 = 2 * u;  // sub-chunk of tk0; tk1 lies in a0 + 1
+      float fl[NB];
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) fl[bb] = Fs[bb * DK + ch];
+      float s0 = 1.f, s1 = 1.f;
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        if (bb > a0) s0 *= fl[bb];
+        if (bb > a0 + 1) s1 *= fl[bb];
+      }
+      float x0[4], x1[4], y0[4], y1[4];
+      Vec4<bf16>::get(*(const R4 *)(XksT + ch * LDC + cm_off<C>(ch, tk0)), x0);
+      Vec4<bf16>::get(*(const R4 *)(XksT + ch * LDC + cm_off<C>(ch, tk1)), x1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y0[j] = x0[j] * s0;
+        y1[j] = x1[j] * s1;
+      }
+      const R4 lo = Vec4<bf16>::put(y0), up = Vec4<bf16>::put(y1);
+      st_stream(blk + W.off_ktt + ((size_t)(ct * NTU + u) * 64 + lane) * 16,
+                make_uint4(lo.x, lo.y, up.x, up.y));
+    };
+    // block j (ap_block order) of A (into LDS) and/or P (into the
+    // workspace); both products share the column operand
+    auto ap_item = [&](int j, bool doA, bool doP) {
+      int aa, bb;
+      ap_block<NB>(j, aa, bb);
+      const bool diag = aa == bb;
+      f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+      if (diag && fallback) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          accA[i] = FbA[(aa * 16 + m16) * 16 + 4 * g4 + i];
+          accP[i] = FbP[(aa * 16 + m16) * 16 + 4 * g4 + i];
+        }
       } else {
-        const bf16 *rb = (isP ? Xqr : Xkr) + (16 * aa + m16) * LDK;
+        const bf16 *kb = Xkr + (16 * aa + m16) * LDK;
+        const bf16 *qb = Xqr + (16 * aa + m16) * LDK;
         const bf16 *cb = (diag ? Xkir : Xks) + (16 * bb + m16) * LDK;
-        frag rf[NKU], cf[NKU];
+        frag kf[NKU], qf[NKU], cf[NKU];
 #pragma unroll
         for (int u = 0; u < NKU; ++u) {
-          rf[u] = M::load_k(rb + KU * u, g4);
           cf[u] = M::load_k(cb + KU * u, g4);
+          if (doA) kf[u] = M::load_k(kb + KU * u, g4);
+          if (doP) qf[u] = M::load_k(qb + KU * u, g4);
         }
         if (aa - bb >= 2) {
+          // decay across the sub-chunks strictly between bb and aa, per
+          // channel, on the column operand (lane slots 32u + 4g4 + e and
+          // 32u + 16 + 4g4 + e)
           const float *mid = Mid + (aa == 2 ? 0 : (bb == 0 ? 1 : 2)) * DK;
 #pragma unroll
-          for (int u = 0; u < NKU; ++u)
+          for (int u = 0; u < NKU; ++u) {
+            const f32x4 m0 = *(const f32x4 *)(mid + KU * u + 4 * g4);
+            const f32x4 m1 = *(const f32x4 *)(mid + KU * u + 16 + 4 * g4);
 #pragma unroll
-            for (int ee = 0; ee < M::NE; ++ee)
-              M::set(cf[u], ee,
-                     M::elem(cf[u], ee) * mid[KU * u + M::koff(g4, ee)]);
+            for (int e = 0; e < 4; ++e) {
+              cf[u][e] = (bf16)((float)cf[u][e] * m0[e]);
+              cf[u][4 + e] = (bf16)((float)cf[u][4 + e] * m1[e]);
+            }
+          }
         }
 #pragma unroll
-        for (int u = 0; u < NKU; ++u) acc = M::mma(cf[u], rf[u], acc);
+        for (int u = 0; u < NKU; ++u) {
+          if (doA) accA = M::mma(cf[u], kf[u], accA);
+          if (doP) accP = M::mma(cf[u], qf[u], accP);
+        }
       }
-      // lane (m16, g4): element j is row 16aa + m16, col 16bb + 4g4 + j
+      // lane (m16, g4): element i is row 16aa + m16, col 16bb + 4g4 + i
       if (diag) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int sc = 4 * g4 + j;
-          if (isP ? !(sc <= m16) : !(sc < m16)) acc[j] = 0.f;
+        for (int i = 0; i < 4; ++i) {
+          const int sc = 4 * g4 + i;
+          if (!(sc < m16)) accA[i] = 0.f;
+          if (!(sc <= m16)) accP[i] = 0.f;
         }
       }
-      if (!isP) {
-        *(f32x4 *)(Af + (16 * aa + m16) * LDA + 16 * bb + 4 * g4) = acc;
-      } else {
+      if (doA)
+        *(f32x4 *)(Af + (16 * aa + m16) * LDA + 16 * bb + 4 * g4) = accA;
+      if (doP) {
         char *dst = blk + W.off_p +
                     ((size_t)(aa * NTU + bb / 2) * 64 + lane) * 16 +
                     (bb % 2) * 8;
-        const float a4[4] = {acc[0], acc[1], acc[2], acc[3]};
+        const float a4[4] = {accP[0], accP[1], accP[2], accP[3]};
         st_stream(dst, Vec4<bf16>::put(a4));
         if (diag && (aa % 2) == 0) {
           const float z[4] = {0.f, 0.f, 0.f, 0.f};
           st_stream(dst + 8, Vec4<bf16>::put(z));
         }
       }
+    };
+    // for the backward pass: A = diag(beta) M and T^T, fp32 (only their
+    // lower and upper triangles are read)
+    float *tat = p.train_at ? p.train_at + ((size_t)bh * p.NC + n) * 2 * C * C
+                            : nullptr;
+
+    // ---- AP: A and P blocks on the matrix cores --------------------------
+    // eight blocks whole (A and P), blocks (0,0) and (1,1) split into their
+    // A and P halves on waves 4-7: 20 products per SIMD (waves w, w + 4);
+    // the three blocks with mid products go to waves 0-2
+    {
+      const int full = wave < 4 ? (wave == 0 ? 2 : wave == 1 ? 3 : wave == 2 ? 7 : 1)
+                                : (wave == 4 ? 4 : wave == 5 ? 6 : wave == 6 ? 8 : 9);
+      ap_item(full, true, true);
+      if (wave >= 4) ap_item(wave < 6 ? 0 : 5, (wave & 1) == 0, (wave & 1) == 1);
     }
-    __syncthreads();  // B3: region A no longer read
+    __syncthreads();  // B3: A complete; beta K rho no longer read
     if (more) load_task<4, GT>(p, task + gridDim.x, st, tid, c0, r0);
 
-    // ---- T1: diagonal inverses (waves 0-3, as in kda_prep_impl.h) while
-    // waves 4-7 zero the upper block (r, r+1) of every even token tile r of
-    // the bf16 T, which the W/U products read as part of whole 32-token units
+    // ---- T1: diagonal inverses (waves 0-3, as in kda_prep_impl.h) beside
+    // part of the Qtil / Ktil^T unit stores (waves 4-7), which no later phase
+    // reads.  Waves 4-7 also zero the upper block (r, r+1) of every even
+    // token tile r of the bf16 T, which the W/U products read as part of
+    // whole 32-token units.
     f32x4 Tcol[NB];
     if (wave < NB) {
       const int aa = wave;
@@ -503,23 +529,33 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
       Y = mma16_f32(L2A, Y, Y);
       Y = mma16_f32(L4A, Y, Y);
       Y = mma16_f32(L8A, Y, Y);
+      // lane (g4, m16) holds T_aa[4 g4 + j][m16]
       Tcol[0] = Y;
-      *(f32x4 *)(Tt + (16 * aa + m16) * LDA + 16 * aa + 4 * g4) = Y;
+      if (tat)
+        *(f32x4 *)(tat + C * C + (16 * aa + m16) * C + 16 * aa + 4 * g4) = Y;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         Taa[(aa * 16 + 4 * g4 + j) * 16 + m16] = Y[j];
         Tb[(16 * aa + 4 * g4 + j) * LDC + 16 * aa + m16] = (bf16)Y[j];
       }
-    } else if (tid - 256 < 64) {
-      // rows 16 rt .. 16 rt + 15 (rt = 0, 2), 16 columns from 16 (rt + 1)
-      const int i = tid - 256;
-      const int rt = 2 * (i / 32), row = (i % 32) / 2, hv = i % 2;
-      *(uint4 *)(Tb + (16 * rt + row) * LDC + 16 * (rt + 1) + 8 * hv) =
-          make_uint4(0u, 0u, 0u, 0u);
+    } else {
+      if (tid - 256 < 64) {
+        // rows 16 rt .. 16 rt + 15 (rt = 0, 2), 16 columns from 16 (rt + 1)
+        const int i = tid - 256;
+        const int rt = 2 * (i / 32), row = (i % 32) / 2, hv = i % 2;
+        *(uint4 *)(Tb + (16 * rt + row) * LDC + 16 * (rt + 1) + 8 * hv) =
+            make_uint4(0u, 0u, 0u, 0u);
+      }
+      // units 0 .. 11 of the 32 Qtil / Ktil^T units (3 per wave)
+      for (int w = wave - NB; w < 12; w += NW - NB) q_unit(w);
+      if (tat)
+        for (int i = tid - 256; i < C * C; i += NT - 256)
+          tat[i] = Af[(i / C) * LDA + i % C];
     }
     __syncthreads();
-    // ---- T2: off-diagonal blocks, one block column per wave ---------------
-    if (wave < NB) {
+    // ---- T2: off-diagonal blocks of T, one block column per wave (waves
+    // 0-2), beside the Qtil and Ktil^T units (waves 3-7)
+    if (wave < NB - 1) {
       const int bb = wave;
 #pragma unroll
       for (int k = 1; k < NB; ++k) {
@@ -535,26 +571,24 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
         const f32x4 ta = *(const f32x4 *)(Taa + (aa * 16 + m16) * 16 + 4 * g4);
         const f32x4 Tn = -mma16_f32(ta, X, f32x4{0.f, 0.f, 0.f, 0.f});
         Tcol[k] = Tn;
-        *(f32x4 *)(Tt + (16 * bb + m16) * LDA + 16 * aa + 4 * g4) = Tn;
+        // lane (n = m16, g4) holds T_ab[4g4 + j][m16]
+        if (tat)
+          *(f32x4 *)(tat + C * C + (16 * bb + m16) * C + 16 * aa + 4 * g4) = Tn;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           Tb[(16 * aa + 4 * g4 + j) * LDC + 16 * bb + m16] = (bf16)Tn[j];
       }
-    } else if (more) {
-      load_task<8, GT>(p, task + gridDim.x, st, tid, c0, r0);
-    }
-    __syncthreads();
-    if (more && wave < NB) load_task<8, GT>(p, task + gridDim.x, st, tid, c0, r0);
-
-    if (p.train_at) {
-      // for the backward pass: A = diag(beta) M and T^T, fp32
-      float *dst = p.train_at + ((size_t)bh * p.NC + n) * 2 * C * C;
-      for (int i = tid; i < C * C; i += NT) {
-        const int r = i / C, c = i % C;
-        dst[i] = Af[r * LDA + c];
-        dst[C * C + i] = Tt[r * LDA + c];
+    } else {
+      // units 12 .. 31 (4 per wave)
+      for (int w = 12 + wave - (NB - 1); w < 2 * NB * NKU; w += NW - (NB - 1)) {
+        if (w < NB * NKU)
+          q_unit(w);
+        else
+          k_unit(w - NB * NKU);
       }
     }
+    __syncthreads();
+    if (more) load_task<8, GT>(p, task + gridDim.x, st, tid, c0, r0);
 
     // ---- WU: -W (A-operand units) and U (accumulator tiles) ----------------
     // token tile rt reads T rows 16 rt .. 16 rt + 15 over token units
