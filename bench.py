@@ -141,6 +141,20 @@ def main():
                 fn()
             torch.cuda.synchronize()
 
+    # per-kernel durations: K back-to-back launches of each kernel alone
+    # (HIP events on the launch stream), so launch gaps are not counted
+    def t_back_to_back(fn, reps=None):
+        reps = reps or K
+        fn()
+        torch.cuda.synchronize()
+        a, b_ = ev(), ev()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b_) / reps
+
     # ---------------- prefill, model-shaped (headline) ----------------------
     c1 = ki.workload(ki.PREFILL)
     B, T, H, Dk, Dv, C = (c1[n] for n in ("B", "T", "H", "Dk", "Dv", "chunk"))
@@ -169,18 +183,6 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / K
-        # per-kernel durations: K back-to-back launches of each kernel alone
-        # (HIP events on the launch stream), so launch gaps are not counted
-        def t_back_to_back(fn):
-            fn()
-            torch.cuda.synchronize()
-            a, b_ = ev(), ev()
-            a.record(stream)
-            for _ in range(K):
-                fn()
-            b_.record(stream)
-            torch.cuda.synchronize()
-            return a.elapsed_time(b_) / K
         tp = t_back_to_back(lambda: kda.kda_prefill_chunk_prep(
             x["q"], x["k"], x["v"], x["g"], x["beta"], ws, chunk=C))
         ts = t_back_to_back(lambda: kda.kda_prefill_state_pass(
@@ -431,7 +433,24 @@ def main():
         extra[name] = dict(ms_per_call=ms,
                                 tokens_per_s=Bc * Tc / (ms * 1e-3),
                                 algo_gbs=gbs, hbm_frac=gbs / HBM_PEAK_GBS)
-        log(f"{tag}: {ms:.3f} ms/call, {gbs:.0f} GB/s algorithmic")
+        kinfo = ""
+        if not conv:
+            # the two kernels alone, back to back
+            tp = t_back_to_back(lambda: kda.kda_prefill_chunk_prep(
+                x["q"], x["k"], x["v"], x["g"], x["beta"], ws, chunk=Cc),
+                reps)
+            ts = t_back_to_back(lambda: kda.kda_prefill_state_pass(
+                ws, o, s_out=s, B=Bc, T=Tc, H=Hc, Dk=Dc, Dv=Dc, chunk=Cc),
+                reps)
+            extra[name]["kernel_ms"] = {"kda_chunk_prep": tp,
+                                        "kda_state_pass": ts}
+            if tag == "gdn" and "prefill" in out:
+                # the scalar-gate prep against the per-channel prep of the
+                # same shape (headline workload)
+                extra[name]["prep_vs_per_channel_prep"] = \
+                    tp / out["prefill"]["kernel_ms"]["kda_chunk_prep"]
+            kinfo = f" (prep {tp*1e3:.1f} us, state {ts*1e3:.1f} us)"
+        log(f"{tag}: {ms:.3f} ms/call{kinfo}, {gbs:.0f} GB/s algorithmic")
         del x, ws, o, s
         torch.cuda.empty_cache()
 

@@ -1107,94 +1107,123 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
         }
       }
       atomicAdd(&dGl[ib], kil);
-      // ---- row role: rowK, rowQ of sub-chunk a
+      // the 4 tokens 16 b + 4 g4 + e of every sub-chunk b at this lane's
+      // channel ib, as the products' per-token factors need them
+      float kx[NB][4], xr[NB][4];
 #pragma unroll
-      for (int a = 0; a < NB; ++a) {
-        f32x4 zk = zero, zq = zero;
-        for (int b = 0; b <= a; ++b) {
-          if (b == a && !dok) continue;
-          frag fk, fq, fb;
-#pragma unroll
-          for (int e = 0; e < MM::NE; ++e) {
-            const int k = MM::koff(g4, e);
-            float vk = 0.f, vq = 0.f, vb = 0.f;
-            if (k < 16) {
-              const int ra = 16 * a + m16, sb = 16 * b + k;
-              vk = dMm[ra * C + sb];
-              vq = dPm[ra * C + sb];
-              const float x = to_f32(ks[sb * DK + ib]);
-              vb = b < a ? x * to_f32(sg[sb * DK + ib]) * mid(a, b, ib)
-                         : x / rho[sb * DK + ib];
-            }
-            MM::set(fk, e, vk);
-            MM::set(fq, e, vq);
-            MM::set(fb, e, vb);
-          }
-          zk = MM::mma(fk, fb, zk);
-          zq = MM::mma(fq, fb, zq);
-        }
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 16 * a + 4 * g4 + e;
-          const float rr = rho[r * DK + ib];
-          float rK = rr * zk[e], rQ = rr * zq[e];
-          if (!dok) {
-            rK += diag_exact(r, ib, true, ks, dMm, true);
-            rQ += diag_exact(r, ib, true, ks, dPm, false);
+          const int sb = 16 * b + 4 * g4 + e;
+          kx[b][e] = to_f32(ks[sb * DK + ib]);
+          xr[b][e] = rho[sb * DK + ib];
+        }
+      // ---- row role: rowK, rowQ of sub-chunk a
+      {
+        // column operand values: k sigma (times mid) off the diagonal,
+        // k / rho on it
+        float ksg[NB][4], kir[NB][4];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int sb = 16 * b + 4 * g4 + e;
+            ksg[b][e] = kx[b][e] * to_f32(sg[sb * DK + ib]);
+            kir[b][e] = kx[b][e] / xr[b][e];
           }
-          aK_[jt][a][e] += rK;
-          aQ_[jt][a][e] += rQ;
-          aG_[jt][a][e] += to_f32(ks[r * DK + ib]) * rK +
-                           to_f32(qs[r * DK + ib]) * rQ;
+#pragma unroll
+        for (int a = 0; a < NB; ++a) {
+          f32x4 zk = zero, zq = zero;
+#pragma unroll
+          for (int b = 0; b <= a; ++b) {
+            if (b == a && !dok) continue;
+            // lane (g4, m16): row 16a + m16, k = 16 b + 4 g4 + e (e < 4)
+            const f32x4 mk = *(const f32x4 *)(dMm + (16 * a + m16) * C + 16 * b +
+                                              4 * g4);
+            const f32x4 mq = *(const f32x4 *)(dPm + (16 * a + m16) * C + 16 * b +
+                                              4 * g4);
+            const float md = mid(a, b, ib);
+            frag fk, fq, fb;
+#pragma unroll
+            for (int e = 0; e < MM::NE; ++e) {
+              const bool lo = e < 4;
+              MM::set(fk, e, lo ? mk[e & 3] : 0.f);
+              MM::set(fq, e, lo ? mq[e & 3] : 0.f);
+              MM::set(fb, e, lo ? (b < a ? ksg[b][e & 3] * md : kir[b][e & 3])
+                                : 0.f);
+            }
+            zk = MM::mma(fk, fb, zk);
+            zq = MM::mma(fq, fb, zq);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * a + 4 * g4 + e;
+            const float rr = xr[a][e];
+            float rK = rr * zk[e], rQ = rr * zq[e];
+            if (!dok) {
+              rK += diag_exact(r, ib, true, ks, dMm, true);
+              rQ += diag_exact(r, ib, true, ks, dPm, false);
+            }
+            aK_[jt][a][e] += rK;
+            aQ_[jt][a][e] += rQ;
+            aG_[jt][a][e] += kx[a][e] * rK + to_f32(qs[r * DK + ib]) * rQ;
+          }
         }
       }
       // ---- column role: colK, colQ of sub-chunk b
+      {
+        // row-side values k rho and q rho of the 4 tokens of every sub-chunk
+        float kr4[NB][4], qr4[NB][4];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        f32x4 ok_ = zero, oq = zero, dk2 = zero, dq2 = zero;
-        for (int a = b; a < NB; ++a) {
-          if (a == b && !dok) continue;
-          frag fk, fq, bk, bq;
+        for (int a = 0; a < NB; ++a)
 #pragma unroll
-          for (int e = 0; e < MM::NE; ++e) {
-            const int k = MM::koff(g4, e);
-            float vk = 0.f, vq = 0.f, xk = 0.f, xq = 0.f;
-            if (k < 16) {
-              const int sb = 16 * b + m16, ra = 16 * a + k;
-              vk = dMm[ra * C + sb];
-              vq = dPm[ra * C + sb];
-              const float f = rho[ra * DK + ib] * (a > b ? mid(a, b, ib) : 1.f);
-              xk = to_f32(ks[ra * DK + ib]) * f;
-              xq = to_f32(qs[ra * DK + ib]) * f;
+          for (int e = 0; e < 4; ++e) {
+            const int ra = 16 * a + 4 * g4 + e;
+            kr4[a][e] = kx[a][e] * xr[a][e];
+            qr4[a][e] = to_f32(qs[ra * DK + ib]) * xr[a][e];
+          }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          f32x4 ok_ = zero, oq = zero, dk2 = zero, dq2 = zero;
+#pragma unroll
+          for (int a = b; a < NB; ++a) {
+            if (a == b && !dok) continue;
+            const float md = a > b ? mid(a, b, ib) : 1.f;
+            frag fk, fq, bk, bq;
+#pragma unroll
+            for (int e = 0; e < MM::NE; ++e) {
+              const bool lo = e < 4;
+              // dM^T: row 16 b + m16, k = 16 a + 4 g4 + e
+              const int ra = 16 * a + 4 * g4 + (e & 3), sb = 16 * b + m16;
+              MM::set(fk, e, lo ? dMm[ra * C + sb] : 0.f);
+              MM::set(fq, e, lo ? dPm[ra * C + sb] : 0.f);
+              MM::set(bk, e, lo ? kr4[a][e & 3] * md : 0.f);
+              MM::set(bq, e, lo ? qr4[a][e & 3] * md : 0.f);
             }
-            MM::set(fk, e, vk);
-            MM::set(fq, e, vq);
-            MM::set(bk, e, xk);
-            MM::set(bq, e, xq);
+            if (a > b) {
+              ok_ = MM::mma(fk, bk, ok_);
+              oq = MM::mma(fq, bq, oq);
+            } else {
+              dk2 = MM::mma(fk, bk, dk2);
+              dq2 = MM::mma(fq, bq, dq2);
+            }
           }
-          if (a > b) {
-            ok_ = MM::mma(fk, bk, ok_);
-            oq = MM::mma(fq, bq, oq);
-          } else {
-            dk2 = MM::mma(fk, bk, dk2);
-            dq2 = MM::mma(fq, bq, dq2);
-          }
-        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int s2 = 16 * b + 4 * g4 + e;
-          const float sgv = to_f32(sg[s2 * DK + ib]);
-          float cK = sgv * ok_[e], cQ = sgv * oq[e];
-          if (dok) {
-            const float ir = 1.f / rho[s2 * DK + ib];
-            cK += dk2[e] * ir;
-            cQ += dq2[e] * ir;
-          } else {
-            cK += diag_exact(s2, ib, false, ks, dMm, true);
-            cQ += diag_exact(s2, ib, false, qs, dPm, false);
+          for (int e = 0; e < 4; ++e) {
+            const int s2 = 16 * b + 4 * g4 + e;
+            const float sgv = to_f32(sg[s2 * DK + ib]);
+            float cK = sgv * ok_[e], cQ = sgv * oq[e];
+            if (dok) {
+              const float ir = 1.f / xr[b][e];
+              cK += dk2[e] * ir;
+              cQ += dq2[e] * ir;
+            } else {
+              cK += diag_exact(s2, ib, false, ks, dMm, true);
+              cQ += diag_exact(s2, ib, false, qs, dPm, false);
+            }
+            aK_[jt][b][e] += cK + cQ;
+            aG_[jt][b][e] -= kx[b][e] * (cK + cQ);
           }
-          aK_[jt][b][e] += cK + cQ;
-          aG_[jt][b][e] -= to_f32(ks[s2 * DK + ib]) * (cK + cQ);
         }
       }
     }
