@@ -84,6 +84,22 @@ def traffic_for(kernel, sources):
     return rec.get("bytes_per_launch")
 
 
+def mfma_busy_for(key, sources):
+    """MFMA busy fractions measured by rocprofv3 counters
+    (profiles/mfma_busy.json), or None if missing or taken on other kernel
+    sources."""
+    p = os.path.join(ROOT, "profiles", "mfma_busy.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except ValueError:
+        return None
+    if d.get("src_hash", {}).get(key) != src_hash(sources):
+        return None
+    return d
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,6 +226,14 @@ def main():
             mfma=dict(achieved=flops / t_k / 1e12,
                       peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
                       frac=flops / t_k / 1e12 / MFMA_BF16_PEAK_TFLOPS))
+        mb = mfma_busy_for("prefill", srcs)
+        if mb is not None:
+            # rocprofv3: SQ_VALU_MFMA_BUSY_CYCLES over all SIMD cycles
+            out["prefill"]["mfma"]["busy_frac_rocprof"] = {
+                "kda_chunk_prep": mb["kernels"]["kda_chunk_prep"]["mfma_busy_frac"],
+                "kda_state_pass": mb["kernels"]["kda_state_pass"]["mfma_busy_frac"],
+                "call": mb["prefill_call_busy_frac"],
+                "source": "profiles/mfma_busy.md"}
         log(f"prefill: {ms*1e3:.1f} us/step (prep {tp*1e3:.1f} us, state "
             f"{ts*1e3:.1f} us), {gbs:.0f} GB/s algorithmic")
         if not args.no_cpu:
