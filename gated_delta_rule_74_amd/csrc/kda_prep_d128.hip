@@ -55,7 +55,14 @@ constexpr size_t oM = oF + (size_t)NB * DK * 4;            // mid products
 constexpr size_t oVote = oM + (size_t)3 * DK * 4;
 constexpr size_t oBeta = oVote + 64;
 constexpr size_t LDS = oBeta + 64 * 4;
-static_assert(LDS <= 160 * 1024, "one workgroup per CU");
+// with the fused conv: the head's taps (one f32x4 per q, k and v channel),
+// per-token L2 scales of q and k (for the exact diagonal path), and the
+// two channel halves' partial sums of squares
+constexpr size_t oTap = LDS;
+constexpr size_t oNrm = oTap + (size_t)(2 * DK + DV) * 16;
+constexpr size_t oL2p = oNrm + (size_t)C * 2 * 4;
+constexpr size_t LDS_CONV = oL2p + (size_t)NW * 16 * 2 * 4;
+static_assert(LDS_CONV <= 160 * 1024, "one workgroup per CU");
 
 // two bf16 values as raw bits
 __device__ __forceinline__ void get2(uint32_t r, float &a, float &b) {
@@ -93,18 +100,23 @@ template <> struct GRaw<bf16> {
 };
 
 // the next task's inputs, one task ahead in registers: 2 channels x 8 tokens
-// of q, k, v and g per thread, and (wave 0) the chunk's betas, token = lane
-template <typename GT> struct Stage {
-  uint32_t q[8], k[8], v[8];
+// of q, k, v and g per thread (with the conv: the raw projections and three
+// earlier rows), and (wave 0) the chunk's betas, token = lane; with the
+// conv, thread t < 384 also holds tap set t of the head
+template <typename GT, bool CONV> struct Stage {
+  static constexpr int XR = CONV ? 11 : 8;
+  uint32_t q[XR], k[XR], v[XR];
   typename GRaw<GT>::raw g[8];
   uint32_t beta;
+  f32x4 tap;
 };
 
-// PART: 1 = g and beta, 2 = q, 4 = k, 8 = v
-template <int PART, typename GT>
+// PART: 1 = g and beta, 2 = q, 4 = k, 8 = v (and the conv taps)
+template <int PART, typename GT, bool CONV>
 __device__ __forceinline__ void load_task(const PrefillParams &p, int task,
-                                          Stage<GT> &st, int tid, int c0,
+                                          Stage<GT, CONV> &st, int tid, int c0,
                                           int r0) {
+  constexpr int XR = Stage<GT, CONV>::XR, XO = CONV ? 3 : 0;
   const int BH = p.B * p.H;
   const int bh = task % BH, n = p.NC - 1 - task / BH;
   const int b = bh / p.H, h = bh % p.H, T = p.T, H = p.H;
@@ -120,21 +132,44 @@ __device__ __forceinline__ void load_task(const PrefillParams &p, int task,
   for (int i = 0; i < 8; ++i) {
     const size_t t = (size_t)min(t0 + r0 + i, tlast);
     if (PART & 1) st.g[i] = GRaw<GT>::load((const GT *)p.g + kb + t * rowK);
-    if (PART & 2) st.q[i] = ld4_stream((const bf16 *)p.q + kb + t * rowK);
-    if (PART & 4) st.k[i] = ld4_stream((const bf16 *)p.k + kb + t * rowK);
+  }
+  const bf16 *xq = (const bf16 *)(CONV ? p.xq : p.q);
+  const bf16 *xk = (const bf16 *)(CONV ? p.xk : p.k);
+  const bf16 *xv = (const bf16 *)(CONV ? p.xv : p.v);
+#pragma unroll
+  for (int i = 0; i < XR; ++i) {
+    const size_t t = (size_t)min(max(t0 + r0 + i - XO, 0), tlast);
+    if (PART & 2) st.q[i] = ld4_stream(xq + kb + t * rowK);
+    if (PART & 4) st.k[i] = ld4_stream(xk + kb + t * rowK);
     if (PART & 8)
-      st.v[i] = ld4_stream((const bf16 *)p.v + (tok0 * H + h) * DV + c0 +
-                           t * (size_t)H * DV);
+      st.v[i] = ld4_stream(xv + (tok0 * H + h) * DV + c0 + t * (size_t)H * DV);
+  }
+  if constexpr (CONV) {
+    // tap set `tid`: q channel, DK + k channel, 2 DK + v channel, right-
+    // aligned (tap u multiplies the row u - 3 tokens back)
+    if ((PART & 8) && tid < 2 * DK + DV) {
+      const float *w = tid < DK ? p.wq + ((size_t)h * DK + tid) * p.cw
+                     : tid < 2 * DK ? p.wk + ((size_t)h * DK + tid - DK) * p.cw
+                                    : p.wv + ((size_t)h * DV + tid - 2 * DK) * p.cw;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int jj = u - (4 - p.cw);
+        st.tap[u] = jj >= 0 ? w[jj] : 0.f;
+      }
+    }
   }
 }
 
-template <typename GT>
+template <typename GT, bool CONV>
 __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
   using M = Mma<bf16>;
   typedef M::frag frag;
   typedef Vec4<bf16>::raw R4;
+  constexpr int XO = CONV ? 3 : 0;  // first own row inside the staged rows
 
-  __shared__ __attribute__((aligned(16))) char sm[LDS];
+  __shared__ __attribute__((aligned(16))) char sm[CONV ? LDS_CONV : LDS];
+  f32x4 *taps = (f32x4 *)(sm + oTap);  // conv only
+  float *nrm = (float *)(sm + oNrm), *l2p = (float *)(sm + oL2p);
   bf16 *Xkr = (bf16 *)(sm + oKR), *Xqr = (bf16 *)(sm + oQR);
   bf16 *Xks = (bf16 *)(sm + oKS), *Xkir = (bf16 *)(sm + oKIR);
   float *Taa = (float *)(sm + oTaa);
@@ -159,13 +194,15 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
   const int r0 = 16 * a + 8 * hh;
   constexpr bool GB = sizeof(GT) == 2;
 
-  Stage<GT> st;
+  Stage<GT, CONV> st;
   int task = blockIdx.x;
-  if (task < ntask) load_task<15, GT>(p, task, st, tid, c0, r0);
+  if (task < ntask) load_task<15, GT, CONV>(p, task, st, tid, c0, r0);
   auto put_beta = [&]() {
     if (wave == 0)
       betas[lane] = GB ? __uint_as_float(st.beta << 16)
                        : __uint_as_float(st.beta);
+    if constexpr (CONV)
+      if (tid < 2 * DK + DV) taps[tid] = st.tap;
   };
   if (task < ntask) put_beta();
   __syncthreads();
@@ -198,10 +235,67 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
         bt[i] = ok ? betas[r0 + i] : 0.f;
         e[i][0] = ok ? __expf(g0) : 1.f;
         e[i][1] = ok ? __expf(g1) : 1.f;
-        get2(st.k[i], kk[i][0], kk[i][1]);
-        get2(st.q[i], qq[i][0], qq[i][1]);
-        if (!ok) kk[i][0] = kk[i][1] = qq[i][0] = qq[i][1] = 0.f;
+        if constexpr (!CONV) {
+          get2(st.k[i], kk[i][0], kk[i][1]);
+          get2(st.q[i], qq[i][0], qq[i][1]);
+        }
       }
+      if constexpr (CONV) {
+        // causal conv over the staged rows (row i + u holds token
+        // t0 + r0 + i + u - 3; rows before the sequence contribute 0)
+        f32x4 tq[2], tk[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          tq[j] = taps[c0 + j];
+          tk[j] = taps[DK + c0 + j];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          qq[i][0] = qq[i][1] = kk[i][0] = kk[i][1] = 0.f;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int t = t0 + r0 + i + u - XO;
+            const bool okt = t >= 0 && t < T;
+            float x0, x1, y0, y1;
+            get2(st.q[i + u], x0, x1);
+            get2(st.k[i + u], y0, y1);
+            qq[i][0] += okt ? tq[0][u] * x0 : 0.f;
+            qq[i][1] += okt ? tq[1][u] * x1 : 0.f;
+            kk[i][0] += okt ? tk[0][u] * y0 : 0.f;
+            kk[i][1] += okt ? tk[1][u] * y1 : 0.f;
+          }
+        }
+        // L2 over the head's 128 channels per token: 64 of them in this
+        // wave's 32 lanes of the token half, 64 in the partner wave (w ^ 1)
+        float sq[8], sk[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          sq[i] = group_sum<32>(qq[i][0] * qq[i][0] + qq[i][1] * qq[i][1]);
+          sk[i] = group_sum<32>(kk[i][0] * kk[i][0] + kk[i][1] * kk[i][1]);
+        }
+        if ((lane & 31) == 0) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            *(float2 *)(l2p + ((wave * 16 + 8 * hh + i) * 2)) =
+                make_float2(sq[i], sk[i]);
+        }
+        __syncthreads();  // conv: partial sums of squares of both halves
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float2 o = *(const float2 *)(l2p + (((wave ^ 1) * 16 + 8 * hh + i) * 2));
+          const float iq = p.l2 ? 1.f / sqrtf(sq[i] + o.x + p.eps) : 1.f;
+          const float ik = p.l2 ? 1.f / sqrtf(sk[i] + o.y + p.eps) : 1.f;
+          qq[i][0] *= iq;
+          qq[i][1] *= iq;
+          kk[i][0] *= ik;
+          kk[i][1] *= ik;
+          if ((wave & 1) == 0 && (lane & 31) == 0)
+            *(float2 *)(nrm + 2 * (r0 + i)) = make_float2(iq, ik);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (!(t0 + r0 + i < T)) kk[i][0] = kk[i][1] = qq[i][0] = qq[i][1] = 0.f;
       // this half's 8-token product, then the other half's (lane ^ 32)
       float ltp[2];
 #pragma unroll
@@ -254,12 +348,31 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
       // (beta V)^T for U: value channels c0, c0 + 1 (beta is 0 past T)
       {
         float bv0[8], bv1[8];
+        if constexpr (CONV) {
+          const f32x4 tv0 = taps[2 * DK + c0], tv1 = taps[2 * DK + c0 + 1];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float v0, v1;
-          get2(st.v[i], v0, v1);
-          bv0[i] = bt[i] * v0;
-          bv1[i] = bt[i] * v1;
+          for (int i = 0; i < 8; ++i) {
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int t = t0 + r0 + i + u - XO;
+              const bool okt = t >= 0 && t < T;
+              float v0, v1;
+              get2(st.v[i + u], v0, v1);
+              a0 += okt ? tv0[u] * v0 : 0.f;
+              a1 += okt ? tv1[u] * v1 : 0.f;
+            }
+            bv0[i] = bt[i] * a0;
+            bv1[i] = bt[i] * a1;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            float v0, v1;
+            get2(st.v[i], v0, v1);
+            bv0[i] = bt[i] * v0;
+            bv1[i] = bt[i] * v1;
+          }
         }
         bf16 *row0 = XvT + c0 * LDC, *row1 = row0 + LDC;
         *(R4 *)(row0 + cm_off<C>(c0, r0)) = Vec4<bf16>::put(&bv0[0]);
@@ -276,7 +389,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
 
     // ---- E2: Qtil and Ktil^T units, gamma_C, (beta K Gam)^T, mid products -
     const bool more = task + (int)gridDim.x < ntask;
-    if (more) load_task<1, GT>(p, task + gridDim.x, st, tid, c0, r0);
+    if (more) load_task<1, GT, CONV>(p, task + gridDim.x, st, tid, c0, r0);
     int anyv = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) anyv |= votes[w];
@@ -319,7 +432,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
     }
     __syncthreads();  // B2
 
-    if (more) load_task<2, GT>(p, task + gridDim.x, st, tid, c0, r0);
+    if (more) load_task<2, GT, CONV>(p, task + gridDim.x, st, tid, c0, r0);
 
     if (fallback) {
       // exact diagonal-block sums: item (sub-chunk aa, column s, 16
@@ -343,11 +456,31 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
                                 : ((const float *)p.g)[gi];
             pr[c] *= (tr < T) ? __expf(gv) : 1.f;
           }
-          const size_t ob = ((tokb + min(ts, T - 1)) * H + h) * DK + ch;
-          const size_t orr = ((tokb + trc) * H + h) * DK + ch;
-          const float ks = ts < T ? (float)((const bf16 *)p.k)[ob] : 0.f;
-          const float kr = tr < T ? (float)((const bf16 *)p.k)[orr] : 0.f;
-          const float qr = tr < T ? (float)((const bf16 *)p.q)[orr] : 0.f;
+          float ks, kr, qr;
+          if constexpr (CONV) {
+            // the conv and L2 of the input rows, recomputed (exact path only)
+            auto cv = [&](const void *x, int item, int t) -> float {
+              const f32x4 tp = taps[item];
+              float acc = 0.f;
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                const int tt = t + u - 3;
+                if (tt >= 0 && tt < T)
+                  acc += tp[u] * (float)((const bf16 *)x)
+                                     [((tokb + tt) * H + h) * DK + ch];
+              }
+              return acc;
+            };
+            ks = ts < T ? cv(p.xk, DK + ch, ts) * nrm[2 * (ts - t0) + 1] : 0.f;
+            kr = tr < T ? cv(p.xk, DK + ch, tr) * nrm[2 * (tr - t0) + 1] : 0.f;
+            qr = tr < T ? cv(p.xq, ch, tr) * nrm[2 * (tr - t0)] : 0.f;
+          } else {
+            const size_t ob = ((tokb + min(ts, T - 1)) * H + h) * DK + ch;
+            const size_t orr = ((tokb + trc) * H + h) * DK + ch;
+            ks = ts < T ? (float)((const bf16 *)p.k)[ob] : 0.f;
+            kr = tr < T ? (float)((const bf16 *)p.k)[orr] : 0.f;
+            qr = tr < T ? (float)((const bf16 *)p.q)[orr] : 0.f;
+          }
           sa += kr * ks * pr[c];
           sp += qr * ks * pr[c];
         }
@@ -502,7 +635,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
       if (wave >= 4) ap_item(wave < 6 ? 0 : 5, (wave & 1) == 0, (wave & 1) == 1);
     }
     __syncthreads();  // B3: A complete; beta K rho no longer read
-    if (more) load_task<4, GT>(p, task + gridDim.x, st, tid, c0, r0);
+    if (more) load_task<4, GT, CONV>(p, task + gridDim.x, st, tid, c0, r0);
 
     // ---- T1: diagonal inverses (waves 0-3, as in kda_prep_impl.h) beside
     // part of the Qtil / Ktil^T unit stores (waves 4-7), which no later phase
@@ -588,7 +721,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
       }
     }
     __syncthreads();
-    if (more) load_task<8, GT>(p, task + gridDim.x, st, tid, c0, r0);
+    if (more) load_task<8, GT, CONV>(p, task + gridDim.x, st, tid, c0, r0);
 
     // ---- WU: -W (A-operand units) and U (accumulator tiles) ----------------
     // token tile rt reads T rows 16 rt .. 16 rt + 15 over token units
@@ -670,19 +803,27 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
 }  // namespace pc
 
 bool prep_d128_applies(const PrefillParams &p, int io_bf16) {
-  return io_bf16 && !p.gate_head && !p.use_conv && p.Dk == pc::DK &&
-         p.Dv == pc::DV && p.C == pc::C;
+  return io_bf16 && !p.gate_head && p.Dk == pc::DK && p.Dv == pc::DV &&
+         p.C == pc::C && (!p.use_conv || (p.cw >= 1 && p.cw <= 4));
+}
+
+template <typename GT>
+static void launch_d128(const PrefillParams &p, unsigned grid, hipStream_t s) {
+  if (p.use_conv)
+    hipLaunchKernelGGL((pc::kda_chunk_prep_d128<GT, true>), dim3(grid),
+                       dim3(pc::NT), 0, s, p);
+  else
+    hipLaunchKernelGGL((pc::kda_chunk_prep_d128<GT, false>), dim3(grid),
+                       dim3(pc::NT), 0, s, p);
 }
 
 hipError_t launch_prefill_prep_d128(const PrefillParams &p, hipStream_t s) {
   const long long ntask = (long long)p.B * p.H * p.NC;
   const unsigned grid = (unsigned)std::min<long long>(ntask, cu_count());
   if (p.gate_bf16)
-    hipLaunchKernelGGL(pc::kda_chunk_prep_d128<bf16>, dim3(grid), dim3(pc::NT),
-                       0, s, p);
+    launch_d128<bf16>(p, grid, s);
   else
-    hipLaunchKernelGGL(pc::kda_chunk_prep_d128<float>, dim3(grid),
-                       dim3(pc::NT), 0, s, p);
+    launch_d128<float>(p, grid, s);
   return hipGetLastError();
 }
 
