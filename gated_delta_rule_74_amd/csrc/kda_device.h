@@ -192,9 +192,9 @@ __host__ __device__ constexpr size_t ws_shared_bytes(int Dk, int C,
       (size_t)Dk * 4);
 }
 
-__host__ __device__ inline WsLayout ws_layout(int Dk, int Dv, int C,
-                                              int io_bytes) {
-  WsLayout L;
+__host__ __device__ constexpr WsLayout ws_layout(int Dk, int Dv, int C,
+                                                 int io_bytes) {
+  WsLayout L{};
   L.nb = C / 16;
   L.nkt = Dk / 16;
   L.nvt = Dv / 16;

@@ -183,11 +183,12 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
   float *betas = (float *)(sm + oBeta);
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave0 = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = wave0;
   const int g4 = lane >> 4, m16 = lane & 15;
   const int BH = p.B * p.H, T = p.T, H = p.H;
   const int ntask = BH * p.NC;
-  const WsLayout W = ws_layout(DK, DV, C, 2);
+  constexpr WsLayout W = ws_layout(DK, DV, C, 2);  // offsets as immediates
   // this thread's share of a task: sub-chunk a, token half hh, 2 channels
   const int a = wave >> 1, hh = lane >> 5;
   const int c0 = 64 * (wave & 1) + 2 * (lane & 31);
@@ -213,6 +214,10 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
     // live across the whole loop, past the 256 registers a lane may hold
     int lid = tid;
     asm volatile("" : "+v"(lid));
+    // the same for the wave index: values derived from it would otherwise
+    // be hoisted too and spill out of the scalar registers
+    int wave = wave0;
+    asm volatile("" : "+s"(wave));
     const int lane = lid & 63, g4 = lane >> 4, m16 = lane & 15;
     const int hh = lane >> 5;
     const int c0 = 64 * (wave & 1) + 2 * (lane & 31);

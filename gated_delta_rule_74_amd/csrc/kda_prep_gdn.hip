@@ -132,10 +132,12 @@ __global__ __launch_bounds__(NT, 2) void kda_chunk_prep_gdn(PrefillParams p) {
         *s_bg = s_e + 384, *s_F = s_e + 448;
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave0 = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = wave0;
   const int BH = p.B * p.H, T = p.T, Dv = p.Dv, nvt = Dv / 16;
   const int ntask = BH * p.NC;
-  const WsLayout W = ws_layout(DK, Dv, C, 2);
+  // the section offsets do not depend on d_v: immediates
+  constexpr WsLayout W = ws_layout(DK, 128, C, 2);
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
   // this thread's staging share: sub-chunk wave / 2, channels
   // 64 (wave % 2) + 2 (lane % 32), +1 of tokens 8 (lane / 32) .. +7
@@ -151,6 +153,10 @@ __global__ __launch_bounds__(NT, 2) void kda_chunk_prep_gdn(PrefillParams p) {
     // derived from them are not kept live across the loop
     int lid = tid;
     asm volatile("" : "+v"(lid));
+    // the same for the wave index: values derived from it would otherwise
+    // be hoisted too and spill out of the scalar registers
+    int wave = wave0;
+    asm volatile("" : "+s"(wave));
     const int lane = lid & 63, g4 = lane >> 4, m16 = lane & 15;
     const int c0 = 64 * (wave & 1) + 2 * (lane & 31);
     const int r0 = 16 * (wave >> 1) + 8 * (lane >> 5);
