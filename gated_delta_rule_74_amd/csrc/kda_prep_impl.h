@@ -24,6 +24,11 @@
 // least 2^-64; otherwise those blocks are summed directly with running
 // products (exact and slow; reached only by extreme forgetting).
 //
+// Which kernel runs: bf16 q/k/v at d_k = d_v = 128 with 64-token chunks is
+// served by kda_prep_d128.hip (per-channel gate, with or without the conv;
+// eight waves per task) or kda_prep_gdn.hip (one gate per token-head); this
+// generic kernel serves every other shape and dtype.
+//
 // Execution: a persistent grid (one workgroup of 256 threads per CU) walks
 // the (batch*head, chunk) tasks, last chunk first: the state pass reads the
 // chunks in order right afterwards, so its early chunks are the most
