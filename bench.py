@@ -100,6 +100,40 @@ def mfma_busy_for(key, sources):
     return d
 
 
+def state_loads_alone(ws, BH, NC, Dk, Dv, C):
+    """Time the probe that pulls the state pass's per-chunk factor bytes into
+    registers with nothing else to do (libkda_probe.so, built beside
+    libkda.so), scaled to the bytes the state pass itself loads: what its
+    loads cost on their own.  None if the probe library is absent or refuses
+    the shape."""
+    import ctypes
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "gated_delta_rule_74_amd", "libkda_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    fn = lib.kda_probe_state_reads
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t] + [ctypes.c_int] * 6 + \
+        [ctypes.POINTER(ctypes.c_double)] * 2
+    import torch
+    torch.cuda.synchronize()
+    us, pb = ctypes.c_double(), ctypes.c_double()
+    if fn(ws.data_ptr(), ws.numel(), BH, NC, Dk, Dv, C, 20, ctypes.byref(us),
+          ctypes.byref(pb)) != 0:
+        return None
+    # what one state-pass workgroup loads per chunk: its 1 KiB units of -W,
+    # Qtil and Ktil^T, the lower units of P, its slab's U tiles, gamma_C
+    nb, nku, ntu = C // 16, Dk // 32, (C // 16 + 1) // 2
+    units = 2 * nb * nku + (Dk // 16) * ntu + sum(rt // 2 + 1 for rt in range(nb))
+    sb = units * 1024 + nb * 64 * 4 * 2 + Dk * 4
+    return dict(probe_us=us.value, probe_bytes_per_wg_chunk=pb.value,
+                state_bytes_per_wg_chunk=sb,
+                loads_alone_us=us.value * sb / pb.value,
+                bytes_per_cu_per_us=pb.value * NC / us.value,
+                source="gated_delta_rule_74_amd/csrc/probe_read_rate.hip")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,6 +270,15 @@ def main():
                 "source": "profiles/mfma_busy.md"}
         log(f"prefill: {ms*1e3:.1f} us/step (prep {tp*1e3:.1f} us, state "
             f"{ts*1e3:.1f} us), {gbs:.0f} GB/s algorithmic")
+        rf = state_loads_alone(ws, B * H, (T + C - 1) // C, Dk, Dv, C)
+        if rf is not None:
+            rf["state_pass_over_loads_alone"] = (ts * 1e3) / rf["loads_alone_us"]
+            out["prefill"]["state_pass_loads_alone"] = rf
+            log(f"prefill: the state pass's loads alone take "
+                f"{rf['loads_alone_us']:.1f} us (probe {rf['probe_us']:.1f} "
+                f"us, {rf['bytes_per_cu_per_us']:.0f} B per workgroup per "
+                f"us); state pass / loads alone = "
+                f"{rf['state_pass_over_loads_alone']:.2f}")
         if not args.no_cpu:
             import oracle
             orc = oracle.get()

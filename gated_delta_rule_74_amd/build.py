@@ -16,6 +16,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
+# measurement only (bench.py): the state pass's load floor
+PROBE_SOURCES = ["probe_read_rate.hip"]
+PROBE_LIB = os.path.join(HERE, "libkda_probe.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 SOURCES = ["kda_api.hip", "kda_prep_f32.hip", "kda_prep_bf16_f32.hip",
@@ -45,12 +48,14 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     jobs = min(len(SOURCES), max(1, (os.cpu_count() or 2)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o",
-           tmp]
-    subprocess.run(cmd, check=True, capture_output=not verbose)
-    os.replace(tmp, LIB)
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    nlib = len(SOURCES)
+    for lib, parts in ((LIB, objs[:nlib]), (PROBE_LIB, objs[nlib:])):
+        tmp = lib + ".tmp"
+        cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *parts,
+               "-o", tmp]
+        subprocess.run(cmd, check=True, capture_output=not verbose)
+        os.replace(tmp, lib)
     return LIB
 
 
