@@ -326,14 +326,17 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
           *(uint32_t *)(Xkr + r * LDK + c0) = put2(xkr[i][0], xkr[i][1]);
           *(uint32_t *)(Xqr + r * LDK + c0) =
               put2(p.scale * qq[i][0] * pr0, p.scale * qq[i][1] * pr1);
-          *(uint32_t *)(Xkir + r * LDK + c0) =
-              put2(kk[i][0] * __builtin_amdgcn_rcpf(pr0),
-                   kk[i][1] * __builtin_amdgcn_rcpf(pr1));
         }
       }
-      // backward: sigma = exclusive suffix within the sub-chunk
+      // backward: sigma = exclusive suffix within the sub-chunk; k / rho,
+      // the diagonal blocks' column operand, as k sigma / F (rho sigma = F):
+      // one reciprocal per channel instead of one per token.  It is read
+      // only when every F of the task is at least 2^-64 (else the exact
+      // diagonal sums replace those blocks), so 1 / F stays finite there.
       {
         float sf0 = hh ? 1.f : ltp[0], sf1 = hh ? 1.f : ltp[1];
+        const float iF0 = __builtin_amdgcn_rcpf(F[0]);
+        const float iF1 = __builtin_amdgcn_rcpf(F[1]);
         float xc0[8], xc1[8];  // the same values by channel
 #pragma unroll
         for (int i = 7; i >= 0; --i) {
@@ -342,6 +345,8 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
           sf0 *= e[i][0];
           sf1 *= e[i][1];
           *(uint32_t *)(Xks + (r0 + i) * LDK + c0) = put2(xc0[i], xc1[i]);
+          *(uint32_t *)(Xkir + (r0 + i) * LDK + c0) =
+              put2(xc0[i] * iF0, xc1[i] * iF1);
         }
         bf16 *row0 = XksT + c0 * LDC, *row1 = row0 + LDC;
         *(R4 *)(row0 + cm_off<C>(c0, r0)) = Vec4<bf16>::put(&xc0[0]);
