@@ -390,16 +390,37 @@ __device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const TA *A, int lda,
   const int m = lane & 15, g = lane >> 4;
   for (int u = 0; u * KU < K; ++u) {
     typename M::frag fa, fb;
+    if constexpr (!AT && sizeof(TA) == 4) {
+      // fp32 rows of A: a lane's k values come in runs of 4 (k = 4g + e and,
+      // for 32-wide units, 16 + 4g + e), one 16-byte read each; K is a
+      // multiple of 16, so a run is wholly inside or outside it
 #pragma unroll
-    for (int e = 0; e < M::NE; ++e) {
-      const int k = KU * u + M::koff(g, e);
-      float av = 0.f, bv = 0.f;
-      if (k < K) {
-        av = to_f32(AT ? A[k * lda + m0 + m] : A[(m0 + m) * lda + k]);
-        bv = to_f32(BT ? B[(n0 + m) * ldb + k] : B[k * ldb + n0 + m]);
+      for (int h = 0; h < M::NE / 4; ++h) {
+        const int k = KU * u + 16 * h + 4 * g;
+        const f32x4 a4 = k < K ? *(const f32x4 *)(A + (m0 + m) * lda + k)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) M::set(fa, 4 * h + e, a4[e]);
       }
-      M::set(fa, e, av);
-      M::set(fb, e, bv);
+#pragma unroll
+      for (int e = 0; e < M::NE; ++e) {
+        const int k = KU * u + M::koff(g, e);
+        M::set(fb, e,
+               k < K ? to_f32(BT ? B[(n0 + m) * ldb + k] : B[k * ldb + n0 + m])
+                     : 0.f);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < M::NE; ++e) {
+        const int k = KU * u + M::koff(g, e);
+        float av = 0.f, bv = 0.f;
+        if (k < K) {
+          av = to_f32(AT ? A[k * lda + m0 + m] : A[(m0 + m) * lda + k]);
+          bv = to_f32(BT ? B[(n0 + m) * ldb + k] : B[k * ldb + n0 + m]);
+        }
+        M::set(fa, e, av);
+        M::set(fb, e, bv);
+      }
     }
     acc = M::mma(fa, fb, acc);
   }
@@ -423,10 +444,45 @@ __device__ __forceinline__ f32x4 tile_mma_rows(f32x4 acc, const IO *A, int lda,
   return acc;
 }
 
+// A as fp32 rows (k contiguous, 16-byte reads, rounded to the product's
+// operand type) and B given by the k-contiguous rows of B^T in the q/k/v
+// dtype (op(B) = B^T rows, whole fragment units per load)
+template <typename IO>
+__device__ __forceinline__ f32x4 tile_mma_f32a(f32x4 acc, const float *A,
+                                               int lda, const IO *Bt, int ldb,
+                                               int m0, int n0, int K,
+                                               int lane) {
+  using M = Mma<IO>;
+  constexpr int KU = 16 * M::TPU;
+  const int m = lane & 15, g = lane >> 4;
+  for (int u = 0; u * KU < K; ++u) {
+    typename M::frag fa;
+#pragma unroll
+    for (int h = 0; h < M::NE / 4; ++h) {
+      const int k = KU * u + 16 * h + 4 * g;
+      const f32x4 a4 = k < K ? *(const f32x4 *)(A + (m0 + m) * lda + k)
+                             : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) M::set(fa, 4 * h + e, a4[e]);
+    }
+    const bool full = KU * u + 16 < K || M::TPU == 1;
+    acc = M::mma(fa, M::load_k(Bt + (n0 + m) * ldb + KU * u, g, full), acc);
+  }
+  return acc;
+}
+
 // per-chunk intermediates: the second kernel writes
 // [Delta C x Dv | dQtil C x Dk | dKtil C x Dk | dW C x Dk | dgam Dk], the
 // third adds [Kd = K*Gam | dKd] (C x Dk each) for its own later phases;
 // fp32
+// dQtil, dKtil and dKd (C x Dk each) are kept tile by tile in the
+// accumulator layout: tile (rt, it) is 64 lanes x 4 floats, lane 16 g + n
+// holding rows 16 rt + 4 g .. + 3 of column 16 it + n, so the lane that
+// produces a tile and the lane that later consumes it move 16 bytes at once
+__host__ __device__ inline size_t bwd_tile_off(int rt, int it, int nkt,
+                                               int lane) {
+  return (((size_t)rt * nkt + it) * 64 + lane) * 4;
+}
 __host__ __device__ inline size_t bwd_gs_floats(int C, int Dk, int Dv) {
   return (size_t)C * (Dv + 5 * Dk) + Dk;
 }
@@ -608,11 +664,12 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
     const int tl = wave + 4 * j;
     if (tl < NTL) {
       const int rt = tl % NB, it = tl / NB;
+      const size_t ot = bwd_tile_off(rt, it, NKT, lane);
+      *(f32x4 *)(gQ + ot) = aQ[j];
+      *(f32x4 *)(gK + ot) = aK[j];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const size_t o = (size_t)(16 * rt + 4 * g4 + e) * DK + 16 * it + m16;
-        gQ[o] = aQ[j][e];
-        gK[o] = aK[j][e];
         gW[o] = -aW[j][e];
       }
     }
@@ -655,7 +712,11 @@ __device__ __forceinline__ void add_rows(float *dst, int r0, const float x[4],
 // ---------------------------------------------------------------------------
 template <typename IO, int DK, int C> struct G2L {
   static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
-  static constexpr size_t CC = (size_t)C * C * 4;
+  // C x C fp32 arrays with rows padded to C + 4: the 16 rows a lane group
+  // reads at once then fall in different banks, and rows stay 16-byte
+  // aligned for f32x4 accesses
+  static constexpr int LCC = C + 4;
+  static constexpr size_t CC = (size_t)C * LCC * 4;
   static constexpr size_t oM = 0, oT = CC, odP = 2 * CC, odM = 3 * CC;
   static constexpr size_t oSm = 4 * CC;  // small arrays
   static constexpr int RG = BWD_THREADS / DK;  // row groups of owner threads
@@ -667,8 +728,16 @@ template <typename IO, int DK, int C> struct G2L {
   // largest phase: k, q, sigma (q/k/v dtype) and e / rho (fp32); two C x Dv
   // arrays; or the C x C product of phase 5
   static constexpr size_t RK = (size_t)C * DK * (3 * sizeof(IO) + 4);
-  static constexpr size_t RV = 2 * (size_t)C * DVMAX_BWD * sizeof(IO);
-  static constexpr size_t RR = RK > RV ? (RK > CC ? RK : CC) : (RV > CC ? RV : CC);
+  // bf16: phases 3 and 4 also keep dDelta^T / dW^T (rows padded to C + 8)
+  // as the k-contiguous operand of T^T dDelta and T^T dW
+  static constexpr bool TRB = sizeof(IO) == 2;
+  static constexpr int LT = C + 8;
+  static constexpr size_t RV = 2 * (size_t)C * DVMAX_BWD * sizeof(IO) +
+                               (TRB ? (size_t)DVMAX_BWD * LT * 2 : 0);
+  static constexpr size_t RW =
+      TRB ? 2 * (size_t)C * DK * 2 + (size_t)DK * LT * 2 : 0;
+  static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
+  static constexpr size_t RR = mx(mx(RK, RV), mx(RW, CC));
   static constexpr size_t total = oR + RR;
 };
 template <typename IO, int DK, int C> struct BwdFits {
@@ -683,6 +752,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   using L = G2L<IO, DK, C>;
   constexpr int NB = C / 16, NKT = DK / 16;
   constexpr int RG = L::RG, RP = C / RG;  // owner rows per thread
+  constexpr int LCC = L::LCC;             // row stride of the C x C arrays
   static_assert(RG * DK == BWD_THREADS && RP * RG == C, "owner mapping");
   constexpr bool GB = sizeof(GT) == 2;
   const PrefillParams &p = bp.f;
@@ -713,6 +783,26 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   const size_t bb0 = (size_t)b * T * H + h;        // token 0, beta
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   const int oi = tid % DK, orh = tid / DK;  // owner: channel, row group
+  // a wave's output tiles (tl = wave, wave + 4, ...) in groups of four: the
+  // four products first, then their epilogues, so the operand reads and
+  // matrix-core steps of one tile overlap another's instead of every tile
+  // waiting out its own chain
+  auto tiles = [&](int ntile, auto prod, auto epi) {
+    constexpr int NBAT = 4;
+    for (int tb = wave; tb < ntile; tb += 4 * NBAT) {
+      f32x4 acc[NBAT];
+#pragma unroll
+      for (int b = 0; b < NBAT; ++b) {
+        const int tl = tb + 4 * b;
+        acc[b] = tl < ntile ? prod(tl) : zero;
+      }
+#pragma unroll
+      for (int b = 0; b < NBAT; ++b) {
+        const int tl = tb + 4 * b;
+        if (tl < ntile) epi(tl, acc[b]);
+      }
+    }
+  };
 
   auto gate_at = [&](int t, int i) -> float {
     const size_t gi = p.gate_head ? bb0 + (size_t)t * H
@@ -760,13 +850,21 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   };
 
   // ---- phase 1: beta, accumulators, M and T from the forward, Kd -----------
-  for (int x = tid; x < C; x += BWD_THREADS) {
-    const int t = t0 + x;
-    bet[x] = t < T ? (GB ? (float)((const bf16 *)p.beta)[bb0 + (size_t)t * H]
-                         : ((const float *)p.beta)[bb0 + (size_t)t * H])
-                   : 0.f;
-    dB[x] = 0.f;
-    dgh[x] = 0.f;
+  static_assert(C <= 64, "one wave holds the chunk's betas");
+  if (tid < 64) {
+    const int x = tid, t = t0 + x;
+    float bv = 0.f;
+    if (x < C) {
+      bv = t < T ? (GB ? (float)((const bf16 *)p.beta)[bb0 + (size_t)t * H]
+                       : ((const float *)p.beta)[bb0 + (size_t)t * H])
+                 : 0.f;
+      bet[x] = bv;
+      dB[x] = 0.f;
+      dgh[x] = 0.f;
+    }
+    // any row inside the sequence with beta = 0 (its M is rebuilt below)
+    const unsigned long long bz = __ballot(x < C && t < T && bv == 0.f);
+    if (x == 0) vote[1] = bz != 0ull;
   }
   for (int x = tid; x < DK; x += BWD_THREADS) dGl[x] = 0.f;
   IO *ks = (IO *)R;
@@ -778,6 +876,15 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
     // the lower triangles are meaningful)
     const float *at = p.train_at + ((size_t)bh * NC + n) * 2 * C * C;
     constexpr int N4 = (C * C / 4 + BWD_THREADS - 1) / BWD_THREADS;
+    // Kd = K*Gam needs each owner thread's prefix product of e over the rows
+    // before its own: every thread multiplies its own RP rows here, and the
+    // products of the earlier row groups are read back after a barrier
+    {
+      float lp = 1.f;
+#pragma unroll
+      for (int j = 0; j < RP; ++j) lp *= es[(orh * RP + j) * DK + oi];
+      tail[orh * DK + oi] = lp;
+    }
     f32x4 la[N4], lt[N4];
 #pragma unroll
     for (int j = 0; j < N4; ++j) {
@@ -789,18 +896,24 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
     for (int j = 0; j < N4; ++j) {
       const int x4 = 4 * (tid + BWD_THREADS * j);
       if (x4 < C * C) {
+        // four consecutive columns of one row (C is a multiple of 4)
+        const int r = x4 / C, c0 = x4 % C;
+        const float br = bet[r];
+        const float ib = br != 0.f ? 1.f / br : 0.f;
+        f32x4 mv, tv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int x = x4 + e, r = x / C, c = x % C;
-          const float br = bet[r];
-          Mm[x] = (c < r && br != 0.f) ? la[j][e] / br : 0.f;
-          TTm[x] = r <= c ? lt[j][e] : 0.f;  // T^T: upper triangle
+          const int c = c0 + e;
+          mv[e] = c < r ? la[j][e] * ib : 0.f;
+          tv[e] = r <= c ? lt[j][e] : 0.f;  // T^T: upper triangle
         }
+        *(f32x4 *)(Mm + r * LCC + c0) = mv;
+        *(f32x4 *)(TTm + r * LCC + c0) = tv;
       }
     }
     // rows with beta = 0 (A carries no M there): M directly, with running
     // products of e over (s, r] -- exact, and rare
-    for (int r = 1; r < C; ++r) {
+    for (int r = 1; r < C && vote[1]; ++r) {
       if (bet[r] != 0.f || t0 + r >= T) continue;
       for (int s2 = tid; s2 < r; s2 += BWD_THREADS) {
         float m = 0.f;
@@ -809,12 +922,18 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
           for (int u = s2 + 1; u <= r; ++u) D *= es[u * DK + i];
           m += to_f32(ks[r * DK + i]) * to_f32(ks[s2 * DK + i]) * D;
         }
-        Mm[r * C + s2] = m;
+        Mm[r * LCC + s2] = m;
       }
     }
+  }
+  __syncthreads();
+  {
     // Kd = K*Gam for the later phases (owner threads: prefix products)
     float G = 1.f;
-    for (int r = 0; r < orh * RP; ++r) G *= es[r * DK + oi];
+#pragma unroll
+    for (int rg = 0; rg < RG - 1; ++rg)
+      if (rg < orh) G *= tail[rg * DK + oi];
+#pragma unroll
     for (int j = 0; j < RP; ++j) {
       const int r = orh * RP + j;
       G *= es[r * DK + oi];
@@ -826,133 +945,245 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   // ---- phase 3: value side: dT = dDelta (beta V)^T, dv = beta T^T dDelta --
   {
     IO *dDs = (IO *)R, *vS = dDs + C * Dv;
+    IO *dDT = vS + C * Dv;  // bf16 only: dDelta^T [Dv][LT]
     constexpr int N8 = (C * DVMAX_BWD / 8 + BWD_THREADS - 1) / BWD_THREADS;
     Row8<IO> lv[N8];
-    Row8<float> ld[N8];
 #pragma unroll
     for (int jj = 0; jj < N8; ++jj) {
       const int x = min(8 * (tid + BWD_THREADS * jj), C * Dv - 8);
       const int r = x / Dv, j = x % Dv, t = min(t0 + r, T - 1);
       lv[jj].load((const IO *)p.v + vb + (size_t)t * vrow + j);
-      ld[jj].load(bp.dD + vb + (size_t)t * vrow + j);
+    }
+    if constexpr (L::TRB) {
+      // dDelta by columns: thread = (column j, 8 consecutive rows), so it
+      // writes the rows of dDelta element by element and the row of
+      // dDelta^T as one 16-byte store; lanes take consecutive columns
+      float dd[N8][8];
+#pragma unroll
+      for (int jj = 0; jj < N8; ++jj) {
+        const int q = min(tid + BWD_THREADS * jj, C * Dv / 8 - 1);
+        const int j = q % Dv, r0 = 8 * (q / Dv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          dd[jj][e] = bp.dD[vb + (size_t)min(t0 + r0 + e, T - 1) * vrow + j];
+      }
+#pragma unroll
+      for (int jj = 0; jj < N8; ++jj) {
+        const int q = tid + BWD_THREADS * jj;
+        if (q < C * Dv / 8) {
+          const int j = q % Dv, r0 = 8 * (q / Dv);
+          float d8[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            d8[e] = t0 + r0 + e < T ? dd[jj][e] : 0.f;
+            dDs[(r0 + e) * Dv + j] = (IO)d8[e];
+          }
+          put8(dDT + j * L::LT + r0, d8);
+        }
+      }
+    } else {
+      Row8<float> ld[N8];
+#pragma unroll
+      for (int jj = 0; jj < N8; ++jj) {
+        const int x = min(8 * (tid + BWD_THREADS * jj), C * Dv - 8);
+        const int r = x / Dv, j = x % Dv, t = min(t0 + r, T - 1);
+        ld[jj].load(bp.dD + vb + (size_t)t * vrow + j);
+      }
+#pragma unroll
+      for (int jj = 0; jj < N8; ++jj) {
+        const int x = 8 * (tid + BWD_THREADS * jj);
+        if (x < C * Dv) {
+          float d8[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            d8[e] = t0 + x / Dv < T ? ld[jj].get(e) : 0.f;
+          put8(dDs + x, d8);
+        }
+      }
     }
 #pragma unroll
     for (int jj = 0; jj < N8; ++jj) {
       const int x = 8 * (tid + BWD_THREADS * jj);
       if (x < C * Dv) {
-        if (t0 + x / Dv >= T) {
-          lv[jj].zero();
-          ld[jj].zero();
-        }
-        float d8[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d8[e] = ld[jj].get(e);
-        put8(dDs + x, d8);
+        if (t0 + x / Dv >= T) lv[jj].zero();
         lv[jj].store(vS + x);
       }
     }
     __syncthreads();
-    for (int tl = wave; tl < NB * NB; tl += 4) {
-      const int rt = tl % NB, st = tl / NB;
-      f32x4 acc = tile_mma_rows<IO>(zero, dDs, Dv, vS, Dv, 16 * rt, 16 * st,
-                                    Dv, lane);
-      const float bs = bet[16 * st + m16];  // (beta V)^T: beta of column s
+    tiles(
+        NB * NB,
+        [&](int tl) {
+          return tile_mma_rows<IO>(zero, dDs, Dv, vS, Dv, 16 * (tl % NB),
+                                   16 * (tl / NB), Dv, lane);
+        },
+        [&](int tl, f32x4 acc) {
+          const int rt = tl % NB, st = tl / NB;
+          const float bs = bet[16 * st + m16];  // (beta V)^T: beta of column s
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        dMm[(16 * rt + 4 * g4 + e) * C + 16 * st + m16] = bs * acc[e];  // dT
-    }
-    for (int tl = wave; tl < NB * nvt; tl += 4) {
-      const int rt = tl % NB, ct = tl / NB;
-      f32x4 acc = tile_mma<IO, false, false>(zero, TTm, C, dDs, Dv, 16 * rt,
-                                            16 * ct, C, lane);
-      float x[4];
+          for (int e = 0; e < 4; ++e)  // dT
+            dMm[(16 * rt + 4 * g4 + e) * LCC + 16 * st + m16] = bs * acc[e];
+        });
+    tiles(
+        NB * nvt,
+        [&](int tl) {
+          const int rt = tl % NB, ct = tl / NB;
+          if constexpr (L::TRB)
+            return tile_mma_f32a<IO>(zero, TTm, LCC, dDT, L::LT, 16 * rt,
+                                     16 * ct, C, lane);
+          else
+            return tile_mma<IO, false, false>(zero, TTm, LCC, dDs, Dv, 16 * rt,
+                                              16 * ct, C, lane);
+        },
+        [&](int tl, f32x4 acc) {
+          const int rt = tl % NB, ct = tl / NB;
+          float x[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rt + 4 * g4 + e, j = 16 * ct + m16, t = t0 + r;
-        if (t < T)
-          ((IO *)bp.dv)[vb + (size_t)t * vrow + j] = from_f32<IO>(bet[r] * acc[e]);
-        x[e] = to_f32(vS[r * Dv + j]) * acc[e];
-      }
-      add_rows(dB, 16 * rt + 4 * g4, x, m16);
-    }
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * rt + 4 * g4 + e, j = 16 * ct + m16, t = t0 + r;
+            if (t < T)
+              ((IO *)bp.dv)[vb + (size_t)t * vrow + j] =
+                  from_f32<IO>(bet[r] * acc[e]);
+            x[e] = to_f32(vS[r * Dv + j]) * acc[e];
+          }
+          add_rows(dB, 16 * rt + 4 * g4, x, m16);
+        });
     __syncthreads();
   }
 
   // ---- phase 4: key side: dT += dW (beta Kd)^T, dKd = beta T^T dW ---------
   {
     IO *dWs = (IO *)R, *KdS = dWs + C * DK;
+    IO *dWT = KdS + C * DK;  // bf16 only: dW^T [DK][LT]
     constexpr int N8 = (C * DK / 8 + BWD_THREADS - 1) / BWD_THREADS;
-    Row8<float> lw[N8], lk[N8];
+    Row8<float> lk[N8];
 #pragma unroll
     for (int j = 0; j < N8; ++j) {
       const int x = min(8 * (tid + BWD_THREADS * j), C * DK - 8);
-      lw[j].load(gW + x);
       lk[j].load(gKd + x);
+    }
+    if constexpr (L::TRB) {
+      // dW by columns, as dDelta in phase 3
+      float dw[N8][8];
+#pragma unroll
+      for (int jj = 0; jj < N8; ++jj) {
+        const int q = min(tid + BWD_THREADS * jj, C * DK / 8 - 1);
+        const int i = q % DK, r0 = 8 * (q / DK);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dw[jj][e] = gW[(r0 + e) * DK + i];
+      }
+#pragma unroll
+      for (int jj = 0; jj < N8; ++jj) {
+        const int q = tid + BWD_THREADS * jj;
+        if (q < C * DK / 8) {
+          const int i = q % DK, r0 = 8 * (q / DK);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dWs[(r0 + e) * DK + i] = (IO)dw[jj][e];
+          put8(dWT + i * L::LT + r0, dw[jj]);
+        }
+      }
+    } else {
+      Row8<float> lw[N8];
+#pragma unroll
+      for (int j = 0; j < N8; ++j) {
+        const int x = min(8 * (tid + BWD_THREADS * j), C * DK - 8);
+        lw[j].load(gW + x);
+      }
+#pragma unroll
+      for (int j = 0; j < N8; ++j) {
+        const int x = 8 * (tid + BWD_THREADS * j);
+        if (x < C * DK) {
+          float w8[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) w8[e] = lw[j].get(e);
+          put8(dWs + x, w8);
+        }
+      }
     }
 #pragma unroll
     for (int j = 0; j < N8; ++j) {
       const int x = 8 * (tid + BWD_THREADS * j);
       if (x < C * DK) {
-        float w8[8], k8[8];
+        float k8[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          w8[e] = lw[j].get(e);
-          k8[e] = lk[j].get(e);
-        }
-        put8(dWs + x, w8);
+        for (int e = 0; e < 8; ++e) k8[e] = lk[j].get(e);
         put8(KdS + x, k8);
       }
     }
     __syncthreads();
-    for (int tl = wave; tl < NB * NB; tl += 4) {
-      const int rt = tl % NB, st = tl / NB;
-      f32x4 acc = tile_mma_rows<IO>(zero, dWs, DK, KdS, DK, 16 * rt, 16 * st,
-                                    DK, lane);
-      const float bs = bet[16 * st + m16];  // (beta Kd)^T: beta of column s
+    tiles(
+        NB * NB,
+        [&](int tl) {
+          return tile_mma_rows<IO>(zero, dWs, DK, KdS, DK, 16 * (tl % NB),
+                                   16 * (tl / NB), DK, lane);
+        },
+        [&](int tl, f32x4 acc) {
+          const int rt = tl % NB, st = tl / NB;
+          const float bs = bet[16 * st + m16];  // (beta Kd)^T: beta of column s
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        dMm[(16 * rt + 4 * g4 + e) * C + 16 * st + m16] += bs * acc[e];
-    }
-    for (int tl = wave; tl < NB * NKT; tl += 4) {
-      const int rt = tl % NB, it = tl / NB;
-      f32x4 acc = tile_mma<IO, false, false>(zero, TTm, C, dWs, DK, 16 * rt,
-                                            16 * it, C, lane);
-      float x[4];
+          for (int e = 0; e < 4; ++e)
+            dMm[(16 * rt + 4 * g4 + e) * LCC + 16 * st + m16] += bs * acc[e];
+        });
+    tiles(
+        NB * NKT,
+        [&](int tl) {
+          const int rt = tl % NB, it = tl / NB;
+          if constexpr (L::TRB)
+            return tile_mma_f32a<IO>(zero, TTm, LCC, dWT, L::LT, 16 * rt,
+                                     16 * it, C, lane);
+          else
+            return tile_mma<IO, false, false>(zero, TTm, LCC, dWs, DK, 16 * rt,
+                                              16 * it, C, lane);
+        },
+        [&](int tl, f32x4 acc) {
+          const int rt = tl % NB, it = tl / NB;
+          float x[4];
+          f32x4 dk4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rt + 4 * g4 + e, i = 16 * it + m16;
-        gdKd[(size_t)r * DK + i] = bet[r] * acc[e];
-        x[e] = to_f32(KdS[r * DK + i]) * acc[e];
-      }
-      add_rows(dB, 16 * rt + 4 * g4, x, m16);
-    }
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * rt + 4 * g4 + e, i = 16 * it + m16;
+            dk4[e] = bet[r] * acc[e];
+            x[e] = to_f32(KdS[r * DK + i]) * acc[e];
+          }
+          *(f32x4 *)(gdKd + bwd_tile_off(rt, it, NKT, lane)) = dk4;
+          add_rows(dB, 16 * rt + 4 * g4, x, m16);
+        });
     __syncthreads();
   }
 
   // ---- phase 5: dA = -T^T dT T^T (strictly lower); dM = beta dA ------------
-  for (int tl = wave; tl < NB * NB; tl += 4) {
-    const int rt = tl % NB, st = tl / NB;
-    f32x4 acc = tile_mma<float, false, false>(zero, dMm, C, TTm, C, 16 * rt,
-                                             16 * st, C, lane);
+  tiles(
+      NB * NB,
+      [&](int tl) {
+        return tile_mma<float, false, false>(zero, dMm, LCC, TTm, LCC,
+                                             16 * (tl % NB), 16 * (tl / NB), C,
+                                             lane);
+      },
+      [&](int tl, f32x4 acc) {
+        const int rt = tl % NB, st = tl / NB;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      Xm[(16 * rt + 4 * g4 + e) * C + 16 * st + m16] = acc[e];
-  }
+        for (int e = 0; e < 4; ++e)
+          Xm[(16 * rt + 4 * g4 + e) * LCC + 16 * st + m16] = acc[e];
+      });
   __syncthreads();
-  for (int tl = wave; tl < NB * NB; tl += 4) {
-    const int rt = tl % NB, st = tl / NB;
-    f32x4 acc = tile_mma<float, false, false>(zero, TTm, C, Xm, C, 16 * rt,
-                                             16 * st, C, lane);
-    float x[4];
+  tiles(
+      NB * NB,
+      [&](int tl) {
+        return tile_mma<float, false, false>(zero, TTm, LCC, Xm, LCC,
+                                             16 * (tl % NB), 16 * (tl / NB), C,
+                                             lane);
+      },
+      [&](int tl, f32x4 acc) {
+        const int rt = tl % NB, st = tl / NB;
+        float x[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * rt + 4 * g4 + e, s = 16 * st + m16;
-      const float dA = s < r ? -acc[e] : 0.f;
-      x[e] = dA * Mm[r * C + s];
-      dMm[r * C + s] = bet[r] * dA;  // read only after the next barrier
-    }
-    add_rows(dB, 16 * rt + 4 * g4, x, m16);
-  }
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rt + 4 * g4 + e, s = 16 * st + m16;
+          const float dA = s < r ? -acc[e] : 0.f;
+          x[e] = dA * Mm[r * LCC + s];
+          dMm[r * LCC + s] = bet[r] * dA;  // read only after the next barrier
+        }
+        add_rows(dB, 16 * rt + 4 * g4, x, m16);
+      });
   __syncthreads();
 
   // ---- phase 6: dPm = scale tril(dO Delta^T) --------------------------------
@@ -981,16 +1212,20 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
       }
     }
     __syncthreads();
-    for (int tl = wave; tl < NB * NB; tl += 4) {
-      const int rt = tl % NB, st = tl / NB;
-      f32x4 acc = tile_mma_rows<IO>(zero, Os, Dv, Ds, Dv, 16 * rt, 16 * st,
-                                    Dv, lane);
+    tiles(
+        NB * NB,
+        [&](int tl) {
+          return tile_mma_rows<IO>(zero, Os, Dv, Ds, Dv, 16 * (tl % NB),
+                                   16 * (tl / NB), Dv, lane);
+        },
+        [&](int tl, f32x4 acc) {
+          const int rt = tl % NB, st = tl / NB;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rt + 4 * g4 + e, s = 16 * st + m16;
-        dPm[r * C + s] = s <= r ? scale * acc[e] : 0.f;
-      }
-    }
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * rt + 4 * g4 + e, s = 16 * st + m16;
+            dPm[r * LCC + s] = s <= r ? scale * acc[e] : 0.f;
+          }
+        });
     __syncthreads();
   }
 
@@ -1040,7 +1275,10 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
   // and keeps dk, dq, dG of those (r, i) in registers.  D_rs = rho_r Mid_ba
   // sigma_s for s in sub-chunk b < a (r in a), rho_r / rho_s inside one.
   constexpr int JT = (NKT + 3) / 4;
-  f32x4 aK_[JT][NB], aQ_[JT][NB], aG_[JT][NB];
+  // dG of the lane's (r, i) stays in registers for the reverse sum after
+  // the barrier; dk and dq are final at the end of a channel tile and go
+  // out straight from registers
+  f32x4 aG_[JT][NB];
   {
     using MM = Mma<IO>;
     typedef typename MM::frag frag;
@@ -1061,13 +1299,13 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
             D *= tu < T ? __expf(gate_at(tu, i)) : 1.f;
           }
           if (!(strict && s2 == r))
-            acc += cm[r * C + s2] * to_f32(xv[s2 * DK + i]) * D;
+            acc += cm[r * LCC + s2] * to_f32(xv[s2 * DK + i]) * D;
         }
       } else {    // sum_{r2>=r in the sub-chunk} c[r2][r] x_r2 prod_{r<u<=r2} e_u
         for (int r2 = r; r2 <= hi; ++r2) {
           if (r2 > r) D *= t0 + r2 < T ? __expf(gate_at(t0 + r2, i)) : 1.f;
           if (!(strict && r2 == r))
-            acc += cm[r2 * C + r] * to_f32(xv[r2 * DK + i]) * D;
+            acc += cm[r2 * LCC + r] * to_f32(xv[r2 * DK + i]) * D;
         }
       }
       return acc;
@@ -1077,11 +1315,22 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
       const int it = wave + 4 * jt;
       if (it >= NKT) continue;
       const int ib = 16 * it + m16;  // B-operand / output column (channel)
+      f32x4 aK_[NB], aQ_[NB];
       // ---- elementwise terms of Kd = K*Gam, Qtil, Ktil = K*gam/Gam, gam
       float Fb[NB];
 #pragma unroll
       for (int a = 0; a < NB; ++a) Fb[a] = Fs[a * DK + ib];
       float kil = 0.f;
+      // this lane's dKd, dQtil, dKtil of every sub-chunk: 16-byte loads
+      // issued together, before any of them is used
+      f32x4 vdkd[NB], vdq[NB], vdk[NB];
+#pragma unroll
+      for (int a = 0; a < NB; ++a) {
+        const size_t ot = bwd_tile_off(a, it, NKT, lane);
+        vdkd[a] = *(const f32x4 *)(gdKd + ot);
+        vdq[a] = *(const f32x4 *)(gQ + ot);
+        vdk[a] = *(const f32x4 *)(gK + ot);
+      }
 #pragma unroll
       for (int a = 0; a < NB; ++a) {
         float pre = 1.f, post = 1.f;
@@ -1093,13 +1342,12 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * a + 4 * g4 + e;
-          const size_t o = (size_t)r * DK + ib;
           const float G = rho[r * DK + ib] * pre;              // Gam_r
           const float sf = to_f32(sg[r * DK + ib]) * post;      // gam / Gam_r
           const float kr = to_f32(ks[r * DK + ib]), qr = to_f32(qs[r * DK + ib]);
-          const float dkd = gdKd[o], dqd = gQ[o], dki = gK[o];
-          aK_[jt][a][e] = dkd * G + dki * sf;
-          aQ_[jt][a][e] = scale * dqd * G;
+          const float dkd = vdkd[a][e], dqd = vdq[a][e], dki = vdk[a][e];
+          aK_[a][e] = dkd * G + dki * sf;
+          aQ_[a][e] = scale * dqd * G;
           float dg = dkd * kr * G + dqd * scale * qr * G - dki * kr * sf;
           if (r == C - 1) dg += gG[ib] * G;  // dgam * gam (G = gam here)
           aG_[jt][a][e] = dg;
@@ -1129,7 +1377,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
           for (int e = 0; e < 4; ++e) {
             const int sb = 16 * b + 4 * g4 + e;
             ksg[b][e] = kx[b][e] * to_f32(sg[sb * DK + ib]);
-            kir[b][e] = kx[b][e] / xr[b][e];
+            kir[b][e] = kx[b][e] * __builtin_amdgcn_rcpf(xr[b][e]);
           }
 #pragma unroll
         for (int a = 0; a < NB; ++a) {
@@ -1138,9 +1386,9 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
           for (int b = 0; b <= a; ++b) {
             if (b == a && !dok) continue;
             // lane (g4, m16): row 16a + m16, k = 16 b + 4 g4 + e (e < 4)
-            const f32x4 mk = *(const f32x4 *)(dMm + (16 * a + m16) * C + 16 * b +
+            const f32x4 mk = *(const f32x4 *)(dMm + (16 * a + m16) * LCC + 16 * b +
                                               4 * g4);
-            const f32x4 mq = *(const f32x4 *)(dPm + (16 * a + m16) * C + 16 * b +
+            const f32x4 mq = *(const f32x4 *)(dPm + (16 * a + m16) * LCC + 16 * b +
                                               4 * g4);
             const float md = mid(a, b, ib);
             frag fk, fq, fb;
@@ -1164,8 +1412,8 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
               rK += diag_exact(r, ib, true, ks, dMm, true);
               rQ += diag_exact(r, ib, true, ks, dPm, false);
             }
-            aK_[jt][a][e] += rK;
-            aQ_[jt][a][e] += rQ;
+            aK_[a][e] += rK;
+            aQ_[a][e] += rQ;
             aG_[jt][a][e] += kx[a][e] * rK + to_f32(qs[r * DK + ib]) * rQ;
           }
         }
@@ -1195,8 +1443,8 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
               const bool lo = e < 4;
               // dM^T: row 16 b + m16, k = 16 a + 4 g4 + e
               const int ra = 16 * a + 4 * g4 + (e & 3), sb = 16 * b + m16;
-              MM::set(fk, e, lo ? dMm[ra * C + sb] : 0.f);
-              MM::set(fq, e, lo ? dPm[ra * C + sb] : 0.f);
+              MM::set(fk, e, lo ? dMm[ra * LCC + sb] : 0.f);
+              MM::set(fq, e, lo ? dPm[ra * LCC + sb] : 0.f);
               MM::set(bk, e, lo ? kr4[a][e & 3] * md : 0.f);
               MM::set(bq, e, lo ? qr4[a][e & 3] * md : 0.f);
             }
@@ -1214,22 +1462,35 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
             const float sgv = to_f32(sg[s2 * DK + ib]);
             float cK = sgv * ok_[e], cQ = sgv * oq[e];
             if (dok) {
-              const float ir = 1.f / xr[b][e];
+              const float ir = __builtin_amdgcn_rcpf(xr[b][e]);
               cK += dk2[e] * ir;
               cQ += dq2[e] * ir;
             } else {
               cK += diag_exact(s2, ib, false, ks, dMm, true);
               cQ += diag_exact(s2, ib, false, qs, dPm, false);
             }
-            aK_[jt][b][e] += cK + cQ;
+            aK_[b][e] += cK + cQ;
             aG_[jt][b][e] -= kx[b][e] * (cK + cQ);
           }
         }
       }
+      // dq and dk of rows 16 a + 4 g4 + e at channel ib (16 lanes write 16
+      // consecutive channels of a row)
+#pragma unroll
+      for (int a = 0; a < NB; ++a)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * a + 4 * g4 + e;
+          if (t0 + r < T) {
+            const size_t o = kb + (size_t)(t0 + r) * krow + ib;
+            ((IO *)bp.dq)[o] = from_f32<IO>(aQ_[a][e]);
+            ((IO *)bp.dk)[o] = from_f32<IO>(aK_[a][e]);
+          }
+        }
     }
   }
   __syncthreads();  // dGl complete; rho no longer read
-  // ---- phase 8: dk, dq out; dg = reverse cumulative sum of dG ------------
+  // ---- phase 8: dg = reverse cumulative sum of dG ---------------------------
   float *dGs = es;  // [C][DK] fp32, in place of rho
 #pragma unroll
   for (int jt = 0; jt < JT; ++jt) {
@@ -1244,27 +1505,11 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
         float dgv = aG_[jt][a][e];
         if (r == C - 1) dgv += dGl[ib];  // sum_r dKtil*Ktil (d log gam)
         dGs[r * DK + ib] = dgv;
-        // dq, dk staged as [C][DK] rows where k and q were (read no more)
-        ks[r * DK + ib] = from_f32<IO>(aQ_[jt][a][e]);
-        qs[r * DK + ib] = from_f32<IO>(aK_[jt][a][e]);
         (void)t;
       }
   }
   __syncthreads();
-  // rows of dq and dk out, 8 channels per lane
   constexpr int NO8 = (C * DK / 8 + BWD_THREADS - 1) / BWD_THREADS;
-#pragma unroll
-  for (int j = 0; j < NO8; ++j) {
-    const int x = 8 * (tid + BWD_THREADS * j), r = x / DK, i = x % DK;
-    if (x < C * DK && t0 + r < T) {
-      const size_t o = kb + (size_t)(t0 + r) * krow + i;
-      Row8<IO> a8, b8;
-      a8.load(ks + x);
-      b8.load(qs + x);
-      a8.store((IO *)bp.dq + o);
-      b8.store((IO *)bp.dk + o);
-    }
-  }
   {
     const int i = oi, R0 = orh * RP;
     float own = 0.f;
