@@ -323,9 +323,11 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_state(BwdParams bp) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = t0 + 16 * rt + 4 * g4 + e;
+        // stored in the q/k/v dtype: every reader rounds it to that type
+        // as an operand anyway, so the results are the same bit for bit
         if (t < T)
-          bp.dD[((size_t)b * T + t) * orow + (size_t)h * Dv + 16 * vt + m16] =
-              acc[e];
+          ((IO *)bp.dD)[((size_t)b * T + t) * orow + (size_t)h * Dv + 16 * vt +
+                        m16] = from_f32<IO>(acc[e]);
       }
       frag *dst = DU + (rt / TPU) * 64 + lane;
       if (TPU == 2) {
@@ -474,7 +476,8 @@ __device__ __forceinline__ f32x4 tile_mma_f32a(f32x4 acc, const float *A,
 // per-chunk intermediates: the second kernel writes
 // [Delta C x Dv | dQtil C x Dk | dKtil C x Dk | dW C x Dk | dgam Dk], the
 // third adds [Kd = K*Gam | dKd] (C x Dk each) for its own later phases;
-// fp32
+// fp32 slots, Delta and dW stored in the q/k/v dtype (their readers only
+// use them as operands of that type)
 // dQtil, dKtil and dKd (C x Dk each) are kept tile by tile in the
 // accumulator layout: tile (rt, it) is 64 lanes x 4 floats, lane 16 g + n
 // holding rows 16 rt + 4 g .. + 3 of column 16 it + n, so the lane that
@@ -560,8 +563,8 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
     // all loads first (clamped addresses, branch-free), then the LDS
     // stores; 8 columns of a row per lane (sv is a multiple of 16)
     constexpr int NO8 = (C * SV / 8 + BWD_THREADS - 1) / BWD_THREADS;
-    Row8<float> la[NGA], lb[NGA], ld[NO8];
-    Row8<IO> lo[NO8];
+    Row8<float> la[NGA], lb[NGA];
+    Row8<IO> lo[NO8], ld[NO8];
 #pragma unroll
     for (int j = 0; j < NGA; ++j) {
       const int i = min(8 * (tid + BWD_THREADS * j), DK * SV - 8);
@@ -575,7 +578,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
       const int r = i / SV, c = min(i % SV, sv - 8), t = min(t0 + r, T - 1);
       const size_t gi = ((size_t)b * T + t) * orow + (size_t)h * Dv + c0 + c;
       lo[j].load((const IO *)bp.dO + gi);
-      ld[j].load(bp.dD + gi);
+      ld[j].load((const IO *)bp.dD + gi);
     }
 #pragma unroll
     for (int j = 0; j < NGA; ++j) {
@@ -628,7 +631,8 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
         const int r = 16 * rt + 4 * g4 + e;
         Ds[r * LS + 16 * ct + m16] = (IO)acc[e];
         if (16 * ct < sv)
-          gs[(size_t)r * Dv + c0 + 16 * ct + m16] = t0 + r < T ? acc[e] : 0.f;
+          ((IO *)gs)[(size_t)r * Dv + c0 + 16 * ct + m16] =
+              from_f32<IO>(t0 + r < T ? acc[e] : 0.f);
       }
     }
     __syncthreads();
@@ -670,7 +674,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const size_t o = (size_t)(16 * rt + 4 * g4 + e) * DK + 16 * it + m16;
-        gW[o] = -aW[j][e];
+        ((IO *)gW)[o] = from_f32<IO>(-aW[j][e]);
       }
     }
   }
@@ -965,7 +969,8 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
         const int j = q % Dv, r0 = 8 * (q / Dv);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          dd[jj][e] = bp.dD[vb + (size_t)min(t0 + r0 + e, T - 1) * vrow + j];
+          dd[jj][e] = to_f32(
+              ((const IO *)bp.dD)[vb + (size_t)min(t0 + r0 + e, T - 1) * vrow + j]);
       }
 #pragma unroll
       for (int jj = 0; jj < N8; ++jj) {
@@ -982,12 +987,12 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
         }
       }
     } else {
-      Row8<float> ld[N8];
+      Row8<IO> ld[N8];
 #pragma unroll
       for (int jj = 0; jj < N8; ++jj) {
         const int x = min(8 * (tid + BWD_THREADS * jj), C * Dv - 8);
         const int r = x / Dv, j = x % Dv, t = min(t0 + r, T - 1);
-        ld[jj].load(bp.dD + vb + (size_t)t * vrow + j);
+        ld[jj].load((const IO *)bp.dD + vb + (size_t)t * vrow + j);
       }
 #pragma unroll
       for (int jj = 0; jj < N8; ++jj) {
@@ -1069,7 +1074,8 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
         const int q = min(tid + BWD_THREADS * jj, C * DK / 8 - 1);
         const int i = q % DK, r0 = 8 * (q / DK);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dw[jj][e] = gW[(r0 + e) * DK + i];
+        for (int e = 0; e < 8; ++e)
+          dw[jj][e] = to_f32(((const IO *)gW)[(r0 + e) * DK + i]);
       }
 #pragma unroll
       for (int jj = 0; jj < N8; ++jj) {
@@ -1082,11 +1088,11 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
         }
       }
     } else {
-      Row8<float> lw[N8];
+      Row8<IO> lw[N8];
 #pragma unroll
       for (int j = 0; j < N8; ++j) {
         const int x = min(8 * (tid + BWD_THREADS * j), C * DK - 8);
-        lw[j].load(gW + x);
+        lw[j].load((const IO *)gW + x);
       }
 #pragma unroll
       for (int j = 0; j < N8; ++j) {
@@ -1191,13 +1197,13 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
     IO *Os = (IO *)R, *Ds = Os + C * Dv;
     constexpr int N8 = (C * DVMAX_BWD / 8 + BWD_THREADS - 1) / BWD_THREADS;
     Row8<IO> lo[N8];
-    Row8<float> ld[N8];
+    Row8<IO> ld[N8];
 #pragma unroll
     for (int jj = 0; jj < N8; ++jj) {
       const int x = min(8 * (tid + BWD_THREADS * jj), C * Dv - 8);
       const int r = x / Dv, j = x % Dv, t = min(t0 + r, T - 1);
       lo[jj].load((const IO *)bp.dO + vb + (size_t)t * vrow + j);
-      ld[jj].load(gD + x);
+      ld[jj].load((const IO *)gD + x);
     }
 #pragma unroll
     for (int jj = 0; jj < N8; ++jj) {

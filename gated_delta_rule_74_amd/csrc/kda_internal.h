@@ -34,7 +34,8 @@ struct BwdParams {
   const void *dO;        // [B,T,H,Dv] in the q/k/v dtype
   const float *dsT;      // [B,H,Dk,Dv] or null
   float *ds0;            // [B,H,Dk,Dv] or null
-  float *dD;             // dDelta, [B,T,H,Dv] fp32 (scratch)
+  float *dD;             // dDelta, [B,T,H,Dv] in the q/k/v dtype (scratch
+                         // sized for fp32)
   float *dSc;            // gradient at the end of every chunk [B,H,NC,Dk,Dv]
   const float *Sc;       // forward state at the start of every chunk
   float *gs;             // per-chunk intermediates (second kernel -> third)
