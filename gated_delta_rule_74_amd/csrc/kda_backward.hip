@@ -514,7 +514,7 @@ template <typename IO, int DK, int C> struct G1L {
 };
 
 template <typename IO, int DK, int C>
-__global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_state(
+__global__ __launch_bounds__(BWD_THREADS, 2) void kda_bwd_chunk_state(
     BwdParams bp) {
   using L = G1L<IO, DK, C>;
   constexpr int SV = L::SV, NB = C / 16, NKT = DK / 16, LK = L::LK, LS = L::LS;
