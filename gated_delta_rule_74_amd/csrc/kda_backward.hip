@@ -260,6 +260,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_state(BwdParams bp) {
   UnitStage<IO, NUK> stK;
   UnitStage<IO, NUQ> stQ, stW;
   Row8<IO> ov;  // lanes 2r, 2r + 1: token r, value columns 8 (tid & 1) + 0..7
+  bool ovz = false;  // the token lies past the sequence: ov counts as zero
   float gv = 0.f;
   auto fetch = [&](int n) {
     const char *blk = p.ws + ((size_t)bh * NC + n) * p.wsb;
@@ -271,7 +272,9 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_state(BwdParams bp) {
       const int r = tid >> 1, t = min(n * C + r, T - 1);
       ov.load((const IO *)bp.dO + ((size_t)b * T + t) * orow + (size_t)h * Dv +
               16 * vt + 8 * (tid & 1));
-      if (n * C + r >= T) ov.zero();
+      // zeroed where it is used: writing the registers of a load in flight
+      // would make the wave wait here for every load just issued
+      ovz = n * C + r >= T;
     }
     if (tid < DK) gv = ((const float *)(blk + W.off_gam))[tid];
   };
@@ -289,11 +292,10 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_state(BwdParams bp) {
       const int r = tid >> 1, c0 = 8 * (tid & 1);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        OT[(c0 + e) * LDC + r] = from_f32<IO>(ov.get(e));
+        OT[(c0 + e) * LDC + r] = from_f32<IO>(ovz ? 0.f : ov.get(e));
     }
     if (tid < DK) Gm[tid] = gv;
     __syncthreads();
-    if (n > 0) fetch(n - 1);
 
     // ---- the gradient at this chunk's end, for the per-chunk kernels
 #pragma unroll
@@ -306,6 +308,10 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_state(BwdParams bp) {
         for (int e = 0; e < 4; ++e) dst[(size_t)e * Dv] = dS[j][e];
       }
     }
+
+    // the next chunk's loads after this chunk's stores: issued first, the
+    // stores would wait behind 56 KiB of loads in the vector-memory queue
+    if (n > 0) fetch(n - 1);
 
     // ---- dDelta = P^T dO + Ktil dS'   (token tile rt = wave)
     if (wave < NB) {
