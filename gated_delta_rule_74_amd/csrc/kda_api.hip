@@ -4,6 +4,7 @@
 #include "../../include/kda.h"
 
 #include <math.h>
+#include <stdlib.h>
 
 #include <mutex>
 
@@ -102,6 +103,15 @@ size_t ws_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
   return (size_t)B * H * nc * L.bytes;
 }
 
+// kda_prefill's workspace: the factor blocks, then the int array of the
+// concurrent mode (task counter and per-chunk-task ready flags)
+size_t prefill_ws_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
+                        kda_dtype io) {
+  const int c = run_chunk(io, Dk, chunk);
+  const int nc = (int)(((long long)T + c - 1) / c);
+  return ws_bytes(B, T, H, Dk, Dv, chunk, io) + kda::sync_bytes(B, H, nc);
+}
+
 // backward workspace: [forward factors | state at every chunk start |
 // gradient at every chunk end | dDelta | per-chunk intermediates | A and
 // T^T of every chunk | the forward's output o, which the backward does not
@@ -182,6 +192,81 @@ kda_status scratch_on_current_device(void **out) {
   return KDA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// The concurrent prefill.  The chunk prep runs on the caller's stream and
+// the state pass on a second stream of the library's (one per GPU, created
+// on first use, default priority, never destroyed), joined by two events so
+// that the call still starts after earlier work on the caller's stream and
+// later work waits for both kernels.  The event pair of a GPU is reused, so
+// the record/wait sequence of one call is kept whole under a per-GPU lock.
+//
+// Both kernels lean on the same per-CU path from the L2 into the vector
+// registers, so running them together gains only where the steady state
+// dominates: measured on the long-context workload (4096 chunks per head)
+// the call is 8 % faster, on the 8192-token one (128 chunks) 3 % slower.
+// The mode is therefore used for sequences of at least CO_MIN_CHUNKS chunks.
+// KDA_CONCURRENT in the environment, read at every call, overrides that:
+// "0" never, "1" for every shape the mode covers.
+constexpr int CO_MAX_DEVICES = 64;
+struct CoStreams {
+  std::once_flag once;
+  hipError_t err = hipSuccess;
+  hipStream_t side = nullptr;
+  hipEvent_t start = nullptr, done = nullptr;
+  std::mutex mu;
+};
+CoStreams co_streams[CO_MAX_DEVICES];
+
+constexpr int CO_MIN_CHUNKS = 1024;
+bool concurrent_wanted(int NC) {
+  const char *e = getenv("KDA_CONCURRENT");
+  if (e && e[0] == '0') return false;
+  if (e && e[0] == '1') return true;
+  return NC >= CO_MIN_CHUNKS;
+}
+
+CoStreams *co_streams_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= CO_MAX_DEVICES)
+    return nullptr;
+  CoStreams &c = co_streams[dev];
+  std::call_once(c.once, [&c]() {
+    hipError_t e = hipStreamCreateWithFlags(&c.side, hipStreamNonBlocking);
+    if (e == hipSuccess)
+      e = hipEventCreateWithFlags(&c.start, hipEventDisableTiming);
+    if (e == hipSuccess)
+      e = hipEventCreateWithFlags(&c.done, hipEventDisableTiming);
+    c.err = e;
+  });
+  return c.err == hipSuccess ? &c : nullptr;
+}
+
+// whether a call on `stream` is being captured into a graph (the concurrent
+// mode is then not used: the capture keeps the plain two-kernel sequence)
+bool capturing(hipStream_t stream) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &st) != hipSuccess) return true;
+  return st != hipStreamCaptureStatusNone;
+}
+
+// clear the sync array, then the prep on `stream` beside the state pass on
+// the side stream; returns hipErrorNotSupported (nothing launched) when the
+// side stream is unavailable
+hipError_t launch_prefill_concurrent(kda::PrefillParams &p,
+                                     hipStream_t stream) {
+  CoStreams *c = co_streams_for_current_device();
+  if (!c) return hipErrorNotSupported;
+  std::lock_guard<std::mutex> lock(c->mu);
+  hipError_t e = kda::launch_sync_clear(p, stream);
+  if (e == hipSuccess) e = hipEventRecord(c->start, stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(c->side, c->start, 0);
+  if (e == hipSuccess) e = kda::launch_prefill_prep(p, 1, stream);
+  if (e == hipSuccess) e = kda::launch_state_pass_concurrent(p, c->side);
+  if (e == hipSuccess) e = hipEventRecord(c->done, c->side);
+  if (e == hipSuccess) e = hipStreamWaitEvent(stream, c->done, 0);
+  return e;
+}
+
 }  // namespace
 
 namespace kda {
@@ -217,7 +302,7 @@ size_t kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv,
   if (B <= 0 || T <= 0 || H <= 0 || !dim_ok(Dk) || !dim_ok(Dv) ||
       !chunk_ok(chunk) || !dtype_valid(qkv_dtype))
     return 0;
-  return ws_bytes(B, T, H, Dk, Dv, chunk, qkv_dtype);
+  return prefill_ws_bytes(B, T, H, Dk, Dv, chunk, qkv_dtype);
 }
 
 kda_status kda_prefill_chunk_prep(const void *q, const void *k, const void *v,
@@ -281,9 +366,20 @@ kda_status kda_prefill(const void *q, const void *k, const void *v,
   p.ws = (char *)workspace;
   p.wsb = kda::ws_layout(Dk, Dv, p.C, qkv_dtype == KDA_BF16 ? 2 : 4).bytes;
   const int bf = qkv_dtype == KDA_BF16;
-  hipError_t e = kda::launch_prefill_prep(p, bf, (hipStream_t)stream);
+  hipStream_t s = (hipStream_t)stream;
+  // the concurrent mode needs the sync array after the factor blocks
+  const size_t fb = ws_bytes(B, T, H, Dk, Dv, chunk, qkv_dtype);
+  if (workspace_bytes >= prefill_ws_bytes(B, T, H, Dk, Dv, chunk, qkv_dtype) &&
+      concurrent_wanted(p.NC) && kda::prefill_concurrent_applies(p, bf) &&
+      !capturing(s)) {
+    p.sync = (int *)((char *)workspace + fb);
+    const hipError_t e = launch_prefill_concurrent(p, s);
+    if (e != hipErrorNotSupported) return hip_status(e);
+    p.sync = nullptr;
+  }
+  hipError_t e = kda::launch_prefill_prep(p, bf, s);
   if (e != hipSuccess) return hip_status(e);
-  return hip_status(kda::launch_state_pass(p, bf, (hipStream_t)stream));
+  return hip_status(kda::launch_state_pass(p, bf, s));
 }
 
 kda_status kda_prefill_noalloc(const void *q, const void *k, const void *v,
@@ -298,7 +394,8 @@ kda_status kda_prefill_noalloc(const void *q, const void *k, const void *v,
                                s_out, o, B, T, H, Dk, Dv, chunk, scale, conv,
                                p);
   if (st != KDA_OK) return st;
-  if (ws_bytes(B, T, H, Dk, Dv, chunk, qkv_dtype) > KDA_NOALLOC_SCRATCH_BYTES)
+  if (prefill_ws_bytes(B, T, H, Dk, Dv, chunk, qkv_dtype) >
+      KDA_NOALLOC_SCRATCH_BYTES)
     return KDA_ENOSPACE;
   void *ws = nullptr;
   st = scratch_on_current_device(&ws);

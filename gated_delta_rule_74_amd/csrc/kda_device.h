@@ -54,6 +54,29 @@ __device__ __forceinline__ void st_stream(void *q, T v) {
   }
 }
 
+// A workspace store.  CO = false: the streaming store above.  CO = true:
+// also written through to the device-coherent level (sc1), so that a
+// workgroup on another XCD whose first read of the line comes after this
+// store has completed sees the new value without any cache write-back (the
+// chunk prep and the state pass run at the same time in that mode).  Stores
+// only; the trailing s_nop covers the wait state that a vector write of the
+// data registers needs after a store of more than 8 bytes.
+template <bool CO, typename T>
+__device__ __forceinline__ void st_ws(void *q, T v) {
+  static_assert(sizeof(T) == 8 || sizeof(T) == 16, "8 or 16 bytes");
+  if constexpr (!CO) {
+    st_stream(q, v);
+  } else if constexpr (sizeof(T) == 16) {
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    asm volatile("global_store_dwordx4 %0, %1, off sc1 nt\n\ts_nop 1"
+                 :: "v"(q), "v"(__builtin_bit_cast(u4, v)));
+  } else {
+    typedef unsigned u2 __attribute__((ext_vector_type(2)));
+    asm volatile("global_store_dwordx2 %0, %1, off sc1 nt\n\ts_nop 1"
+                 :: "v"(q), "v"(__builtin_bit_cast(u2, v)));
+  }
+}
+
 // sum over aligned groups of G lanes (G a power of two, at most 32), every
 // lane of a group getting the total: DPP moves within a 16-lane row (quad
 // swaps, then rotations by 4 and 8 or the half-row mirror), one shuffle

@@ -26,7 +26,24 @@ struct PrefillParams {
                               // of every chunk, [B,H,NC,Dk,Dv] fp32
   float *train_at;            // chunk prep: if set, per (bh, chunk) the
                               // matrix A then T^T, C x C fp32 each
+  int *sync;                  // concurrent prefill only (else null): task
+                              // counter, wait-timeout flag, then one ready
+                              // flag per chunk task (see SYNC_* below)
 };
+
+// The concurrent prefill (chunk prep and state pass running at the same
+// time on the same CUs, bf16 q/k/v, d_k = d_v = 128, chunk 64, per-channel
+// gate, no conv): layout of its int array `sync`, cleared before each call.
+//   sync[SYNC_NEXT]    next chunk task to claim (chunk-major: task
+//                      t = n * B*H + bh)
+//   sync[SYNC_TIMEOUT] set to 1 if a state-pass wave gave up waiting
+//   sync[SYNC_FLAGS + bh * NC + n]  1 once the factors of chunk n of
+//                      batch*head bh are in memory (a head's flags are
+//                      contiguous: one vector load reads 64 of them)
+constexpr int SYNC_NEXT = 0, SYNC_TIMEOUT = 1, SYNC_FLAGS = 64;
+inline size_t sync_bytes(int B, int H, int NC) {
+  return (((size_t)SYNC_FLAGS + (size_t)B * H * NC) * 4 + 255) & ~(size_t)255;
+}
 
 // gradient of the chunked prefill (kda_backward.hip)
 struct BwdParams {
@@ -94,6 +111,12 @@ bool prep_d128_applies(const PrefillParams &p, int io_bf16);
 hipError_t launch_prefill_prep_d128(const PrefillParams &p, hipStream_t s);
 hipError_t launch_state_pass(const PrefillParams &p, int io_bf16,
                              hipStream_t s);
+// the concurrent prefill: whether p (with p.sync set) qualifies, the
+// clearing of p.sync, and its state pass (the prep is the d128 launcher's,
+// which takes the concurrent path when p.sync is set)
+bool prefill_concurrent_applies(const PrefillParams &p, int io_bf16);
+hipError_t launch_sync_clear(const PrefillParams &p, hipStream_t s);
+hipError_t launch_state_pass_concurrent(const PrefillParams &p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams &p, int io_bf16, hipStream_t s);
 // the three backward kernels (the forward's prep and state pass, with state
 // checkpoints, must have filled bp.f.ws and bp.Sc first)

@@ -55,6 +55,8 @@ constexpr size_t oM = oF + (size_t)NB * DK * 4;            // mid products
 constexpr size_t oVote = oM + (size_t)3 * DK * 4;
 constexpr size_t oBeta = oVote + 64;
 constexpr size_t LDS = oBeta + 64 * 4;
+constexpr size_t oClaim = LDS;           // concurrent mode: the next task
+constexpr size_t LDS_CO = oClaim + 16;
 // with the fused conv: the head's taps (one f32x4 per q, k and v channel),
 // per-token L2 scales of q and k (for the exact diagonal path), and the
 // two channel halves' partial sums of squares
@@ -111,14 +113,23 @@ template <typename GT, bool CONV> struct Stage {
   f32x4 tap;
 };
 
+// task -> (batch*head, chunk): last chunk first (the state pass launched
+// after the prep then finds its first chunks in the memory-side cache), or
+// with CO first chunk first (the concurrent state pass consumes them in
+// that order)
+template <bool CO>
+__device__ __forceinline__ int task_chunk(int task, int BH, int NC) {
+  return CO ? task / BH : NC - 1 - task / BH;
+}
+
 // PART: 1 = g and beta, 2 = q, 4 = k, 8 = v (and the conv taps)
-template <int PART, typename GT, bool CONV>
+template <int PART, typename GT, bool CONV, bool CO>
 __device__ __forceinline__ void load_task(const PrefillParams &p, int task,
                                           Stage<GT, CONV> &st, int tid, int c0,
                                           int r0) {
   constexpr int XR = Stage<GT, CONV>::XR, XO = CONV ? 3 : 0;
   const int BH = p.B * p.H;
-  const int bh = task % BH, n = p.NC - 1 - task / BH;
+  const int bh = task % BH, n = task_chunk<CO>(task, BH, p.NC);
   const int b = bh / p.H, h = bh % p.H, T = p.T, H = p.H;
   const int t0 = n * C, tlast = T - 1;
   const size_t tok0 = (size_t)b * T;
@@ -160,14 +171,23 @@ __device__ __forceinline__ void load_task(const PrefillParams &p, int task,
   }
 }
 
-template <typename GT, bool CONV>
+// CO: the concurrent mode (no conv, no backward outputs).  Tasks are claimed
+// one at a time from p.sync[SYNC_NEXT] in chunk order, so a workgroup that
+// is not yet resident holds up nothing; the workspace is written with
+// device-coherent stores; and once every wave has waited for its stores of
+// a task (just before the next task's first barrier), thread 0 sets the
+// task's ready flag for the state pass running beside the prep.
+template <typename GT, bool CONV, bool CO>
 __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
+  static_assert(!(CO && CONV), "the concurrent mode has no conv");
   using M = Mma<bf16>;
   typedef M::frag frag;
   typedef Vec4<bf16>::raw R4;
   constexpr int XO = CONV ? 3 : 0;  // first own row inside the staged rows
 
-  __shared__ __attribute__((aligned(16))) char sm[CONV ? LDS_CONV : LDS];
+  __shared__ __attribute__((aligned(16))) char sm[CONV ? LDS_CONV
+                                                  : CO ? LDS_CO : LDS];
+  int *claim = (int *)(sm + oClaim);  // CO only
   f32x4 *taps = (f32x4 *)(sm + oTap);  // conv only
   float *nrm = (float *)(sm + oNrm), *l2p = (float *)(sm + oL2p);
   bf16 *Xkr = (bf16 *)(sm + oKR), *Xqr = (bf16 *)(sm + oQR);
@@ -197,7 +217,17 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
 
   Stage<GT, CONV> st;
   int task = blockIdx.x;
-  if (task < ntask) load_task<15, GT, CONV>(p, task, st, tid, c0, r0);
+  if constexpr (CO) {
+    if (tid == 0)
+      claim[0] = __hip_atomic_fetch_add(p.sync + SYNC_NEXT, 1,
+                                        __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    task = claim[0];
+  }
+  int done = -1;  // CO, thread 0: flag index of the finished task not yet
+                  // published
+  if (task < ntask) load_task<15, GT, CONV, CO>(p, task, st, tid, c0, r0);
   auto put_beta = [&]() {
     if (wave == 0)
       betas[lane] = GB ? __uint_as_float(st.beta << 16)
@@ -208,7 +238,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
   if (task < ntask) put_beta();
   __syncthreads();
 
-  for (; task < ntask; task += gridDim.x) {
+  while (task < ntask) {
     // per-lane indices are rebuilt from an opaque copy every task: the
     // compiler would otherwise keep dozens of addresses derived from them
     // live across the whole loop, past the 256 registers a lane may hold
@@ -222,10 +252,17 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
     const int hh = lane >> 5;
     const int c0 = 64 * (wave & 1) + 2 * (lane & 31);
     const int r0 = 16 * a + 8 * hh;
-    const int bh = task % BH, n = p.NC - 1 - task / BH;
+    const int bh = task % BH, n = task_chunk<CO>(task, BH, p.NC);
     const int b = bh / H, h = bh % H;
     const int t0 = n * C;
     char *blk = p.ws + ((size_t)bh * p.NC + n) * p.wsb;
+    if constexpr (CO) {
+      // the task after this one (read back after B1)
+      if (tid == 0)
+        claim[0] = __hip_atomic_fetch_add(p.sync + SYNC_NEXT, 1,
+                                          __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     // ---- E1: decay, running products, A/P operands, (beta V)^T -----------
     float F[2], xkr[8][2];
@@ -395,11 +432,21 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
       const unsigned long long bal = __ballot(vote);
       if (lane == 0) votes[wave] = bal != 0ull;
     }
+    // CO: the previous task's workspace stores complete (nothing else is in
+    // flight here: this task's inputs were consumed above)
+    if constexpr (CO) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // B1: region A, (K sigma)^T, (beta V)^T, Fs, votes
+    if constexpr (CO) {
+      if (tid == 0 && done >= 0)
+        __hip_atomic_store(p.sync + SYNC_FLAGS + done, 1, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      done = bh * p.NC + n;  // the flag of this task
+    }
 
     // ---- E2: Qtil and Ktil^T units, gamma_C, (beta K Gam)^T, mid products -
-    const bool more = task + (int)gridDim.x < ntask;
-    if (more) load_task<1, GT, CONV>(p, task + gridDim.x, st, tid, c0, r0);
+    const int next = CO ? claim[0] : task + (int)gridDim.x;
+    const bool more = next < ntask;
+    if (more) load_task<1, GT, CONV, CO>(p, next, st, tid, c0, r0);
     int anyv = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) anyv |= votes[w];
@@ -426,8 +473,8 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
       *(R4 *)(row1 + cm_off<C>(c0 + 1, r0)) = Vec4<bf16>::put(&k1[0]);
       *(R4 *)(row1 + cm_off<C>(c0 + 1, r0 + 4)) = Vec4<bf16>::put(&k1[4]);
       if (a == NB - 1 && hh == 1)
-        *(float2 *)((float *)(blk + W.off_gam) + c0) =
-            make_float2(fp0 * F[0], fp1 * F[1]);
+        st_ws<CO>((float *)(blk + W.off_gam) + c0,
+                  make_float2(fp0 * F[0], fp1 * F[1]));
     }
     // mid products M_{b->a} = prod_{b<d<a} F_d for sub-chunk pairs a-b >= 2:
     // pairs (2,0), (3,0), (3,1) at index 0, 1, 2
@@ -442,7 +489,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
     }
     __syncthreads();  // B2
 
-    if (more) load_task<2, GT, CONV>(p, task + gridDim.x, st, tid, c0, r0);
+    if (more) load_task<2, GT, CONV, CO>(p, next, st, tid, c0, r0);
 
     if (fallback) {
       // exact diagonal-block sums: item (sub-chunk aa, column s, 16
@@ -530,7 +577,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
         y1[j] = x1[j] * f1[j];
       }
       const R4 lo = Vec4<bf16>::put(y0), up = Vec4<bf16>::put(y1);
-      st_stream(blk + W.off_qt + ((size_t)(aa * NKU + u) * 64 + lane) * 16,
+      st_ws<CO>(blk + W.off_qt + ((size_t)(aa * NKU + u) * 64 + lane) * 16,
                 make_uint4(lo.x, lo.y, up.x, up.y));
     };
     // Ktil^T = (K*Gam_C/Gam)^T, unit w (channel tile w / 2, token unit w % 2)
@@ -557,7 +604,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
         y1[j] = x1[j] * s1;
       }
       const R4 lo = Vec4<bf16>::put(y0), up = Vec4<bf16>::put(y1);
-      st_stream(blk + W.off_ktt + ((size_t)(ct * NTU + u) * 64 + lane) * 16,
+      st_ws<CO>(blk + W.off_ktt + ((size_t)(ct * NTU + u) * 64 + lane) * 16,
                 make_uint4(lo.x, lo.y, up.x, up.y));
     };
     // block j (ap_block order) of A (into LDS) and/or P (into the
@@ -622,10 +669,10 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
                     ((size_t)(aa * NTU + bb / 2) * 64 + lane) * 16 +
                     (bb % 2) * 8;
         const float a4[4] = {accP[0], accP[1], accP[2], accP[3]};
-        st_stream(dst, Vec4<bf16>::put(a4));
+        st_ws<CO>(dst, Vec4<bf16>::put(a4));
         if (diag && (aa % 2) == 0) {
           const float z[4] = {0.f, 0.f, 0.f, 0.f};
-          st_stream(dst + 8, Vec4<bf16>::put(z));
+          st_ws<CO>(dst + 8, Vec4<bf16>::put(z));
         }
       }
     };
@@ -645,7 +692,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
       if (wave >= 4) ap_item(wave < 6 ? 0 : 5, (wave & 1) == 0, (wave & 1) == 1);
     }
     __syncthreads();  // B3: A complete; beta K rho no longer read
-    if (more) load_task<4, GT, CONV>(p, task + gridDim.x, st, tid, c0, r0);
+    if (more) load_task<4, GT, CONV, CO>(p, next, st, tid, c0, r0);
 
     // ---- T1: diagonal inverses (waves 0-3, as in kda_prep_impl.h) beside
     // part of the Qtil / Ktil^T unit stores (waves 4-7), which no later phase
@@ -731,7 +778,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
       }
     }
     __syncthreads();
-    if (more) load_task<8, GT, CONV>(p, task + gridDim.x, st, tid, c0, r0);
+    if (more) load_task<8, GT, CONV, CO>(p, next, st, tid, c0, r0);
 
     // ---- WU: -W (A-operand units) and U (accumulator tiles) ----------------
     // token tile rt reads T rows 16 rt .. 16 rt + 15 over token units
@@ -765,7 +812,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
               acc[h2] = M::mma(xa[uu][h2], tb[uu], acc[h2]);
-        st_stream(blk + W.off_negw + ((size_t)(rt * NKU + u) * 64 + lane) * 16,
+        st_ws<CO>(blk + W.off_negw + ((size_t)(rt * NKU + u) * 64 + lane) * 16,
                   M::pack(-acc[0], -acc[1]));
       }
     };
@@ -786,7 +833,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
         bf16 *dst = (bf16 *)(blk + W.off_u) +
                     ((size_t)(vt * NB + rt) * 64 + lane) * 4;
         const float a4[4] = {acc[0], acc[1], acc[2], acc[3]};
-        st_stream(dst, Vec4<bf16>::put(a4));
+        st_ws<CO>(dst, Vec4<bf16>::put(a4));
       }
     };
     if (wave < 4) {
@@ -807,6 +854,15 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
     }
     if (more) put_beta();  // the current task's betas were last read in E1
     __syncthreads();       // B5: LDS free for the next task
+    task = next;
+  }
+  if constexpr (CO) {
+    // the last task's flag, once every wave's stores have completed
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0 && done >= 0)
+      __hip_atomic_store(p.sync + SYNC_FLAGS + done, 1, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -820,10 +876,13 @@ bool prep_d128_applies(const PrefillParams &p, int io_bf16) {
 template <typename GT>
 static void launch_d128(const PrefillParams &p, unsigned grid, hipStream_t s) {
   if (p.use_conv)
-    hipLaunchKernelGGL((pc::kda_chunk_prep_d128<GT, true>), dim3(grid),
+    hipLaunchKernelGGL((pc::kda_chunk_prep_d128<GT, true, false>), dim3(grid),
+                       dim3(pc::NT), 0, s, p);
+  else if (p.sync)
+    hipLaunchKernelGGL((pc::kda_chunk_prep_d128<GT, false, true>), dim3(grid),
                        dim3(pc::NT), 0, s, p);
   else
-    hipLaunchKernelGGL((pc::kda_chunk_prep_d128<GT, false>), dim3(grid),
+    hipLaunchKernelGGL((pc::kda_chunk_prep_d128<GT, false, false>), dim3(grid),
                        dim3(pc::NT), 0, s, p);
 }
 

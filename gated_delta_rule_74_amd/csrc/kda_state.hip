@@ -437,6 +437,271 @@ __global__ __launch_bounds__(STATE_THREADS, 1) void kda_state_pass(
 }
 
 // ---------------------------------------------------------------------------
+// Concurrent variant: bf16 q/k/v, d_k = d_v = 128, chunk 64, one 16-column
+// value slab per workgroup, running at the same time as the chunk prep
+// (kda_chunk_prep_d128 in its concurrent mode) on the same CUs.  The prep
+// holds one workgroup of eight waves per CU with two waves per SIMD; this
+// workgroup has four waves, one per SIMD, and fits beside it: at most 144
+// registers per lane (2 x 184 + 144 = 512 per SIMD) and 6 KiB of LDS.
+//
+// Wave w has both roles of the kernel above for token tile w and key unit
+// w: Delta rows (from -W, U), the state rows of key channels 32w .. 32w + 31
+// (from Ktil^T, gamma_C) and the O rows (from Qtil, P).  Each group of its
+// factors is fetched for the next chunk right after its last use in this
+// one, into the same registers, so every fetch has about one chunk step to
+// arrive.  The whole S is read from LDS once per chunk, before the Delta
+// barrier, and kept for O, so the state update may overwrite SU as soon as
+// that barrier is passed: two barriers per chunk, as above.
+//
+// Before fetching chunk n a wave must know that its ready flag is set: the
+// prep sets it after the chunk's (device-coherent) workspace stores have
+// completed, and the flags are read with device-coherent loads.  No line of
+// the block is touched before that, so the XCD's L2 cannot hold an older
+// copy of it (the kernel starts with the L2 invalidated).  The flags of a
+// head are contiguous, so one vector load reads 64 of them: a wave polls
+// only when it reaches a chunk it does not yet know to be ready, and then
+// learns the whole run of ready chunks after it.  The wait is bounded (about
+// a second, after which it sets sync[SYNC_TIMEOUT] and stops waiting), so a
+// mistake can only give wrong values, never a hang.
+//
+// Every load of the main loop is issued on every path (indices clamped
+// instead of branches): the compiler counts the vector-memory operations
+// issued after each load to wait for exactly that load, and a load that is
+// skipped on some path would make those counts, and the waits, coarser.
+// Once chunk n + PF is known ready, its block is pulled into L2 (4 bytes of
+// every line, direct-to-LDS into a sink that nothing reads) so the factor
+// loads a few chunks later hit the L2.  That load is written in inline asm:
+// as a builtin, the compiler would make later LDS accesses wait for it.  An
+// operation the compiler does not count can only make its waits stricter
+// (a wait for at most k outstanding operations then also covers one more),
+// never looser.
+namespace co {
+constexpr int DK = 128, DV = 128, C = 64, NB = 4, NKU = 4, NTU = 2;
+constexpr int THREADS = 256;
+constexpr int PF = 3;                // chunks between warming and use
+// polls of about 3 us each (a long sleep between them: a thousand waves
+// polling device-coherent lines load the memory side that the prep beside
+// them writes to)
+constexpr long SPIN_MAX = 1L << 18;
+constexpr int POLL_SLEEP = 100;  // s_sleep units of 64 clocks
+
+struct Factors {  // one wave's factors of one chunk
+  typedef Mma<bf16>::frag frag;
+  frag w[NKU];     // -W, token tile w
+  uint2 u;         // U, token tile w, the slab's 16 columns
+  frag k[2][NTU];  // Ktil^T, key tiles 2w, 2w + 1
+  f32x4 gm[2];     // gamma_C of those key tiles
+  frag q[NKU];     // Qtil, token tile w
+  frag p[NTU];     // P, token tile w (unit 1 is zero for w < 2)
+};
+}  // namespace co
+
+__global__ __launch_bounds__(co::THREADS, 1) void kda_state_pass_co(
+    PrefillParams p) {
+  using namespace co;
+  using M = Mma<bf16>;
+  using V4 = Vec4T<bf16>;
+  typedef M::frag frag;
+  constexpr WsLayout W = ws_layout(DK, DV, C, 2);
+  __shared__ __attribute__((aligned(1024))) char sm[(NKU + NTU) * 1024];
+  __shared__ __attribute__((aligned(256))) char sink[256];  // warm-up only
+  frag *SU = (frag *)sm;                 // S as second operand, NKU units
+  frag *DU = (frag *)(sm + NKU * 1024);  // Delta as second operand, NTU units
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m16 = lane & 15, g4 = lane >> 4;
+  const int H = p.H, T = p.T, BH = p.B * p.H, NC = p.NC;
+  constexpr int ng = DV / 16;
+  int bh, grp;
+  {
+    // a head's slab workgroups on one XCD, as in kda_state_pass
+    const int b = blockIdx.x;
+    if ((BH & 7) == 0) {
+      const int x = b & 7, jj = b >> 3;
+      bh = (jj / ng) * 8 + x;
+      grp = jj % ng;
+    } else {
+      bh = b / ng;
+      grp = b % ng;
+    }
+  }
+  const int bb = bh / H, h = bh % H, vt = grp;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  const char *ws0 = p.ws + (size_t)bh * NC * p.wsb;
+  const int *hflags = p.sync + SYNC_FLAGS + (size_t)bh * NC;  // [n]
+
+  // chunks below `ready` are known to be in memory (wave-uniform)
+  int ready = 0;
+  bool gave_up = false;
+  // wait for chunk n (the chunks before it are already known): lane i
+  // reads the flag of chunk n + i, and the run of set flags from n on
+  // extends `ready`
+  auto wait_ready = [&](int n) {
+    if (n < ready) return;
+    long it = 0;
+    while (true) {
+      const int f = __hip_atomic_load(hflags + min(n + lane, NC - 1),
+                                      __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned long long set = __ballot(f != 0 || n + lane >= NC);
+      const int run = (~set == 0ull) ? 64 : __builtin_ctzll(~set);
+      if (run > 0 || gave_up) {
+        ready = n + max(run, 1);
+        break;
+      }
+      if (++it > SPIN_MAX) {
+        if (lane == 0)
+          __hip_atomic_store(p.sync + SYNC_TIMEOUT, 1, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        gave_up = true;
+      }
+      __builtin_amdgcn_s_sleep(POLL_SLEEP);
+    }
+    // no load of the block may be moved above the wait
+    asm volatile("" ::: "memory");
+  };
+  // 4 bytes of every 128-byte line of chunk n's block: the head's ng
+  // workgroups split the lines, the four waves split a workgroup's share
+  const unsigned sink_lds =
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) void *)sink;
+  auto warm = [&](int n) {
+    constexpr int nline = (int)((W.bytes + 127) / 128);
+    constexpr int share = (nline + ng - 1) / ng;
+    constexpr int per = (share + 3) / 4;
+    static_assert(per <= 64, "one load per wave");
+    // lanes past the wave's share repeat its last line
+    const int i = min(per * w + min(lane, per - 1), share - 1);
+    const int line = min(grp * share + i, nline - 1);
+    const char *a = ws0 + (size_t)n * p.wsb + (size_t)line * 128;
+    int m0save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(m0save)
+        : "v"(a), "s"(sink_lds)
+        : "memory");
+  };
+  auto load_wu = [&](Factors &f, const char *blk) {
+    const frag *Lw = (const frag *)(blk + W.off_negw) + lane;
+#pragma unroll
+    for (int u = 0; u < NKU; ++u) f.w[u] = Lw[(w * NKU + u) * 64];
+    f.u = ((const uint2 *)(blk + W.off_u) + lane)[(vt * NB + w) * 64];
+  };
+  auto load_kg = [&](Factors &f, const char *blk) {
+    const frag *Lk = (const frag *)(blk + W.off_ktt) + lane;
+    const float *Lg = (const float *)(blk + W.off_gam) + 4 * g4;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int t = 2 * w + h2;
+#pragma unroll
+      for (int u = 0; u < NTU; ++u) f.k[h2][u] = Lk[(t * NTU + u) * 64];
+      f.gm[h2] = *(const f32x4 *)(Lg + 16 * t);
+    }
+  };
+  auto load_qp = [&](Factors &f, const char *blk) {
+    const frag *Lq = (const frag *)(blk + W.off_qt) + lane;
+#pragma unroll
+    for (int u = 0; u < NKU; ++u) f.q[u] = Lq[(w * NKU + u) * 64];
+    // P units above the diagonal are never written by the prep: unit 1 of
+    // tiles 0 and 1 is loaded (inside the block) but never multiplied
+    const frag *Lp = (const frag *)(blk + W.off_p) + lane;
+#pragma unroll
+    for (int u = 0; u < NTU; ++u) f.p[u] = Lp[(w * NTU + u) * 64];
+  };
+
+  // state rows of key tiles 2w, 2w + 1 (accumulator layout)
+  f32x4 S[2];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    S[h2] = zero;
+    if (p.s0) {
+      const float *s0 = p.s0 + ((size_t)bh * DK + 16 * (2 * w + h2) + 4 * g4) *
+                                   DV + 16 * vt + m16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[h2][e] = s0[(size_t)e * DV];
+    }
+  }
+  SU[w * 64 + lane] = M::pack(S[0], S[1]);
+
+  Factors f;
+  wait_ready(0);
+  load_wu(f, ws0);
+  load_kg(f, ws0);
+  load_qp(f, ws0);
+  lds_barrier();  // S0 in SU
+
+  bf16 *obase = (bf16 *)p.o + ((size_t)bb * T * H + h) * DV + 16 * vt + 4 * g4;
+  const size_t orow = (size_t)H * DV;  // elements between tokens
+  for (int n = 0; n < NC; ++n) {
+    // the next chunk's block (the last chunk fetches its own again)
+    const bool more = n + 1 < NC;
+    const char *nb = ws0 + (size_t)(more ? n + 1 : n) * p.wsb;
+    // the whole S of the chunk start, for Delta now and for O later
+    frag sb[NKU];
+#pragma unroll
+    for (int u = 0; u < NKU; ++u) sb[u] = SU[u * 64 + lane];
+    // Delta rows of token tile w: U - W S
+    f32x4 d = V4::get(f.u);
+#pragma unroll
+    for (int u = 0; u < NKU; ++u) d = M::mma(f.w[u], sb[u], d);
+    {
+      const bf16x4 v4 = {(bf16)d[0], (bf16)d[1], (bf16)d[2], (bf16)d[3]};
+      *(bf16x4 *)((char *)(DU + (w / 2) * 64 + lane) + 8 * (w & 1)) = v4;
+    }
+    if (more) wait_ready(n + 1);
+    load_wu(f, nb);
+    lds_barrier();  // Delta complete in DU; every wave has read SU
+    frag db[NTU];
+#pragma unroll
+    for (int u = 0; u < NTU; ++u) db[u] = DU[u * 64 + lane];
+    // S <- diag(gamma_C) S + Ktil^T Delta on key tiles 2w, 2w + 1
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      f32x4 sn = S[h2] * f.gm[h2];
+#pragma unroll
+      for (int u = 0; u < NTU; ++u) sn = M::mma(f.k[h2][u], db[u], sn);
+      S[h2] = sn;
+    }
+    SU[w * 64 + lane] = M::pack(S[0], S[1]);
+    load_kg(f, nb);
+    // O^T (value columns x tokens of tile w) = S^T Qtil^T + Delta^T P^T
+    f32x4 ot = zero;
+#pragma unroll
+    for (int u = 0; u < NKU; ++u) ot = M::mma(sb[u], f.q[u], ot);
+#pragma unroll
+    for (int u = 0; u < NTU; ++u)
+      if (u <= w / 2) ot = M::mma(db[u], f.p[u], ot);
+    // lane (g4, m16): token 16 w + m16, value columns 4 g4 .. 4 g4 + 3
+    const int tok = n * C + 16 * w + m16;
+    if (tok < T) *(uint2 *)(obase + (size_t)tok * orow) = V4::put(ot);
+    load_qp(f, nb);
+    // (a chunk already known ready when n + PF is not)
+    warm(n + PF < ready ? n + PF : ready - 1);
+    lds_barrier();  // S complete in SU; every wave has read DU
+  }
+  if (p.s_out) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      float *so = p.s_out + ((size_t)bh * DK + 16 * (2 * w + h2) + 4 * g4) * DV +
+                  16 * vt + m16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) so[(size_t)e * DV] = S[h2][e];
+    }
+  }
+  // nothing in flight when the wave ends (the warm-up loads included)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+__global__ void kda_sync_clear(int *sync, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) sync[i] = 0;
+}
+
+// ---------------------------------------------------------------------------
 static int state_cu_count() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -493,6 +758,30 @@ KDA_DISPATCH(state_one)
 hipError_t launch_state_pass(const PrefillParams &p, int io_bf16,
                              hipStream_t s) {
   return io_bf16 ? state_one_dk<bf16>(p, s) : state_one_dk<float>(p, s);
+}
+
+bool prefill_concurrent_applies(const PrefillParams &p, int io_bf16) {
+  // the prep's concurrent mode: the d128 per-channel prep without conv or
+  // backward outputs; the state pass: one slab workgroup per CU at most, so
+  // every one of them is resident beside a prep workgroup
+  return prep_d128_applies(p, io_bf16) && !p.use_conv && !p.ckpt &&
+         !p.train_at && p.Dv == co::DV &&
+         (long long)p.B * p.H * (co::DV / 16) <= state_cu_count();
+}
+
+hipError_t launch_sync_clear(const PrefillParams &p, hipStream_t s) {
+  const int n = SYNC_FLAGS + p.B * p.H * p.NC;
+  hipLaunchKernelGGL(kda_sync_clear, dim3((n + 255) / 256), dim3(256), 0, s,
+                     p.sync, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_pass_concurrent(const PrefillParams &p,
+                                        hipStream_t s) {
+  const unsigned nblk = (unsigned)(p.B * p.H) * (co::DV / 16);
+  hipLaunchKernelGGL(kda_state_pass_co, dim3(nblk), dim3(co::THREADS), 0, s,
+                     p);
+  return hipGetLastError();
 }
 
 }  // namespace kda

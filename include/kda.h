@@ -31,8 +31,11 @@
  * Conventions shared by every entry point.
  *  - All pointers are DEVICE pointers owned by the caller; the library
  *    never allocates device memory (the prefill workspace is passed in) and
- *    keeps no global mutable state, with one exception: the fixed scratch
- *    array of kda_prefill_noalloc (below).  Calls are thread-safe.
+ *    keeps no global mutable state, with two exceptions: the fixed scratch
+ *    array of kda_prefill_noalloc (below), and one extra stream and two
+ *    events per GPU that kda_prefill creates on first use when it runs its
+ *    two phases concurrently (below) and keeps until the process ends.
+ *    Calls are thread-safe.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream) and never synchronises.
  *  - Tensors are dense, contiguous, row-major.  Pointers must be 16-byte
@@ -121,7 +124,9 @@ const char *kda_status_string(kda_status s);
 
 /* Bytes of device workspace kda_prefill needs for these sizes (0 if the
  * sizes are invalid or unsupported).  The workspace holds the chunk-local
- * factors of every (batch, head, chunk); contents need no initialisation. */
+ * factors of every (batch, head, chunk), then a small int array (a counter
+ * and one flag per (batch, head, chunk), 256-byte aligned) that the
+ * concurrent mode of kda_prefill uses; contents need no initialisation. */
 size_t kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv,
                                   int chunk, kda_dtype qkv_dtype);
 
@@ -138,7 +143,22 @@ size_t kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv,
  *   scale     output scale (1.0 reproduces o_t = S_t^T q_t)
  *   conv      NULL, or the fused conv prologue above
  *   workspace device buffer of at least kda_prefill_workspace_size() bytes
- * Runs kda_prefill_chunk_prep then kda_prefill_state_pass on `stream`. */
+ *             (a buffer that holds only the factor blocks, as
+ *             kda_prefill_chunk_prep requires, is accepted and runs the
+ *             two phases one after the other)
+ * Runs kda_prefill_chunk_prep then kda_prefill_state_pass on `stream`.
+ * Concurrent mode: for bf16 q/k/v, Dk = Dv = 128, chunk 64, a gate per key
+ * channel, no conv, B*H*8 <= the GPU's compute units, and at least 1024
+ * chunks per sequence, the two phases run at the same time on the same
+ * compute units instead: the chunk prep on `stream` publishes each chunk's
+ * factors with a ready flag in the workspace, and the state pass, on a
+ * second stream of the library's that waits for `stream` and that `stream`
+ * then waits for, consumes them in order.  Results are bit for bit those of
+ * the two phases run in turn, and work queued on `stream` after the call
+ * still sees them.  The mode is not used while `stream` is being captured
+ * into a graph.  KDA_CONCURRENT in the environment (read at every call)
+ * overrides the choice: "0" never, "1" for every shape above whatever the
+ * sequence length. */
 kda_status kda_prefill(const void *q, const void *k, const void *v,
                        kda_dtype qkv_dtype, const void *g, const void *beta,
                        kda_dtype gate_dtype, const float *s0, float *s_out,
@@ -155,9 +175,9 @@ kda_status kda_prefill(const void *q, const void *k, const void *v,
  * up once per GPU, on the first call made with that GPU current (the
  * caller's current device must be the one `stream` belongs to).  Requests
  * whose kda_prefill_workspace_size() exceeds the array return KDA_ENOSPACE
- * before anything is launched (64 MiB holds 904 chunk-heads at
- * Dk = Dv = 128, chunk 64, bf16: B*H*ceil(T/64) <= 904, e.g. T <= 1792 at
- * B = 1, H = 32).  The call allocates nothing, host or device.  Every call
+ * before anything is launched (64 MiB holds 903 chunk-heads at
+ * Dk = Dv = 128, chunk 64, bf16: B*H*ceil(T/64) <= 903, e.g. T <= 1792 at
+ * B = 1, H = 32).  It always runs the two phases one after the other.  The call allocates nothing, host or device.  Every call
  * on one GPU shares that GPU's array: calls that overlap in time on one
  * GPU (on different streams, or from several threads) race and corrupt
  * each other's results; serialise them (one stream, or events).  The

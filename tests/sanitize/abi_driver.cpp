@@ -21,6 +21,9 @@ hipError_t launch_prefill_prep_gdn(const PrefillParams &, hipStream_t) { ++launc
 bool prep_d128_applies(const PrefillParams &, int) { return false; }
 hipError_t launch_prefill_prep_d128(const PrefillParams &, hipStream_t) { ++launches; return hipErrorInvalidValue; }
 hipError_t launch_state_pass(const PrefillParams &, int, hipStream_t) { ++launches; return hipErrorInvalidValue; }
+bool prefill_concurrent_applies(const PrefillParams &, int) { return false; }
+hipError_t launch_sync_clear(const PrefillParams &, hipStream_t) { ++launches; return hipErrorInvalidValue; }
+hipError_t launch_state_pass_concurrent(const PrefillParams &, hipStream_t) { ++launches; return hipErrorInvalidValue; }
 hipError_t launch_decode(const DecodeParams &, int, hipStream_t) { ++launches; return hipErrorInvalidValue; }
 hipError_t launch_backward(const BwdParams &, int, hipStream_t) { ++launches; return hipErrorInvalidValue; }
 bool backward_fits(int, int, int) { return true; }
