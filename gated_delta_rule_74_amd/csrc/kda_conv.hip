@@ -64,7 +64,7 @@ __global__ __launch_bounds__(CONV_THREADS) void kda_conv_fwd(ConvParams p) {
                  acc[3] * acc[3];
       for (int off = NQ / 2; off >= 1; off >>= 1)
         ss += __shfl_xor(ss, off, 64);
-      acc *= 1.f / sqrtf(ss + p.eps);
+      acc *= l2_inv_norm(ss + p.eps);
     }
     if (t < T) {
       IO *dst = y + ((size_t)b * T + t) * row + (size_t)h * D + 4 * q4;

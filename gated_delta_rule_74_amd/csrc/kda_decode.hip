@@ -233,8 +233,8 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode(DecodeParams p) {
       }
       float rq = 1.f, rk = 1.f;
       if (l2) {
-        rq = 1.f / sqrtf(q2 + p.eps);
-        rk = 1.f / sqrtf(k2 + p.eps);
+        rq = l2_inv_norm(q2 + p.eps);
+        rk = l2_inv_norm(k2 + p.eps);
       }
       const f32x4 vv = *(const f32x4 *)&s_v[pb][4 * q4];
       const float bt = dec_val(cur.b, p.gate_bf16);

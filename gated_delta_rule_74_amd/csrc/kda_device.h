@@ -77,6 +77,13 @@ __device__ __forceinline__ void st_ws(void *q, T v) {
   }
 }
 
+// 1 / sqrt(x) for the per-head L2 norm, x >= eps > 0: the hardware
+// reciprocal square root (within 1 ulp; the correctly rounded sqrt and
+// division it replaces cost about 25 instructions)
+__device__ __forceinline__ float l2_inv_norm(float x) {
+  return __builtin_amdgcn_rsqf(x);
+}
+
 // sum over aligned groups of G lanes (G a power of two, at most 32), every
 // lane of a group getting the total: DPP moves within a 16-lane row (quad
 // swaps, then rotations by 4 and 8 or the half-row mirror), one shuffle

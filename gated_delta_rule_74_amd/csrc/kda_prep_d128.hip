@@ -284,7 +284,13 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
       }
       if constexpr (CONV) {
         // causal conv over the staged rows (row i + u holds token
-        // t0 + r0 + i + u - 3; rows before the sequence contribute 0)
+        // t0 + r0 + i + u - 3; rows before the sequence start or past its
+        // end, loaded clamped, count as zero: cleared once per row here)
+#pragma unroll
+        for (int j = 0; j < Stage<GT, CONV>::XR; ++j) {
+          const int t = t0 + r0 + j - XO;
+          if (!(t >= 0 && t < T)) st.q[j] = st.k[j] = st.v[j] = 0u;
+        }
         f32x4 tq[2], tk[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -296,15 +302,13 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
           qq[i][0] = qq[i][1] = kk[i][0] = kk[i][1] = 0.f;
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const int t = t0 + r0 + i + u - XO;
-            const bool okt = t >= 0 && t < T;
             float x0, x1, y0, y1;
             get2(st.q[i + u], x0, x1);
             get2(st.k[i + u], y0, y1);
-            qq[i][0] += okt ? tq[0][u] * x0 : 0.f;
-            qq[i][1] += okt ? tq[1][u] * x1 : 0.f;
-            kk[i][0] += okt ? tk[0][u] * y0 : 0.f;
-            kk[i][1] += okt ? tk[1][u] * y1 : 0.f;
+            qq[i][0] += tq[0][u] * x0;
+            qq[i][1] += tq[1][u] * x1;
+            kk[i][0] += tk[0][u] * y0;
+            kk[i][1] += tk[1][u] * y1;
           }
         }
         // L2 over the head's 128 channels per token: 64 of them in this
@@ -325,8 +329,8 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float2 o = *(const float2 *)(l2p + (((wave ^ 1) * 16 + 8 * hh + i) * 2));
-          const float iq = p.l2 ? 1.f / sqrtf(sq[i] + o.x + p.eps) : 1.f;
-          const float ik = p.l2 ? 1.f / sqrtf(sk[i] + o.y + p.eps) : 1.f;
+          const float iq = p.l2 ? l2_inv_norm(sq[i] + o.x + p.eps) : 1.f;
+          const float ik = p.l2 ? l2_inv_norm(sk[i] + o.y + p.eps) : 1.f;
           qq[i][0] *= iq;
           qq[i][1] *= iq;
           kk[i][0] *= ik;
@@ -402,12 +406,10 @@ __global__ __launch_bounds__(NT, 1) void kda_chunk_prep_d128(PrefillParams p) {
             float a0 = 0.f, a1 = 0.f;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-              const int t = t0 + r0 + i + u - XO;
-              const bool okt = t >= 0 && t < T;
               float v0, v1;
               get2(st.v[i + u], v0, v1);
-              a0 += okt ? tv0[u] * v0 : 0.f;
-              a1 += okt ? tv1[u] * v1 : 0.f;
+              a0 += tv0[u] * v0;
+              a1 += tv1[u] * v1;
             }
             bv0[i] = bt[i] * a0;
             bv1[i] = bt[i] * a1;

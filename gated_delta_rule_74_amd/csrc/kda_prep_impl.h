@@ -420,8 +420,8 @@ __global__ __launch_bounds__(PREP_THREADS, 1) void kda_chunk_prep(
             // per-token sum over the head: the NQ lanes sharing this token
             sq = group_sum<NQ>(sq);
             sk = group_sum<NQ>(sk);
-            const float iq = 1.f / sqrtf(sq + p.eps);
-            const float ik = 1.f / sqrtf(sk + p.eps);
+            const float iq = l2_inv_norm(sq + p.eps);
+            const float ik = l2_inv_norm(sk + p.eps);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               qq[i][j] *= iq;
