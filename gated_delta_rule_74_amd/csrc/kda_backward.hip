@@ -186,8 +186,14 @@ template <typename IO, int DK, int C> struct BL {  // reverse-pass LDS layout
   static constexpr size_t total = oGm + DK * 4;
 };
 
+// the reverse pass's workgroup: the four working waves and one L2 warm-up
+// wave
+constexpr int BWD_STATE_THREADS = BWD_THREADS + 64;
+constexpr int BWD_STATE_PF = 4;  // chunks between warming and use
+
 template <typename IO, int DK, int C>
-__global__ __launch_bounds__(BWD_THREADS) void kda_bwd_state(BwdParams bp) {
+__global__ __launch_bounds__(BWD_STATE_THREADS) void kda_bwd_state(
+    BwdParams bp) {
   using M = Mma<IO>;
   using L = BL<IO, DK, C>;
   typedef typename M::frag frag;
@@ -207,11 +213,61 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_state(BwdParams bp) {
   const int m16 = lane & 15, g4 = lane >> 4;
   const int Dv = p.Dv, H = p.H, T = p.T, NC = p.NC;
   const int nvt = Dv / 16;
-  const int bh = blockIdx.x / nvt, vt = blockIdx.x % nvt;
+  int bh, vt;
+  {
+    // a head's slab workgroups on one XCD (blocks go round-robin over the
+    // 8 XCDs), so they read the head's factors through one L2
+    const int blk = blockIdx.x, BH = p.B * H;
+    if (nvt > 1 && (BH & 7) == 0) {
+      const int x = blk & 7, jj = blk >> 3;
+      bh = (jj / nvt) * 8 + x;
+      vt = jj % nvt;
+    } else {
+      bh = blk / nvt;
+      vt = blk % nvt;
+    }
+  }
   const int b = bh / H, h = bh % H;
   const WsLayout W = ws_layout(DK, Dv, C, (int)sizeof(IO));
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   const size_t orow = (size_t)H * Dv;  // elements between tokens
+
+  if (wave == BWD_THREADS / 64) {
+    // L2 warm-up wave: while chunk n is worked on, touches 4 bytes of every
+    // 128-byte line of chunk n - PF's factor block (the head's nvt
+    // workgroups split the lines) and of the chunk's dO rows of this slab,
+    // as direct-to-LDS loads into a sink that nothing reads.  It takes part
+    // in every barrier of the other waves (one before the loop, three per
+    // chunk) without waiting for its loads.
+    __shared__ __attribute__((aligned(256))) char sink[256];
+    const int nline = (int)((p.wsb + 127) / 128);
+    const int share = (nline + nvt - 1) / nvt;
+    const char *ws0 = p.ws + (size_t)bh * NC * p.wsb;
+    auto warm = [&](int n) {
+      const char *blk = ws0 + (size_t)n * p.wsb;
+      for (int k0 = 0; k0 < share; k0 += 64) {
+        const int ln = min(vt * share + min(k0 + lane, share - 1), nline - 1);
+        __builtin_amdgcn_global_load_lds(
+            (const void *)(blk + (size_t)ln * 128),
+            (__attribute__((address_space(3))) void *)sink, 4, 0, 0);
+      }
+      const int t = min(n * C + min(lane, C - 1), T - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const void *)((const IO *)bp.dO + ((size_t)b * T + t) * orow +
+                         (size_t)h * Dv + 16 * vt),
+          (__attribute__((address_space(3))) void *)sink, 4, 0, 0);
+    };
+    for (int n = NC - 1; n >= 0 && n >= NC - BWD_STATE_PF; --n) warm(n);
+    barrier_keep_vmem();
+    for (int n = NC - 1; n >= 0; --n) {
+      if (n - BWD_STATE_PF >= 0) warm(n - BWD_STATE_PF);
+      barrier_keep_vmem();
+      barrier_keep_vmem();
+      barrier_keep_vmem();
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    return;
+  }
 
   // dS key tiles owned by this wave: t = wave + 4 j (accumulator layout:
   // lane 16 g + n holds column n, rows 4g..4g+3 of the tile)
@@ -1580,7 +1636,7 @@ static hipError_t bwd_one(const BwdParams &bp, hipStream_t s) {
     const PrefillParams &p = bp.f;
     const unsigned heads = (unsigned)(p.B * p.H);
     hipLaunchKernelGGL((kda_bwd_state<IO, DK, C>), dim3(heads * (p.Dv / 16)),
-                       dim3(BWD_THREADS), 0, s, bp);
+                       dim3(BWD_STATE_THREADS), 0, s, bp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((kda_bwd_chunk_state<IO, DK, C>), dim3(heads * p.NC),

@@ -77,6 +77,13 @@ __device__ __forceinline__ void st_ws(void *q, T v) {
   }
 }
 
+// workgroup barrier after this wave's LDS accesses are done, leaving its
+// global loads in flight (unlike __syncthreads, whose fence also waits for
+// them)
+__device__ __forceinline__ void barrier_keep_vmem() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // 1 / sqrt(x) for the per-head L2 norm, x >= eps > 0: the hardware
 // reciprocal square root (within 1 ulp; the correctly rounded sqrt and
 // division it replaces cost about 25 instructions)
