@@ -148,7 +148,9 @@ def main():
                          "headline prefill with one gate per token-head; "
                          "bwd = the gradient of the headline prefill; "
                          "copy = a plain 1 GiB device copy, the reference "
-                         "for scaling HBM byte counters)")
+                         "for scaling HBM byte counters, and a 512 MiB "
+                         "in-place scale, the practical streaming ceiling "
+                         "for the decode step; every part runs by default)")
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="time fewer decode steps than the workload's 1000 "
                          "(profiling runs)")
@@ -158,7 +160,7 @@ def main():
                            "gdn", "bwd", "copy"}
     if bad:
         ap.error(f"unknown --only part(s): {sorted(bad)}")
-    sel = lambda part: (only is None and part != "copy") or \
+    sel = lambda part: only is None or \
         (only is not None and part in only)
     if args.gpus != 1:
         print(f"bench.py: the KDA library runs on one GPU (asked for "
@@ -634,7 +636,8 @@ def main():
         torch.cuda.empty_cache()
 
     # ---------------- copy reference for the byte counters -----------------
-    if only is not None and "copy" in only:
+    # (and the practical streaming ceiling the decode step is compared with)
+    if sel("copy"):
         n = 1 << 30
         a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
         b2 = torch.empty_like(a)
@@ -669,6 +672,12 @@ def main():
         log(f"in-place scale of 512 MiB fp32: {ms2:.3f} ms, "
             f"{2 * sref.numel() * 4 / (ms2 * 1e-3) / 1e9:.0f} GB/s read+write")
         del sref
+        dec = out.get("decode")
+        if dec is not None:
+            # the decode step's state traffic against the same read-modify-
+            # write pattern with next to no arithmetic
+            dec["vs_inplace_scale"] = dec["state_gbs"] / (
+                2 * (1 << 27) * 4 / (ms2 * 1e-3) / 1e9)
 
     pf = out.get("prefill")
     line = {
