@@ -503,6 +503,20 @@ def main():
                                 tokens_per_s=Bc * Tc / (ms * 1e-3),
                                 algo_gbs=gbs, hbm_frac=gbs / HBM_PEAK_GBS)
         kinfo = ""
+        if conv:
+            # the conv + L2 prologue on its own (the unfused prologue):
+            # the raw projections read once, q, k, v written once
+            qc, kc, vc = (torch.empty_like(o) for _ in range(3))
+            tcv = t_back_to_back(lambda: kda.kda_conv_prologue(
+                x["xq"], x["xk"], x["xv"], x["wq"], x["wk"], x["wv"], H=Hc,
+                Dk=Dc, Dv=Dc, q=qc, k=kc, v=vc), reps)
+            cb = 6 * Bc * Tc * Hc * Dc * 2 + 3 * Hc * Dc * c["conv_width"] * 4
+            extra[name]["conv_prologue_alone"] = dict(
+                ms=tcv, algo_bytes=cb, algo_gbs=cb / (tcv * 1e-3) / 1e9,
+                hbm_frac=cb / (tcv * 1e-3) / 1e9 / HBM_PEAK_GBS)
+            kinfo = (f" (the conv prologue alone {tcv*1e3:.1f} us, "
+                     f"{cb / (tcv * 1e-3) / 1e9:.0f} GB/s)")
+            del qc, kc, vc
         if not conv:
             # the two kernels alone, back to back
             tp = t_back_to_back(lambda: kda.kda_prefill_chunk_prep(

@@ -113,33 +113,40 @@ def test_decode_tokens(orc, kda, qkv, gate, Dk, Dv, L):
     assert s2 is st2 and torch.equal(o2, o) and torch.equal(st2, s_out)
 
 
-@pytest.mark.parametrize("dt,D,W,T,hist", [
-    ("bf16", 128, 4, 300, False), ("bf16", 128, 4, 300, True),
-    ("f32", 16, 2, 70, True), ("f32", 64, 3, 1, True), ("bf16", 32, 4, 65, False)])
-def test_conv_prologue(orc, kda, dt, D, W, T, hist):
-    say(f"conv prologue dt={dt} D={D} W={W} T={T} hist={hist}")
+@pytest.mark.parametrize("dt,Dk,Dv,W,T,hist", [
+    ("bf16", 128, 128, 4, 300, False), ("bf16", 128, 128, 4, 300, True),
+    ("f32", 16, 16, 2, 70, True), ("f32", 64, 64, 3, 1, True),
+    ("bf16", 32, 32, 4, 65, False),
+    # d_k != d_v: the streams' lane groups differ in size and run length
+    ("bf16", 128, 64, 4, 700, True), ("f32", 32, 128, 3, 200, False),
+    ("bf16", 16, 128, 2, 1100, True)])
+def test_conv_prologue(orc, kda, dt, Dk, Dv, W, T, hist):
+    say(f"conv prologue dt={dt} Dk={Dk} Dv={Dv} W={W} T={T} hist={hist}")
     B, H = 2, 3
-    x = ki.prefill_inputs(B, T, H, D, D, qkv=dt, conv_width=W, seed=21,
+    Dm = max(Dk, Dv)
+    x = ki.prefill_inputs(B, T, H, Dk, Dv, qkv=dt, conv_width=W, seed=21,
                           device="cuda")
     state = None
     old = None
     if hist:
-        state = torch.randn((B, 3, H * D, W - 1), device="cuda")
+        state = torch.randn((B, 3, H * Dm, W - 1), device="cuda")
         old = to_cpu64(state)
     q, k, v = kda.kda_conv_prologue(x["xq"], x["xk"], x["xv"], x["wq"],
-                                    x["wk"], x["wv"], H=H, Dk=D, Dv=D,
+                                    x["wk"], x["wv"], H=H, Dk=Dk, Dv=Dv,
                                     conv_state=state, eps=1e-6)
     torch.cuda.synchronize()
-    hist_in = None if old is None else (old[:, 0], old[:, 1], old[:, 2])
+    Ds = (Dk, Dk, Dv)
+    hist_in = None if old is None else tuple(
+        old[:, i, :H * Ds[i]] for i in range(3))
     rq, rk, rv, rh = orc.conv_prologue(x["xq"], x["xk"], x["xv"], x["wq"],
-                                       x["wk"], x["wv"], H, D, D, 1e-6, True,
+                                       x["wk"], x["wv"], H, Dk, Dv, 1e-6, True,
                                        hist_in)
     for name, a, r in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
         e = rel_err(a, r)
         assert e <= TOL[dt], (name, e)
     if hist:
         for i in range(3):
-            assert rel_err(state[:, i], rh[i]) <= 1e-6
+            assert rel_err(state[:, i, :H * Ds[i]], rh[i]) <= 1e-6
 
 
 def test_fused_prologue_matches_standalone(kda):
