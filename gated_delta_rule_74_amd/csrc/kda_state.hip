@@ -82,15 +82,29 @@ template <typename IO, int DK, int C, int NS> struct SP {
 };
 
 // a state wave's factors of one chunk: its rows of -W and U, and of Ktil^T
-// with gamma_C for its key units
+// with gamma_C for its key units.  gamma_C comes as one value per lane (lane
+// l: entry 16 ((l >> 4) % TPU) + (l & 15) of the unit's 16 TPU entries) and
+// is spread to the lanes' state rows by gamma_rows: a wave moves 256 bytes
+// for it instead of 16 bytes per lane and key tile
 template <typename IO, int DK, int C, int NS> struct SFrag {
   using G = SP<IO, DK, C, NS>;
   typedef typename Mma<IO>::frag frag;
   frag w[G::NKU];
   typename Vec4T<IO>::raw u[NS];
   frag k[G::KUW][G::TPU][G::NTU];
-  f32x4 gm[G::KUW][G::TPU];
+  float gr[G::KUW];
 };
+
+// gamma_C of the 4 state rows a lane holds in key tile TPU u + hh (rows
+// 16 (TPU u + hh) + 4 g4 + e), read from the lanes that loaded them
+__device__ __forceinline__ f32x4 gamma_rows(float gr, int hh, int g4) {
+  f32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    r[e] = __int_as_float(__builtin_amdgcn_ds_bpermute(
+        4 * (16 * hh + 4 * g4 + e), __float_as_int(gr)));
+  return r;
+}
 // an output wave's factors of one chunk: its rows of Qtil and P
 template <typename IO, int DK, int C, int NS> struct OFrag {
   using G = SP<IO, DK, C, NS>;
@@ -117,9 +131,13 @@ __device__ __forceinline__ void load_state(SFrag<IO, DK, C, NS> &f,
     for (int s = 0; s < NS; ++s) f.u[s] = Lu[((vt0 + s) * G::NB + rtc) * 64];
   } else {
     const frag *Lk = (const frag *)(blk + W.off_ktt) + lane;
-    const float *Lg = (const float *)(blk + W.off_gam) + 4 * g4;
+    const float *Lg = (const float *)(blk + W.off_gam) + (lane & 15);
 #pragma unroll
-    for (int j = 0; j < G::KUW; ++j)
+    for (int j = 0; j < G::KUW; ++j) {
+      // gamma_C first: it is needed one phase before the Ktil^T units
+      const int tg = min(G::TPU * (w4 + SW * j) + (lane >> 4) % G::TPU,
+                         G::NKT - 1);
+      f.gr[j] = Lg[16 * tg];
 #pragma unroll
       for (int h = 0; h < G::TPU; ++h) {
         // key tile of (unit w4 + SW j, half h), clamped to a valid one
@@ -127,8 +145,8 @@ __device__ __forceinline__ void load_state(SFrag<IO, DK, C, NS> &f,
 #pragma unroll
         for (int u = 0; u < G::NTU; ++u)
           f.k[j][h][u] = Lk[(t * G::NTU + u) * 64];
-        f.gm[j][h] = *(const f32x4 *)(Lg + 16 * t);
       }
+    }
   }
 }
 
@@ -279,6 +297,11 @@ __global__ __launch_bounds__(STATE_THREADS, 1) void kda_state_pass(
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int u = 0; u < NKU; ++u) sb[s][u] = SU[(s * NKU + u) * 64 + lane];
+      f32x4 gm[KUW][TPU];
+#pragma unroll
+      for (int j = 0; j < KUW; ++j)
+#pragma unroll
+        for (int hh = 0; hh < TPU; ++hh) gm[j][hh] = gamma_rows(f.gr[j], hh, g4);
       // Delta rows of token tile rtc: U - W S  (-W is stored)
       f32x4 d[NS];
 #pragma unroll
@@ -316,14 +339,14 @@ __global__ __launch_bounds__(STATE_THREADS, 1) void kda_state_pass(
         for (int hh = 0; hh < TPU; ++hh)
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
-            f32x4 sn = S[j][hh][s] * f.gm[j][hh];
+            f32x4 sn = S[j][hh][s] * gm[j][hh];
 #pragma unroll
             for (int u = 0; u < NTU; ++u)
               sn = M::mma(f.k[j][hh][u], db[s][u], sn);
             S[j][hh][s] = sn;
           }
       publish_s();
-      interleave_loads<NS * NTU, KUW * TPU * NS * NTU, KUW * TPU * (NTU + 1)>();
+      interleave_loads<NS * NTU, KUW * TPU * NS * NTU, KUW * (TPU * NTU + 1)>();
       lds_barrier();  // S complete in SU
     };
 
