@@ -19,6 +19,9 @@ namespace kda {
 
 constexpr int BWD_THREADS = 256;
 constexpr int DVMAX_BWD = 128;
+// the widest contraction of the tile products below (d_k, d_v <= 128,
+// chunk <= 64): they issue the reads of that many k for every tile
+constexpr int TILE_KMAX = 128;
 
 // 8 consecutive elements of a row as one 16-byte (bf16) or two 16-byte
 // (fp32) accesses: raw copies between global memory and LDS, and
@@ -450,44 +453,53 @@ __device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const TA *A, int lda,
                                           const TB *B, int ldb, int m0, int n0,
                                           int K, int lane) {
   using M = Mma<IO>;
+  typedef typename M::frag frag;
   constexpr int KU = 16 * M::TPU;
+  constexpr int NU = TILE_KMAX / KU;
   const int m = lane & 15, g = lane >> 4;
-  for (int u = 0; u * KU < K; ++u) {
-    typename M::frag fa, fb;
+  const int ulast = (K - 1) / KU;
+  // every unit's operands first, then the products: the reads overlap
+  // instead of each product waiting for its own
+  frag fa[NU], fb[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int uu = min(u, ulast);  // units past K re-read the last one
     if constexpr (!AT && sizeof(TA) == 4) {
       // fp32 rows of A: a lane's k values come in runs of 4 (k = 4g + e and,
       // for 32-wide units, 16 + 4g + e), one 16-byte read each; K is a
       // multiple of 16, so a run is wholly inside or outside it
 #pragma unroll
       for (int h = 0; h < M::NE / 4; ++h) {
-        const int k = KU * u + 16 * h + 4 * g;
+        const int k = KU * uu + 16 * h + 4 * g;
         const f32x4 a4 = k < K ? *(const f32x4 *)(A + (m0 + m) * lda + k)
                                : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) M::set(fa, 4 * h + e, a4[e]);
+        for (int e = 0; e < 4; ++e) M::set(fa[u], 4 * h + e, a4[e]);
       }
 #pragma unroll
       for (int e = 0; e < M::NE; ++e) {
-        const int k = KU * u + M::koff(g, e);
-        M::set(fb, e,
+        const int k = KU * uu + M::koff(g, e);
+        M::set(fb[u], e,
                k < K ? to_f32(BT ? B[(n0 + m) * ldb + k] : B[k * ldb + n0 + m])
                      : 0.f);
       }
     } else {
 #pragma unroll
       for (int e = 0; e < M::NE; ++e) {
-        const int k = KU * u + M::koff(g, e);
+        const int k = KU * uu + M::koff(g, e);
         float av = 0.f, bv = 0.f;
         if (k < K) {
           av = to_f32(AT ? A[k * lda + m0 + m] : A[(m0 + m) * lda + k]);
           bv = to_f32(BT ? B[(n0 + m) * ldb + k] : B[k * ldb + n0 + m]);
         }
-        M::set(fa, e, av);
-        M::set(fb, e, bv);
+        M::set(fa[u], e, av);
+        M::set(fb[u], e, bv);
       }
     }
-    acc = M::mma(fa, fb, acc);
   }
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+    if (u <= ulast) acc = M::mma(fa[u], fb[u], acc);
   return acc;
 }
 
@@ -498,13 +510,22 @@ __device__ __forceinline__ f32x4 tile_mma_rows(f32x4 acc, const IO *A, int lda,
                                                const IO *B, int ldb, int m0,
                                                int n0, int K, int lane) {
   using M = Mma<IO>;
+  typedef typename M::frag frag;
   constexpr int KU = 16 * M::TPU;
+  constexpr int NU = TILE_KMAX / KU;
   const int m = lane & 15, g = lane >> 4;
-  for (int u = 0; u * KU < K; ++u) {
-    const bool full = KU * u + 16 < K || M::TPU == 1;
-    acc = M::mma(M::load_k(A + (m0 + m) * lda + KU * u, g, full),
-                 M::load_k(B + (n0 + m) * ldb + KU * u, g, full), acc);
+  const int ulast = (K - 1) / KU;
+  frag fa[NU], fb[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int uu = min(u, ulast);
+    const bool full = KU * uu + 16 < K || M::TPU == 1;
+    fa[u] = M::load_k(A + (m0 + m) * lda + KU * uu, g, full);
+    fb[u] = M::load_k(B + (n0 + m) * ldb + KU * uu, g, full);
   }
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+    if (u <= ulast) acc = M::mma(fa[u], fb[u], acc);
   return acc;
 }
 
@@ -517,21 +538,29 @@ __device__ __forceinline__ f32x4 tile_mma_f32a(f32x4 acc, const float *A,
                                                int m0, int n0, int K,
                                                int lane) {
   using M = Mma<IO>;
+  typedef typename M::frag frag;
   constexpr int KU = 16 * M::TPU;
+  constexpr int NU = TILE_KMAX / KU;
   const int m = lane & 15, g = lane >> 4;
-  for (int u = 0; u * KU < K; ++u) {
-    typename M::frag fa;
+  const int ulast = (K - 1) / KU;
+  frag fa[NU], fb[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int uu = min(u, ulast);
 #pragma unroll
     for (int h = 0; h < M::NE / 4; ++h) {
-      const int k = KU * u + 16 * h + 4 * g;
+      const int k = KU * uu + 16 * h + 4 * g;
       const f32x4 a4 = k < K ? *(const f32x4 *)(A + (m0 + m) * lda + k)
                              : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) M::set(fa, 4 * h + e, a4[e]);
+      for (int e = 0; e < 4; ++e) M::set(fa[u], 4 * h + e, a4[e]);
     }
-    const bool full = KU * u + 16 < K || M::TPU == 1;
-    acc = M::mma(fa, M::load_k(Bt + (n0 + m) * ldb + KU * u, g, full), acc);
+    const bool full = KU * uu + 16 < K || M::TPU == 1;
+    fb[u] = M::load_k(Bt + (n0 + m) * ldb + KU * uu, g, full);
   }
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+    if (u <= ulast) acc = M::mma(fa[u], fb[u], acc);
   return acc;
 }
 
@@ -798,10 +827,17 @@ template <typename IO, int DK, int C> struct G2L {
   // as the k-contiguous operand of T^T dDelta and T^T dW
   static constexpr bool TRB = sizeof(IO) == 2;
   static constexpr int LT = C + 8;
-  static constexpr size_t RV = 2 * (size_t)C * DVMAX_BWD * sizeof(IO) +
+  // the C x Dv and C x DK operand arrays of phases 3, 4 and 6 have rows
+  // padded by 16 bytes: unpadded, a row is a whole number of bank rows, so
+  // the 16 rows that a fragment read takes at once would all hit the same
+  // banks
+  static constexpr int PE = 16 / (int)sizeof(IO);
+  static constexpr int LKP = DK + PE;
+  static constexpr size_t RV = 2 * (size_t)C * (DVMAX_BWD + PE) * sizeof(IO) +
                                (TRB ? (size_t)DVMAX_BWD * LT * 2 : 0);
   static constexpr size_t RW =
-      TRB ? 2 * (size_t)C * DK * 2 + (size_t)DK * LT * 2 : 0;
+      TRB ? 2 * (size_t)C * LKP * 2 + (size_t)DK * LT * 2
+          : 2 * (size_t)C * LKP * sizeof(IO);
   static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
   static constexpr size_t RR = mx(mx(RK, RV), mx(RW, CC));
   static constexpr size_t total = oR + RR;
@@ -1010,8 +1046,9 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
 
   // ---- phase 3: value side: dT = dDelta (beta V)^T, dv = beta T^T dDelta --
   {
-    IO *dDs = (IO *)R, *vS = dDs + C * Dv;
-    IO *dDT = vS + C * Dv;  // bf16 only: dDelta^T [Dv][LT]
+    const int LV = Dv + L::PE;  // padded row stride of dDs and vS
+    IO *dDs = (IO *)R, *vS = dDs + C * LV;
+    IO *dDT = vS + C * LV;  // bf16 only: dDelta^T [Dv][LT]
     constexpr int N8 = (C * DVMAX_BWD / 8 + BWD_THREADS - 1) / BWD_THREADS;
     Row8<IO> lv[N8];
 #pragma unroll
@@ -1043,7 +1080,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             d8[e] = t0 + r0 + e < T ? dd[jj][e] : 0.f;
-            dDs[(r0 + e) * Dv + j] = (IO)d8[e];
+            dDs[(r0 + e) * LV + j] = (IO)d8[e];
           }
           put8(dDT + j * L::LT + r0, d8);
         }
@@ -1064,7 +1101,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
 #pragma unroll
           for (int e = 0; e < 8; ++e)
             d8[e] = t0 + x / Dv < T ? ld[jj].get(e) : 0.f;
-          put8(dDs + x, d8);
+          put8(dDs + (x / Dv) * LV + x % Dv, d8);
         }
       }
     }
@@ -1073,14 +1110,14 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
       const int x = 8 * (tid + BWD_THREADS * jj);
       if (x < C * Dv) {
         if (t0 + x / Dv >= T) lv[jj].zero();
-        lv[jj].store(vS + x);
+        lv[jj].store(vS + (x / Dv) * LV + x % Dv);
       }
     }
     __syncthreads();
     tiles(
         NB * NB,
         [&](int tl) {
-          return tile_mma_rows<IO>(zero, dDs, Dv, vS, Dv, 16 * (tl % NB),
+          return tile_mma_rows<IO>(zero, dDs, LV, vS, LV, 16 * (tl % NB),
                                    16 * (tl / NB), Dv, lane);
         },
         [&](int tl, f32x4 acc) {
@@ -1098,7 +1135,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
             return tile_mma_f32a<IO>(zero, TTm, LCC, dDT, L::LT, 16 * rt,
                                      16 * ct, C, lane);
           else
-            return tile_mma<IO, false, false>(zero, TTm, LCC, dDs, Dv, 16 * rt,
+            return tile_mma<IO, false, false>(zero, TTm, LCC, dDs, LV, 16 * rt,
                                               16 * ct, C, lane);
         },
         [&](int tl, f32x4 acc) {
@@ -1110,7 +1147,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
             if (t < T)
               ((IO *)bp.dv)[vb + (size_t)t * vrow + j] =
                   from_f32<IO>(bet[r] * acc[e]);
-            x[e] = to_f32(vS[r * Dv + j]) * acc[e];
+            x[e] = to_f32(vS[r * LV + j]) * acc[e];
           }
           add_rows(dB, 16 * rt + 4 * g4, x, m16);
         });
@@ -1119,8 +1156,9 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
 
   // ---- phase 4: key side: dT += dW (beta Kd)^T, dKd = beta T^T dW ---------
   {
-    IO *dWs = (IO *)R, *KdS = dWs + C * DK;
-    IO *dWT = KdS + C * DK;  // bf16 only: dW^T [DK][LT]
+    constexpr int LKP = L::LKP;  // padded row stride of dWs and KdS
+    IO *dWs = (IO *)R, *KdS = dWs + C * LKP;
+    IO *dWT = KdS + C * LKP;  // bf16 only: dW^T [DK][LT]
     constexpr int N8 = (C * DK / 8 + BWD_THREADS - 1) / BWD_THREADS;
     Row8<float> lk[N8];
 #pragma unroll
@@ -1145,7 +1183,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
         if (q < C * DK / 8) {
           const int i = q % DK, r0 = 8 * (q / DK);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) dWs[(r0 + e) * DK + i] = (IO)dw[jj][e];
+          for (int e = 0; e < 8; ++e) dWs[(r0 + e) * LKP + i] = (IO)dw[jj][e];
           put8(dWT + i * L::LT + r0, dw[jj]);
         }
       }
@@ -1163,7 +1201,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
           float w8[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) w8[e] = lw[j].get(e);
-          put8(dWs + x, w8);
+          put8(dWs + (x / DK) * LKP + x % DK, w8);
         }
       }
     }
@@ -1174,14 +1212,14 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
         float k8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) k8[e] = lk[j].get(e);
-        put8(KdS + x, k8);
+        put8(KdS + (x / DK) * LKP + x % DK, k8);
       }
     }
     __syncthreads();
     tiles(
         NB * NB,
         [&](int tl) {
-          return tile_mma_rows<IO>(zero, dWs, DK, KdS, DK, 16 * (tl % NB),
+          return tile_mma_rows<IO>(zero, dWs, LKP, KdS, LKP, 16 * (tl % NB),
                                    16 * (tl / NB), DK, lane);
         },
         [&](int tl, f32x4 acc) {
@@ -1199,7 +1237,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
             return tile_mma_f32a<IO>(zero, TTm, LCC, dWT, L::LT, 16 * rt,
                                      16 * it, C, lane);
           else
-            return tile_mma<IO, false, false>(zero, TTm, LCC, dWs, DK, 16 * rt,
+            return tile_mma<IO, false, false>(zero, TTm, LCC, dWs, LKP, 16 * rt,
                                               16 * it, C, lane);
         },
         [&](int tl, f32x4 acc) {
@@ -1210,7 +1248,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
           for (int e = 0; e < 4; ++e) {
             const int r = 16 * rt + 4 * g4 + e, i = 16 * it + m16;
             dk4[e] = bet[r] * acc[e];
-            x[e] = to_f32(KdS[r * DK + i]) * acc[e];
+            x[e] = to_f32(KdS[r * LKP + i]) * acc[e];
           }
           *(f32x4 *)(gdKd + bwd_tile_off(rt, it, NKT, lane)) = dk4;
           add_rows(dB, 16 * rt + 4 * g4, x, m16);
@@ -1256,7 +1294,8 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
 
   // ---- phase 6: dPm = scale tril(dO Delta^T) --------------------------------
   {
-    IO *Os = (IO *)R, *Ds = Os + C * Dv;
+    const int LV = Dv + L::PE;  // padded row stride of Os and Ds
+    IO *Os = (IO *)R, *Ds = Os + C * LV;
     constexpr int N8 = (C * DVMAX_BWD / 8 + BWD_THREADS - 1) / BWD_THREADS;
     Row8<IO> lo[N8];
     Row8<IO> ld[N8];
@@ -1272,18 +1311,18 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_bwd_chunk_grad(
       const int x = 8 * (tid + BWD_THREADS * jj);
       if (x < C * Dv) {
         if (t0 + x / Dv >= T) lo[jj].zero();
-        lo[jj].store(Os + x);
+        lo[jj].store(Os + (x / Dv) * LV + x % Dv);
         float d8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) d8[e] = ld[jj].get(e);
-        put8(Ds + x, d8);
+        put8(Ds + (x / Dv) * LV + x % Dv, d8);
       }
     }
     __syncthreads();
     tiles(
         NB * NB,
         [&](int tl) {
-          return tile_mma_rows<IO>(zero, Os, Dv, Ds, Dv, 16 * (tl % NB),
+          return tile_mma_rows<IO>(zero, Os, LV, Ds, LV, 16 * (tl % NB),
                                    16 * (tl / NB), Dv, lane);
         },
         [&](int tl, f32x4 acc) {
