@@ -106,16 +106,22 @@ struct UnitStage {
     using M = Mma<IO>;
 #pragma unroll
     for (int j = 0; j < NU; ++j) {
-      const int w = tid + BWD_THREADS * j;
+      // every slot loads (past the end: the last unit again), so that the
+      // compiler counts the loads exactly; store_t skips or zeroes the
+      // slots that carry nothing
+      // (units above the diagonal of a lower-triangular factor: the
+      // diagonal unit of the row again, an L1 hit)
+      const int w = min(tid + BWD_THREADS * j, nrt * nku * 64 - 1);
       const int unit = w >> 6, a = unit / nku, u = unit % nku;
-      if (w < nrt * nku * 64 && !(lower && u > a / M::TPU))
-        raw[j] = *(const uint4 *)(sec + (size_t)w * 16);
-      else
-        raw[j] = make_uint4(0u, 0u, 0u, 0u);
+      const int ws = (lower && u > a / M::TPU)
+                         ? ((a * nku + a / M::TPU) << 6) + (w & 63)
+                         : w;
+      raw[j] = *(const uint4 *)(sec + (size_t)ws * 16);
     }
   }
   __device__ __forceinline__ void store_t(int nrt, int nku, int kmax, IO *XT,
-                                          int ldt, int tid) const {
+                                          int ldt, int tid,
+                                          bool lower = false) const {
     using M = Mma<IO>;
     typedef typename M::frag frag;
     constexpr int KU = 16 * M::TPU;
@@ -126,7 +132,11 @@ struct UnitStage {
       const int lane = w & 63, unit = w >> 6;
       const int a = unit / nku, u = unit % nku;
       const int m = lane & 15, g = lane >> 4;
-      const frag f = __builtin_bit_cast(frag, raw[j]);
+      // units above the diagonal of a lower-triangular factor hold nothing
+      // the prep wrote: zeros
+      const uint4 rw = (lower && u > a / M::TPU) ? make_uint4(0u, 0u, 0u, 0u)
+                                                 : raw[j];
+      const frag f = __builtin_bit_cast(frag, rw);
 #pragma unroll
       for (int e = 0; e < M::NE; ++e) {
         const int k = KU * u + M::koff(g, e);
@@ -321,12 +331,9 @@ __global__ __launch_bounds__(BWD_STATE_THREADS) void kda_bwd_state(
   Row8<IO> ov;  // lanes 2r, 2r + 1: token r, value columns 8 (tid & 1) + 0..7
   bool ovz = false;  // the token lies past the sequence: ov counts as zero
   float gv = 0.f;
-  auto fetch = [&](int n) {
-    const char *blk = p.ws + ((size_t)bh * NC + n) * p.wsb;
-    stP.fetch(blk + W.off_p, NB, NTU, true, tid);
-    stK.fetch(blk + W.off_ktt, NKT, NTU, false, tid);
-    stQ.fetch(blk + W.off_qt, NB, NKU, false, tid);
-    stW.fetch(blk + W.off_negw, NB, NKU, false, tid);
+  auto blk_of = [&](int n) { return p.ws + ((size_t)bh * NC + n) * p.wsb; };
+  auto fetch_ov = [&](int n) {
+    const char *blk = blk_of(n);
     if (tid < 2 * C) {
       const int r = tid >> 1, t = min(n * C + r, T - 1);
       ov.load((const IO *)bp.dO + ((size_t)b * T + t) * orow + (size_t)h * Dv +
@@ -337,15 +344,30 @@ __global__ __launch_bounds__(BWD_STATE_THREADS) void kda_bwd_state(
     }
     if (tid < DK) gv = ((const float *)(blk + W.off_gam))[tid];
   };
-  fetch(NC - 1);
+  {
+    const char *blk = blk_of(NC - 1);
+    stP.fetch(blk + W.off_p, NB, NTU, true, tid);
+    stK.fetch(blk + W.off_ktt, NKT, NTU, false, tid);
+    stQ.fetch(blk + W.off_qt, NB, NKU, false, tid);
+    stW.fetch(blk + W.off_negw, NB, NKU, false, tid);
+    fetch_ov(NC - 1);
+  }
 
   for (int n = NC - 1; n >= 0; --n) {
     const int t0 = n * C;
-    // ---- stage the chunk's factors, transposed where the products need it
-    stP.store_t(NB, NTU, C, PT, LDC, tid);
+    // ---- stage the chunk's factors, transposed where the products need it;
+    // each part's registers take the next chunk's loads as soon as they are
+    // staged (chunk 0 loads itself again), so the waves' waits at issue for
+    // the texture units overlap the LDS writes of the other parts
+    const char *nblk = blk_of(max(n - 1, 0));
+    stP.store_t(NB, NTU, C, PT, LDC, tid, true);
+    stP.fetch(nblk + W.off_p, NB, NTU, true, tid);
     stK.store_t(NKT, NTU, C, KK, LDK, tid);
+    stK.fetch(nblk + W.off_ktt, NKT, NTU, false, tid);
     stQ.store_t(NB, NKU, DK, QT, LDC, tid);
+    stQ.fetch(nblk + W.off_qt, NB, NKU, false, tid);
     stW.store_t(NB, NKU, DK, WT, LDC, tid);
+    stW.fetch(nblk + W.off_negw, NB, NKU, false, tid);
     if (tid < 2 * C) {
       // dO slab transposed: OT[value column][token]
       const int r = tid >> 1, c0 = 8 * (tid & 1);
@@ -354,6 +376,7 @@ __global__ __launch_bounds__(BWD_STATE_THREADS) void kda_bwd_state(
         OT[(c0 + e) * LDC + r] = from_f32<IO>(ovz ? 0.f : ov.get(e));
     }
     if (tid < DK) Gm[tid] = gv;
+    fetch_ov(max(n - 1, 0));
     __syncthreads();
 
     // ---- the gradient at this chunk's end, for the per-chunk kernels
@@ -367,10 +390,6 @@ __global__ __launch_bounds__(BWD_STATE_THREADS) void kda_bwd_state(
         for (int e = 0; e < 4; ++e) dst[(size_t)e * Dv] = dS[j][e];
       }
     }
-
-    // the next chunk's loads after this chunk's stores: issued first, the
-    // stores would wait behind 56 KiB of loads in the vector-memory queue
-    if (n > 0) fetch(n - 1);
 
     // ---- dDelta = P^T dO + Ktil dS'   (token tile rt = wave)
     if (wave < NB) {
