@@ -15,6 +15,8 @@
 #include "kda_device.h"
 #include "kda_internal.h"
 
+#include <type_traits>
+
 namespace kda {
 
 constexpr int BWD_THREADS = 256;
@@ -653,28 +655,20 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void kda_bwd_chunk_state(
   const size_t orow = (size_t)H * Dv;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-  units_to_lds<IO>(blk + W.off_negw, NB, NKU, DK, nW, LK, tid);  // -W[r][i]
-  for (int i = tid; i < DK; i += BWD_THREADS) dgs[i] = 0.f;
-  __syncthreads();
-
-  f32x4 aQ[TW], aK[TW], aW[TW];
-#pragma unroll
-  for (int j = 0; j < TW; ++j) aQ[j] = aK[j] = aW[j] = zero;
-  // dgam = rowsum(dS' * S): this thread's 8 columns of key row
-  // 8 (tid + 256 j) / SV, summed over the value slabs here and over the SV / 8
-  // lanes of a row at the end
   constexpr int NGA = (DK * SV / 8 + BWD_THREADS - 1) / BWD_THREADS;
-  float dga[NGA];
-#pragma unroll
-  for (int j = 0; j < NGA; ++j) dga[j] = 0.f;
-
-  for (int c0 = 0; c0 < Dv; c0 += SV) {
+  // a slab's global loads (clamped addresses, branch-free): rows of S and
+  // dS', 8 columns of a row per lane (sv is a multiple of 16), rows of dO
+  // and dDelta, and this wave's U tiles (accumulator layout, 4 elements per
+  // lane).  The next slab's are issued as soon as this slab's have gone to
+  // LDS, so they arrive while this slab's products run.
+  constexpr int NO8 = (C * SV / 8 + BWD_THREADS - 1) / BWD_THREADS;
+  constexpr int NUT = (NB * (SV / 16) + 3) / 4;
+  typedef std::conditional_t<sizeof(IO) == 2, uint2, uint4> U4;
+  Row8<float> la[NGA], lb[NGA];
+  Row8<IO> lo[NO8], ld[NO8];
+  U4 ur[NUT];
+  auto issue = [&](int c0) {
     const int sv = min(SV, Dv - c0);
-    // all loads first (clamped addresses, branch-free), then the LDS
-    // stores; 8 columns of a row per lane (sv is a multiple of 16)
-    constexpr int NO8 = (C * SV / 8 + BWD_THREADS - 1) / BWD_THREADS;
-    Row8<float> la[NGA], lb[NGA];
-    Row8<IO> lo[NO8], ld[NO8];
 #pragma unroll
     for (int j = 0; j < NGA; ++j) {
       const int i = min(8 * (tid + BWD_THREADS * j), DK * SV - 8);
@@ -690,6 +684,32 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void kda_bwd_chunk_state(
       lo[j].load((const IO *)bp.dO + gi);
       ld[j].load((const IO *)bp.dD + gi);
     }
+#pragma unroll
+    for (int j = 0; j < NUT; ++j) {
+      const int tl = min(wave + 4 * j, NB * (SV / 16) - 1);
+      const int rt = tl % NB, vt = min((c0 >> 4) + tl / NB, Dv / 16 - 1);
+      ur[j] = *((const U4 *)(blk + W.off_u) + (size_t)(vt * NB + rt) * 64 + lane);
+    }
+  };
+
+  units_to_lds<IO>(blk + W.off_negw, NB, NKU, DK, nW, LK, tid);  // -W[r][i]
+  for (int i = tid; i < DK; i += BWD_THREADS) dgs[i] = 0.f;
+  __syncthreads();
+  // (issued before the -W staging instead, the first slab's loads slow it)
+  issue(0);
+
+  f32x4 aQ[TW], aK[TW], aW[TW];
+#pragma unroll
+  for (int j = 0; j < TW; ++j) aQ[j] = aK[j] = aW[j] = zero;
+  // dgam = rowsum(dS' * S): this thread's 8 columns of key row
+  // 8 (tid + 256 j) / SV, summed over the value slabs here and over the SV / 8
+  // lanes of a row at the end
+  float dga[NGA];
+#pragma unroll
+  for (int j = 0; j < NGA; ++j) dga[j] = 0.f;
+
+  for (int c0 = 0; c0 < Dv; c0 += SV) {
+    const int sv = min(SV, Dv - c0);
 #pragma unroll
     for (int j = 0; j < NGA; ++j) {
       const int i = 8 * (tid + BWD_THREADS * j), r = i / SV, c = i % SV;
@@ -722,15 +742,20 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void kda_bwd_chunk_state(
         put8(dDs + r * LS + c, d8);
       }
     }
+    U4 uc[NUT];
+#pragma unroll
+    for (int j = 0; j < NUT; ++j) uc[j] = ur[j];
+    if (c0 + SV < Dv) issue(c0 + SV);
     __syncthreads();
     // Delta = U - W S on this slab (U in accumulator tiles [vt][rt])
-    for (int tl = wave; tl < NB * (SV / 16); tl += 4) {
+#pragma unroll
+    for (int j = 0; j < NUT; ++j) {
+      const int tl = wave + 4 * j;
+      if (tl >= NB * (SV / 16)) break;
       const int rt = tl % NB, ct = tl / NB;
-      const int vt = (c0 >> 4) + ct;
       f32x4 acc = zero;
       if (16 * ct < sv) {
-        const IO *us = (const IO *)(blk + W.off_u) +
-                       ((size_t)(vt * NB + rt) * 64 + lane) * 4;
+        const IO *us = (const IO *)&uc[j];
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] = to_f32(us[e]);
         acc = tile_mma_rows<IO>(acc, nW, LK, STs, LK, 16 * rt, 16 * ct, DK,
